@@ -1,0 +1,217 @@
+"""Oracle: the owner-local Muon step and the RMNP comparator, in float64 numpy.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): the product path never
+imports this module.
+
+What is computed, and where the pages define it
+------------------------------------------------
+Blog post "Optimizers In A Sharded World: Muon's O(mn) Vs RMNP's Zero":
+
+* Section 1: momentum is heavy ball, ``V_t = mu * V_{t-1} + G_t``; Muon's target
+  direction is the orthogonalized ``(V V^T)^{-1/2} V``, approximated by a
+  Newton-Schulz iteration ("five iterations with three matrix multiplications
+  per iteration"); RMNP's direction divides each row of ``V_t`` by its L2 norm.
+* Appendix "The Code That Ran": the Newton-Schulz routine (coefficients
+  (3.4445, -4.7750, 2.0315), 5 steps, ``eps = 1e-7`` added to the Frobenius
+  norm, transpose when rows > cols and back at the end); the ``muon_sc`` step
+  (momentum in place, Newton-Schulz on the updated momentum, update scaled by
+  ``sqrt(max(1, rows/cols))``); the ``rmnp_local`` step (momentum in place,
+  fp32 row normalisation with the library default ``max(||v||, 1e-12)``
+  clamp, the same update scale).
+
+MatrixFSDP (arXiv 2607.05895), section 3 and section 4.4: each owner applies
+this update to the whole 2D matrices it owns, independently per matrix; there
+is no cross-matrix coupling, which is why every function below works on one
+matrix at a time.
+
+Readings taken where the pages leave a step open (each is listed in the design
+notes with its reason):
+
+* The iteration is written in the factored form ``A = X X^T``,
+  ``B = b A + c A A``, ``X = a X + B X``.  It equals the page's printed form
+  (``B = A X``, ``X = a X + b B + c A B``) in exact arithmetic; the printed form
+  is kept as ``ns_orthogonalize_page_form`` and the two are pinned together.
+* Scalar parameters are the float32 values a caller passes through the C ABI,
+  widened exactly to float64 (``f32_param``).
+* Momentum is rounded once to the storage dtype (the page rounds twice, once per
+  in-place op); the update ``W - lr*s*O`` is rounded once.
+* Newton-Schulz consumes the *stored* updated momentum.
+* ``rounding="bf16"`` is the bf16 storage model: the tensors a bf16 engine keeps
+  in bf16 between matrix products are rounded to bf16 (round to nearest even) at
+  exactly those points -- A, B and every iterate except the last -- while
+  the Frobenius scale ``1/(||V||+eps)`` is carried as an exact factor into the
+  first iteration's products instead of being rounded into a bf16 copy of V.
+  All accumulation stays float64.  ``rounding="exact"`` rounds nothing.
+
+Parity status
+-------------
+Every public function here is pinned by ``tests/test_oracle_pins.py`` against
+closed forms (the SVD action of the iteration on singular values, the rank-1
+trajectory, the cubic polar iteration, orthogonal and transpose equivariance,
+the diagonal-Gram identity linking Muon and RMNP, degenerate parameters, exact
+row-split invariance of RMNP) and against library routines (numpy/LAPACK SVD,
+torch's bfloat16 conversion).  No function is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Constants printed in the blog post's appendix ("The Code That Ran").
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+NS_STEPS = 5
+NS_EPS = 1e-7
+MOMENTUM = 0.95
+# The row normalisation in the appendix calls the library default clamp.
+RMNP_EPS = 1e-12
+
+
+def f32_param(p: float) -> float:
+    """The float32 value of a scalar parameter, widened exactly to float64."""
+    return float(np.float32(p))
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 value of each entry (ties to even), returned as float64.
+
+    bfloat16 keeps 8 significant bits.  ``frexp`` writes ``x = m * 2**e`` with
+    ``0.5 <= |m| < 1``; ``m * 256`` then has 8 integer bits and ``rint`` rounds it
+    half-to-even.  A carry to ``|m| = 1`` is exact under ``ldexp``.  Valid for the
+    normal bfloat16 range (|x| >= 2**-126); zeros, infinities and NaN pass
+    through.  Subnormal and overflowing magnitudes never occur in this workload.
+    """
+    x = _f64(x)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def round_storage(x, dtype: str) -> np.ndarray:
+    """Round to the storage dtype ('bf16' or 'f32'); returned as float64."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f32":
+        return _f64(x).astype(np.float32).astype(np.float64)
+    raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+def momentum(v, g, mu: float, dtype: str) -> np.ndarray:
+    """Heavy-ball momentum ``V_t = mu V_{t-1} + G_t`` (blog post, section 1),
+    rounded once to the storage dtype."""
+    return round_storage(f32_param(mu) * _f64(v) + _f64(g), dtype)
+
+
+def frobenius_scale(v, eps: float = NS_EPS) -> float:
+    """``1 / (||V||_F + eps)``: the normalisation that opens the appendix's
+    Newton-Schulz routine (eps added to the norm, not a clamp)."""
+    v = _f64(v)
+    return 1.0 / (float(np.sqrt(np.sum(v * v))) + f32_param(eps))
+
+
+def update_scale(rows: int, cols: int) -> float:
+    """``sqrt(max(1, rows/cols))`` on the matrix's own shape (appendix, the
+    ``muon_sc`` and ``rmnp_local`` steps)."""
+    return float(np.sqrt(max(1.0, rows / cols)))
+
+
+def ns_orthogonalize(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
+                     eps: float = NS_EPS, rounding: str = "exact") -> np.ndarray:
+    """Newton-Schulz orthogonalization of one matrix (appendix routine, factored).
+
+    1. ``X0 = x / (||x||_F + eps)``.
+    2. If rows > cols (strict), work on the transpose.
+    3. ``steps`` times: ``A = X X^T``; ``B = b A + c A A``; ``X = a X + B X``.
+    4. Transpose back.
+
+    ``rounding="bf16"`` applies the bf16 storage model described in the module
+    header; the returned matrix (the last iterate) is never rounded.
+    """
+    if rounding not in ("exact", "bf16"):
+        raise ValueError(rounding)
+    a, b, c = (f32_param(t) for t in coeffs)
+    x = _f64(x)
+    rows, cols = x.shape
+    scale = frobenius_scale(x, eps)
+    tall = rows > cols
+    X = x.T if tall else x
+    if rounding == "exact":
+        X = X * scale
+        s = 1.0
+    else:
+        s = scale  # carried exactly into the first iteration's products
+    for k in range(steps):
+        A = (s * s) * (X @ X.T)
+        if rounding == "bf16":
+            A = round_bf16(A)
+        B = b * A + c * (A @ A)
+        if rounding == "bf16":
+            B = round_bf16(B)
+        Xn = s * (a * X + B @ X)
+        if rounding == "bf16" and k < steps - 1:
+            Xn = round_bf16(Xn)
+        X = Xn
+        s = 1.0
+    X = s * X  # only ns_steps == 0 leaves the scale unapplied
+    return X.T if tall else X
+
+
+def ns_orthogonalize_page_form(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
+                               eps: float = NS_EPS) -> np.ndarray:
+    """The iteration in the association the appendix prints:
+    ``A = X X^T``, ``B = A X``, ``X = a X + b B + c A B`` (exact arithmetic)."""
+    a, b, c = (f32_param(t) for t in coeffs)
+    x = _f64(x)
+    rows, cols = x.shape
+    X = x * frobenius_scale(x, eps)
+    if rows > cols:
+        X = X.T
+    for _ in range(steps):
+        A = X @ X.T
+        B = A @ X
+        X = a * X + b * B + c * (A @ B)
+    if rows > cols:
+        X = X.T
+    return X
+
+
+def muon_step(w, g, v, mu: float = MOMENTUM, lr: float = 0.02,
+              steps: int = NS_STEPS, coeffs=NS_COEFFS, eps: float = NS_EPS,
+              dtype: str = "bf16", rounding: str = "exact"):
+    """One owner-local Muon step on one whole matrix.
+
+    ``V_new = round(mu V + G)``; ``O = NS(V_new)``;
+    ``W_new = round(W - lr * sqrt(max(1, rows/cols)) * O)``.
+    Returns ``(W_new, V_new, O)`` as float64 arrays.
+    """
+    w = _f64(w)
+    v_new = momentum(v, g, mu, dtype)
+    o = ns_orthogonalize(v_new, steps, coeffs, eps, rounding)
+    rows, cols = w.shape
+    s = update_scale(rows, cols)
+    w_new = round_storage(w - f32_param(lr) * s * o, dtype)
+    return w_new, v_new, o
+
+
+def rmnp_direction(v, eps: float = RMNP_EPS) -> np.ndarray:
+    """RMNP direction: each row divided by ``max(||row||_2, eps)``
+    (blog post, section 1; the clamp is the library default the appendix uses)."""
+    v = _f64(v)
+    nrm = np.sqrt(np.sum(v * v, axis=1))
+    return v / np.maximum(nrm, f32_param(eps))[:, None]
+
+
+def rmnp_step(w, g, v, mu: float = MOMENTUM, lr: float = 0.02,
+              eps: float = RMNP_EPS, dtype: str = "bf16"):
+    """One RMNP step on one matrix: momentum, row-normalized direction, update
+    scaled by ``sqrt(max(1, rows/cols))`` (appendix, ``rmnp_local``).
+    Returns ``(W_new, V_new, U)``."""
+    w = _f64(w)
+    v_new = momentum(v, g, mu, dtype)
+    u = rmnp_direction(v_new, eps)
+    rows, cols = w.shape
+    s = update_scale(rows, cols)
+    w_new = round_storage(w - f32_param(lr) * s * u, dtype)
+    return w_new, v_new, u

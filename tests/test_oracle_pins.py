@@ -1,0 +1,375 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: closed forms
+(the action of one Newton-Schulz step on singular values, rank-1 and
+diagonal-Gram constructions, the cubic polar iteration), library routines
+(LAPACK SVD through numpy, torch's bfloat16 conversion and row normalisation),
+invariances, and the constants and ledger the blog post prints
+(``tests/golden/``).  Inputs are small so the whole file runs in seconds.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import (NS_COEFFS, f32_param, momentum, ns_orthogonalize,
+                    ns_orthogonalize_page_form, muon_step, rmnp_direction,
+                    rmnp_step, round_bf16, round_storage)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+A, B, C = (f32_param(t) for t in NS_COEFFS)
+
+
+def relF(x, y):
+    return np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-300)
+
+
+def p(s, k=1, a=A, b=B, c=C):
+    """k-fold scalar map of one Newton-Schulz step on a singular value."""
+    s = np.asarray(s, np.float64)
+    for _ in range(k):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+def svd_closed_form(x, k, eps=1e-7, coeffs=NS_COEFFS):
+    """``X0 = U S V^T`` (LAPACK) => k Newton-Schulz steps give ``U p^k(S) V^T``,
+    because ``X X^T = U S^2 U^T`` makes every step act on S alone."""
+    a, b, c = (f32_param(t) for t in coeffs)
+    x = np.asarray(x, np.float64)
+    x0 = x / (np.linalg.norm(x) + f32_param(eps))
+    u, s, vt = np.linalg.svd(x0, full_matrices=False)
+    return (u * p(s, k, a, b, c)[None, :]) @ vt
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# golden constants and ledger printed on the pages
+# --------------------------------------------------------------------------
+
+def test_constants_match_page_appendix():
+    g = json.load(open(os.path.join(GOLDEN, "ns_constants.json")))
+    assert tuple(g["ns_coefficients"]) == oracle.NS_COEFFS
+    assert g["ns_steps"] == oracle.NS_STEPS
+    assert g["ns_eps"] == oracle.NS_EPS
+    assert g["momentum"] == oracle.MOMENTUM
+    assert g["rmnp_row_norm_clamp"]["value"] == oracle.RMNP_EPS
+
+
+def test_gpt2_large_workload_matches_page_ledger():
+    import workloads
+    g = json.load(open(os.path.join(GOLDEN, "gpt2_large_ledger.json")))
+    wl = workloads.get("gpt2_large_144")
+    assert len(wl.shapes) == g["matrices"]
+    assert round(wl.numel / 1e6) == g["params_millions_rounded"]
+    gather = sum(7 / 8 * r * c * 2 for r, c in wl.shapes) / 2 ** 20
+    assert round(gather) == g["gather_mib_per_gpu_8way_rounded"]
+    assert 5120 * 1280 * 2 / 2 ** 20 == g["c_fc_bf16_mib"]
+    assert (5120, 1280) in wl.shapes
+    # page rows ([out, in]) are this workload's columns
+    sum_rows_page = sum(c for _, c in wl.shapes)
+    assert abs(sum_rows_page - g["row_vector_len_approx"]) <= \
+        g["row_vector_len_rel_tol"] * g["row_vector_len_approx"]
+
+
+# --------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    torch = pytest.importorskip("torch")
+    r = rng(0)
+    x = np.concatenate([
+        r.standard_normal(20000).astype(np.float32),
+        (r.standard_normal(20000) * 1e-3).astype(np.float32),
+        (r.standard_normal(2000) * 1e30).astype(np.float32),
+    ])
+    # constructed ties: low 16 bits exactly 0x8000 (odd and even kept parts)
+    bits = r.integers(0x3F000000 >> 16, 0x4100, size=4000).astype(np.uint32) << 16
+    ties = (bits | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1.0])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = round_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_round_bf16_is_direct_from_float64():
+    # 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7: ties to even -> 1.
+    assert round_bf16(1 + 2.0 ** -8) == 1.0
+    # 1 + 3*2^-8 is the midpoint of 1+2^-7 (odd) and 1+2^-6 (even) -> 1+2^-6.
+    assert round_bf16(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    # Just above the midpoint rounds up even though a float32 hop would tie.
+    assert round_bf16(1 + 2.0 ** -8 + 2.0 ** -40) == 1 + 2.0 ** -7
+    assert round_bf16(-(1 + 2.0 ** -8 + 2.0 ** -40)) == -(1 + 2.0 ** -7)
+    # carry into the exponent
+    assert round_bf16(2.0 - 2.0 ** -9) == 2.0
+    assert np.isnan(round_bf16(np.nan)) and round_bf16(np.inf) == np.inf
+
+
+def test_round_storage_f32_is_float32():
+    x = rng(1).standard_normal(1000)
+    np.testing.assert_array_equal(round_storage(x, "f32"),
+                                  x.astype(np.float32).astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# Newton-Schulz: closed forms
+# --------------------------------------------------------------------------
+
+SHAPES = [(1, 1), (1, 5), (5, 1), (8, 16), (16, 8), (32, 64), (64, 64), (3, 200),
+          (200, 3), (48, 20)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("k", [0, 1, 2, 5])
+def test_ns_matches_svd_closed_form(shape, k):
+    x = rng(hash(shape) % 1000 + k).standard_normal(shape)
+    got = ns_orthogonalize(x, steps=k)
+    ref = svd_closed_form(x, k)
+    assert relF(got, ref) <= 1e-12
+
+
+def test_ns_band_of_singular_values_gaussian_256x512():
+    # sup over [0,1] of p^5 is 1.20237...; every singular value above 0.0015
+    # maps into [0.6818, 1.2024] (scalar map of the printed coefficients).
+    grid = np.linspace(0, 1, 200001)
+    sup = p(grid, 5).max()
+    assert 1.2023 < sup < 1.2025
+    x = rng(2).standard_normal((256, 512))
+    s_in = np.linalg.svd(x / (np.linalg.norm(x) + 1e-7), compute_uv=False)
+    assert s_in.min() > 0.0015
+    s = np.linalg.svd(ns_orthogonalize(x), compute_uv=False)
+    assert s.max() <= sup + 1e-12
+    assert s.min() >= 0.6818 - 1e-12
+
+
+def test_ns_cubic_coefficients_converge_to_polar_factor():
+    # (1.5, -0.5, 0) is the classic cubic iteration for the polar factor U V^T.
+    r = rng(3)
+    u, _ = np.linalg.qr(r.standard_normal((24, 24)))
+    v, _ = np.linalg.qr(r.standard_normal((40, 24)))
+    s = np.linspace(0.1, 1.0, 24)
+    x = (u * s) @ v.T
+    got = ns_orthogonalize(x, steps=40, coeffs=(1.5, -0.5, 0.0))
+    assert relF(got, u @ v.T) <= 1e-12
+
+
+def test_ns_quintic_within_convergence_band_of_polar_factor():
+    r = rng(4)
+    u, _ = np.linalg.qr(r.standard_normal((16, 16)))
+    v, _ = np.linalg.qr(r.standard_normal((48, 16)))
+    s = np.linspace(0.2, 2.0, 16)
+    x = (u * s) @ v.T
+    sh = np.linalg.svd(x / (np.linalg.norm(x) + 1e-7), compute_uv=False)
+    bound = np.abs(p(sh, 5) - 1).max()
+    err = np.linalg.norm(ns_orthogonalize(x) - u @ v.T, 2)
+    assert err <= bound + 1e-12
+    assert bound < 0.32
+
+
+def test_ns_rank_one_closed_form():
+    r = rng(5)
+    a = r.standard_normal(7)
+    b = r.standard_normal(11)
+    x = np.outer(a, b)
+    nu = np.linalg.norm(a) * np.linalg.norm(b)
+    sig = nu / (nu + f32_param(1e-7))
+    ref = p(sig, 5) * np.outer(a / np.linalg.norm(a), b / np.linalg.norm(b))
+    assert relF(ns_orthogonalize(x), ref) <= 1e-13
+    # trajectory of the scalar map from sigma = 1
+    traj = [1.0]
+    for _ in range(5):
+        traj.append(float(p(traj[-1])))
+    np.testing.assert_allclose(traj[1:], [0.701, 1.11362, 0.72071, 1.08997, 0.69644],
+                               atol=1e-5)
+    # 1x1 matrix: O = p^5(|v|/(|v|+eps)) * sign(v)
+    for val in (3.0, -0.25):
+        o = ns_orthogonalize(np.array([[val]]))
+        assert abs(o[0, 0] - np.sign(val) * p(abs(val) / (abs(val) + f32_param(1e-7)), 5)) < 1e-14
+
+
+def test_ns_page_association_equals_factored_form():
+    for shape in [(16, 40), (40, 16), (33, 33)]:
+        x = rng(6).standard_normal(shape)
+        assert relF(ns_orthogonalize(x), ns_orthogonalize_page_form(x)) <= 1e-13
+
+
+def test_ns_transpose_equivariance():
+    for shape in [(12, 30), (30, 12), (1, 9)]:
+        x = rng(7).standard_normal(shape)
+        assert np.array_equal(ns_orthogonalize(x.T), ns_orthogonalize(x).T)
+    # the tall branch agrees with the closed form of the untransposed matrix
+    x = rng(8).standard_normal((50, 20))
+    assert relF(ns_orthogonalize(x), svd_closed_form(x, 5)) <= 1e-12
+
+
+def test_ns_orthogonal_invariance():
+    r = rng(9)
+    x = r.standard_normal((20, 36))
+    q1, _ = np.linalg.qr(r.standard_normal((20, 20)))
+    q2, _ = np.linalg.qr(r.standard_normal((36, 36)))
+    lhs = ns_orthogonalize(q1 @ x @ q2)
+    rhs = q1 @ ns_orthogonalize(x) @ q2
+    assert relF(lhs, rhs) <= 1e-12
+
+
+def test_diagonal_gram_links_muon_and_rmnp():
+    # V = diag(d) Q with orthonormal rows: V V^T is diagonal, and Muon's
+    # direction is row-wise RMNP scaled by p^k of each row's singular value.
+    r = rng(10)
+    q, _ = np.linalg.qr(r.standard_normal((40, 12)))
+    q = q.T                                  # 12 x 40, orthonormal rows
+    d = r.uniform(0.5, 2.0, 12) * np.sign(r.standard_normal(12))
+    v = d[:, None] * q
+    gram = v @ v.T
+    assert np.abs(gram - np.diag(np.diag(gram))).max() < 1e-13
+    sig = np.abs(d) / (np.linalg.norm(d) + f32_param(1e-7))
+    o = ns_orthogonalize(v)
+    u = rmnp_direction(v)
+    assert relF(o, p(sig, 5)[:, None] * u) <= 1e-13
+    # with the cubic polar iteration both directions coincide
+    o_polar = ns_orthogonalize(v, steps=60, coeffs=(1.5, -0.5, 0.0))
+    assert relF(o_polar, u) <= 1e-12
+
+
+def test_ns_zero_matrix():
+    o = ns_orthogonalize(np.zeros((4, 9)))
+    assert np.array_equal(o, np.zeros((4, 9)))
+
+
+def test_ns_steps_zero_is_normalisation():
+    x = rng(11).standard_normal((6, 10))
+    ref = x / (np.linalg.norm(x) + f32_param(1e-7))
+    assert relF(ns_orthogonalize(x, steps=0), ref) <= 1e-15
+    assert relF(ns_orthogonalize(x, steps=0, rounding="bf16"), ref) <= 1e-15
+
+
+# --------------------------------------------------------------------------
+# bf16 storage model
+# --------------------------------------------------------------------------
+
+def test_bf16_model_rounds_exactly_a_b_and_iterates():
+    # x has orthonormal rows scaled by 1 (4 of 8 unit columns), ||x||_F = 2 and
+    # eps = 0, so the Frobenius scale is exactly 1/2 and X X^T = I.  One step:
+    # A = I/4 (bf16-exact), B = b/4 + c/16 times I (rounded to bf16), and the
+    # last iterate 0.5*(a x + B x) is not rounded.
+    x = np.zeros((4, 8))
+    x[np.arange(4), [1, 3, 5, 7]] = 1.0
+    model = ns_orthogonalize(x, steps=1, eps=0.0, rounding="bf16")
+    b_model = round_bf16(B * 0.25 + C * 0.0625)
+    assert b_model != B * 0.25 + C * 0.0625
+    assert np.array_equal(model, 0.5 * (A * x + b_model * x))
+    exact = ns_orthogonalize(x, steps=1, eps=0.0)
+    assert np.array_equal(exact, 0.5 * (A + B * 0.25 + C * 0.0625) * x)
+    # two steps: the first iterate is rounded to bf16 before the second step
+    x1 = round_bf16(0.5 * (A + b_model))
+    a2 = round_bf16(x1 * x1)
+    b2 = round_bf16(B * a2 + C * a2 * a2)
+    ref2 = (A * x1 + b2 * x1) * x
+    assert np.array_equal(ns_orthogonalize(x, steps=2, eps=0.0, rounding="bf16"), ref2)
+
+
+def test_bf16_model_close_to_exact_on_gaussian():
+    x = round_bf16(rng(12).standard_normal((64, 192)) * 1e-3)
+    e = ns_orthogonalize(x)
+    m = ns_orthogonalize(x, rounding="bf16")
+    err = relF(m, e)
+    assert 1e-4 < err < 2e-2
+
+
+# --------------------------------------------------------------------------
+# full Muon step
+# --------------------------------------------------------------------------
+
+def test_momentum_heavy_ball_and_mu_zero():
+    r = rng(13)
+    v = r.standard_normal((5, 7))
+    g = r.standard_normal((5, 7))
+    got = momentum(v, g, 0.95, "f32")
+    ref = (np.float64(np.float32(0.95)) * v + g).astype(np.float32).astype(np.float64)
+    assert np.array_equal(got, ref)
+    gb = round_bf16(g)
+    assert np.array_equal(momentum(v, gb, 0.0, "bf16"), gb)
+
+
+@pytest.mark.parametrize("shape,scale", [((8, 2), 2.0), ((2, 8), 1.0), ((18, 2), 3.0),
+                                         ((6, 6), 1.0)])
+def test_muon_step_update_and_scale(shape, scale):
+    r = rng(14)
+    w = r.standard_normal(shape) * 0.02
+    v = r.standard_normal(shape)
+    g = r.standard_normal(shape)
+    w_new, v_new, o = muon_step(w, g, v, mu=0.9, lr=0.5, dtype="f32")
+    v_ref = (np.float64(np.float32(0.9)) * v + g).astype(np.float32).astype(np.float64)
+    assert np.array_equal(v_new, v_ref)
+    o_ref = svd_closed_form(v_ref, 5)
+    assert relF(o, o_ref) <= 1e-12
+    w_ref = (w - 0.5 * scale * o).astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(w_new, w_ref, rtol=0, atol=1e-6)
+
+
+def test_muon_step_lr_zero_leaves_weights():
+    r = rng(15)
+    w = round_bf16(r.standard_normal((6, 9)) * 0.02)
+    w_new, _, _ = muon_step(w, r.standard_normal((6, 9)), r.standard_normal((6, 9)),
+                            lr=0.0, dtype="bf16")
+    assert np.array_equal(w_new, w)
+
+
+def test_muon_step_zero_momentum_and_gradient():
+    w = round_bf16(rng(16).standard_normal((5, 11)) * 0.02)
+    z = np.zeros((5, 11))
+    w_new, v_new, o = muon_step(w, z, z, dtype="bf16")
+    assert not v_new.any() and not o.any()
+    assert np.array_equal(w_new, w)
+
+
+# --------------------------------------------------------------------------
+# RMNP
+# --------------------------------------------------------------------------
+
+def test_rmnp_unit_rows_and_library_normalize():
+    torch = pytest.importorskip("torch")
+    x = rng(17).standard_normal((30, 70))
+    u = rmnp_direction(x)
+    np.testing.assert_allclose(np.linalg.norm(u, axis=1), 1.0, atol=1e-15)
+    ref = torch.nn.functional.normalize(torch.from_numpy(x), p=2, dim=-1).numpy()
+    assert np.abs(u - ref).max() <= 1e-15
+
+
+def test_rmnp_row_split_invariance_exact():
+    # the blog post's exactness check: 512x384, 8 row shards, max |diff| = 0
+    x = np.random.default_rng(7).standard_normal((512, 384))
+    full = rmnp_direction(x)
+    for k in range(8):
+        sl = slice(k * 64, (k + 1) * 64)
+        assert np.array_equal(rmnp_direction(x[sl]), full[sl])
+
+
+def test_rmnp_zero_row_gives_zero_update():
+    r = rng(18)
+    w = round_bf16(r.standard_normal((4, 16)) * 0.02)
+    v = round_bf16(r.standard_normal((4, 16)))
+    g = round_bf16(r.standard_normal((4, 16)))
+    v[2] = 0.0
+    g[2] = 0.0
+    w_new, v_new, u = rmnp_step(w, g, v, dtype="bf16")
+    assert not u[2].any()
+    assert np.array_equal(w_new[2], w[2])
+    np.testing.assert_allclose(np.linalg.norm(u[[0, 1, 3]], axis=1), 1.0, atol=1e-15)
+
+
+def test_rmnp_step_scale_tall():
+    r = rng(19)
+    w = r.standard_normal((32, 8)) * 0.02
+    v = r.standard_normal((32, 8))
+    g = r.standard_normal((32, 8))
+    w_new, v_new, u = rmnp_step(w, g, v, mu=0.95, lr=0.1, dtype="f32")
+    ref = (w - 0.1 * 2.0 * v_new / np.linalg.norm(v_new, axis=1, keepdims=True))
+    np.testing.assert_allclose(w_new, ref.astype(np.float32), rtol=0, atol=1e-7)
