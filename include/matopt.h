@@ -1,0 +1,161 @@
+/*
+ * matopt.h -- C ABI of the owner-local Muon step engine for MI355X (gfx950).
+ *
+ * The library runs, on one GPU, the optimizer step an owner rank applies to the
+ * whole 2D matrices it owns (MatrixFSDP, arXiv 2607.05895, sections 3 and 4.4),
+ * with the step itself as the blog post "Optimizers In A Sharded World: Muon's
+ * O(mn) Vs RMNP's Zero" defines it (section 1; appendix "The Code That Ran"):
+ *
+ *   momentum        V <- mu*V + G                              (heavy ball)
+ *   normalisation   X0 = V / (||V||_F + eps)
+ *   transpose       work on X0^T when rows > cols (strict)
+ *   ns_steps times  A = X X^T ; B = b*A + c*A*A ; X = a*X + B*X
+ *   update          W <- W - lr * sqrt(max(1, rows/cols)) * O     (O = last X,
+ *                                                                 transposed back)
+ *
+ * and the RMNP comparator (same post, section 1 and the appendix's rmnp_local):
+ *
+ *   V <- mu*V + G ;  u_i = V_i / max(||V_i||_2, eps) ;  W <- W - lr*s*u
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All matrix pointers are DEVICE pointers to contiguous row-major storage owned
+ *   by the caller.  The library keeps no pointer after a call returns.
+ * - Host-side arrays (matopt_mat lists, row/col arrays, pointer arrays) are read
+ *   during the call only.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *   the call returns without synchronising.  Keep every buffer alive until the
+ *   stream has completed the work.
+ * - Argument errors are detected before anything is enqueued and leave every
+ *   buffer untouched.  A failed launch returns MATOPT_ERR_HIP.  A device fault
+ *   surfaces at the caller's next synchronisation.  matopt_last_error_detail()
+ *   returns a thread-local text for the last non-OK status of the calling thread.
+ * - Scalars are float32; NaN/Inf in matrix data propagate and are not checked.
+ * - W, G, V (and the workspace) must not overlap each other (MATOPT_ERR_ALIAS is
+ *   reported for exactly equal base pointers and for overlapping ranges).
+ * - count == 0 is a no-op returning MATOPT_OK.
+ * - Calls on one stream are ordered.  Calls that share a workspace must not run
+ *   concurrently on different streams.
+ * - The first call with a given (shapes, pointers, workspace) list builds a small
+ *   device-side plan (matrix descriptors and tile tables), which allocates device
+ *   memory and synchronises `stream` once; later calls with the same list reuse
+ *   it and allocate nothing.
+ */
+#ifndef MATOPT_H
+#define MATOPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MATOPT_F32 = 0,  /* IEEE float32 */
+    MATOPT_BF16 = 1  /* bfloat16 (round to nearest even on every store) */
+} matopt_dtype;
+
+typedef enum {
+    MATOPT_OK = 0,
+    MATOPT_ERR_NULL = 1,       /* a required pointer is NULL */
+    MATOPT_ERR_SHAPE = 2,      /* rows or cols < 1, or a size too large */
+    MATOPT_ERR_DTYPE = 3,      /* unsupported dtype or dtype combination */
+    MATOPT_ERR_PARAM = 4,      /* non-finite scalar, ns_steps outside [0, 64], count < 0 */
+    MATOPT_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required */
+    MATOPT_ERR_ALIAS = 6,      /* two buffers overlap */
+    MATOPT_ERR_ALIGN = 7,      /* a pointer is not 16-byte aligned */
+    MATOPT_ERR_DEVICE = 8,     /* the current device is not gfx950 / no device */
+    MATOPT_ERR_HIP = 9,        /* a HIP runtime call or a launch failed */
+    MATOPT_ERR_INTERNAL = 10
+} matopt_status;
+
+/* One matrix of a batch: W (in/out), G (in), V (in/out), all rows x cols,
+ * contiguous row-major, same dtype, 16-byte aligned. */
+typedef struct {
+    void* w;
+    const void* g;
+    void* v;
+    int64_t rows;
+    int64_t cols;
+} matopt_mat;
+
+/*
+ * Bytes of device workspace muon_step_batched / ns_orthogonalize_batched need for
+ * this list of shapes in dtype `dt` (the compute dtype: BF16 selects the bf16
+ * MFMA path, F32 the float32 path).  Returns 0 on invalid arguments.  Pure host
+ * function; the result depends on the shapes only.
+ */
+size_t matopt_workspace_bytes(const int64_t* rows, const int64_t* cols,
+                              int32_t count, matopt_dtype dt);
+
+/*
+ * One Muon step on every matrix of `mats` (blog post, appendix muon_sc step on a
+ * whole matrix; MatrixFSDP section 4.4 owner-local step).
+ *   dt          storage and compute dtype of W, G, V: MATOPT_BF16 (bf16 storage,
+ *               bf16 MFMA products with float32 accumulation) or MATOPT_F32
+ *               (float32 storage and float32 products).
+ *   mu          momentum (0.95 on the pages); lr learning rate.
+ *   ns_steps    Newton-Schulz iterations, 0..64 (5 on the pages).
+ *   a, b, c     Newton-Schulz coefficients ((3.4445, -4.7750, 2.0315) on the pages).
+ *   eps         added to the Frobenius norm (1e-7 on the pages), >= 0.
+ *   workspace   device buffer of at least matopt_workspace_bytes(...) bytes,
+ *               256-byte aligned, contents on entry irrelevant, clobbered.
+ * V and W are updated in place; G is read only.
+ */
+matopt_status muon_step_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                float mu, float lr, int32_t ns_steps,
+                                float a, float b, float c, float eps,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One RMNP step on every matrix of `mats` (blog post, section 1 RMNP direction and
+ * the appendix's rmnp_local step): V <- mu*V + G (one rounding to storage); row
+ * sums of squares of the stored V in float32; W <- W - lr*sqrt(max(1,rows/cols)) *
+ * V_i / max(||V_i||, eps) (one rounding).  eps: 1e-12 on the pages, >= 0.
+ * Needs no workspace.
+ */
+matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                float mu, float lr, float eps, void* stream);
+
+/*
+ * Newton-Schulz only (the appendix's routine): o[i] = NS(x[i]) for each matrix,
+ * in the original orientation.  x[i]: rows[i] x cols[i] in `in_dt` (selects the
+ * compute path as `dt` does above); o[i]: same shape in `out_dt` (F32 or BF16).
+ * x is read only.  Used to read the orthogonalized direction out directly.
+ */
+matopt_status ns_orthogonalize_batched(const void* const* x, void* const* o,
+                                       const int64_t* rows, const int64_t* cols,
+                                       int32_t count, matopt_dtype in_dt,
+                                       matopt_dtype out_dt, int32_t ns_steps,
+                                       float a, float b, float c, float eps,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* matopt_status_string(matopt_status s);
+
+/* Thread-local detail text of the last non-OK status returned to this thread. */
+const char* matopt_last_error_detail(void);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int32_t matopt_version(void);
+
+/*
+ * Kernel timing for benchmarks.  While enabled, every launch of the library is
+ * bracketed by hipEvents on the stream it is launched on, and per-kernel-class
+ * elapsed times are accumulated when matopt_profile_read() is called (which
+ * synchronises on those events).  Classes: 0 momentum+norm+X0 build,
+ * 1 norm finalize, 2 Gram X X^T, 3 polynomial b*A+c*A*A, 4 apply a*X+B*X
+ * (incl. fused update on the last step), 5 ns_steps==0 output, 6 RMNP.
+ */
+#define MATOPT_PROFILE_CLASSES 7
+matopt_status matopt_profile_enable(int32_t on);
+/* ms[k], launches[k] for k < MATOPT_PROFILE_CLASSES; resets the accumulators. */
+matopt_status matopt_profile_read(double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MATOPT_H */

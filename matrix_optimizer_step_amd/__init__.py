@@ -1,0 +1,235 @@
+"""Python binding of libmatopt: the owner-local Muon step and the RMNP comparator
+as hand-written HIP kernels for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the library's
+kernels.  torch supplies device memory (tensors, the workspace) and the current
+stream; nothing here computes.  If ``libmatopt.so`` has not been built, every
+entry point raises ``MatoptError`` -- there is no fallback.
+
+Entry points mirror the C ABI (``include/matopt.h``):
+
+* ``muon_step_batched(weights, grads, moms, mu, lr, ns_steps, coeffs, eps)``
+* ``rmnp_step_batched(weights, grads, moms, mu, lr, eps)``
+* ``ns_orthogonalize_batched(xs, out_dtype, ns_steps, coeffs, eps)``
+* ``workspace_bytes(shapes, dtype)``, ``profile_enable``, ``profile_read``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
+           "rmnp_step_batched", "ns_orthogonalize_batched", "profile_enable",
+           "profile_read", "PROFILE_CLASSES", "LIB_PATH", "EXPORTS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmatopt.so")
+
+F32, BF16 = 0, 1
+PROFILE_CLASSES = ("prep", "finalize", "gram", "poly", "apply", "scale_out", "rmnp")
+
+# Defaults printed on the pages (blog post appendix).
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+class MatoptError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+class _Mat(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("g", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+_vp, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                              ctypes.c_float, ctypes.c_size_t)
+
+# symbol -> (restype, argtypes); every function include/matopt.h declares
+EXPORTS = {
+    "matopt_workspace_bytes": (_sz, [ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, _i32]),
+    "muon_step_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _i32, _f32,
+                                 _f32, _f32, _f32, _vp, _sz, _vp]),
+    "rmnp_step_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _vp]),
+    "ns_orthogonalize_batched": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                        ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32,
+                                        _i32, _i32, _i32, _f32, _f32, _f32, _f32, _vp, _sz,
+                                        _vp]),
+    "matopt_status_string": (ctypes.c_char_p, [_i32]),
+    "matopt_last_error_detail": (ctypes.c_char_p, []),
+    "matopt_version": (_i32, []),
+    "matopt_profile_enable": (_i32, [_i32]),
+    "matopt_profile_read": (_i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """The loaded ``libmatopt.so`` (ctypes), with argument types set."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise MatoptError(-1, "MATOPT_NOT_BUILT",
+                                  f"{LIB_PATH} is missing; run __graft_entry__.build() or "
+                                  "python -m matrix_optimizer_step_amd.build")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in EXPORTS.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        name = L.matopt_status_string(status).decode()
+        detail = L.matopt_last_error_detail().decode()
+        raise MatoptError(status, name, detail)
+
+
+def _dt(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dtype} (bfloat16 or float32)")
+
+
+def _check_mat(t: torch.Tensor, what: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a CUDA (HIP) tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream_ptr(device, stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+def workspace_bytes(shapes, dtype) -> int:
+    n = len(shapes)
+    rows = (_i64 * max(n, 1))(*[int(r) for r, _ in shapes])
+    cols = (_i64 * max(n, 1))(*[int(c) for _, c in shapes])
+    return int(lib().matopt_workspace_bytes(rows, cols, n, _dt(dtype)))
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(device, dtype, shapes, workspace):
+    need = workspace_bytes(shapes, dtype)
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace too small: need {need} bytes")
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+    key = (str(device), _dt(dtype), tuple(shapes))
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    base = ws.data_ptr()
+    off = (-base) % 256
+    return base + off, need, ws
+
+
+def clear_workspace_cache():
+    _ws_cache.clear()
+
+
+def _mats(weights, grads, moms):
+    if not (len(weights) == len(grads) == len(moms)):
+        raise ValueError("weights, grads and moms must have the same length")
+    n = len(weights)
+    arr = (_Mat * max(n, 1))()
+    dtype = weights[0].dtype if n else torch.bfloat16
+    for i, (w, g, v) in enumerate(zip(weights, grads, moms)):
+        _check_mat(w, f"weights[{i}]", dtype)
+        _check_mat(g, f"grads[{i}]", dtype)
+        _check_mat(v, f"moms[{i}]", dtype)
+        if not (w.shape == g.shape == v.shape):
+            raise ValueError(f"matrix {i}: W, G, V shapes differ")
+        arr[i] = _Mat(w.data_ptr(), g.data_ptr(), v.data_ptr(), w.shape[0], w.shape[1])
+    return arr, n, dtype
+
+
+def muon_step_batched(weights, grads, moms, mu=0.95, lr=0.02, ns_steps=5,
+                      coeffs=NS_COEFFS, eps=1e-7, workspace=None, stream=None):
+    """One Muon step on every (W, G, V) triple; W and V are updated in place."""
+    arr, n, dtype = _mats(weights, grads, moms)
+    if n == 0:
+        return
+    device = weights[0].device
+    shapes = [tuple(w.shape) for w in weights]
+    wp, wb, _keep = _workspace(device, dtype, shapes, workspace)
+    a, b, c = coeffs
+    _check(lib().muon_step_batched(arr, n, _dt(dtype), mu, lr, ns_steps, a, b, c, eps,
+                                   wp, wb, _stream_ptr(device, stream)))
+
+
+def rmnp_step_batched(weights, grads, moms, mu=0.95, lr=0.02, eps=1e-12, stream=None):
+    """One RMNP step on every (W, G, V) triple; W and V are updated in place."""
+    arr, n, dtype = _mats(weights, grads, moms)
+    if n == 0:
+        return
+    device = weights[0].device
+    _check(lib().rmnp_step_batched(arr, n, _dt(dtype), mu, lr, eps,
+                                   _stream_ptr(device, stream)))
+
+
+def ns_orthogonalize_batched(xs, out_dtype=torch.float32, ns_steps=5, coeffs=NS_COEFFS,
+                             eps=1e-7, outs=None, workspace=None, stream=None):
+    """Newton-Schulz only: returns (or fills ``outs`` with) O for every x."""
+    n = len(xs)
+    if n == 0:
+        return []
+    in_dtype = xs[0].dtype
+    device = xs[0].device
+    for i, x in enumerate(xs):
+        _check_mat(x, f"xs[{i}]", in_dtype)
+    if outs is None:
+        outs = [torch.empty(x.shape, dtype=out_dtype, device=device) for x in xs]
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        _check_mat(o, f"outs[{i}]", out_dtype)
+        if o.shape != x.shape:
+            raise ValueError(f"outs[{i}] shape differs from xs[{i}]")
+    shapes = [tuple(x.shape) for x in xs]
+    wp, wb, _keep = _workspace(device, in_dtype, shapes, workspace)
+    xp = (_vp * n)(*[x.data_ptr() for x in xs])
+    op = (_vp * n)(*[o.data_ptr() for o in outs])
+    rows = (_i64 * n)(*[s[0] for s in shapes])
+    cols = (_i64 * n)(*[s[1] for s in shapes])
+    a, b, c = coeffs
+    _check(lib().ns_orthogonalize_batched(xp, op, rows, cols, n, _dt(in_dtype), _dt(out_dtype),
+                                          ns_steps, a, b, c, eps, wp, wb,
+                                          _stream_ptr(device, stream)))
+    return outs
+
+
+def profile_enable(on: bool = True):
+    _check(lib().matopt_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """Accumulated kernel milliseconds and launch counts per class (resets them)."""
+    k = len(PROFILE_CLASSES)
+    ms = (ctypes.c_double * k)()
+    n = (_i64 * k)()
+    _check(lib().matopt_profile_read(ms, n))
+    return {name: (ms[i], n[i]) for i, name in enumerate(PROFILE_CLASSES)}

@@ -1,0 +1,123 @@
+// Internal declarations shared by the host side and the kernels of libmatopt.
+//
+// Data layout in HBM (one matrix of a batch; "X orientation" is the matrix the
+// Newton-Schulz iteration works on: the stored matrix, or its transpose when it
+// has more rows than columns, so that X is m x n with m <= n):
+//
+//   caller buffers   W, G, V: rows x cols, row-major, storage dtype.
+//   workspace        X[0], X[1]: mp x np (ping-pong iterates, X orientation)
+//                    A, B:       mp x mp (Gram and polynomial; only the tiles on
+//                                         or above the diagonal are written)
+//                    partials:   one float per prep tile (sum of squares)
+//                    xs:         one float per matrix, 1/(||V||_F + eps)
+//   mp, np are m, n rounded up to the GEMM tile (256 for bf16, 64 for fp32); the
+//   padding is written as zeros by the prep kernel and stays zero through the
+//   iteration, so the GEMM main loop needs no bounds checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace matopt {
+
+enum Dtype : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+
+// Output of the last Newton-Schulz apply stage.
+enum OutKind : int32_t {
+  OUT_NEXT_X = 0,   // not the last iteration: write X_next (workspace)
+  OUT_O = 1,        // ns_orthogonalize: write O in the original orientation
+  OUT_W_UPDATE = 2  // muon step: W <- W - lr*s*O in the original orientation
+};
+
+struct MatDesc {
+  void* w;              // caller W (muon) or unused
+  const void* g;        // caller G (muon) or unused
+  void* v;              // caller V (muon) / NS input x (read only)
+  void* o;              // NS output (ns_orthogonalize) or unused
+  int64_t rows, cols;   // original shape
+  int32_t m, n;         // X orientation, m <= n
+  int32_t mp, np;       // padded to the GEMM tile
+  int32_t transposed;   // rows > cols
+  int32_t vec_ok;       // cols is a multiple of the 16-byte vector width
+  float upd_scale;      // sqrt(max(1, rows/cols))
+  int32_t prep_tiles_c; // prep tiles along the padded original columns
+  void* x[2];           // iterates, mp x np, leading dimension np
+  void* a;              // Gram,       mp x mp, leading dimension mp
+  void* b;              // polynomial, mp x mp, leading dimension mp
+  float* xs;            // this matrix's Frobenius scale
+  float* partials;      // this matrix's first prep-tile partial
+  int32_t n_prep;       // prep tiles of this matrix
+  int32_t pad_;
+};
+
+// Prep tile: 64 x 64 block of the padded original-orientation matrix.
+struct PrepTile {
+  int32_t mat, tr, tc, idx;   // idx: tile index within the matrix
+};
+
+// GEMM output tile (ti, tj) of matrix `mat`.
+struct GemmTile {
+  int32_t mat, ti, tj, pad_;
+};
+
+struct PrepParams {
+  const MatDesc* mats;
+  const PrepTile* tiles;
+  float mu;
+  int32_t momentum;   // 1: V <- mu V + G and store V;  0: read x only
+};
+
+struct FinalizeParams {
+  const MatDesc* mats;
+  float eps;
+};
+
+struct GemmParams {
+  const MatDesc* mats;
+  const GemmTile* tiles;
+  int32_t stage;      // 0: A = X X^T, 1: B = b A + c A A, 2: X' = a X + B X
+  int32_t cur;        // index of the current iterate buffer
+  int32_t first;      // first iteration: fold the Frobenius scale in
+  int32_t out_kind;   // OutKind (stage 2)
+  int32_t out_dt;     // dtype of O for OUT_O
+  float a, b, c, lr;
+};
+
+// ns_steps == 0: O = xs * V directly (prep tiles over the original orientation).
+struct ScaleOutParams {
+  const MatDesc* mats;
+  const PrepTile* tiles;
+  int32_t out_kind;   // OUT_O or OUT_W_UPDATE
+  int32_t out_dt;
+  float lr;
+};
+
+// RMNP: a block handles `rows_per_block` consecutive rows of one matrix.
+struct RmnpTask {
+  int32_t mat, row0;
+};
+
+struct RmnpParams {
+  const MatDesc* mats;
+  const RmnpTask* tasks;
+  float mu, lr, eps;
+};
+
+// Tile geometry.
+constexpr int kPrepTile = 64;
+constexpr int kTileBf16 = 256;
+constexpr int kTileF32 = 64;
+
+// Launchers (each defined next to its kernel).
+hipError_t launch_prep(int dt, const PrepParams& p, int n_tiles, hipStream_t s);
+hipError_t launch_finalize(const FinalizeParams& p, int count, hipStream_t s);
+hipError_t launch_scale_out(int dt, const ScaleOutParams& p, int n_tiles, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmParams& p, int n_tiles, hipStream_t s);
+// RMNP kernel variants: rows of one wave (wpr=1) or of a whole block (wpr=4),
+// holding `nch` 16-byte chunks per lane in registers; nch == 0 selects the
+// streaming two-pass variant (any width, scalar loads).
+hipError_t launch_rmnp(int dt, int wpr, int nch, const RmnpParams& p, int n_tasks,
+                       hipStream_t s);
+
+}  // namespace matopt

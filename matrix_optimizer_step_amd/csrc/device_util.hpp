@@ -1,0 +1,108 @@
+// Small device helpers: bfloat16 <-> float, vector element access, reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace matopt {
+
+// bfloat16 is handled as its 16-bit pattern.
+__device__ __forceinline__ float bf2f(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+// float -> bfloat16, round to nearest even (lowers to v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// float64 -> float32 with round-to-odd: when x is not a float32, take the
+// neighbour of x whose last significand bit is 1.  A value rounded to odd with
+// p >= q + 2 bits and then rounded to nearest-even with q bits equals the direct
+// nearest-even rounding of x (float32 24 bits >= bfloat16 8 bits + 2).
+__device__ __forceinline__ float f64_to_f32_odd(double x) {
+  float f = (float)x;
+  const double back = (double)f;
+  if (back != x) {
+    uint32_t u = __float_as_uint(f);
+    if (!(u & 1u)) u += (fabs(x) > fabs(back)) ? 1u : 0xffffffffu;
+    f = __uint_as_float(u);
+  }
+  return f;
+}
+
+// Nearest-even bfloat16 of a float64 value, rounded once.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+  return f2bf(f64_to_f32_odd(x));
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+__device__ __forceinline__ float lo_bf(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
+
+// Element traits: 16-byte vectors hold E elements of T.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int E = 4;
+  __device__ static void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+  // a*b + c rounded once to storage (float32 fma is exact-then-round)
+  __device__ static float fma_store(float a, float b, float c) { return fmaf(a, b, c); }
+  __device__ static float load1(const void* p, int64_t i) {
+    return ((const float*)p)[i];
+  }
+  __device__ static void store1(void* p, int64_t i, float f) { ((float*)p)[i] = f; }
+};
+template <> struct Elem<uint16_t> {  // bfloat16
+  static constexpr int E = 8;
+  __device__ static void unpack(const uint4& v, float* f) {
+    f[0] = lo_bf(v.x); f[1] = hi_bf(v.x); f[2] = lo_bf(v.y); f[3] = hi_bf(v.y);
+    f[4] = lo_bf(v.z); f[5] = hi_bf(v.z); f[6] = lo_bf(v.w); f[7] = hi_bf(v.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]),
+                      pack_bf2(f[4], f[5]), pack_bf2(f[6], f[7]));
+  }
+  // a*b + c rounded once to bfloat16.  The float64 fma is exact whenever the
+  // result fits 53 bits -- always for float32 * bfloat16 + bfloat16 (the
+  // momentum); otherwise its own rounding sits 45 bits below bfloat16 precision.
+  __device__ static float fma_store(float a, float b, float c) {
+    return bf2f(f64_to_bf16(fma((double)a, (double)b, (double)c)));
+  }
+  __device__ static float load1(const void* p, int64_t i) {
+    return bf2f(((const uint16_t*)p)[i]);
+  }
+  __device__ static void store1(void* p, int64_t i, float f) {
+    ((uint16_t*)p)[i] = (uint16_t)f2bf(f);
+  }
+};
+
+// Store n (<= 8) consecutive values of dtype dt at element index i of p.
+__device__ __forceinline__ void store_any(void* p, int dt, int64_t i, float f) {
+  if (dt == 1) ((uint16_t*)p)[i] = (uint16_t)f2bf(f);
+  else ((float*)p)[i] = f;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace matopt

@@ -1,0 +1,718 @@
+// Host side of libmatopt: the C ABI declared in include/matopt.h.
+//
+// Each entry point validates its arguments synchronously, looks up (or builds
+// once) a device-side plan for the exact list of shapes and pointers -- matrix
+// descriptors plus the tile tables of every launch -- and enqueues the whole
+// step on the caller's stream as a fixed sequence of grouped launches (every
+// launch covers every matrix of the batch):
+//
+//   muon_step_batched        prep (momentum, norm partials, X0) -> finalize ->
+//                            ns_steps x {Gram, polynomial, apply} (the last apply
+//                            folds the update into W) | scale_out if ns_steps==0
+//   ns_orthogonalize_batched same with no momentum; the last apply writes O
+//   rmnp_step_batched        one fused row kernel launch per width class
+//
+// Tile tables are ordered longest-K first (largest work first, the greedy the
+// MatrixFSDP owner planner uses for roles, section 4.1, Algorithm 1), so that
+// the tail of each launch is made of short tiles.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <list>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/matopt.h"
+#include "common.hpp"
+
+using namespace matopt;
+
+namespace {
+
+thread_local std::string g_detail;
+
+matopt_status fail(matopt_status s, const std::string& msg) {
+  g_detail = msg;
+  return s;
+}
+
+// ---------------------------------------------------------------- device check
+std::mutex g_dev_mu;
+std::map<int, bool> g_dev_ok;
+
+matopt_status check_device(int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MATOPT_ERR_DEVICE, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_dev_ok.find(dev);
+  if (it == g_dev_ok.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(MATOPT_ERR_DEVICE, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = g_dev_ok.emplace(dev, ok).first;
+    if (!ok) g_detail = std::string("device arch ") + prop.gcnArchName + " is not gfx950";
+  }
+  if (!it->second) return fail(MATOPT_ERR_DEVICE, "current device is not gfx950 (MI355X)");
+  *dev_out = dev;
+  return MATOPT_OK;
+}
+
+// ---------------------------------------------------------------- geometry
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int esize(int dt) { return dt == DT_BF16 ? 2 : 4; }
+int gemm_tile(int dt) { return dt == DT_BF16 ? kTileBf16 : kTileF32; }
+
+struct Geo {
+  int64_t rows, cols;
+  int m, n, mp, np;
+  bool transposed;
+  int prep_tr, prep_tc;
+};
+
+Geo geometry(int64_t rows, int64_t cols, int dt) {
+  Geo g;
+  g.rows = rows;
+  g.cols = cols;
+  g.transposed = rows > cols;
+  g.m = (int)(g.transposed ? cols : rows);
+  g.n = (int)(g.transposed ? rows : cols);
+  const int t = gemm_tile(dt);
+  g.mp = (int)round_up(g.m, t);
+  g.np = (int)round_up(g.n, t);
+  const int rows_p = g.transposed ? g.np : g.mp;
+  const int cols_p = g.transposed ? g.mp : g.np;
+  g.prep_tr = rows_p / kPrepTile;
+  g.prep_tc = cols_p / kPrepTile;
+  return g;
+}
+
+struct Layout {
+  std::vector<size_t> x0, x1, a, b;
+  size_t partials = 0, xs = 0, total = 0;
+  int n_prep = 0;
+  std::vector<int> prep_off;
+};
+
+constexpr int64_t kMaxSide = 1 << 20;
+constexpr int64_t kMaxElems = int64_t(1) << 32;
+
+Layout layout(const std::vector<Geo>& geo, int dt) {
+  Layout L;
+  const size_t es = esize(dt);
+  size_t off = 0;
+  for (const Geo& g : geo) {
+    const size_t xb = align256((size_t)g.mp * g.np * es);
+    const size_t ab = align256((size_t)g.mp * g.mp * es);
+    L.x0.push_back(off); off += xb;
+    L.x1.push_back(off); off += xb;
+    L.a.push_back(off); off += ab;
+    L.b.push_back(off); off += ab;
+    L.prep_off.push_back(L.n_prep);
+    L.n_prep += g.prep_tr * g.prep_tc;
+  }
+  L.partials = off;
+  off += align256((size_t)L.n_prep * 4);
+  L.xs = off;
+  off += align256(geo.size() * 4);
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- validation
+bool finite(float x) { return std::isfinite(x); }
+
+matopt_status check_shape(int64_t rows, int64_t cols, int i) {
+  if (rows < 1 || cols < 1 || rows > kMaxSide || cols > kMaxSide || rows * cols > kMaxElems)
+    return fail(MATOPT_ERR_SHAPE, "matrix " + std::to_string(i) + ": invalid shape " +
+                                      std::to_string(rows) + "x" + std::to_string(cols));
+  return MATOPT_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;
+  std::string what;
+};
+
+matopt_status check_overlap(std::vector<Span>& spans) {
+  std::sort(spans.begin(), spans.end(), [](const Span& x, const Span& y) { return x.lo < y.lo; });
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].lo < spans[i - 1].hi)
+      return fail(MATOPT_ERR_ALIAS, spans[i - 1].what + " overlaps " + spans[i].what);
+  return MATOPT_OK;
+}
+
+// ---------------------------------------------------------------- profiling
+std::atomic<bool> g_prof{false};
+std::mutex g_prof_mu;
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+};
+std::vector<ProfRec> g_prof_pending;
+std::vector<hipEvent_t> g_ev_free;
+double g_prof_ms[MATOPT_PROFILE_CLASSES];
+int64_t g_prof_n[MATOPT_PROFILE_CLASSES];
+
+hipEvent_t take_event() {
+  if (!g_ev_free.empty()) {
+    hipEvent_t e = g_ev_free.back();
+    g_ev_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+hipError_t timed(int cls, hipStream_t s, F&& launch) {
+  if (!g_prof.load(std::memory_order_relaxed)) return launch();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  g_prof_pending.push_back({cls, a, b});
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- plans
+enum PlanKind { PK_MUON = 1, PK_NS = 2, PK_RMNP = 3 };
+
+struct RmnpGroup {
+  int wpr, nch, n;
+  size_t off;  // byte offset of its task table in the plan buffer
+};
+
+struct Plan {
+  int device = -1;
+  void* dbuf = nullptr;
+  MatDesc* d_mats = nullptr;
+  PrepTile* d_prep = nullptr;
+  GemmTile* d_k3 = nullptr;
+  GemmTile* d_k4 = nullptr;
+  GemmTile* d_k5 = nullptr;
+  int count = 0, n_prep = 0, n_gram = 0, n_apply = 0;
+  std::vector<RmnpGroup> rmnp;
+  // Evicted plans are freed on their own device after it has drained (a queued
+  // launch may still read the tables).  Plans alive at process exit are never
+  // destroyed: the cache is a leaked singleton, so no HIP call runs during
+  // static destruction.
+  ~Plan() {
+    if (!dbuf) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (device >= 0 && device != cur) (void)hipSetDevice(device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(dbuf);
+    if (device >= 0 && device != cur) (void)hipSetDevice(cur);
+  }
+};
+
+using PlanKey = std::vector<uint64_t>;
+constexpr size_t kPlanCap = 64;
+std::mutex g_plan_mu;
+using PlanList = std::list<std::pair<PlanKey, std::shared_ptr<Plan>>>;
+PlanList& g_plans = *new PlanList();  // front = most recent; never destroyed
+
+std::shared_ptr<Plan> plan_lookup(const PlanKey& key) {
+  for (auto it = g_plans.begin(); it != g_plans.end(); ++it)
+    if (it->first == key) {
+      g_plans.splice(g_plans.begin(), g_plans, it);
+      return g_plans.front().second;
+    }
+  return nullptr;
+}
+
+void plan_insert(const PlanKey& key, std::shared_ptr<Plan> p) {
+  g_plans.emplace_front(key, std::move(p));
+  while (g_plans.size() > kPlanCap) g_plans.pop_back();
+}
+
+struct HostBuf {
+  std::vector<uint8_t> bytes;
+  template <typename T>
+  size_t put(const std::vector<T>& v) {
+    size_t off = align256(bytes.size());
+    bytes.resize(off + align256(v.size() * sizeof(T) + 1));
+    if (!v.empty()) std::memcpy(bytes.data() + off, v.data(), v.size() * sizeof(T));
+    return off;
+  }
+};
+
+matopt_status upload(Plan& p, HostBuf& hb, hipStream_t s) {
+  hipError_t e = hipMalloc(&p.dbuf, hb.bytes.size());
+  if (e != hipSuccess) return fail(MATOPT_ERR_HIP, std::string("plan hipMalloc: ") + hipGetErrorString(e));
+  e = hipMemcpyAsync(p.dbuf, hb.bytes.data(), hb.bytes.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(MATOPT_ERR_HIP, std::string("plan upload: ") + hipGetErrorString(e));
+  return MATOPT_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return (T*)((uint8_t*)base + off);
+}
+
+// Builds the descriptors and tile tables of a Newton-Schulz plan (muon / ns).
+matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& geo,
+                            const std::vector<const void*>& wv, const std::vector<const void*>& gv,
+                            const std::vector<const void*>& vv, const std::vector<const void*>& ov,
+                            void* ws, hipStream_t s) {
+  const int count = (int)geo.size();
+  const Layout L = layout(geo, dt);
+  const int tile = gemm_tile(dt);
+  std::vector<MatDesc> mats(count);
+  std::vector<PrepTile> prep;
+  std::vector<GemmTile> k3, k4, k5;
+  std::vector<int64_t> k3c, k4c, k5c;
+  prep.reserve(L.n_prep);
+  for (int i = 0; i < count; ++i) {
+    const Geo& g = geo[i];
+    MatDesc& d = mats[i];
+    std::memset(&d, 0, sizeof(d));
+    d.w = (void*)wv[i];
+    d.g = gv[i];
+    d.v = (void*)vv[i];
+    d.o = (void*)ov[i];
+    d.rows = g.rows;
+    d.cols = g.cols;
+    d.m = g.m;
+    d.n = g.n;
+    d.mp = g.mp;
+    d.np = g.np;
+    d.transposed = g.transposed ? 1 : 0;
+    d.vec_ok = (g.cols % (16 / esize(dt))) == 0 ? 1 : 0;
+    d.upd_scale = (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
+    d.prep_tiles_c = g.prep_tc;
+    d.x[0] = at<void>(ws, L.x0[i]);
+    d.x[1] = at<void>(ws, L.x1[i]);
+    d.a = at<void>(ws, L.a[i]);
+    d.b = at<void>(ws, L.b[i]);
+    d.xs = at<float>(ws, L.xs) + i;
+    d.partials = at<float>(ws, L.partials) + L.prep_off[i];
+    d.n_prep = g.prep_tr * g.prep_tc;
+    int idx = 0;
+    for (int tr = 0; tr < g.prep_tr; ++tr)
+      for (int tc = 0; tc < g.prep_tc; ++tc) prep.push_back({i, tr, tc, idx++});
+    const int tm = g.mp / tile, tn = g.np / tile;
+    for (int ti = 0; ti < tm; ++ti)
+      for (int tj = ti; tj < tm; ++tj) {
+        k3.push_back({i, ti, tj, 0});
+        k3c.push_back(g.np);
+        k4.push_back({i, ti, tj, 0});
+        k4c.push_back(g.mp);
+      }
+    for (int ti = 0; ti < tm; ++ti)
+      for (int tj = 0; tj < tn; ++tj) {
+        k5.push_back({i, ti, tj, 0});
+        k5c.push_back(g.mp);
+      }
+  }
+  auto lpt = [](std::vector<GemmTile>& t, const std::vector<int64_t>& cost) {
+    std::vector<size_t> idx(t.size());
+    for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+    std::stable_sort(idx.begin(), idx.end(), [&](size_t x, size_t y) { return cost[x] > cost[y]; });
+    std::vector<GemmTile> out(t.size());
+    for (size_t i = 0; i < idx.size(); ++i) out[i] = t[idx[i]];
+    t.swap(out);
+  };
+  lpt(k3, k3c);
+  lpt(k4, k4c);
+  lpt(k5, k5c);
+
+  HostBuf hb;
+  const size_t o_mats = hb.put(mats);
+  const size_t o_prep = hb.put(prep);
+  const size_t o_k3 = hb.put(k3);
+  const size_t o_k4 = hb.put(k4);
+  const size_t o_k5 = hb.put(k5);
+  matopt_status st = upload(P, hb, s);
+  if (st != MATOPT_OK) return st;
+  P.d_mats = at<MatDesc>(P.dbuf, o_mats);
+  P.d_prep = at<PrepTile>(P.dbuf, o_prep);
+  P.d_k3 = at<GemmTile>(P.dbuf, o_k3);
+  P.d_k4 = at<GemmTile>(P.dbuf, o_k4);
+  P.d_k5 = at<GemmTile>(P.dbuf, o_k5);
+  P.count = count;
+  P.n_prep = (int)prep.size();
+  P.n_gram = (int)k3.size();
+  P.n_apply = (int)k5.size();
+  (void)kind;
+  return MATOPT_OK;
+}
+
+matopt_status build_rmnp_plan(Plan& P, int dt, const matopt_mat* mats, int count, hipStream_t s) {
+  const int E = 16 / esize(dt);
+  std::vector<MatDesc> descs(count);
+  std::map<std::pair<int, int>, std::vector<RmnpTask>> groups;
+  for (int i = 0; i < count; ++i) {
+    MatDesc& d = descs[i];
+    std::memset(&d, 0, sizeof(d));
+    d.w = mats[i].w;
+    d.g = mats[i].g;
+    d.v = mats[i].v;
+    d.rows = mats[i].rows;
+    d.cols = mats[i].cols;
+    d.upd_scale = (float)std::sqrt(std::max(1.0, (double)d.rows / (double)d.cols));
+    const bool vec = d.cols % E == 0;
+    const int64_t nchunks = d.cols / E;
+    int wpr = 4, nch = 0;
+    if (vec && nchunks <= 64 * 16) {
+      wpr = 1;
+      for (int c : {1, 2, 4, 8, 16})
+        if (64 * c >= nchunks) { nch = c; break; }
+    } else if (vec && nchunks <= 256 * 16) {
+      wpr = 4;
+      for (int c : {4, 8, 16})
+        if (256 * c >= nchunks) { nch = c; break; }
+    }
+    auto& tasks = groups[{wpr, nch}];
+    const int step = (wpr == 1 && nch > 0) ? 4 : 1;
+    for (int64_t r = 0; r < d.rows; r += step) tasks.push_back({i, (int32_t)r});
+  }
+  HostBuf hb;
+  const size_t o_mats = hb.put(descs);
+  for (auto& kv : groups) {
+    RmnpGroup g;
+    g.wpr = kv.first.first;
+    g.nch = kv.first.second;
+    g.n = (int)kv.second.size();
+    g.off = hb.put(kv.second);
+    P.rmnp.push_back(g);
+  }
+  matopt_status st = upload(P, hb, s);
+  if (st != MATOPT_OK) return st;
+  P.d_mats = at<MatDesc>(P.dbuf, o_mats);
+  P.count = count;
+  return MATOPT_OK;
+}
+
+matopt_status hip_fail(const char* what, hipError_t e) {
+  return fail(MATOPT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Enqueue the Newton-Schulz pipeline of a plan.
+matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, int ns_steps,
+                     float a, float b, float c, float eps, int out_kind, int out_dt,
+                     hipStream_t s) {
+  hipError_t e;
+  PrepParams pp{P.d_mats, P.d_prep, mu, momentum ? 1 : 0};
+  e = timed(0, s, [&] { return launch_prep(dt, pp, P.n_prep, s); });
+  if (e != hipSuccess) return hip_fail("prep launch", e);
+  FinalizeParams fp{P.d_mats, eps};
+  e = timed(1, s, [&] { return launch_finalize(fp, P.count, s); });
+  if (e != hipSuccess) return hip_fail("finalize launch", e);
+  auto gemm = [&](const GemmParams& g, int n) {
+    return dt == DT_BF16 ? launch_gemm_bf16(g, n, s) : launch_gemm_f32(g, n, s);
+  };
+  for (int it = 0; it < ns_steps; ++it) {
+    GemmParams g;
+    std::memset(&g, 0, sizeof(g));
+    g.mats = P.d_mats;
+    g.cur = it & 1;
+    g.first = it == 0 ? 1 : 0;
+    g.out_dt = out_dt;
+    g.a = a;
+    g.b = b;
+    g.c = c;
+    g.lr = lr;
+    g.stage = 0;
+    g.tiles = P.d_k3;
+    g.out_kind = OUT_NEXT_X;
+    e = timed(2, s, [&] { return gemm(g, P.n_gram); });
+    if (e != hipSuccess) return hip_fail("gram launch", e);
+    g.stage = 1;
+    g.tiles = P.d_k4;
+    e = timed(3, s, [&] { return gemm(g, P.n_gram); });
+    if (e != hipSuccess) return hip_fail("poly launch", e);
+    g.stage = 2;
+    g.tiles = P.d_k5;
+    g.out_kind = it == ns_steps - 1 ? out_kind : OUT_NEXT_X;
+    e = timed(4, s, [&] { return gemm(g, P.n_apply); });
+    if (e != hipSuccess) return hip_fail("apply launch", e);
+  }
+  if (ns_steps == 0) {
+    ScaleOutParams sp{P.d_mats, P.d_prep, out_kind, out_dt, lr};
+    e = timed(5, s, [&] { return launch_scale_out(dt, sp, P.n_prep, s); });
+    if (e != hipSuccess) return hip_fail("scale_out launch", e);
+  }
+  return MATOPT_OK;
+}
+
+matopt_status check_common(int32_t count, int dt) {
+  if (count < 0) return fail(MATOPT_ERR_PARAM, "count < 0");
+  if (dt != DT_F32 && dt != DT_BF16) return fail(MATOPT_ERR_DTYPE, "dtype must be MATOPT_F32 or MATOPT_BF16");
+  return MATOPT_OK;
+}
+
+matopt_status check_ns_params(int32_t ns_steps, float a, float b, float c, float eps) {
+  if (ns_steps < 0 || ns_steps > 64) return fail(MATOPT_ERR_PARAM, "ns_steps outside [0, 64]");
+  if (!finite(a) || !finite(b) || !finite(c)) return fail(MATOPT_ERR_PARAM, "non-finite Newton-Schulz coefficient");
+  if (!finite(eps) || eps < 0.f) return fail(MATOPT_ERR_PARAM, "eps must be finite and >= 0");
+  return MATOPT_OK;
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+extern "C" {
+
+int32_t matopt_version(void) { return 10000; }
+
+const char* matopt_status_string(matopt_status s) {
+  switch (s) {
+    case MATOPT_OK: return "MATOPT_OK";
+    case MATOPT_ERR_NULL: return "MATOPT_ERR_NULL";
+    case MATOPT_ERR_SHAPE: return "MATOPT_ERR_SHAPE";
+    case MATOPT_ERR_DTYPE: return "MATOPT_ERR_DTYPE";
+    case MATOPT_ERR_PARAM: return "MATOPT_ERR_PARAM";
+    case MATOPT_ERR_WORKSPACE: return "MATOPT_ERR_WORKSPACE";
+    case MATOPT_ERR_ALIAS: return "MATOPT_ERR_ALIAS";
+    case MATOPT_ERR_ALIGN: return "MATOPT_ERR_ALIGN";
+    case MATOPT_ERR_DEVICE: return "MATOPT_ERR_DEVICE";
+    case MATOPT_ERR_HIP: return "MATOPT_ERR_HIP";
+    case MATOPT_ERR_INTERNAL: return "MATOPT_ERR_INTERNAL";
+  }
+  return "MATOPT_ERR_UNKNOWN";
+}
+
+const char* matopt_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t matopt_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count,
+                              matopt_dtype dt) {
+  if (count < 0 || (count > 0 && (!rows || !cols))) return 0;
+  if (dt != MATOPT_F32 && dt != MATOPT_BF16) return 0;
+  std::vector<Geo> geo;
+  for (int i = 0; i < count; ++i) {
+    if (check_shape(rows[i], cols[i], i) != MATOPT_OK) return 0;
+    geo.push_back(geometry(rows[i], cols[i], dt));
+  }
+  return layout(geo, dt).total;
+}
+
+matopt_status muon_step_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                float mu, float lr, int32_t ns_steps, float a, float b,
+                                float c, float eps, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  matopt_status st = check_common(count, dt);
+  if (st != MATOPT_OK) return st;
+  if (count == 0) return MATOPT_OK;
+  if (!mats) return fail(MATOPT_ERR_NULL, "mats is NULL");
+  if (!finite(mu) || !finite(lr)) return fail(MATOPT_ERR_PARAM, "non-finite mu or lr");
+  if ((st = check_ns_params(ns_steps, a, b, c, eps)) != MATOPT_OK) return st;
+  std::vector<Geo> geo;
+  std::vector<Span> spans;
+  std::vector<const void*> wv, gv, vv, ov;
+  const size_t es = esize(dt);
+  for (int i = 0; i < count; ++i) {
+    const matopt_mat& m = mats[i];
+    if (!m.w || !m.g || !m.v) return fail(MATOPT_ERR_NULL, "matrix " + std::to_string(i) + ": NULL pointer");
+    if ((st = check_shape(m.rows, m.cols, i)) != MATOPT_OK) return st;
+    if (!aligned16(m.w) || !aligned16(m.g) || !aligned16(m.v))
+      return fail(MATOPT_ERR_ALIGN, "matrix " + std::to_string(i) + ": pointer not 16-byte aligned");
+    const size_t bytes = (size_t)m.rows * m.cols * es;
+    const std::string tag = "matrix " + std::to_string(i);
+    spans.push_back({(uintptr_t)m.w, (uintptr_t)m.w + bytes, tag + " W"});
+    spans.push_back({(uintptr_t)m.g, (uintptr_t)m.g + bytes, tag + " G"});
+    spans.push_back({(uintptr_t)m.v, (uintptr_t)m.v + bytes, tag + " V"});
+    geo.push_back(geometry(m.rows, m.cols, dt));
+    wv.push_back(m.w);
+    gv.push_back(m.g);
+    vv.push_back(m.v);
+    ov.push_back(nullptr);
+  }
+  const size_t need = layout(geo, dt).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MATOPT_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                          std::to_string(workspace ? workspace_bytes : 0));
+  if (((uintptr_t)workspace & 255) != 0) return fail(MATOPT_ERR_ALIGN, "workspace not 256-byte aligned");
+  spans.push_back({(uintptr_t)workspace, (uintptr_t)workspace + need, "workspace"});
+  if ((st = check_overlap(spans)) != MATOPT_OK) return st;
+  int dev;
+  if ((st = check_device(&dev)) != MATOPT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+
+  PlanKey key{PK_MUON, (uint64_t)dt, (uint64_t)dev, (uint64_t)(uintptr_t)workspace, (uint64_t)count};
+  for (int i = 0; i < count; ++i) {
+    key.push_back((uint64_t)mats[i].rows);
+    key.push_back((uint64_t)mats[i].cols);
+    key.push_back((uint64_t)(uintptr_t)mats[i].w);
+    key.push_back((uint64_t)(uintptr_t)mats[i].g);
+    key.push_back((uint64_t)(uintptr_t)mats[i].v);
+  }
+  std::shared_ptr<Plan> plan;
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    plan = plan_lookup(key);
+    if (!plan) {
+      plan = std::make_shared<Plan>();
+      plan->device = dev;
+      if ((st = build_ns_plan(*plan, PK_MUON, dt, geo, wv, gv, vv, ov, workspace, s)) != MATOPT_OK) return st;
+      plan_insert(key, plan);
+    }
+  }
+  return run_ns(*plan, dt, true, mu, lr, ns_steps, a, b, c, eps, OUT_W_UPDATE, dt, s);
+}
+
+matopt_status ns_orthogonalize_batched(const void* const* x, void* const* o, const int64_t* rows,
+                                       const int64_t* cols, int32_t count, matopt_dtype in_dt,
+                                       matopt_dtype out_dt, int32_t ns_steps, float a, float b,
+                                       float c, float eps, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  matopt_status st = check_common(count, in_dt);
+  if (st != MATOPT_OK) return st;
+  if (out_dt != MATOPT_F32 && out_dt != MATOPT_BF16) return fail(MATOPT_ERR_DTYPE, "invalid out_dt");
+  if (count == 0) return MATOPT_OK;
+  if (!x || !o || !rows || !cols) return fail(MATOPT_ERR_NULL, "NULL argument array");
+  if ((st = check_ns_params(ns_steps, a, b, c, eps)) != MATOPT_OK) return st;
+  std::vector<Geo> geo;
+  std::vector<Span> spans;
+  std::vector<const void*> wv, gv, vv, ov;
+  const size_t es_in = esize(in_dt), es_out = esize(out_dt);
+  for (int i = 0; i < count; ++i) {
+    if (!x[i] || !o[i]) return fail(MATOPT_ERR_NULL, "matrix " + std::to_string(i) + ": NULL pointer");
+    if ((st = check_shape(rows[i], cols[i], i)) != MATOPT_OK) return st;
+    if (!aligned16(x[i]) || !aligned16(o[i]))
+      return fail(MATOPT_ERR_ALIGN, "matrix " + std::to_string(i) + ": pointer not 16-byte aligned");
+    const size_t n = (size_t)rows[i] * cols[i];
+    const std::string tag = "matrix " + std::to_string(i);
+    spans.push_back({(uintptr_t)x[i], (uintptr_t)x[i] + n * es_in, tag + " x"});
+    spans.push_back({(uintptr_t)o[i], (uintptr_t)o[i] + n * es_out, tag + " o"});
+    geo.push_back(geometry(rows[i], cols[i], in_dt));
+    wv.push_back(nullptr);
+    gv.push_back(nullptr);
+    vv.push_back(x[i]);
+    ov.push_back(o[i]);
+  }
+  const size_t need = layout(geo, in_dt).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MATOPT_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                          std::to_string(workspace ? workspace_bytes : 0));
+  if (((uintptr_t)workspace & 255) != 0) return fail(MATOPT_ERR_ALIGN, "workspace not 256-byte aligned");
+  spans.push_back({(uintptr_t)workspace, (uintptr_t)workspace + need, "workspace"});
+  if ((st = check_overlap(spans)) != MATOPT_OK) return st;
+  int dev;
+  if ((st = check_device(&dev)) != MATOPT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+
+  PlanKey key{PK_NS, (uint64_t)in_dt, (uint64_t)dev, (uint64_t)(uintptr_t)workspace, (uint64_t)count};
+  for (int i = 0; i < count; ++i) {
+    key.push_back((uint64_t)rows[i]);
+    key.push_back((uint64_t)cols[i]);
+    key.push_back((uint64_t)(uintptr_t)x[i]);
+    key.push_back((uint64_t)(uintptr_t)o[i]);
+  }
+  std::shared_ptr<Plan> plan;
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    plan = plan_lookup(key);
+    if (!plan) {
+      plan = std::make_shared<Plan>();
+      plan->device = dev;
+      if ((st = build_ns_plan(*plan, PK_NS, in_dt, geo, wv, gv, vv, ov, workspace, s)) != MATOPT_OK) return st;
+      plan_insert(key, plan);
+    }
+  }
+  return run_ns(*plan, in_dt, false, 0.f, 0.f, ns_steps, a, b, c, eps, OUT_O, out_dt, s);
+}
+
+matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt, float mu,
+                                float lr, float eps, void* stream) {
+  matopt_status st = check_common(count, dt);
+  if (st != MATOPT_OK) return st;
+  if (count == 0) return MATOPT_OK;
+  if (!mats) return fail(MATOPT_ERR_NULL, "mats is NULL");
+  if (!finite(mu) || !finite(lr) || !finite(eps) || eps < 0.f)
+    return fail(MATOPT_ERR_PARAM, "non-finite mu/lr/eps or eps < 0");
+  std::vector<Span> spans;
+  const size_t es = esize(dt);
+  for (int i = 0; i < count; ++i) {
+    const matopt_mat& m = mats[i];
+    if (!m.w || !m.g || !m.v) return fail(MATOPT_ERR_NULL, "matrix " + std::to_string(i) + ": NULL pointer");
+    if ((st = check_shape(m.rows, m.cols, i)) != MATOPT_OK) return st;
+    if (!aligned16(m.w) || !aligned16(m.g) || !aligned16(m.v))
+      return fail(MATOPT_ERR_ALIGN, "matrix " + std::to_string(i) + ": pointer not 16-byte aligned");
+    const size_t bytes = (size_t)m.rows * m.cols * es;
+    const std::string tag = "matrix " + std::to_string(i);
+    spans.push_back({(uintptr_t)m.w, (uintptr_t)m.w + bytes, tag + " W"});
+    spans.push_back({(uintptr_t)m.g, (uintptr_t)m.g + bytes, tag + " G"});
+    spans.push_back({(uintptr_t)m.v, (uintptr_t)m.v + bytes, tag + " V"});
+  }
+  if ((st = check_overlap(spans)) != MATOPT_OK) return st;
+  int dev;
+  if ((st = check_device(&dev)) != MATOPT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  PlanKey key{PK_RMNP, (uint64_t)dt, (uint64_t)dev, (uint64_t)count};
+  for (int i = 0; i < count; ++i) {
+    key.push_back((uint64_t)mats[i].rows);
+    key.push_back((uint64_t)mats[i].cols);
+    key.push_back((uint64_t)(uintptr_t)mats[i].w);
+    key.push_back((uint64_t)(uintptr_t)mats[i].g);
+    key.push_back((uint64_t)(uintptr_t)mats[i].v);
+  }
+  std::shared_ptr<Plan> plan;
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    plan = plan_lookup(key);
+    if (!plan) {
+      plan = std::make_shared<Plan>();
+      plan->device = dev;
+      if ((st = build_rmnp_plan(*plan, dt, mats, count, s)) != MATOPT_OK) return st;
+      plan_insert(key, plan);
+    }
+  }
+  RmnpParams rp{plan->d_mats, nullptr, mu, lr, eps};
+  for (const RmnpGroup& g : plan->rmnp) {
+    rp.tasks = at<RmnpTask>(plan->dbuf, g.off);
+    hipError_t e = timed(6, s, [&] { return launch_rmnp(dt, g.wpr, g.nch, rp, g.n, s); });
+    if (e != hipSuccess) return hip_fail("rmnp launch", e);
+  }
+  return MATOPT_OK;
+}
+
+matopt_status matopt_profile_enable(int32_t on) {
+  g_prof.store(on != 0);
+  return MATOPT_OK;
+}
+
+matopt_status matopt_profile_read(double* ms, int64_t* launches) {
+  if (!ms || !launches) return fail(MATOPT_ERR_NULL, "NULL output");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const ProfRec& r : g_prof_pending) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess) return hip_fail("profile event", e);
+    g_prof_ms[r.cls] += t;
+    g_prof_n[r.cls] += 1;
+    g_ev_free.push_back(r.a);
+    g_ev_free.push_back(r.b);
+  }
+  g_prof_pending.clear();
+  for (int k = 0; k < MATOPT_PROFILE_CLASSES; ++k) {
+    ms[k] = g_prof_ms[k];
+    launches[k] = g_prof_n[k];
+    g_prof_ms[k] = 0.0;
+    g_prof_n[k] = 0;
+  }
+  return MATOPT_OK;
+}
+
+}  // extern "C"

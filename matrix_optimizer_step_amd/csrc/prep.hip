@@ -1,0 +1,201 @@
+// Memory-bound kernels that open and (for ns_steps == 0) close the Muon step.
+//
+// prep_kernel      one 64x64 tile of the padded original-orientation matrix:
+//                  momentum V <- mu*V + G (blog post, section 1: heavy ball; one
+//                  rounding to storage: see Elem::fma_store), partial sum of squares of the stored V
+//                  (the Frobenius norm that opens the appendix's Newton-Schulz
+//                  routine), and the first iterate X0 written into the workspace
+//                  in X orientation (transposed through LDS when rows > cols,
+//                  the routine's transpose), zero in the padding.  X0 is the
+//                  stored V itself: the scale 1/(||V||+eps) is applied in float32
+//                  inside the first iteration's products, not rounded into X0.
+//                  Algorithmic HBM bytes per element: bf16 read G,V + write V,X0
+//                  = 8 (fp32: 16).
+// finalize_kernel  xs = 1/(sqrt(sum partials) + eps), one block per matrix, fixed
+//                  summation order (deterministic, batch independent).
+// scale_out_kernel ns_steps == 0: O = xs*V, written as O or applied to W.
+#include "common.hpp"
+#include "device_util.hpp"
+
+namespace matopt {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float block_sum4(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams P) {
+  using Tr = Elem<T>;
+  constexpr int E = Tr::E;              // elements per 16-byte chunk
+  constexpr int CPR = kPrepTile / E;    // chunks per tile row
+  constexpr int NCH = kPrepTile * kPrepTile / (kThreads * E);  // chunks per thread
+  __shared__ float tileT[kPrepTile][kPrepTile + 1];
+  __shared__ float red[4];
+
+  const PrepTile tile = P.tiles[blockIdx.x];
+  const MatDesc& d = P.mats[tile.mat];
+  const int64_t rows = d.rows, cols = d.cols;
+  const int r_base = tile.tr * kPrepTile, c_base = tile.tc * kPrepTile;
+  const bool vec = d.vec_ok != 0;
+  const bool transposed = d.transposed != 0;
+  const int64_t ldx = d.np;
+  T* __restrict__ x0 = (T*)d.x[0];
+
+  float vals[NCH][E];
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < NCH; ++p) {
+    const int q = threadIdx.x + kThreads * p;
+    const int rr = q / CPR, cc = (q % CPR) * E;
+    const int64_t r = r_base + rr, c = c_base + cc;
+    float vn[E];
+    if (r < rows && c < cols) {
+      const int64_t off = r * cols + c;
+      if (vec) {
+        float vv[E];
+        Tr::unpack(*(const uint4*)((const T*)d.v + off), vv);
+        if (P.momentum) {
+          float gg[E];
+          Tr::unpack(*(const uint4*)((const T*)d.g + off), gg);
+#pragma unroll
+          for (int e = 0; e < E; ++e) vn[e] = Tr::fma_store(P.mu, vv[e], gg[e]);
+          *(uint4*)((T*)d.v + off) = Tr::pack(vn);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) vn[e] = vv[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          vn[e] = 0.f;
+          if (c + e < cols) {
+            float vv = Tr::load1(d.v, off + e);
+            if (P.momentum) {
+              vv = Tr::fma_store(P.mu, vv, Tr::load1(d.g, off + e));
+              Tr::store1(d.v, off + e, vv);
+            }
+            vn[e] = vv;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) vn[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      ss = fmaf(vn[e], vn[e], ss);
+      vals[p][e] = vn[e];
+    }
+    if (!transposed) {
+      *(uint4*)(x0 + r * ldx + c) = Tr::pack(vn);
+    }
+  }
+
+  if (transposed) {
+#pragma unroll
+    for (int p = 0; p < NCH; ++p) {
+      const int q = threadIdx.x + kThreads * p;
+      const int rr = q / CPR, cc = (q % CPR) * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) tileT[rr][cc + e] = vals[p][e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NCH; ++p) {
+      const int q = threadIdx.x + kThreads * p;
+      const int xr = q / CPR;        // original column within the tile
+      const int xc = (q % CPR) * E;  // original row offset within the tile
+      float t[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) t[e] = tileT[xc + e][xr];
+      *(uint4*)(x0 + (int64_t)(c_base + xr) * ldx + r_base + xc) = Tr::pack(t);
+    }
+  }
+
+  const float tot = block_sum4(ss, red);
+  if (threadIdx.x == 0) d.partials[tile.idx] = tot;
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeParams P) {
+  __shared__ double red[4];
+  const MatDesc& d = P.mats[blockIdx.x];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < d.n_prep; i += kThreads) s += (double)d.partials[i];
+  s = wave_sum_d(s);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) red[w] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+    d.xs[0] = (float)(1.0 / (sqrt(tot) + (double)P.eps));
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void scale_out_kernel(ScaleOutParams P) {
+  using Tr = Elem<T>;
+  constexpr int E = Tr::E;
+  constexpr int CPR = kPrepTile / E;
+  constexpr int NCH = kPrepTile * kPrepTile / (kThreads * E);
+  const PrepTile tile = P.tiles[blockIdx.x];
+  const MatDesc& d = P.mats[tile.mat];
+  const int64_t rows = d.rows, cols = d.cols;
+  const float xs = d.xs[0];
+  const float step = -P.lr * d.upd_scale;
+#pragma unroll
+  for (int p = 0; p < NCH; ++p) {
+    const int q = threadIdx.x + kThreads * p;
+    const int64_t r = tile.tr * kPrepTile + q / CPR;
+    const int64_t c0 = tile.tc * kPrepTile + (q % CPR) * E;
+    if (r >= rows) continue;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t c = c0 + e;
+      if (c >= cols) break;
+      const int64_t off = r * cols + c;
+      const float o = xs * Tr::load1(d.v, off);
+      if (P.out_kind == OUT_O) {
+        store_any(d.o, P.out_dt, off, o);
+      } else {
+        Tr::store1(d.w, off, Tr::fma_store(step, o, Tr::load1(d.w, off)));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prep(int dt, const PrepParams& p, int n_tiles, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(prep_kernel<uint16_t>, dim3(n_tiles), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(prep_kernel<float>, dim3(n_tiles), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FinalizeParams& p, int count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3(count), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_out(int dt, const ScaleOutParams& p, int n_tiles, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(scale_out_kernel<uint16_t>, dim3(n_tiles), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(scale_out_kernel<float>, dim3(n_tiles), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace matopt

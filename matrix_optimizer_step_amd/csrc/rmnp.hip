@@ -1,0 +1,157 @@
+// RMNP comparator step, one fused memory-bound pass per row (blog post,
+// section 1: each row of the momentum divided by its L2 norm; appendix
+// rmnp_local: momentum in place, float32 row sums, update scaled by
+// sqrt(max(1, rows/cols))):
+//
+//   V_i <- mu*V_i + G_i            (one rounding to storage, stored once)
+//   n_i  = ||V_i||_2               (float32 sum of squares of the stored V_i)
+//   W_i <- W_i - lr*s * V_i / max(n_i, eps)   (one rounding)
+//
+// Register-resident variants keep the updated row in VGPRs between the norm
+// and the update, so each element moves 10 bytes (bf16: read G, V, W; write V,
+// W) -- the algorithmic minimum.  A row belongs to one wave (WPR = 1, four rows
+// per workgroup) or to a whole workgroup (WPR = 4); each lane holds NCH
+// 16-byte chunks.  The streaming variant (any width, scalar accesses) makes two
+// passes and recomputes the momentum in the second one; it serves rows wider
+// than the register capacity or widths that are not a multiple of the vector.
+//
+// Roofline: HBM bandwidth; algorithmic bytes per element 10 (bf16) / 20 (fp32).
+#include "common.hpp"
+#include "device_util.hpp"
+
+namespace matopt {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T, int WPR, int NCH>
+__global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
+  using Tr = Elem<T>;
+  constexpr int E = Tr::E;
+  constexpr int LPR = 64 * WPR;   // lanes per row
+  __shared__ float red[4];
+
+  const RmnpTask task = P.tasks[blockIdx.x];
+  const MatDesc& d = P.mats[task.mat];
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = task.row0 + (WPR == 1 ? wave : 0);
+  const int lr_idx = (WPR == 1 ? (threadIdx.x & 63) : threadIdx.x);
+  const bool active = row < d.rows;
+  const int64_t cols = d.cols;
+  const int64_t nchunks = cols / E;
+
+  T* vrow = (T*)d.v + row * cols;
+  const T* grow = (const T*)d.g + row * cols;
+  T* wrow = (T*)d.w + row * cols;
+
+  uint4 vreg[NCH], wreg[NCH];
+  float ss = 0.f;
+  if (active) {
+#pragma unroll
+    for (int p = 0; p < NCH; ++p) {
+      const int64_t ch = lr_idx + (int64_t)LPR * p;
+      if (ch < nchunks) {
+        const uint4 vv = *(const uint4*)(vrow + ch * E);
+        const uint4 gg = *(const uint4*)(grow + ch * E);
+        wreg[p] = *(const uint4*)(wrow + ch * E);
+        float fv[E], fg[E];
+        Tr::unpack(vv, fv);
+        Tr::unpack(gg, fg);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          fv[e] = Tr::fma_store(P.mu, fv[e], fg[e]);
+          ss = fmaf(fv[e], fv[e], ss);
+        }
+        vreg[p] = Tr::pack(fv);
+        *(uint4*)(vrow + ch * E) = vreg[p];
+      }
+    }
+  }
+  float tot = wave_sum(ss);
+  if (WPR > 1) {
+    if ((threadIdx.x & 63) == 0) red[wave] = tot;
+    __syncthreads();
+    tot = (red[0] + red[1]) + (red[2] + red[3]);
+  }
+  if (!active) return;
+  const float inv = 1.f / fmaxf(sqrtf(tot), P.eps);
+  const float step = -P.lr * d.upd_scale * inv;
+#pragma unroll
+  for (int p = 0; p < NCH; ++p) {
+    const int64_t ch = lr_idx + (int64_t)LPR * p;
+    if (ch < nchunks) {
+      float fv[E], fw[E];
+      Tr::unpack(vreg[p], fv);
+      Tr::unpack(wreg[p], fw);
+#pragma unroll
+      for (int e = 0; e < E; ++e) fw[e] = Tr::fma_store(step, fv[e], fw[e]);
+      *(uint4*)(wrow + ch * E) = Tr::pack(fw);
+    }
+  }
+}
+
+// Streaming two-pass variant: one row per workgroup, scalar accesses.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rmnp_stream_kernel(RmnpParams P) {
+  using Tr = Elem<T>;
+  __shared__ float red[4];
+  const RmnpTask task = P.tasks[blockIdx.x];
+  const MatDesc& d = P.mats[task.mat];
+  const int64_t row = task.row0;
+  const int64_t cols = d.cols;
+  T* vrow = (T*)d.v + row * cols;
+  const T* grow = (const T*)d.g + row * cols;
+  T* wrow = (T*)d.w + row * cols;
+  float ss = 0.f;
+  for (int64_t c = threadIdx.x; c < cols; c += kThreads) {
+    const float v = Tr::fma_store(P.mu, Tr::load1(vrow, c), Tr::load1(grow, c));
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.f / fmaxf(sqrtf(tot), P.eps);
+  const float step = -P.lr * d.upd_scale * inv;
+  for (int64_t c = threadIdx.x; c < cols; c += kThreads) {
+    const float v = Tr::fma_store(P.mu, Tr::load1(vrow, c), Tr::load1(grow, c));
+    Tr::store1(vrow, c, v);
+    Tr::store1(wrow, c, Tr::fma_store(step, v, Tr::load1(wrow, c)));
+  }
+}
+
+template <typename T>
+hipError_t launch_t(int wpr, int nch, const RmnpParams& p, int n, hipStream_t s) {
+  dim3 g(n), b(kThreads);
+#define MATOPT_RMNP_CASE(W, N)                                                   \
+  if (wpr == W && nch == N) {                                                    \
+    hipLaunchKernelGGL((rmnp_kernel<T, W, N>), g, b, 0, s, p);                   \
+    return hipGetLastError();                                                    \
+  }
+  MATOPT_RMNP_CASE(1, 1)
+  MATOPT_RMNP_CASE(1, 2)
+  MATOPT_RMNP_CASE(1, 4)
+  MATOPT_RMNP_CASE(1, 8)
+  MATOPT_RMNP_CASE(1, 16)
+  MATOPT_RMNP_CASE(4, 4)
+  MATOPT_RMNP_CASE(4, 8)
+  MATOPT_RMNP_CASE(4, 16)
+#undef MATOPT_RMNP_CASE
+  if (nch == 0) {
+    hipLaunchKernelGGL(rmnp_stream_kernel<T>, g, b, 0, s, p);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_rmnp(int dt, int wpr, int nch, const RmnpParams& p, int n_tasks,
+                       hipStream_t s) {
+  if (n_tasks <= 0) return hipSuccess;
+  return dt == DT_BF16 ? launch_t<uint16_t>(wpr, nch, p, n_tasks, s)
+                       : launch_t<float>(wpr, nch, p, n_tasks, s);
+}
+
+}  // namespace matopt
