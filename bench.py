@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rmnp", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (float32), the "
+                         "known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -140,6 +143,15 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f} s)")
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
     def step():
         mo.muon_step_batched(W, G, V, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps)

@@ -6,6 +6,24 @@
 
 namespace matopt {
 
+// Device memory is accessed through address-space-1 (global) pointers so that
+// loads and stores compile to global_* instructions: generic (flat) accesses
+// would also count against the LDS counter and make every LDS wait also wait
+// for outstanding HBM traffic.
+#define MATOPT_GAS __attribute__((address_space(1)))
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+  return *(const MATOPT_GAS T*)p;
+}
+template <typename T>
+__device__ __forceinline__ void gstore(void* p, T v) {
+  *(MATOPT_GAS T*)p = v;
+}
+
 // bfloat16 is handled as its 16-bit pattern.
 __device__ __forceinline__ float bf2f(uint32_t h16) {
   return __uint_as_float(h16 << 16);
@@ -48,30 +66,30 @@ __device__ __forceinline__ float hi_bf(uint32_t d) { return __uint_as_float(d & 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int E = 4;
-  __device__ static void unpack(const uint4& v, float* f) {
+  __device__ static void unpack(const u32x4& v, float* f) {
     f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
   }
-  __device__ static uint4 pack(const float* f) {
-    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
-                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+  __device__ static u32x4 pack(const float* f) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]),
+                 __float_as_uint(f[2]), __float_as_uint(f[3])};
   }
   // a*b + c rounded once to storage (float32 fma is exact-then-round)
   __device__ static float fma_store(float a, float b, float c) { return fmaf(a, b, c); }
   __device__ static float load1(const void* p, int64_t i) {
-    return ((const float*)p)[i];
+    return gload<float>((const float*)p + i);
   }
-  __device__ static void store1(void* p, int64_t i, float f) { ((float*)p)[i] = f; }
+  __device__ static void store1(void* p, int64_t i, float f) { gstore<float>((float*)p + i, f); }
 };
 template <> struct Elem<uint16_t> {  // bfloat16
   static constexpr int E = 8;
-  __device__ static void unpack(const uint4& v, float* f) {
+  __device__ static void unpack(const u32x4& v, float* f) {
     f[0] = lo_bf(v.x); f[1] = hi_bf(v.x); f[2] = lo_bf(v.y); f[3] = hi_bf(v.y);
     f[4] = lo_bf(v.z); f[5] = hi_bf(v.z); f[6] = lo_bf(v.w); f[7] = hi_bf(v.w);
   }
-  __device__ static uint4 pack(const float* f) {
-    return make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]),
-                      pack_bf2(f[4], f[5]), pack_bf2(f[6], f[7]));
+  __device__ static u32x4 pack(const float* f) {
+    return u32x4{pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]),
+                 pack_bf2(f[4], f[5]), pack_bf2(f[6], f[7])};
   }
   // a*b + c rounded once to bfloat16.  The float64 fma is exact whenever the
   // result fits 53 bits -- always for float32 * bfloat16 + bfloat16 (the
@@ -80,17 +98,17 @@ template <> struct Elem<uint16_t> {  // bfloat16
     return bf2f(f64_to_bf16(fma((double)a, (double)b, (double)c)));
   }
   __device__ static float load1(const void* p, int64_t i) {
-    return bf2f(((const uint16_t*)p)[i]);
+    return bf2f(gload<uint16_t>((const uint16_t*)p + i));
   }
   __device__ static void store1(void* p, int64_t i, float f) {
-    ((uint16_t*)p)[i] = (uint16_t)f2bf(f);
+    gstore<uint16_t>((uint16_t*)p + i, (uint16_t)f2bf(f));
   }
 };
 
 // Store n (<= 8) consecutive values of dtype dt at element index i of p.
 __device__ __forceinline__ void store_any(void* p, int dt, int64_t i, float f) {
-  if (dt == 1) ((uint16_t*)p)[i] = (uint16_t)f2bf(f);
-  else ((float*)p)[i] = f;
+  if (dt == 1) gstore<uint16_t>((uint16_t*)p + i, (uint16_t)f2bf(f));
+  else gstore<float>((float*)p + i, f);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

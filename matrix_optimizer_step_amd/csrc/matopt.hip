@@ -30,6 +30,7 @@
 
 #include "../../include/matopt.h"
 #include "common.hpp"
+#include "tile_schedule.hpp"
 
 using namespace matopt;
 
@@ -280,8 +281,7 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
   const int tile = gemm_tile(dt);
   std::vector<MatDesc> mats(count);
   std::vector<PrepTile> prep;
-  std::vector<GemmTile> k3, k4, k5;
-  std::vector<int64_t> k3c, k4c, k5c;
+  std::vector<TileUnit> u3, u4, u5;
   prep.reserve(L.n_prep);
   for (int i = 0; i < count; ++i) {
     const Geo& g = geo[i];
@@ -312,30 +312,12 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
     for (int tr = 0; tr < g.prep_tr; ++tr)
       for (int tc = 0; tc < g.prep_tc; ++tc) prep.push_back({i, tr, tc, idx++});
     const int tm = g.mp / tile, tn = g.np / tile;
-    for (int ti = 0; ti < tm; ++ti)
-      for (int tj = ti; tj < tm; ++tj) {
-        k3.push_back({i, ti, tj, 0});
-        k3c.push_back(g.np);
-        k4.push_back({i, ti, tj, 0});
-        k4c.push_back(g.mp);
-      }
-    for (int ti = 0; ti < tm; ++ti)
-      for (int tj = 0; tj < tn; ++tj) {
-        k5.push_back({i, ti, tj, 0});
-        k5c.push_back(g.mp);
-      }
+    units_triangle(i, tm, g.np, u3);
+    units_triangle(i, tm, g.mp, u4);
+    units_full(i, tm, tn, g.mp, u5);
   }
-  auto lpt = [](std::vector<GemmTile>& t, const std::vector<int64_t>& cost) {
-    std::vector<size_t> idx(t.size());
-    for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
-    std::stable_sort(idx.begin(), idx.end(), [&](size_t x, size_t y) { return cost[x] > cost[y]; });
-    std::vector<GemmTile> out(t.size());
-    for (size_t i = 0; i < idx.size(); ++i) out[i] = t[idx[i]];
-    t.swap(out);
-  };
-  lpt(k3, k3c);
-  lpt(k4, k4c);
-  lpt(k5, k5c);
+  static_assert(sizeof(TileRef) == sizeof(GemmTile), "tile record layout");
+  const std::vector<TileRef> k3 = xcd_schedule(u3), k4 = xcd_schedule(u4), k5 = xcd_schedule(u5);
 
   HostBuf hb;
   const size_t o_mats = hb.put(mats);

@@ -33,15 +33,15 @@ __device__ __forceinline__ void load_op(const OpSrc& o, int k0, float (*s)[PITCH
   const bool tr = o.mode == MODE_TRANS || (o.mode == MODE_SYM && (k0 / TM) < (o.r0 / TM));
   if (!tr) {
     const int row = t >> 2, kc = (t & 3) * 4;
-    const float4 v = *(const float4*)(o.ptr + (int64_t)(o.r0 + row) * o.ld + k0 + kc);
+    const f32x4 v = gload<f32x4>(o.ptr + (int64_t)(o.r0 + row) * o.ld + k0 + kc);
     s[kc + 0][row] = v.x;
     s[kc + 1][row] = v.y;
     s[kc + 2][row] = v.z;
     s[kc + 3][row] = v.w;
   } else {
     const int k = t >> 4, rc = (t & 15) * 4;
-    const float4 v = *(const float4*)(o.ptr + (int64_t)(k0 + k) * o.ld + o.r0 + rc);
-    *(float4*)&s[k][rc] = v;
+    const f32x4 v = gload<f32x4>(o.ptr + (int64_t)(k0 + k) * o.ld + o.r0 + rc);
+    *(f32x4*)&s[k][rc] = v;
   }
 }
 
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
   __shared__ __attribute__((aligned(16))) float qs[TK][PITCH];
 
   const GemmTile tile = P.tiles[blockIdx.x];
+  if (tile.mat < 0) return;   // idle entry padding an XCD stream
   const MatDesc d = P.mats[tile.mat];
   const int stage = P.stage;
   const int i0 = tile.ti * TM, j0 = tile.tj * TM;
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
     __syncthreads();
   }
 
-  const float xs = d.xs[0];
+  const float xs = gload<float>(d.xs);
   const float s_first = P.first ? xs : 1.f;
   const int64_t rows = d.rows, cols = d.cols;
   const float upd = -P.lr * d.upd_scale;
@@ -103,24 +104,24 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
     const float s2 = s_first * s_first;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      *(float4*)((float*)d.a + (ib + r) * mp + jb) =
-          make_float4(acc[r][0] * s2, acc[r][1] * s2, acc[r][2] * s2, acc[r][3] * s2);
+      gstore<f32x4>((float*)d.a + (ib + r) * mp + jb,
+                    f32x4{acc[r][0] * s2, acc[r][1] * s2, acc[r][2] * s2, acc[r][3] * s2});
     return;
   }
   if (stage == 1) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float4 ain = *(const float4*)((const float*)d.a + (ib + r) * mp + jb);
-      *(float4*)((float*)d.b + (ib + r) * mp + jb) =
-          make_float4(fmaf(P.b, ain.x, P.c * acc[r][0]), fmaf(P.b, ain.y, P.c * acc[r][1]),
-                      fmaf(P.b, ain.z, P.c * acc[r][2]), fmaf(P.b, ain.w, P.c * acc[r][3]));
+      const f32x4 ain = gload<f32x4>((const float*)d.a + (ib + r) * mp + jb);
+      gstore<f32x4>((float*)d.b + (ib + r) * mp + jb,
+                    f32x4{fmaf(P.b, ain.x, P.c * acc[r][0]), fmaf(P.b, ain.y, P.c * acc[r][1]),
+                          fmaf(P.b, ain.z, P.c * acc[r][2]), fmaf(P.b, ain.w, P.c * acc[r][3])});
     }
     return;
   }
   float val[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float4 xin = *(const float4*)(xcur + (ib + r) * np + jb);
+    const f32x4 xin = gload<f32x4>(xcur + (ib + r) * np + jb);
     val[r][0] = s_first * fmaf(P.a, xin.x, acc[r][0]);
     val[r][1] = s_first * fmaf(P.a, xin.y, acc[r][1]);
     val[r][2] = s_first * fmaf(P.a, xin.z, acc[r][2]);
@@ -129,8 +130,7 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
   if (P.out_kind == OUT_NEXT_X) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      *(float4*)(xnext + (ib + r) * np + jb) =
-          make_float4(val[r][0], val[r][1], val[r][2], val[r][3]);
+      gstore<f32x4>(xnext + (ib + r) * np + jb, f32x4{val[r][0], val[r][1], val[r][2], val[r][3]});
     return;
   }
   // Last iteration: original orientation (transposed back when rows > cols).
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
       if (P.out_kind == OUT_O) {
         store_any(d.o, P.out_dt, off, val[r][c]);
       } else {
-        float* w = (float*)d.w;
-        w[off] = fmaf(upd, val[r][c], w[off]);
+        float* w = (float*)d.w + off;
+        gstore<float>(w, fmaf(upd, val[r][c], gload<float>(w)));
       }
     }
 }

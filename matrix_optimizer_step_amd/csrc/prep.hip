@@ -61,13 +61,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams P) {
       const int64_t off = r * cols + c;
       if (vec) {
         float vv[E];
-        Tr::unpack(*(const uint4*)((const T*)d.v + off), vv);
+        Tr::unpack(gload<u32x4>((const T*)d.v + off), vv);
         if (P.momentum) {
           float gg[E];
-          Tr::unpack(*(const uint4*)((const T*)d.g + off), gg);
+          Tr::unpack(gload<u32x4>((const T*)d.g + off), gg);
 #pragma unroll
           for (int e = 0; e < E; ++e) vn[e] = Tr::fma_store(P.mu, vv[e], gg[e]);
-          *(uint4*)((T*)d.v + off) = Tr::pack(vn);
+          gstore<u32x4>((T*)d.v + off, Tr::pack(vn));
         } else {
 #pragma unroll
           for (int e = 0; e < E; ++e) vn[e] = vv[e];
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams P) {
       vals[p][e] = vn[e];
     }
     if (!transposed) {
-      *(uint4*)(x0 + r * ldx + c) = Tr::pack(vn);
+      gstore<u32x4>(x0 + r * ldx + c, Tr::pack(vn));
     }
   }
 
@@ -117,26 +117,26 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams P) {
       float t[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) t[e] = tileT[xc + e][xr];
-      *(uint4*)(x0 + (int64_t)(c_base + xr) * ldx + r_base + xc) = Tr::pack(t);
+      gstore<u32x4>(x0 + (int64_t)(c_base + xr) * ldx + r_base + xc, Tr::pack(t));
     }
   }
 
   const float tot = block_sum4(ss, red);
-  if (threadIdx.x == 0) d.partials[tile.idx] = tot;
+  if (threadIdx.x == 0) gstore<float>(d.partials + tile.idx, tot);
 }
 
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeParams P) {
   __shared__ double red[4];
   const MatDesc& d = P.mats[blockIdx.x];
   double s = 0.0;
-  for (int i = threadIdx.x; i < d.n_prep; i += kThreads) s += (double)d.partials[i];
+  for (int i = threadIdx.x; i < d.n_prep; i += kThreads) s += (double)gload<float>(d.partials + i);
   s = wave_sum_d(s);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) red[w] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
     const double tot = (red[0] + red[1]) + (red[2] + red[3]);
-    d.xs[0] = (float)(1.0 / (sqrt(tot) + (double)P.eps));
+    gstore<float>(d.xs, (float)(1.0 / (sqrt(tot) + (double)P.eps)));
   }
 }
 
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void scale_out_kernel(ScaleOutParams P) {
   const PrepTile tile = P.tiles[blockIdx.x];
   const MatDesc& d = P.mats[tile.mat];
   const int64_t rows = d.rows, cols = d.cols;
-  const float xs = d.xs[0];
+  const float xs = gload<float>(d.xs);
   const float step = -P.lr * d.upd_scale;
 #pragma unroll
   for (int p = 0; p < NCH; ++p) {

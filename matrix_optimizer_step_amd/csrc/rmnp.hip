@@ -45,16 +45,16 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
   const T* grow = (const T*)d.g + row * cols;
   T* wrow = (T*)d.w + row * cols;
 
-  uint4 vreg[NCH], wreg[NCH];
+  u32x4 vreg[NCH], wreg[NCH];
   float ss = 0.f;
   if (active) {
 #pragma unroll
     for (int p = 0; p < NCH; ++p) {
       const int64_t ch = lr_idx + (int64_t)LPR * p;
       if (ch < nchunks) {
-        const uint4 vv = *(const uint4*)(vrow + ch * E);
-        const uint4 gg = *(const uint4*)(grow + ch * E);
-        wreg[p] = *(const uint4*)(wrow + ch * E);
+        const u32x4 vv = gload<u32x4>(vrow + ch * E);
+        const u32x4 gg = gload<u32x4>(grow + ch * E);
+        wreg[p] = gload<u32x4>(wrow + ch * E);
         float fv[E], fg[E];
         Tr::unpack(vv, fv);
         Tr::unpack(gg, fg);
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
           ss = fmaf(fv[e], fv[e], ss);
         }
         vreg[p] = Tr::pack(fv);
-        *(uint4*)(vrow + ch * E) = vreg[p];
+        gstore<u32x4>(vrow + ch * E, vreg[p]);
       }
     }
   }
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
       Tr::unpack(wreg[p], fw);
 #pragma unroll
       for (int e = 0; e < E; ++e) fw[e] = Tr::fma_store(step, fv[e], fw[e]);
-      *(uint4*)(wrow + ch * E) = Tr::pack(fw);
+      gstore<u32x4>(wrow + ch * E, Tr::pack(fw));
     }
   }
 }

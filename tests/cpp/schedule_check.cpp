@@ -1,0 +1,70 @@
+// Host check of the grouped-launch tile schedule (tile_schedule.hpp).
+// Reads "tm tn k_gram k_apply" lines (one matrix each) from stdin and checks,
+// for the Gram/polynomial (triangle) and apply (full) tables:
+//   * every tile (ti <= tj, resp. every ti, tj) appears exactly once,
+//   * all tiles of one unit sit at positions of the same residue mod 8,
+//   * the largest XCD load exceeds the mean by at most one unit's cost.
+// Prints "ok <table sizes>" or the first violation; exit status 0 iff ok.
+#include <cstdio>
+#include <map>
+#include <set>
+#include <tuple>
+#include <vector>
+
+#include "tile_schedule.hpp"
+
+using namespace matopt;
+
+static int check(const std::vector<TileUnit>& units, const std::vector<TileRef>& table,
+                 const char* what) {
+  std::map<std::tuple<int, int, int>, int> pos;
+  for (size_t p = 0; p < table.size(); ++p) {
+    const TileRef& t = table[p];
+    if (t.mat < 0) continue;
+    auto key = std::make_tuple(t.mat, t.ti, t.tj);
+    if (pos.count(key)) { std::printf("%s: duplicate tile\n", what); return 1; }
+    pos[key] = (int)p;
+  }
+  size_t n = 0;
+  int64_t total = 0, maxunit = 0;
+  std::vector<int64_t> load(kXcds, 0);
+  for (const TileUnit& u : units) {
+    n += u.tiles.size();
+    total += u.cost;
+    maxunit = std::max(maxunit, u.cost);
+    std::set<int> res;
+    for (const TileRef& t : u.tiles) {
+      auto it = pos.find(std::make_tuple(t.mat, t.ti, t.tj));
+      if (it == pos.end()) { std::printf("%s: missing tile\n", what); return 1; }
+      res.insert(it->second % kXcds);
+    }
+    if (res.size() != 1) { std::printf("%s: unit split across XCDs\n", what); return 1; }
+    load[*res.begin()] += u.cost;
+  }
+  if (n != pos.size()) { std::printf("%s: tile count mismatch\n", what); return 1; }
+  if (table.size() % kXcds) { std::printf("%s: table not a multiple of 8\n", what); return 1; }
+  int64_t mx = 0;
+  for (int64_t l : load) mx = std::max(mx, l);
+  if (mx * kXcds > total + (int64_t)kXcds * maxunit) {
+    std::printf("%s: imbalance max %lld mean %lld unit %lld\n", what, (long long)mx,
+                (long long)(total / kXcds), (long long)maxunit);
+    return 1;
+  }
+  return 0;
+}
+
+int main() {
+  std::vector<TileUnit> tri, full;
+  int tm, tn;
+  long long kg, ka;
+  int mat = 0;
+  while (std::scanf("%d %d %lld %lld", &tm, &tn, &kg, &ka) == 4) {
+    units_triangle(mat, tm, kg, tri);
+    units_full(mat, tm, tn, ka, full);
+    ++mat;
+  }
+  const auto t1 = xcd_schedule(tri), t2 = xcd_schedule(full);
+  if (check(tri, t1, "triangle") || check(full, t2, "full")) return 1;
+  std::printf("ok %zu %zu\n", t1.size(), t2.size());
+  return 0;
+}

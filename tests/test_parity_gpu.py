@@ -290,9 +290,19 @@ def test_rmnp_step(mo, dtype):
         r, c = w.shape
         exp = oracle.round_storage(f64(w0) - oracle.f32_param(0.02) * oracle.update_scale(r, c) * u,
                                    dtype)
-        d = ulp_distance(w.cpu(), torch.from_numpy(exp).to(w.dtype))
-        assert d.max() <= 1, (w.shape, d.max())
-        assert (d == 0).mean() >= 0.99
+        if dtype == "bf16":
+            d = ulp_distance(w.cpu(), torch.from_numpy(exp).to(w.dtype))
+            assert d.max() <= 1, (w.shape, d.max())
+            assert (d == 0).mean() >= 0.99
+        else:
+            # float32: the row norm is summed in float32 (relative error ~1e-7
+            # of the update); where W - lr*s*u cancels towards zero an ulp of
+            # the result is far smaller than that, so bound the error by one
+            # ulp of the result plus 1e-6 of the update.
+            upd = np.abs(oracle.f32_param(0.02) * oracle.update_scale(r, c) * u)
+            err = np.abs(f64(w) - exp)
+            allowed = np.spacing(np.abs(exp).astype(np.float32)).astype(np.float64) + 1e-6 * upd
+            assert (err <= allowed).all(), (w.shape, float((err / allowed).max()))
 
 
 def test_rmnp_row_split_invariance_bitwise(mo):
