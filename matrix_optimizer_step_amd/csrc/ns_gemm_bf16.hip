@@ -221,6 +221,43 @@ __device__ __forceinline__ void stage_stripe(const f32x16 (&acc)[4][4], float* s
     }
 }
 
+// Final output of 4 consecutive original-orientation columns c0..c0+3 of row r:
+// O (float32 or bf16) or the fused weight update W <- W + upd * val rounded
+// once.  Vector accesses when the row is a whole number of 16-byte chunks and
+// the 4 columns are in range, element accesses at a ragged edge.
+template <int OUT>
+__device__ __forceinline__ void write_out4(const MatDesc& d, const GemmParams& P, int64_t r,
+                                           int64_t c0, const float (&v)[4], float upd) {
+  const int64_t cols = d.cols;
+  const int64_t off = r * cols + c0;
+  if (d.vec_ok && c0 + 3 < cols) {
+    if (OUT == OUT_O) {
+      if (P.out_dt == DT_F32) gstore<f32x4>((float*)d.o + off, f32x4{v[0], v[1], v[2], v[3]});
+      else gstore<u32x2>((uint16_t*)d.o + off, u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])});
+    } else {
+      uint16_t* w = (uint16_t*)d.w + off;
+      const u32x2 wo = gload<u32x2>(w);
+      const float w4[4] = {lo_bf(wo.x), hi_bf(wo.x), lo_bf(wo.y), hi_bf(wo.y)};
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = f64_to_bf16(fma((double)upd, (double)v[e], (double)w4[e]));
+      gstore<u32x2>(w, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (c0 + e >= cols) break;
+    if (OUT == OUT_O) {
+      store_any(d.o, P.out_dt, off + e, v[e]);
+    } else {
+      uint16_t* w = (uint16_t*)d.w + off + e;
+      const float wo = bf2f(gload<uint16_t>(w));
+      gstore<uint16_t>(w, (uint16_t)f64_to_bf16(fma((double)upd, (double)v[e], (double)wo)));
+    }
+  }
+}
+
 // Epilogue of one wave's 128 x 128 sub-tile, one 32-row stripe at a time (a
 // rolled loop: only the accumulator staging is specialised per stripe, which
 // keeps the kernel small enough for the instruction cache).  Each stripe is
@@ -281,21 +318,10 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
           gstore<u32x2>(out + i * ld_out + j, o);
         } else if (out_trans) {
           *(f32x4*)(stg + rr * EP_PITCH + c4) = val;   // transposed pass below
-        } else if (i < rows) {
+        } else if (i < rows && j < cols) {
           // original orientation == X orientation: row i, columns j..j+3
           const float vv[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (j + e >= cols) break;
-            const int64_t off = i * cols + j + e;
-            if (OUT == OUT_O) {
-              store_any(d.o, P.out_dt, off, vv[e]);
-            } else {
-              uint16_t* w = (uint16_t*)d.w + off;
-              const float wo = bf2f(gload<uint16_t>(w));
-              gstore<uint16_t>(w, (uint16_t)f64_to_bf16(fma((double)upd, (double)vv[e], (double)wo)));
-            }
-          }
+          write_out4<OUT>(d, P, i, j, vv, upd);
         }
       }
     }
@@ -309,21 +335,11 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
         const int ic = q & 7, jj = q >> 3;
         const int64_t jr = j0 + jj;
         const int64_t ic0 = ib + 4 * ic;
-        if (jr >= rows) continue;
+        if (jr >= rows || ic0 >= cols) continue;
+        float vv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t ccol = ic0 + e;
-          if (ccol >= cols) break;
-          const float val = stg[(4 * ic + e) * EP_PITCH + jj];
-          const int64_t off = jr * cols + ccol;
-          if (OUT == OUT_O) {
-            store_any(d.o, P.out_dt, off, val);
-          } else {
-            uint16_t* w = (uint16_t*)d.w + off;
-            const float wo = bf2f(gload<uint16_t>(w));
-            gstore<uint16_t>(w, (uint16_t)f64_to_bf16(fma((double)upd, (double)val, (double)wo)));
-          }
-        }
+        for (int e = 0; e < 4; ++e) vv[e] = stg[(4 * ic + e) * EP_PITCH + jj];
+        write_out4<OUT>(d, P, jr, ic0, vv, upd);
       }
     }
     __builtin_amdgcn_wave_barrier();
