@@ -2,32 +2,38 @@
 // batch of matrices: one launch per stage covers every matrix of the batch.
 //
 // The three products of one iteration (blog post, appendix Newton-Schulz
-// routine, written in factored form) all reduce to C[i][j] = sum_k P[i][k]Q[j][k]
-// with both operands staged in LDS as [row][k] tiles:
+// routine, written in factored form) all reduce to C[i][j] = sum_k P[i][k]Q[j][k]:
 //
 //   stage 0 (Gram)    A = s^2 * X X^T     P = Q = X rows (k contiguous in HBM)
 //                     only tiles ti <= tj are computed (A is symmetric).
 //   stage 1 (poly)    B = b*A + c*A A     P = Q = A rows; A A = A A^T.  Only the
 //                     upper tiles of A exist: a k-block left of the diagonal
-//                     block is read from the mirrored upper tile and transposed
-//                     on its way into LDS.  Only tiles ti <= tj are computed.
-//   stage 2 (apply)   X' = s*(a*X + B X)  P = B rows (mirrored reads as above),
-//                     Q = X^T rows: X is read k-row-major and transposed into
-//                     LDS.  Every tile is computed.
+//                     block is taken from the mirrored upper tile, i.e. read
+//                     k-major.  Only tiles ti <= tj are computed.
+//   stage 2 (apply)   X' = s*(a*X + B X)  P = B rows (mirrored blocks as above),
+//                     Q = X^T rows: X is read k-major.  Every tile is computed.
 //
 // s is the Frobenius scale 1/(||V||+eps) on the first iteration, 1 afterwards.
 //
-// Tile: 256 x 256 outputs per workgroup of 4 waves (each wave 128 x 128 =
-// 4 x 4 blocks of v_mfma_f32_32x32x16_bf16), K step 64, two LDS stages of
-// 2 x 256 x 64 bf16 (128 KB total).  LDS rows are 128 bytes; the 16-byte chunk
-// index is XOR-swizzled with (row >> 1) & 7 so that MFMA fragment reads (16
-// rows, one chunk), direct and transposed stores (two rows, 8 chunks each) are
-// free of bank conflicts, and the fragment address of every 32-row block is a
-// constant offset from one per-lane base.
+// Engine.  A 256 x 256 output tile per workgroup of 4 waves (each wave 128 x
+// 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, accumulators in AGPRs).  The
+// K loop runs in steps of 32 through NS = 5 LDS stages of 32 KB (one 256 x 32
+// tile per operand), filled by global_load_lds_dwordx4 (HBM -> LDS without
+// registers) three steps ahead of use.  An operand tile is stored as it lies in
+// HBM: row-major (k contiguous, 64-byte rows) when its rows are contiguous
+// along k, k-major (512-byte k rows) when it is read as a transpose.  MFMA
+// fragments come from ds_read_b128 (row-major) or from two ds_read_b64_tr_b16
+// (k-major: the LDS transpose read hands lane i of each 16-lane group element
+// i & 3 of the 64-bit chunks addressed by lanes 4e + (i >> 2), e = 0..3).
+// Both layouts are XOR-swizzled so that the 16 lanes of a 16-byte access or
+// the 32 lanes of an 8-byte access hit distinct LDS banks (64 banks of 4 B);
+// the DMA lanes pick their source addresses to realise the swizzle.
 //
-// Main loop: global loads of step t+1 are issued first, the 64 MFMAs of step t
-// run on double-buffered fragments, and the LDS stores of step t+1 are issued
-// between the second and third k16 sub-steps, while queued MFMAs execute.
+// One barrier per K step, placed between its two k16 sub-steps: before it each
+// wave waits for its own DMA of the next step (explicit vmcnt), after it the
+// DMA of a step three ahead is issued into the stage everyone has finished
+// with, and the next step's first fragments are read while the second half of
+// the current step's MFMAs runs.
 //
 // Epilogue: each wave stages its accumulators through its own LDS region
 // (float32) so that every global store is a contiguous row segment; the
@@ -46,117 +52,173 @@ namespace matopt {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define MATOPT_LDS __attribute__((address_space(3)))
 
-constexpr int BM = 256;            // tile rows == tile cols == symmetric block
-constexpr int BK = 64;             // K step
+constexpr int BM = 256;               // tile rows == tile cols == symmetric block
+constexpr int BK = 32;                // K step
+constexpr int NS = 5;                 // LDS stages
 constexpr int NTHR = 256;
-constexpr int OPB = BM * BK * 2;   // bytes of one operand tile in LDS (32 KB)
-constexpr int STG = 2 * OPB;       // one pipeline stage (P and Q)
-constexpr int LDS_BYTES = 2 * STG; // two stages
-constexpr int EP_PITCH = 132;      // float pitch of the epilogue staging rows
+constexpr int OPB = BM * BK * 2;      // bytes of one operand tile (16 KB)
+constexpr int STG = 2 * OPB;          // one stage: P then Q (32 KB)
+constexpr int LDS_BYTES = NS * STG;   // 160 KB
+constexpr int DMA_PER_STEP = 8;       // DMA instructions per wave per step (4 P + 4 Q)
+constexpr int EP_PITCH = 132;         // float pitch of the epilogue staging rows
 constexpr int EP_WAVE_BYTES = 32 * EP_PITCH * 4;
 static_assert(4 * EP_WAVE_BYTES <= LDS_BYTES, "epilogue staging must fit");
 
-// LDS has 64 banks of 4 bytes and serves 16 lanes of a 16-byte access per
-// cycle: even rows occupy banks 0-31, odd rows banks 32-63.  The chunk swizzle
-// (row >> 1) & 7 makes 16 consecutive rows at one logical chunk (an MFMA
-// fragment read) hit 16 distinct bank groups.
-__device__ __forceinline__ uint32_t lds_off(uint32_t row, uint32_t chunk) {
-  return row * 128u + ((chunk ^ ((row >> 1) & 7u)) << 4);
+// ---------------------------------------------------------------- LDS layouts
+// Row-major tile: 256 rows x 32 k = 64-byte rows of four 16-byte chunks; the
+// chunk index is XORed with (row >> 2) & 3.  Sixteen consecutive rows at one
+// logical chunk (an MFMA fragment read) land on 16 distinct bank groups.
+__device__ __forceinline__ uint32_t rm_off(uint32_t row, uint32_t chunk) {
+  return row * 64u + ((chunk ^ ((row >> 2) & 3u)) << 4);
 }
 
-struct OpRegs {
-  u32x4 r[8];
+// k-major tile: 32 k rows x 256 operand rows = 512-byte k rows of eight 64-byte
+// units; the unit index is XORed with (k & 3).  Four consecutive k rows at one
+// logical unit land in the four distinct 64-byte bank quarters.
+__device__ __forceinline__ uint32_t km_off(uint32_t k, uint32_t col) {
+  return k * 512u + ((((col >> 5) ^ (k & 3u)) & 7u) << 6) + ((col & 31u) << 1);
+}
+
+// DMA of one operand tile for one K step (k0..k0+31), 4 instructions per wave.
+// Each instruction writes 1 KB of LDS at dst + 16*lane; lane L therefore loads
+// the 16 source bytes that belong at that (swizzled) position.
+//   row-major: block b covers rows 16b..16b+15; lane L -> row 16b + L/4,
+//              logical chunk (L & 3) ^ ((L >> 4) & 3).
+//   k-major:   block b covers k rows 2b, 2b+1; lane L -> k row 2b + L/32, unit
+//              ((L & 31) >> 2) ^ ((2b + L/32) & 3), 16-byte piece L & 3.
+// Addresses are a wave-uniform 64-bit base plus a 32-bit lane offset relative
+// to the tile origin (so that the load takes its base from scalar registers).
+struct OperandDma {
+  const char* org_rm;    // row-major source: byte address of element (r0, 0)
+  const char* org_km;    // k-major source: byte address of stored element (0, r0)
+  uint32_t ldb;          // row pitch in bytes
+  uint32_t off_rm;       // lane offset, row-major blocks
+  uint32_t off_km0;      // lane offset, k-major blocks with b even
+  uint32_t off_km1;      // lane offset, k-major blocks with b odd
+  int t_km;              // number of leading K steps read k-major
+
+  __device__ void init(const uint16_t* src, int64_t ld, int r0, int tkm, int lane) {
+    org_rm = (const char*)(src + (int64_t)r0 * ld);
+    org_km = (const char*)(src + r0);
+    ldb = (uint32_t)(ld * 2);
+    t_km = tkm;
+    off_rm = (uint32_t)(lane >> 2) * ldb + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    // (2b + L/32) & 3 is L/32 for even b and 2 + L/32 for odd b
+    const uint32_t lo = (uint32_t)(lane >> 5) * ldb + 16u * (lane & 3);
+    off_km0 = lo + 64u * (((lane & 31) >> 2) ^ (lane >> 5));
+    off_km1 = lo + 64u * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
+  }
 };
 
-// Rows r0..r0+255 of a row-major matrix, k columns k0..k0+63.  Thread t loads
-// 16-byte chunk (t & 7) of rows (t >> 3) + 32q.
-__device__ __forceinline__ void load_direct(const uint16_t* src, int64_t ld, int r0, int k0,
-                                            OpRegs& R) {
-  const int t = threadIdx.x;
-  const uint16_t* p = src + (int64_t)(r0 + (t >> 3)) * ld + k0 + (t & 7) * 8;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) R.r[q] = gload<u32x4>(p + (int64_t)(32 * q) * ld);
+template <int Q>
+__device__ __forceinline__ void dma_block(const OperandDma& o, bool km, int t, uint8_t* tile,
+                                          int wave) {
+  const int b = 4 * wave + Q;
+  const char* base = km ? o.org_km + (int64_t)(t * BK + 2 * b) * o.ldb
+                        : o.org_rm + (int64_t)(16 * b) * o.ldb + t * BK * 2;   // wave-uniform
+  // per-lane offset, chosen arithmetically (km is uniform)
+  const uint32_t kmoff = (Q & 1) ? o.off_km1 : o.off_km0;
+  const uint32_t off = o.off_rm ^ ((o.off_rm ^ kmoff) & (km ? 0xffffffffu : 0u));
+  __builtin_amdgcn_global_load_lds((const MATOPT_GAS void*)(base + off),
+                                   (MATOPT_LDS void*)(tile + 1024 * b), 16, 0, 0);
 }
 
-__device__ __forceinline__ void store_direct(uint8_t* lds, const OpRegs& R) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) *(u32x4*)(lds + lds_off((t >> 3) + 32 * q, t & 7)) = R.r[q];
+__device__ __forceinline__ void dma_op(const OperandDma& o, int t, uint8_t* tile, int wave) {
+  const bool km = t < o.t_km;
+  dma_block<0>(o, km, t, tile, wave);
+  dma_block<1>(o, km, t, tile, wave);
+  dma_block<2>(o, km, t, tile, wave);
+  dma_block<3>(o, km, t, tile, wave);
 }
 
-// Operand rows r0..r0+255 taken from the COLUMNS of rows k0..k0+63 of a
-// row-major matrix (i.e. the transpose).  Thread t = (b = t & 7, a = t >> 3)
-// loads the 8x8 block k0+8b.., r0+8a.. (eight 16-byte row segments; one load
-// instruction covers 8 rows x 128 contiguous bytes per wave).
-__device__ __forceinline__ void load_trans(const uint16_t* src, int64_t ld, int r0, int k0,
-                                           OpRegs& R) {
-  const int t = threadIdx.x;
-  const uint16_t* p = src + (int64_t)(k0 + 8 * (t & 7)) * ld + r0 + 8 * (t >> 3);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) R.r[e] = gload<u32x4>(p + (int64_t)e * ld);
+__device__ __forceinline__ void dma_step(const OperandDma& p, const OperandDma& q, int t,
+                                         uint8_t* stage, int wave) {
+  dma_op(p, t, stage, wave);
+  dma_op(q, t, stage + OPB, wave);
 }
 
-// 8x8 transpose of 16-bit elements: R.r[e] holds k = 8b+e for operand rows
-// 8a..8a+7; output row 8a+c gets k = 8b..8b+7 as one 16-byte LDS chunk b.
-// Eight consecutive lanes write the 8 chunks of one row; lanes with odd a
-// write rows in the order c ^ 1, so the two 8-lane halves of a 16-lane group
-// land in opposite bank halves (conflict free).
-__device__ __forceinline__ void store_trans(uint8_t* lds, const OpRegs& R) {
-  const int t = threadIdx.x;
-  const int a = t >> 3, b = t & 7;
-  const uint32_t flip = (uint32_t)(a & 1);
-  const uint32_t sel_even = flip ? 0x07060302u : 0x05040100u;
-  const uint32_t sel_odd = flip ? 0x05040100u : 0x07060302u;
+// Per-lane LDS offsets of the MFMA fragments (relative to the wave's operand
+// row origin inside an operand tile).  A fragment covers 32 operand rows and a
+// k16 sub-step kk: lane l holds row (l & 31), k = 16kk + 8(l >> 5) .. +7.
+//   row-major: one ds_read_b128 at rm_off(row, 2kk + (l >> 5)); the 32-row
+//              block bb adds 2048*bb (the swizzle depends on row & 12 only).
+//   k-major:   two ds_read_b64_tr_b16.  16-lane group G covers rows
+//              16(G & 1) .. +15 and k rows 16kk + 8(G >> 1) .. +7; lane c = 4e + h
+//              of the group points at k row (.. + e) and rows +4h .. +4h+3 (and
+//              k row + 4 for the second read), so lane c receives row +c at 4
+//              consecutive k.  The unit swizzle (bb ^ e) differs per lane and
+//              block, hence one offset per block; kk and the second read are
+//              immediates (8192*kk, 2048).
+struct FragOffsets {
+  uint32_t rm[2];   // by kk
+  uint32_t km[4];   // by block bb (kk = 0, first read)
+  __device__ void init(int lane) {
+    const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? sel_odd : sel_even;   // row 8a + (c ^ flip)
-    const int d = c >> 1;
-    u32x4 o;
-    o.x = __builtin_amdgcn_perm(R.r[1][d], R.r[0][d], sel);
-    o.y = __builtin_amdgcn_perm(R.r[3][d], R.r[2][d], sel);
-    o.z = __builtin_amdgcn_perm(R.r[5][d], R.r[4][d], sel);
-    o.w = __builtin_amdgcn_perm(R.r[7][d], R.r[6][d], sel);
-    *(u32x4*)(lds + lds_off(8 * a + (c ^ flip), b)) = o;
+    for (int kk = 0; kk < 2; ++kk) rm[kk] = rm_off(r, 2 * kk + hi);
+    const int G = lane >> 4, c = lane & 15, e = c >> 2, h = c & 3;
+    const int kr = 8 * (G >> 1) + e;
+    const int col = 16 * (G & 1) + 4 * h;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) km[bb] = kr * 512 + ((bb ^ e) << 6) + 2 * col;
+  }
+};
+
+template <bool KM>
+__device__ __forceinline__ bf16x8 frag(const uint8_t* tile, int wo, int bb, int kk,
+                                       const FragOffsets& fo) {
+  if (!KM) {
+    return *(const bf16x8*)(tile + wo * 64 + 2048 * bb + fo.rm[kk]);
+  } else {
+    // wo is a multiple of 128: its unit bits (wo >> 5) never meet the swizzle
+    const uint8_t* base = tile + (wo >> 5) * 64 + fo.km[bb] + 8192 * kk;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base + 2048));
+    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
   }
 }
-
-struct Operands {
-  const uint16_t* p;   // P source
-  const uint16_t* q;   // Q source
-  int64_t ldp, ldq;
-  int rp0, rq0;        // operand row origins (i0, j0)
-};
 
 struct WaveGeo {
   int wi0, wj0, frow, fkc;
 };
 
-// MFMA fragments of k16 sub-step kk: P rows wi0 + 32bi + (lane & 31) and Q rows
-// wj0 + 32bj + (lane & 31), k chunk 2kk + (lane >> 5).
-__device__ __forceinline__ void read_frags(const uint8_t* base, int kk, const WaveGeo& g,
+template <bool PKM, bool QKM>
+__device__ __forceinline__ void read_frags_t(const uint8_t* stage, int kk, const WaveGeo& g,
+                                             const FragOffsets& fo, bf16x8 (&p)[4],
+                                             bf16x8 (&q)[4]) {
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) p[bi] = frag<PKM>(stage, g.wi0, bi, kk, fo);
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) q[bj] = frag<QKM>(stage + OPB, g.wj0, bj, kk, fo);
+}
+
+// Operand modes that occur: stage 0 reads both operands row-major; stage 1
+// reads P k-major for t < i0/BK and Q k-major for t < j0/BK with i0 <= j0;
+// stage 2 always reads Q (X) k-major.
+template <int STAGE>
+__device__ __forceinline__ void read_frags(int t, int tP, int tQ, const uint8_t* stage, int kk,
+                                           const WaveGeo& g, const FragOffsets& fo,
                                            bf16x8 (&p)[4], bf16x8 (&q)[4]) {
-#pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
-    p[bi] = *(const bf16x8*)(base + lds_off(g.wi0 + 32 * bi + g.frow, 2 * kk + g.fkc));
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj)
-    q[bj] = *(const bf16x8*)(base + OPB + lds_off(g.wj0 + 32 * bj + g.frow, 2 * kk + g.fkc));
+  if (STAGE == 0) {
+    read_frags_t<false, false>(stage, kk, g, fo, p, q);
+  } else if (STAGE == 1) {
+    if (t < tP) read_frags_t<true, true>(stage, kk, g, fo, p, q);
+    else if (t < tQ) read_frags_t<false, true>(stage, kk, g, fo, p, q);
+    else read_frags_t<false, false>(stage, kk, g, fo, p, q);
+  } else {
+    if (t < tP) read_frags_t<true, true>(stage, kk, g, fo, p, q);
+    else read_frags_t<false, true>(stage, kk, g, fo, p, q);
+  }
 }
 
-__device__ __forceinline__ void op_load_rt(bool tr, const uint16_t* src, int64_t ld, int r0,
-                                           int k0, OpRegs& R) {
-  if (tr) load_trans(src, ld, r0, k0, R);
-  else load_direct(src, ld, r0, k0, R);
-}
-
-__device__ __forceinline__ void op_store_rt(bool tr, uint8_t* lds, const OpRegs& R) {
-  if (tr) store_trans(lds, R);
-  else store_direct(lds, R);
-}
-
-// 16 MFMAs of one k16 sub-step.
+// 16 MFMAs of one k16 sub-step (operands swapped: acc[bi][bj] holds C^T blocks,
+// i.e. 4 consecutive output columns per register group).
 __device__ __forceinline__ void mfma16(f32x16 (&acc)[4][4], const bf16x8 (&p)[4],
                                        const bf16x8 (&q)[4]) {
 #pragma unroll
@@ -166,42 +228,31 @@ __device__ __forceinline__ void mfma16(f32x16 (&acc)[4][4], const bf16x8 (&p)[4]
       acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[bj], p[bi], acc[bi][bj], 0, 0, 0);
 }
 
-// The 64 MFMAs of one K step on LDS stage `cur`.  Fragments of sub-step kk+1 are
-// read while the MFMAs of sub-step kk run.  When `store`, the staged operand
-// registers are written to LDS stage `nxt` between sub-steps 1 and 2 (the
-// writes drain while the queued MFMAs execute).  Scheduling fences keep every
-// sub-step's loads next to its MFMAs, which bounds the registers in flight.
-__device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], const uint8_t* cur, uint8_t* nxt,
-                                      bool store, bool tp, bool tq, const OpRegs& rp,
-                                      const OpRegs& rq, const WaveGeo& g) {
-  bf16x8 pa[4], qa[4], pb[4], qb[4];
-  read_frags(cur, 0, g, pa, qa);
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags(cur, 1, g, pb, qb);
-  mfma16(acc, pa, qa);
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags(cur, 2, g, pa, qa);
-  mfma16(acc, pb, qb);
-  __builtin_amdgcn_sched_barrier(0);
-  if (store) {
-    op_store_rt(tp, nxt, rp);
-    op_store_rt(tq, nxt + OPB, rq);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags(cur, 3, g, pb, qb);
-  mfma16(acc, pa, qa);
-  __builtin_amdgcn_sched_barrier(0);
-  mfma16(acc, pb, qb);
-  __builtin_amdgcn_sched_barrier(0);
+// Wait until at most n_steps DMA steps of this wave are still in flight (the
+// wait count must be an immediate).
+__device__ __forceinline__ void wait_dma(int n_steps) {
+  static_assert(NS - 2 <= 3 && DMA_PER_STEP == 8, "wait table");
+  if (n_steps <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (n_steps == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n_steps == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every DMA
+// in flight); LDS ordering is explicit through wait_dma and lgkmcnt waits.
+__device__ __forceinline__ void bar() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void prefetch_stripe(const uint16_t* src, int64_t ld, int64_t row0,
                                                 int64_t col0, int lane, u32x2 (&dst)[16]) {
+  // lane q = lane + 64p reads row row0 + q/32, columns col0 + 4(q & 31) .. +3
+  const char* base = (const char*)(src + row0 * ld + col0);
+  const uint32_t off = (uint32_t)(((lane >> 5) * ld + (lane & 31) * 4) * 2);
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const int q = lane + 64 * p;
-    dst[p] = gload<u32x2>(src + (row0 + (q >> 5)) * ld + col0 + (q & 31) * 4);
-  }
+  for (int p = 0; p < 16; ++p) dst[p] = gload<u32x2>(base + (int64_t)(4 * p) * ld + off);
 }
 
 // Stage acc[BI][*] (32 rows of the wave's 128 x 128 sub-tile) into the wave's
@@ -350,12 +401,34 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
   }
 }
 
+// One K step (not the last).  The three stage pointers name distinct stages
+// (NS >= 3); declaring them restrict tells the compiler that the fragment reads
+// never alias the DMA writes issued here, so it adds no wait of its own for
+// the DMA before an LDS read -- the ordering comes from wait_dma and bar.
+template <int STAGE>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], bf16x8 (&pa)[4], bf16x8 (&qa)[4],
+                                      bf16x8 (&pb)[4], bf16x8 (&qb)[4], int t, int nk,
+                                      const OperandDma& dp, const OperandDma& dq,
+                                      const WaveGeo& g, const FragOffsets& fo, int wave,
+                                      const uint8_t* __restrict__ cur,
+                                      const uint8_t* __restrict__ nxt,
+                                      uint8_t* __restrict__ dma_dst) {
+  read_frags<STAGE>(t, dp.t_km, dq.t_km, cur, 1, g, fo, pb, qb);
+  mfma16(acc, pa, qa);
+  // every wave's DMA of step t+1 has landed; step t-1's stage is free
+  wait_dma(min(NS - 3, nk - 2 - t));
+  bar();
+  if (t + NS - 1 < nk) dma_step(dp, dq, t + NS - 1, dma_dst, wave);
+  read_frags<STAGE>(t + 1, dp.t_km, dq.t_km, nxt, 0, g, fo, pa, qa);
+  mfma16(acc, pb, qb);
+}
+
 // One kernel per stage (and, for apply, per output kind), so that each carries
 // only its own operand modes and epilogue.
 template <int STAGE, int OUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_bf16_kernel(GemmParams P) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
   const GemmTile tile = P.tiles[blockIdx.x];
   if (tile.mat < 0) return;   // idle entry padding an XCD stream
@@ -365,34 +438,34 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   const uint16_t* xcur = (const uint16_t*)(P.cur ? d.x[1] : d.x[0]);
   uint16_t* xnext = (uint16_t*)(P.cur ? d.x[0] : d.x[1]);
 
-  // Operands and the number of leading K steps each one is read transposed:
-  // symmetric storage transposes the k-blocks left of the operand's row block.
-  Operands op;
-  int K, tP, tQ;
+  // Operands; symmetric storage reads the k-blocks left of the operand's row
+  // block from the mirrored tile (k-major).
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  OperandDma dp, dq;
+  int K;
   if (STAGE == 0) {
-    op = {xcur, xcur, np, np, i0, j0};
+    dp.init(xcur, np, i0, 0, lane);
+    dq.init(xcur, np, j0, 0, lane);
     K = (int)np;
-    tP = tQ = 0;
   } else if (STAGE == 1) {
-    op = {(const uint16_t*)d.a, (const uint16_t*)d.a, mp, mp, i0, j0};
+    dp.init((const uint16_t*)d.a, mp, i0, i0 / BK, lane);
+    dq.init((const uint16_t*)d.a, mp, j0, j0 / BK, lane);
     K = (int)mp;
-    tP = i0 / BK;
-    tQ = j0 / BK;
   } else {
-    op = {(const uint16_t*)d.b, xcur, mp, np, i0, j0};
+    dp.init((const uint16_t*)d.b, mp, i0, i0 / BK, lane);
+    dq.init(xcur, np, j0, (int)mp / BK, lane);
     K = (int)mp;
-    tP = i0 / BK;
-    tQ = K / BK;
   }
   const int nk = K / BK;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   WaveGeo g;
   g.wi0 = (wave >> 1) * 128;   // wave sub-tile origin (rows)
   g.wj0 = (wave & 1) * 128;    // wave sub-tile origin (cols)
-  g.frow = lane & 31;          // fragment row within a 32-block
-  g.fkc = lane >> 5;           // fragment k chunk (0/1) within a k16 step
+  g.frow = lane & 31;
+  g.fkc = lane >> 5;
+  FragOffsets fo;
+  fo.init(lane);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -402,32 +475,25 @@ void ns_gemm_bf16_kernel(GemmParams P) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
-  // prologue: step 0 into stage 0.  Operand P (Q) is read transposed for the
-  // first tP (tQ) K steps.
-  OpRegs rp, rq;
-  op_load_rt(tP > 0, op.p, op.ldp, op.rp0, 0, rp);
-  op_load_rt(tQ > 0, op.q, op.ldq, op.rq0, 0, rq);
-  op_store_rt(tP > 0, lds, rp);
-  op_store_rt(tQ > 0, lds + OPB, rq);
-  __syncthreads();
+  // prologue: DMA steps 0 .. NS-2, wait for step 0, read its first fragments
+  for (int t = 0; t < NS - 1 && t < nk; ++t) dma_step(dp, dq, t, lds + t * STG, wave);
+  wait_dma(min(NS - 2, nk - 1));
+  bar();
+  bf16x8 pa[4], qa[4], pb[4], qb[4];
+  read_frags<STAGE>(0, dp.t_km, dq.t_km, lds, 0, g, fo, pa, qa);
 
-  // steps 1..nk-1: load step t, compute step t-1
-  for (int t = 1; t < nk; ++t) {
-    const bool tp = t < tP, tq = t < tQ;
-    op_load_rt(tp, op.p, op.ldp, op.rp0, t * BK, rp);
-    op_load_rt(tq, op.q, op.ldq, op.rq0, t * BK, rq);
-    __builtin_amdgcn_sched_barrier(0);
-    kstep(acc, lds + ((t - 1) & 1) * STG, lds + (t & 1) * STG, true, tp, tq, rp, rq, g);
-    __syncthreads();
-  }
-
-  // last K step; prefetch the first epilogue stripe meanwhile
+  for (int t = 0; t + 1 < nk; ++t)
+    kstep<STAGE>(acc, pa, qa, pb, qb, t, nk, dp, dq, g, fo, wave, lds + (t % NS) * STG,
+                 lds + ((t + 1) % NS) * STG, lds + ((t + NS - 1) % NS) * STG);
+  // last K step; the first epilogue stripe is fetched meanwhile
   const int64_t ep_ld = STAGE == 1 ? mp : np;
   const uint16_t* ep_src = STAGE == 1 ? (const uint16_t*)d.a : xcur;
   u32x2 ecur[16];
+  read_frags<STAGE>(nk - 1, dp.t_km, dq.t_km, lds + ((nk - 1) % NS) * STG, 1, g, fo, pb, qb);
+  mfma16(acc, pa, qa);
   if (STAGE != 0) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
-  kstep(acc, lds + ((nk - 1) & 1) * STG, nullptr, false, false, false, rp, rq, g);
-  __syncthreads();
+  mfma16(acc, pb, qb);
+  bar();   // all fragment reads done: the stages become epilogue staging
 
   uint16_t* out = STAGE == 0 ? (uint16_t*)d.a : STAGE == 1 ? (uint16_t*)d.b : xnext;
   const int64_t ld_out = STAGE == 2 ? np : mp;
