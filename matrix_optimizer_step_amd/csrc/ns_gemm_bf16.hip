@@ -5,35 +5,36 @@
 // routine, written in factored form) all reduce to C[i][j] = sum_k P[i][k]Q[j][k]:
 //
 //   stage 0 (Gram)    A = s^2 * X X^T     P = Q = X rows (k contiguous in HBM)
-//                     only tiles ti <= tj are computed (A is symmetric).
-//   stage 1 (poly)    B = b*A + c*A A     P = Q = A rows; A A = A A^T.  Only the
-//                     upper tiles of A exist: a k-block left of the diagonal
-//                     block is taken from the mirrored upper tile, i.e. read
-//                     k-major.  Only tiles ti <= tj are computed.
-//   stage 2 (apply)   X' = s*(a*X + B X)  P = B rows (mirrored blocks as above),
-//                     Q = X^T rows: X is read k-major.  Every tile is computed.
+//   stage 1 (poly)    B = b*A + c*A A     P = Q = A rows = A columns (symmetric)
+//   stage 2 (apply)   X' = s*(a*X + B X)  P = B columns (= rows), Q = X columns
 //
 // s is the Frobenius scale 1/(||V||+eps) on the first iteration, 1 afterwards.
+// A and B are symmetric: only tiles ti <= tj are computed, and the epilogue
+// writes each off-diagonal tile twice, as itself and transposed into the
+// mirror position, so both are stored whole and bitwise symmetric.  Stages 1
+// and 2 then read every operand through its columns (k-major: each k row of
+// an operand tile is 512 contiguous bytes in HBM); stage 0 reads X rows
+// (row-major, 64 contiguous bytes per row and K step).  Each stage therefore
+// has one fixed operand layout and a straight-line K step.
 //
 // Engine.  A 256 x 256 output tile per workgroup of 4 waves (each wave 128 x
 // 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, accumulators in AGPRs).  The
 // K loop runs in steps of 32 through NS = 5 LDS stages of 32 KB (one 256 x 32
 // tile per operand), filled by global_load_lds_dwordx4 (HBM -> LDS without
-// registers) three steps ahead of use.  An operand tile is stored as it lies in
-// HBM: row-major (k contiguous, 64-byte rows) when its rows are contiguous
-// along k, k-major (512-byte k rows) when it is read as a transpose.  MFMA
-// fragments come from ds_read_b128 (row-major) or from two ds_read_b64_tr_b16
-// (k-major: the LDS transpose read hands lane i of each 16-lane group element
-// i & 3 of the 64-bit chunks addressed by lanes 4e + (i >> 2), e = 0..3).
-// Both layouts are XOR-swizzled so that the 16 lanes of a 16-byte access or
-// the 32 lanes of an 8-byte access hit distinct LDS banks (64 banks of 4 B);
-// the DMA lanes pick their source addresses to realise the swizzle.
+// registers) three steps ahead of use, in the layout the tile has in HBM.
+// MFMA fragments come from ds_read_b128 (row-major) or from two
+// ds_read_b64_tr_b16 (k-major: the LDS transpose read hands lane i of each
+// 16-lane group element i & 3 of the 64-bit chunks addressed by lanes
+// 4e + (i >> 2), e = 0..3).  Both layouts are XOR-swizzled so that the 16
+// lanes of a 16-byte access or the 32 lanes of an 8-byte access hit distinct
+// LDS banks (64 banks of 4 B); the DMA lanes pick their source addresses to
+// realise the swizzle.
 //
 // One barrier per K step, placed between its two k16 sub-steps: before it each
 // wave waits for its own DMA of the next step (explicit vmcnt), after it the
 // DMA of a step three ahead is issued into the stage everyone has finished
-// with, and the next step's first fragments are read while the second half of
-// the current step's MFMAs runs.
+// with.  The fragment reads of the next sub-step are interleaved with the
+// MFMAs of the current one (explicit scheduling groups).
 //
 // Epilogue: each wave stages its accumulators through its own LDS region
 // (float32) so that every global store is a contiguous row segment; the
@@ -93,54 +94,44 @@ __device__ __forceinline__ uint32_t km_off(uint32_t k, uint32_t col) {
 //              ((L & 31) >> 2) ^ ((2b + L/32) & 3), 16-byte piece L & 3.
 // Addresses are a wave-uniform 64-bit base plus a 32-bit lane offset relative
 // to the tile origin (so that the load takes its base from scalar registers).
+template <bool KM>
 struct OperandDma {
-  const char* org_rm;    // row-major source: byte address of element (r0, 0)
-  const char* org_km;    // k-major source: byte address of stored element (0, r0)
-  uint32_t ldb;          // row pitch in bytes
-  uint32_t off_rm;       // lane offset, row-major blocks
-  uint32_t off_km0;      // lane offset, k-major blocks with b even
-  uint32_t off_km1;      // lane offset, k-major blocks with b odd
-  int t_km;              // number of leading K steps read k-major
+  const char* org;   // row-major: element (r0, 0); k-major: stored element (0, r0)
+  uint32_t ldb;      // row pitch in bytes
+  uint32_t off0;     // lane offset of blocks b even (row-major: every block)
+  uint32_t off1;     // lane offset of blocks b odd
 
-  __device__ void init(const uint16_t* src, int64_t ld, int r0, int tkm, int lane) {
-    org_rm = (const char*)(src + (int64_t)r0 * ld);
-    org_km = (const char*)(src + r0);
+  __device__ void init(const uint16_t* src, int64_t ld, int r0, int lane) {
     ldb = (uint32_t)(ld * 2);
-    t_km = tkm;
-    off_rm = (uint32_t)(lane >> 2) * ldb + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    // (2b + L/32) & 3 is L/32 for even b and 2 + L/32 for odd b
-    const uint32_t lo = (uint32_t)(lane >> 5) * ldb + 16u * (lane & 3);
-    off_km0 = lo + 64u * (((lane & 31) >> 2) ^ (lane >> 5));
-    off_km1 = lo + 64u * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
+    if (!KM) {
+      org = (const char*)(src + (int64_t)r0 * ld);
+      off0 = off1 = (uint32_t)(lane >> 2) * ldb + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    } else {
+      org = (const char*)(src + r0);
+      // (2b + L/32) & 3 is L/32 for even b and 2 + L/32 for odd b
+      const uint32_t lo = (uint32_t)(lane >> 5) * ldb + 16u * (lane & 3);
+      off0 = lo + 64u * (((lane & 31) >> 2) ^ (lane >> 5));
+      off1 = lo + 64u * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
+    }
+  }
+
+  template <int Q>
+  __device__ __forceinline__ void block(int t, uint8_t* tile, int wave) const {
+    const int b = 4 * wave + Q;
+    const char* base = KM ? org + (int64_t)(t * BK + 2 * b) * ldb
+                          : org + (int64_t)(16 * b) * ldb + t * BK * 2;   // wave-uniform
+    const uint32_t off = (Q & 1) ? off1 : off0;
+    __builtin_amdgcn_global_load_lds((const MATOPT_GAS void*)(base + off),
+                                     (MATOPT_LDS void*)(tile + 1024 * b), 16, 0, 0);
+  }
+
+  __device__ __forceinline__ void issue(int t, uint8_t* tile, int wave) const {
+    block<0>(t, tile, wave);
+    block<1>(t, tile, wave);
+    block<2>(t, tile, wave);
+    block<3>(t, tile, wave);
   }
 };
-
-template <int Q>
-__device__ __forceinline__ void dma_block(const OperandDma& o, bool km, int t, uint8_t* tile,
-                                          int wave) {
-  const int b = 4 * wave + Q;
-  const char* base = km ? o.org_km + (int64_t)(t * BK + 2 * b) * o.ldb
-                        : o.org_rm + (int64_t)(16 * b) * o.ldb + t * BK * 2;   // wave-uniform
-  // per-lane offset, chosen arithmetically (km is uniform)
-  const uint32_t kmoff = (Q & 1) ? o.off_km1 : o.off_km0;
-  const uint32_t off = o.off_rm ^ ((o.off_rm ^ kmoff) & (km ? 0xffffffffu : 0u));
-  __builtin_amdgcn_global_load_lds((const MATOPT_GAS void*)(base + off),
-                                   (MATOPT_LDS void*)(tile + 1024 * b), 16, 0, 0);
-}
-
-__device__ __forceinline__ void dma_op(const OperandDma& o, int t, uint8_t* tile, int wave) {
-  const bool km = t < o.t_km;
-  dma_block<0>(o, km, t, tile, wave);
-  dma_block<1>(o, km, t, tile, wave);
-  dma_block<2>(o, km, t, tile, wave);
-  dma_block<3>(o, km, t, tile, wave);
-}
-
-__device__ __forceinline__ void dma_step(const OperandDma& p, const OperandDma& q, int t,
-                                         uint8_t* stage, int wave) {
-  dma_op(p, t, stage, wave);
-  dma_op(q, t, stage + OPB, wave);
-}
 
 // Per-lane LDS offsets of the MFMA fragments (relative to the wave's operand
 // row origin inside an operand tile).  A fragment covers 32 operand rows and a
@@ -188,33 +179,14 @@ struct WaveGeo {
   int wi0, wj0, frow, fkc;
 };
 
-template <bool PKM, bool QKM>
-__device__ __forceinline__ void read_frags_t(const uint8_t* stage, int kk, const WaveGeo& g,
-                                             const FragOffsets& fo, bf16x8 (&p)[4],
-                                             bf16x8 (&q)[4]) {
+template <bool KM>
+__device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, const WaveGeo& g,
+                                           const FragOffsets& fo, bf16x8 (&p)[4],
+                                           bf16x8 (&q)[4]) {
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi) p[bi] = frag<PKM>(stage, g.wi0, bi, kk, fo);
+  for (int bi = 0; bi < 4; ++bi) p[bi] = frag<KM>(stage, g.wi0, bi, kk, fo);
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) q[bj] = frag<QKM>(stage + OPB, g.wj0, bj, kk, fo);
-}
-
-// Operand modes that occur: stage 0 reads both operands row-major; stage 1
-// reads P k-major for t < i0/BK and Q k-major for t < j0/BK with i0 <= j0;
-// stage 2 always reads Q (X) k-major.
-template <int STAGE>
-__device__ __forceinline__ void read_frags(int t, int tP, int tQ, const uint8_t* stage, int kk,
-                                           const WaveGeo& g, const FragOffsets& fo,
-                                           bf16x8 (&p)[4], bf16x8 (&q)[4]) {
-  if (STAGE == 0) {
-    read_frags_t<false, false>(stage, kk, g, fo, p, q);
-  } else if (STAGE == 1) {
-    if (t < tP) read_frags_t<true, true>(stage, kk, g, fo, p, q);
-    else if (t < tQ) read_frags_t<false, true>(stage, kk, g, fo, p, q);
-    else read_frags_t<false, false>(stage, kk, g, fo, p, q);
-  } else {
-    if (t < tP) read_frags_t<true, true>(stage, kk, g, fo, p, q);
-    else read_frags_t<false, true>(stage, kk, g, fo, p, q);
-  }
+  for (int bj = 0; bj < 4; ++bj) q[bj] = frag<KM>(stage + OPB, g.wj0, bj, kk, fo);
 }
 
 // 16 MFMAs of one k16 sub-step (operands swapped: acc[bi][bj] holds C^T blocks,
@@ -228,23 +200,25 @@ __device__ __forceinline__ void mfma16(f32x16 (&acc)[4][4], const bf16x8 (&p)[4]
       acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[bj], p[bi], acc[bi][bj], 0, 0, 0);
 }
 
-// Wait until at most n_steps DMA steps of this wave are still in flight (the
-// wait count must be an immediate).
-__device__ __forceinline__ void wait_dma(int n_steps) {
-  static_assert(NS - 2 <= 3 && DMA_PER_STEP == 8, "wait table");
-  if (n_steps <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (n_steps == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (n_steps == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+// Wait until at most N DMA instructions of this wave are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier without a memory fence (a fence would wait for every DMA
-// in flight); LDS ordering is explicit through wait_dma and lgkmcnt waits.
-__device__ __forceinline__ void bar() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+// in flight); LDS ordering is explicit through wait_vm and the K-step
+// structure.
+__device__ __forceinline__ void bar_raw() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// Scheduling-group masks (AMDGPU sched_group_barrier).
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_VMEM_RD = 0x020;
+constexpr int SG_DS_RD = 0x100;
 
 __device__ __forceinline__ void prefetch_stripe(const uint16_t* src, int64_t ld, int64_t row0,
                                                 int64_t col0, int lane, u32x2 (&dst)[16]) {
@@ -321,10 +295,12 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          const f32x16 (&acc)[4][4], float* stg,
                                          const uint16_t* ep_src, int64_t ep_ld, uint16_t* out,
                                          int64_t ld_out, int i0, int j0, int lane, int frow,
-                                         int fkc, float s_first, u32x2 (&ecur)[16]) {
+                                         int fkc, float s_first, bool tile_off_diag,
+                                         u32x2 (&ecur)[16]) {
   constexpr bool EP_IN = STAGE != 0;
   const int64_t rows = d.rows, cols = d.cols;
   const bool out_trans = OUT != OUT_NEXT_X && d.transposed;
+  const bool mirror = STAGE != 2 && tile_off_diag;
   const float upd = -P.lr * d.upd_scale;
   u32x2 enext[16];
 #pragma unroll 1
@@ -346,16 +322,19 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
       const int64_t i = ib + rr;
       const int64_t j = j0 + c4;
       const f32x4 v = *(const f32x4*)(stg + rr * EP_PITCH + c4);
-      if (STAGE == 0) {
-        const float s2 = s_first * s_first;
-        const u32x2 o = {pack_bf2(v.x * s2, v.y * s2), pack_bf2(v.z * s2, v.w * s2)};
-        gstore<u32x2>(out + i * ld_out + j, o);
-      } else if (STAGE == 1) {
-        const u32x2 ain = ecur[p];
-        const float b = P.b, c = P.c;
-        const u32x2 o = {pack_bf2(fmaf(b, lo_bf(ain.x), c * v.x), fmaf(b, hi_bf(ain.x), c * v.y)),
-                         pack_bf2(fmaf(b, lo_bf(ain.y), c * v.z), fmaf(b, hi_bf(ain.y), c * v.w))};
-        gstore<u32x2>(out + i * ld_out + j, o);
+      if (STAGE != 2) {
+        f32x4 val;
+        if (STAGE == 0) {
+          const float s2 = s_first * s_first;
+          val = f32x4{v.x * s2, v.y * s2, v.z * s2, v.w * s2};
+        } else {
+          const u32x2 ain = ecur[p];
+          const float b = P.b, c = P.c;
+          val = f32x4{fmaf(b, lo_bf(ain.x), c * v.x), fmaf(b, hi_bf(ain.x), c * v.y),
+                      fmaf(b, lo_bf(ain.y), c * v.z), fmaf(b, hi_bf(ain.y), c * v.w)};
+        }
+        gstore<u32x2>(out + i * ld_out + j, u32x2{pack_bf2(val.x, val.y), pack_bf2(val.z, val.w)});
+        if (mirror) *(f32x4*)(stg + rr * EP_PITCH + c4) = val;   // mirror pass below
       } else {
         const u32x2 xin = ecur[p];
         const float a = P.a;
@@ -374,6 +353,21 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
           const float vv[4] = {val.x, val.y, val.z, val.w};
           write_out4<OUT>(d, P, i, j, vv, upd);
         }
+      }
+    }
+    if (STAGE != 2 && mirror) {
+      __builtin_amdgcn_wave_barrier();
+      // Mirror tile: row j0+jj of the output holds this stripe's column jj,
+      // i.e. the 32 values of rows ib .. ib+31 (4 per lane item).
+#pragma unroll 4
+      for (int p = 0; p < 16; ++p) {
+        const int q = lane + 64 * p;
+        const int ic = q & 7, jj = q >> 3;
+        float vv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = stg[(4 * ic + e) * EP_PITCH + jj];
+        gstore<u32x2>(out + (int64_t)(j0 + jj) * ld_out + ib + 4 * ic,
+                      u32x2{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3])});
       }
     }
     if (OUT != OUT_NEXT_X && out_trans) {
@@ -401,34 +395,84 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
   }
 }
 
-// One K step (not the last).  The three stage pointers name distinct stages
-// (NS >= 3); declaring them restrict tells the compiler that the fragment reads
-// never alias the DMA writes issued here, so it adds no wait of its own for
-// the DMA before an LDS read -- the ordering comes from wait_dma and bar.
-template <int STAGE>
+// One K step t (not the last): sub-step 0 from fragments read earlier, then
+// the wave waits for its DMA of step t+1, meets the other waves, issues the DMA
+// of step t+NS-1 (when DMA) into the stage of step t-1 and reads the first
+// fragments of step t+1 during sub-step 1.  VMW is the vmcnt that leaves only
+// the DMA of steps after t+1 in flight.
+//
+// The three stage pointers name distinct stages (NS >= 3); declaring them
+// restrict tells the compiler that these fragment reads never alias the DMA
+// written here, so it adds no wait of its own for the DMA before an LDS read.
+// No LDS-read wait is needed before the barrier either: every read of step
+// t-1's stage was consumed by an MFMA of step t-1, before this point.
+template <bool KM, int VMW, bool DMA, class OpP, class OpQ>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], bf16x8 (&pa)[4], bf16x8 (&qa)[4],
-                                      bf16x8 (&pb)[4], bf16x8 (&qb)[4], int t, int nk,
-                                      const OperandDma& dp, const OperandDma& dq,
-                                      const WaveGeo& g, const FragOffsets& fo, int wave,
-                                      const uint8_t* __restrict__ cur,
+                                      bf16x8 (&pb)[4], bf16x8 (&qb)[4], int t, const OpP& dp,
+                                      const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
+                                      int wave, const uint8_t* __restrict__ cur,
                                       const uint8_t* __restrict__ nxt,
-                                      uint8_t* __restrict__ dma_dst) {
-  read_frags<STAGE>(t, dp.t_km, dq.t_km, cur, 1, g, fo, pb, qb);
+                                      uint8_t* __restrict__ dst) {
+  constexpr int RD = KM ? 16 : 8;   // LDS read instructions per k16 sub-step
+  read_frags<KM>(cur, 1, g, fo, pb, qb);
   mfma16(acc, pa, qa);
-  // every wave's DMA of step t+1 has landed; step t-1's stage is free
-  wait_dma(min(NS - 3, nk - 2 - t));
-  bar();
-  if (t + NS - 1 < nk) dma_step(dp, dq, t + NS - 1, dma_dst, wave);
-  read_frags<STAGE>(t + 1, dp.t_km, dq.t_km, nxt, 0, g, fo, pa, qa);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD / 8, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  wait_vm<VMW>();
+  bar_raw();
+  if (DMA) {
+    dp.issue(t + NS - 1, dst, wave);
+    dq.issue(t + NS - 1, dst + OPB, wave);
+  }
+  read_frags<KM>(nxt, 0, g, fo, pa, qa);
   mfma16(acc, pb, qb);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    if (DMA) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD / 8, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Prologue: DMA of steps 0 .. NS-2, wait for step 0, first fragments.  The
+// reads alias only the DMA of step 0 (s0); the compiler's own wait for it is
+// the same vmcnt as the explicit one.
+template <bool KM, class OpP, class OpQ>
+__device__ __forceinline__ void kprologue(bf16x8 (&pa)[4], bf16x8 (&qa)[4], const OpP& dp,
+                                          const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
+                                          int wave, uint8_t* __restrict__ s0,
+                                          uint8_t* __restrict__ rest) {
+  dp.issue(0, s0, wave);
+  dq.issue(0, s0 + OPB, wave);
+#pragma unroll
+  for (int t = 1; t < NS - 1; ++t) {
+    dp.issue(t, rest + (t - 1) * STG, wave);
+    dq.issue(t, rest + (t - 1) * STG + OPB, wave);
+  }
+  wait_vm<DMA_PER_STEP * (NS - 2)>();
+  bar_raw();
+  read_frags<KM>(s0, 0, g, fo, pa, qa);
+}
+
+__device__ __forceinline__ uint32_t stage_wrap(uint32_t x) {
+  return x >= (uint32_t)LDS_BYTES ? x - (uint32_t)LDS_BYTES : x;
 }
 
 // One kernel per stage (and, for apply, per output kind), so that each carries
-// only its own operand modes and epilogue.
+// only its own operand layout and epilogue.
 template <int STAGE, int OUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_bf16_kernel(GemmParams P) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  constexpr bool KM = STAGE != 0;
 
   const GemmTile tile = P.tiles[blockIdx.x];
   if (tile.mat < 0) return;   // idle entry padding an XCD stream
@@ -438,26 +482,21 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   const uint16_t* xcur = (const uint16_t*)(P.cur ? d.x[1] : d.x[0]);
   uint16_t* xnext = (uint16_t*)(P.cur ? d.x[0] : d.x[1]);
 
-  // Operands; symmetric storage reads the k-blocks left of the operand's row
-  // block from the mirrored tile (k-major).
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  OperandDma dp, dq;
-  int K;
+  OperandDma<KM> dp, dq;
   if (STAGE == 0) {
-    dp.init(xcur, np, i0, 0, lane);
-    dq.init(xcur, np, j0, 0, lane);
-    K = (int)np;
+    dp.init(xcur, np, i0, lane);
+    dq.init(xcur, np, j0, lane);
   } else if (STAGE == 1) {
-    dp.init((const uint16_t*)d.a, mp, i0, i0 / BK, lane);
-    dq.init((const uint16_t*)d.a, mp, j0, j0 / BK, lane);
-    K = (int)mp;
+    dp.init((const uint16_t*)d.a, mp, i0, lane);
+    dq.init((const uint16_t*)d.a, mp, j0, lane);
   } else {
-    dp.init((const uint16_t*)d.b, mp, i0, i0 / BK, lane);
-    dq.init(xcur, np, j0, (int)mp / BK, lane);
-    K = (int)mp;
+    dp.init((const uint16_t*)d.b, mp, i0, lane);
+    dq.init(xcur, np, j0, lane);
   }
-  const int nk = K / BK;
+  // K is a multiple of 256, so nk >= 8 > NS - 1
+  const int nk = (int)(STAGE == 0 ? np : mp) / BK;
 
   WaveGeo g;
   g.wi0 = (wave >> 1) * 128;   // wave sub-tile origin (rows)
@@ -475,31 +514,48 @@ void ns_gemm_bf16_kernel(GemmParams P) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
-  // prologue: DMA steps 0 .. NS-2, wait for step 0, read its first fragments
-  for (int t = 0; t < NS - 1 && t < nk; ++t) dma_step(dp, dq, t, lds + t * STG, wave);
-  wait_dma(min(NS - 2, nk - 1));
-  bar();
   bf16x8 pa[4], qa[4], pb[4], qb[4];
-  read_frags<STAGE>(0, dp.t_km, dq.t_km, lds, 0, g, fo, pa, qa);
+  kprologue<KM>(pa, qa, dp, dq, g, fo, wave, lds, lds + STG);
 
-  for (int t = 0; t + 1 < nk; ++t)
-    kstep<STAGE>(acc, pa, qa, pb, qb, t, nk, dp, dq, g, fo, wave, lds + (t % NS) * STG,
-                 lds + ((t + 1) % NS) * STG, lds + ((t + NS - 1) % NS) * STG);
+  // steps 0 .. nk-NS issue DMA; nk-NS+1 .. nk-2 drain it; nk-1 is the last
+  uint32_t sc = 0;   // LDS offset of step t's stage
+  constexpr int VM2 = DMA_PER_STEP * 2;
+  int t = 0;
+  for (; t <= nk - NS; ++t) {
+    kstep<KM, VM2, true>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
+                         lds + stage_wrap(sc + STG), lds + stage_wrap(sc + (NS - 1) * STG));
+    sc = stage_wrap(sc + STG);
+  }
+  kstep<KM, DMA_PER_STEP * 2, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
+                                     lds + stage_wrap(sc + STG), lds);
+  sc = stage_wrap(sc + STG);
+  ++t;
+  kstep<KM, DMA_PER_STEP, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
+                                 lds + stage_wrap(sc + STG), lds);
+  sc = stage_wrap(sc + STG);
+  ++t;
+  kstep<KM, 0, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
+                      lds + stage_wrap(sc + STG), lds);
+  sc = stage_wrap(sc + STG);
+
   // last K step; the first epilogue stripe is fetched meanwhile
   const int64_t ep_ld = STAGE == 1 ? mp : np;
   const uint16_t* ep_src = STAGE == 1 ? (const uint16_t*)d.a : xcur;
   u32x2 ecur[16];
-  read_frags<STAGE>(nk - 1, dp.t_km, dq.t_km, lds + ((nk - 1) % NS) * STG, 1, g, fo, pb, qb);
+  read_frags<KM>(lds + sc, 1, g, fo, pb, qb);
   mfma16(acc, pa, qa);
   if (STAGE != 0) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
   mfma16(acc, pb, qb);
-  bar();   // all fragment reads done: the stages become epilogue staging
+  // all fragment reads done (consumed above): the stages become epilogue staging
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  bar_raw();
 
   uint16_t* out = STAGE == 0 ? (uint16_t*)d.a : STAGE == 1 ? (uint16_t*)d.b : xnext;
   const int64_t ld_out = STAGE == 2 ? np : mp;
   const float s_first = P.first ? gload<float>(d.xs) : 1.f;
   epilogue<STAGE, OUT>(d, P, acc, (float*)(lds + wave * EP_WAVE_BYTES), ep_src, ep_ld, out,
-                       ld_out, i0 + g.wi0, j0 + g.wj0, lane, g.frow, g.fkc, s_first, ecur);
+                       ld_out, i0 + g.wi0, j0 + g.wj0, lane, g.frow, g.fkc, s_first,
+                       tile.ti != tile.tj, ecur);
 }
 
 }  // namespace
