@@ -395,56 +395,59 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
   }
 }
 
-// One K step t (not the last): sub-step 0 from fragments read earlier, then
-// the wave waits for its DMA of step t+1, meets the other waves, issues the DMA
-// of step t+NS-1 (when DMA) into the stage of step t-1 and reads the first
-// fragments of step t+1 during sub-step 1.  VMW is the vmcnt that leaves only
-// the DMA of steps after t+1 in flight.
+// One K step t (not the last).  Sub-step 0 runs on fragments read earlier
+// while the sub-step-1 fragments of step t are read and (DQ) the Q half of the
+// DMA of step t+NS-2 is issued into the stage of step t-2; then the wave waits
+// for its DMA of step t+1, meets the other waves, and runs sub-step 1 while the
+// sub-step-0 fragments of step t+1 are read and (DP) the P half of the DMA of
+// step t+NS-1 is issued into the stage of step t-1.  Splitting each step's DMA
+// over both halves keeps the address unit's queue short, so a DMA instruction
+// never holds up the MFMAs behind it.  VMW is the vmcnt that leaves in flight
+// only the DMA issued after that of step t+1.
 //
-// The three stage pointers name distinct stages (NS >= 3); declaring them
-// restrict tells the compiler that these fragment reads never alias the DMA
-// written here, so it adds no wait of its own for the DMA before an LDS read.
-// No LDS-read wait is needed before the barrier either: every read of step
-// t-1's stage was consumed by an MFMA of step t-1, before this point.
-template <bool KM, int VMW, bool DMA, class OpP, class OpQ>
+// The stage pointers name distinct stages (NS >= 4); declaring them restrict
+// tells the compiler that these fragment reads never alias the DMA written
+// here, so it adds no wait of its own for the DMA before an LDS read.  No
+// LDS-read wait is needed before the barrier either: every read of step t-1's
+// stage was consumed by an MFMA of step t-1, before this point.
+template <bool KM, int VMW, bool DQ, bool DP, class OpP, class OpQ>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], bf16x8 (&pa)[4], bf16x8 (&qa)[4],
                                       bf16x8 (&pb)[4], bf16x8 (&qb)[4], int t, const OpP& dp,
                                       const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
                                       int wave, const uint8_t* __restrict__ cur,
                                       const uint8_t* __restrict__ nxt,
-                                      uint8_t* __restrict__ dst) {
+                                      uint8_t* __restrict__ dst_q, uint8_t* __restrict__ dst_p) {
   constexpr int RD = KM ? 16 : 8;   // LDS read instructions per k16 sub-step
   read_frags<KM>(cur, 1, g, fo, pb, qb);
+  if (DQ) dq.issue(t + NS - 2, dst_q + OPB, wave);
   mfma16(acc, pa, qa);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD / 8, 0);
+    if (DQ && (i & 1)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
 
   wait_vm<VMW>();
   bar_raw();
-  if (DMA) {
-    dp.issue(t + NS - 1, dst, wave);
-    dq.issue(t + NS - 1, dst + OPB, wave);
-  }
+  if (DP) dp.issue(t + NS - 1, dst_p, wave);
   read_frags<KM>(nxt, 0, g, fo, pa, qa);
   mfma16(acc, pb, qb);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    if (DMA) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD / 8, 0);
+    if (DP && (i & 1)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Prologue: DMA of steps 0 .. NS-2, wait for step 0, first fragments.  The
-// reads alias only the DMA of step 0 (s0); the compiler's own wait for it is
-// the same vmcnt as the explicit one.
+// Prologue: DMA of steps 0 .. NS-3 and the P half of step NS-2, wait for step
+// 0, first fragments.  The reads alias only the DMA of step 0 (s0); the
+// compiler's own wait for it is the same vmcnt as the explicit one.
 template <bool KM, class OpP, class OpQ>
 __device__ __forceinline__ void kprologue(bf16x8 (&pa)[4], bf16x8 (&qa)[4], const OpP& dp,
                                           const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
@@ -453,11 +456,12 @@ __device__ __forceinline__ void kprologue(bf16x8 (&pa)[4], bf16x8 (&qa)[4], cons
   dp.issue(0, s0, wave);
   dq.issue(0, s0 + OPB, wave);
 #pragma unroll
-  for (int t = 1; t < NS - 1; ++t) {
+  for (int t = 1; t < NS - 2; ++t) {
     dp.issue(t, rest + (t - 1) * STG, wave);
     dq.issue(t, rest + (t - 1) * STG + OPB, wave);
   }
-  wait_vm<DMA_PER_STEP * (NS - 2)>();
+  dp.issue(NS - 2, rest + (NS - 3) * STG, wave);
+  wait_vm<DMA_PER_STEP * (NS - 3) + DMA_PER_STEP / 2>();
   bar_raw();
   read_frags<KM>(s0, 0, g, fo, pa, qa);
 }
@@ -517,25 +521,28 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   bf16x8 pa[4], qa[4], pb[4], qb[4];
   kprologue<KM>(pa, qa, dp, dq, g, fo, wave, lds, lds + STG);
 
-  // steps 0 .. nk-NS issue DMA; nk-NS+1 .. nk-2 drain it; nk-1 is the last
+  // Steps 0 .. nk-NS issue both DMA halves; step nk-NS+1 only the Q half of
+  // step nk-1; the last two steps before the final one drain the DMA.
   uint32_t sc = 0;   // LDS offset of step t's stage
   constexpr int VM2 = DMA_PER_STEP * 2;
   int t = 0;
   for (; t <= nk - NS; ++t) {
-    kstep<KM, VM2, true>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
-                         lds + stage_wrap(sc + STG), lds + stage_wrap(sc + (NS - 1) * STG));
+    kstep<KM, VM2, true, true>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
+                               lds + stage_wrap(sc + STG), lds + stage_wrap(sc + (NS - 2) * STG),
+                               lds + stage_wrap(sc + (NS - 1) * STG));
     sc = stage_wrap(sc + STG);
   }
-  kstep<KM, DMA_PER_STEP * 2, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
-                                     lds + stage_wrap(sc + STG), lds);
+  kstep<KM, VM2, true, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
+                              lds + stage_wrap(sc + STG), lds + stage_wrap(sc + (NS - 2) * STG),
+                              lds);
   sc = stage_wrap(sc + STG);
   ++t;
-  kstep<KM, DMA_PER_STEP, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
-                                 lds + stage_wrap(sc + STG), lds);
+  kstep<KM, DMA_PER_STEP, false, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
+                                        lds + stage_wrap(sc + STG), lds, lds);
   sc = stage_wrap(sc + STG);
   ++t;
-  kstep<KM, 0, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
-                      lds + stage_wrap(sc + STG), lds);
+  kstep<KM, 0, false, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
+                             lds + stage_wrap(sc + STG), lds, lds);
   sc = stage_wrap(sc + STG);
 
   // last K step; the first epilogue stripe is fetched meanwhile
