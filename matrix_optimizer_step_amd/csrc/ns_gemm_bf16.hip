@@ -283,6 +283,76 @@ __device__ __forceinline__ void write_out4(const MatDesc& d, const GemmParams& P
   }
 }
 
+// Last-iteration output of one staged stripe (rows ib .. ib+31 of the X
+// orientation, the wave's 128 columns from j0), in the original orientation:
+// item p of lane q = lane + 64p covers 4 consecutive original columns of one
+// original row -- row ib + q/32, columns j0 + 4(q & 31) when not transposed;
+// row j0 + q/8, columns ib + 4(q & 7) when transposed.  Stripes that lie
+// wholly inside a matrix with 16-byte rows take an unrolled path with vector
+// accesses, the stripe's 16 W chunks per lane all read before the first is
+// used; others a rolled per-item path.
+template <int OUT, bool TRANS>
+__device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P, const float* stg,
+                                           int64_t ib, int64_t j0, int lane, float upd) {
+  const int64_t rows = d.rows, cols = d.cols;
+  const bool full = d.vec_ok && (TRANS ? (j0 + 128 <= rows && ib + 32 <= cols)
+                                       : (ib + 32 <= rows && j0 + 128 <= cols));
+  auto item = [&](int p, int64_t& r, int64_t& c, float (&vv)[4]) {
+    const int q = lane + 64 * p;
+    if (!TRANS) {
+      const int rr = q >> 5, c4 = (q & 31) * 4;
+      r = ib + rr;
+      c = j0 + c4;
+      const f32x4 v = *(const f32x4*)(stg + rr * EP_PITCH + c4);
+      vv[0] = v.x; vv[1] = v.y; vv[2] = v.z; vv[3] = v.w;
+    } else {
+      const int ic = q & 7, jj = q >> 3;
+      r = j0 + jj;
+      c = ib + 4 * ic;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = stg[(4 * ic + e) * EP_PITCH + jj];
+    }
+  };
+  if (full) {
+    u32x2 wpre[16];
+    if (OUT == OUT_W_UPDATE) {
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int q = lane + 64 * p;
+        const int64_t r = TRANS ? j0 + (q >> 3) : ib + (q >> 5);
+        const int64_t c = TRANS ? ib + 4 * (q & 7) : j0 + (q & 31) * 4;
+        wpre[p] = gload<u32x2>((const uint16_t*)d.w + r * cols + c);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      int64_t r, c;
+      float vv[4];
+      item(p, r, c, vv);
+      const int64_t off = r * cols + c;
+      if (OUT == OUT_O) {
+        if (P.out_dt == DT_F32) gstore<f32x4>((float*)d.o + off, f32x4{vv[0], vv[1], vv[2], vv[3]});
+        else gstore<u32x2>((uint16_t*)d.o + off, u32x2{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3])});
+      } else {
+        const u32x2 wo = wpre[p];
+        const float w4[4] = {lo_bf(wo.x), hi_bf(wo.x), lo_bf(wo.y), hi_bf(wo.y)};
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = f64_to_bf16(fma((double)upd, (double)vv[e], (double)w4[e]));
+        gstore<u32x2>((uint16_t*)d.w + off, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int p = 0; p < 16; ++p) {
+      int64_t r, c;
+      float vv[4];
+      item(p, r, c, vv);
+      if (r < rows && c < cols) write_out4<OUT>(d, P, r, c, vv, upd);
+    }
+  }
+}
+
 // Epilogue of one wave's 128 x 128 sub-tile, one 32-row stripe at a time (a
 // rolled loop: only the accumulator staging is specialised per stripe, which
 // keeps the kernel small enough for the instruction cache).  Each stripe is
@@ -346,12 +416,8 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
         if (OUT == OUT_NEXT_X) {
           const u32x2 o = {pack_bf2(val.x, val.y), pack_bf2(val.z, val.w)};
           gstore<u32x2>(out + i * ld_out + j, o);
-        } else if (out_trans) {
-          *(f32x4*)(stg + rr * EP_PITCH + c4) = val;   // transposed pass below
-        } else if (i < rows && j < cols) {
-          // original orientation == X orientation: row i, columns j..j+3
-          const float vv[4] = {val.x, val.y, val.z, val.w};
-          write_out4<OUT>(d, P, i, j, vv, upd);
+        } else {
+          *(f32x4*)(stg + rr * EP_PITCH + c4) = val;   // final pass below
         }
       }
     }
@@ -370,22 +436,10 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                       u32x2{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3])});
       }
     }
-    if (OUT != OUT_NEXT_X && out_trans) {
+    if (OUT != OUT_NEXT_X) {
       __builtin_amdgcn_wave_barrier();
-      // Output row jr (original) = X column j0+jj; original columns are the X
-      // rows ib + 4ic .. +3.
-#pragma unroll 2
-      for (int p = 0; p < 16; ++p) {
-        const int q = lane + 64 * p;
-        const int ic = q & 7, jj = q >> 3;
-        const int64_t jr = j0 + jj;
-        const int64_t ic0 = ib + 4 * ic;
-        if (jr >= rows || ic0 >= cols) continue;
-        float vv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = stg[(4 * ic + e) * EP_PITCH + jj];
-        write_out4<OUT>(d, P, jr, ic0, vv, upd);
-      }
+      if (out_trans) final_pass<OUT, true>(d, P, stg, ib, j0, lane, upd);
+      else final_pass<OUT, false>(d, P, stg, ib, j0, lane, upd);
     }
     __builtin_amdgcn_wave_barrier();
     if (EP_IN) {
