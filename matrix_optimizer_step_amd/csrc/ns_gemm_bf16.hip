@@ -5,17 +5,20 @@
 // routine, written in factored form) all reduce to C[i][j] = sum_k P[i][k]Q[j][k]:
 //
 //   stage 0 (Gram)    A = s^2 * X X^T     P = Q = X rows (k contiguous in HBM)
-//   stage 1 (poly)    B = b*A + c*A A     P = Q = A rows = A columns (symmetric)
-//   stage 2 (apply)   X' = s*(a*X + B X)  P = B columns (= rows), Q = X columns
+//   stage 1 (poly)    B = b*A + c*A A     P = Q = A columns (A A = A A^T)
+//   stage 2 (apply)   X' = s*(a*X + B X)  P = B rows, Q = X columns
 //
 // s is the Frobenius scale 1/(||V||+eps) on the first iteration, 1 afterwards.
-// A and B are symmetric: only tiles ti <= tj are computed, and the epilogue
+// A and B are symmetric: only tiles ti <= tj are computed.  The Gram epilogue
 // writes each off-diagonal tile twice, as itself and transposed into the
-// mirror position, so both are stored whole and bitwise symmetric.  Stages 1
-// and 2 then read every operand through its columns (k-major: each k row of
-// an operand tile is 512 contiguous bytes in HBM); stage 0 reads X rows
-// (row-major, 64 contiguous bytes per row and K step).  Each stage therefore
-// has one fixed operand layout and a straight-line K step.
+// mirror position, so A is stored whole (and bitwise symmetric) and the
+// polynomial reads it through its columns in one fixed layout (k-major: each
+// k row of an operand tile is 512 contiguous bytes).  B keeps its upper tiles
+// only (the mirror writes cost more in the polynomial than they save): apply
+// reads a B row block k-major from the mirrored upper tile for the k-blocks
+// left of its diagonal block and row-major (64 contiguous bytes per row and K
+// step) from there on.  X is read row-major by the Gram and k-major (through
+// its columns) by apply.
 //
 // Engine.  A 256 x 256 output tile per workgroup of 4 waves (each wave 128 x
 // 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, accumulators in AGPRs).  The
@@ -94,42 +97,51 @@ __device__ __forceinline__ uint32_t km_off(uint32_t k, uint32_t col) {
 //              ((L & 31) >> 2) ^ ((2b + L/32) & 3), 16-byte piece L & 3.
 // Addresses are a wave-uniform 64-bit base plus a 32-bit lane offset relative
 // to the tile origin (so that the load takes its base from scalar registers).
-template <bool KM>
-struct OperandDma {
-  const char* org;   // row-major: element (r0, 0); k-major: stored element (0, r0)
-  uint32_t ldb;      // row pitch in bytes
-  uint32_t off0;     // lane offset of blocks b even (row-major: every block)
-  uint32_t off1;     // lane offset of blocks b odd
+// Operand read modes over the K loop: always row-major, always k-major, or
+// k-major for the steps left of the operand's diagonal block (t < t_km, read
+// from the mirrored upper tile of a symmetric matrix) and row-major after.
+enum OpKind { OP_RM = 0, OP_KM = 1, OP_SPLIT = 2 };
 
-  __device__ void init(const uint16_t* src, int64_t ld, int r0, int lane) {
+template <int KIND>
+struct OperandDma {
+  const char* org_rm;   // byte address of element (r0, 0)
+  const char* org_km;   // byte address of stored element (0, r0)
+  uint32_t ldb;         // row pitch in bytes
+  uint32_t off_rm;      // lane offset of row-major blocks
+  uint32_t off_km0;     // lane offset of k-major blocks with b even
+  uint32_t off_km1;     // lane offset of k-major blocks with b odd
+  int t_km;             // steps t < t_km are k-major
+
+  __device__ void init(const uint16_t* src, int64_t ld, int r0, int tkm, int lane) {
     ldb = (uint32_t)(ld * 2);
-    if (!KM) {
-      org = (const char*)(src + (int64_t)r0 * ld);
-      off0 = off1 = (uint32_t)(lane >> 2) * ldb + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    } else {
-      org = (const char*)(src + r0);
-      // (2b + L/32) & 3 is L/32 for even b and 2 + L/32 for odd b
-      const uint32_t lo = (uint32_t)(lane >> 5) * ldb + 16u * (lane & 3);
-      off0 = lo + 64u * (((lane & 31) >> 2) ^ (lane >> 5));
-      off1 = lo + 64u * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
-    }
+    org_rm = (const char*)(src + (int64_t)r0 * ld);
+    org_km = (const char*)(src + r0);
+    t_km = tkm;
+    off_rm = (uint32_t)(lane >> 2) * ldb + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    // (2b + L/32) & 3 is L/32 for even b and 2 + L/32 for odd b
+    const uint32_t lo = (uint32_t)(lane >> 5) * ldb + 16u * (lane & 3);
+    off_km0 = lo + 64u * (((lane & 31) >> 2) ^ (lane >> 5));
+    off_km1 = lo + 64u * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
   }
 
   template <int Q>
-  __device__ __forceinline__ void block(int t, uint8_t* tile, int wave) const {
+  __device__ __forceinline__ void block(bool km, int t, uint8_t* tile, int wave) const {
     const int b = 4 * wave + Q;
-    const char* base = KM ? org + (int64_t)(t * BK + 2 * b) * ldb
-                          : org + (int64_t)(16 * b) * ldb + t * BK * 2;   // wave-uniform
-    const uint32_t off = (Q & 1) ? off1 : off0;
+    const char* base = km ? org_km + (int64_t)(t * BK + 2 * b) * ldb
+                          : org_rm + (int64_t)(16 * b) * ldb + t * BK * 2;   // wave-uniform
+    const uint32_t kmoff = (Q & 1) ? off_km1 : off_km0;
+    // per-lane offset chosen arithmetically (km is uniform)
+    const uint32_t off = off_rm ^ ((off_rm ^ kmoff) & (km ? 0xffffffffu : 0u));
     __builtin_amdgcn_global_load_lds((const MATOPT_GAS void*)(base + off),
                                      (MATOPT_LDS void*)(tile + 1024 * b), 16, 0, 0);
   }
 
   __device__ __forceinline__ void issue(int t, uint8_t* tile, int wave) const {
-    block<0>(t, tile, wave);
-    block<1>(t, tile, wave);
-    block<2>(t, tile, wave);
-    block<3>(t, tile, wave);
+    const bool km = KIND == OP_KM || (KIND == OP_SPLIT && t < t_km);
+    block<0>(km, t, tile, wave);
+    block<1>(km, t, tile, wave);
+    block<2>(km, t, tile, wave);
+    block<3>(km, t, tile, wave);
   }
 };
 
@@ -179,14 +191,14 @@ struct WaveGeo {
   int wi0, wj0, frow, fkc;
 };
 
-template <bool KM>
+template <bool PKM, bool QKM>
 __device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, const WaveGeo& g,
                                            const FragOffsets& fo, bf16x8 (&p)[4],
                                            bf16x8 (&q)[4]) {
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi) p[bi] = frag<KM>(stage, g.wi0, bi, kk, fo);
+  for (int bi = 0; bi < 4; ++bi) p[bi] = frag<PKM>(stage, g.wi0, bi, kk, fo);
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) q[bj] = frag<KM>(stage + OPB, g.wj0, bj, kk, fo);
+  for (int bj = 0; bj < 4; ++bj) q[bj] = frag<QKM>(stage + OPB, g.wj0, bj, kk, fo);
 }
 
 // 16 MFMAs of one k16 sub-step (operands swapped: acc[bi][bj] holds C^T blocks,
@@ -370,7 +382,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
   constexpr bool EP_IN = STAGE != 0;
   const int64_t rows = d.rows, cols = d.cols;
   const bool out_trans = OUT != OUT_NEXT_X && d.transposed;
-  const bool mirror = STAGE != 2 && tile_off_diag;
+  const bool mirror = STAGE == 0 && tile_off_diag;   // A is stored whole
   const float upd = -P.lr * d.upd_scale;
   u32x2 enext[16];
 #pragma unroll 1
@@ -421,7 +433,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
         }
       }
     }
-    if (STAGE != 2 && mirror) {
+    if (STAGE == 0 && mirror) {
       __builtin_amdgcn_wave_barrier();
       // Mirror tile: row j0+jj of the output holds this stripe's column jj,
       // i.e. the 32 values of rows ib .. ib+31 (4 per lane item).
@@ -457,28 +469,30 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
 // step t+NS-1 is issued into the stage of step t-1.  Splitting each step's DMA
 // over both halves keeps the address unit's queue short, so a DMA instruction
 // never holds up the MFMAs behind it.  VMW is the vmcnt that leaves in flight
-// only the DMA issued after that of step t+1.
+// only the DMA issued after that of step t+1.  (P0, Q0) are the operand
+// layouts of step t, (P1, Q1) those of step t+1 (true: k-major).
 //
 // The stage pointers name distinct stages (NS >= 4); declaring them restrict
 // tells the compiler that these fragment reads never alias the DMA written
 // here, so it adds no wait of its own for the DMA before an LDS read.  No
 // LDS-read wait is needed before the barrier either: every read of step t-1's
 // stage was consumed by an MFMA of step t-1, before this point.
-template <bool KM, int VMW, bool DQ, bool DP, class OpP, class OpQ>
+template <bool P0, bool Q0, bool P1, bool Q1, int VMW, bool DQ, bool DP, class OpP, class OpQ>
 __device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], bf16x8 (&pa)[4], bf16x8 (&qa)[4],
                                       bf16x8 (&pb)[4], bf16x8 (&qb)[4], int t, const OpP& dp,
                                       const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
                                       int wave, const uint8_t* __restrict__ cur,
                                       const uint8_t* __restrict__ nxt,
                                       uint8_t* __restrict__ dst_q, uint8_t* __restrict__ dst_p) {
-  constexpr int RD = KM ? 16 : 8;   // LDS read instructions per k16 sub-step
-  read_frags<KM>(cur, 1, g, fo, pb, qb);
+  constexpr int RD0 = (P0 ? 8 : 4) + (Q0 ? 8 : 4);   // LDS reads of a k16 sub-step
+  constexpr int RD1 = (P1 ? 8 : 4) + (Q1 ? 8 : 4);
+  read_frags<P0, Q0>(cur, 1, g, fo, pb, qb);
   if (DQ) dq.issue(t + NS - 2, dst_q + OPB, wave);
   mfma16(acc, pa, qa);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD0 / 8, 0);
     if (DQ && (i & 1)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
@@ -487,12 +501,12 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], bf16x8 (&pa)[4], bf16
   wait_vm<VMW>();
   bar_raw();
   if (DP) dp.issue(t + NS - 1, dst_p, wave);
-  read_frags<KM>(nxt, 0, g, fo, pa, qa);
+  read_frags<P1, Q1>(nxt, 0, g, fo, pa, qa);
   mfma16(acc, pb, qb);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD1 / 8, 0);
     if (DP && (i & 1)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
@@ -500,9 +514,10 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], bf16x8 (&pa)[4], bf16
 }
 
 // Prologue: DMA of steps 0 .. NS-3 and the P half of step NS-2, wait for step
-// 0, first fragments.  The reads alias only the DMA of step 0 (s0); the
-// compiler's own wait for it is the same vmcnt as the explicit one.
-template <bool KM, class OpP, class OpQ>
+// 0, first fragments (layouts P0, Q0 of step 0).  The reads alias only the DMA
+// of step 0 (s0); the compiler's own wait for it is the same vmcnt as the
+// explicit one.
+template <bool P0, bool Q0, class OpP, class OpQ>
 __device__ __forceinline__ void kprologue(bf16x8 (&pa)[4], bf16x8 (&qa)[4], const OpP& dp,
                                           const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
                                           int wave, uint8_t* __restrict__ s0,
@@ -517,20 +532,81 @@ __device__ __forceinline__ void kprologue(bf16x8 (&pa)[4], bf16x8 (&qa)[4], cons
   dp.issue(NS - 2, rest + (NS - 3) * STG, wave);
   wait_vm<DMA_PER_STEP * (NS - 3) + DMA_PER_STEP / 2>();
   bar_raw();
-  read_frags<KM>(s0, 0, g, fo, pa, qa);
+  read_frags<P0, Q0>(s0, 0, g, fo, pa, qa);
 }
 
 __device__ __forceinline__ uint32_t stage_wrap(uint32_t x) {
   return x >= (uint32_t)LDS_BYTES ? x - (uint32_t)LDS_BYTES : x;
 }
 
+// Register state of one tile's K loop and the stage of its current step.
+struct KState {
+  f32x16 acc[4][4];
+  bf16x8 pa[4], qa[4], pb[4], qb[4];
+  uint32_t sc;   // LDS offset of step t's stage
+  int t;
+};
+
+// Steady steps t < t_end with both DMA halves and layouts (P0, Q0) -> (P1, Q1).
+template <bool P0, bool Q0, bool P1, bool Q1, class OpP, class OpQ>
+__device__ __forceinline__ void ksteps(KState& k, int t_end, const OpP& dp, const OpQ& dq,
+                                       const WaveGeo& g, const FragOffsets& fo, int wave,
+                                       uint8_t* lds) {
+  for (; k.t < t_end; ++k.t) {
+    kstep<P0, Q0, P1, Q1, DMA_PER_STEP * 2, true, true>(
+        k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
+        lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + (NS - 2) * STG),
+        lds + stage_wrap(k.sc + (NS - 1) * STG));
+    k.sc = stage_wrap(k.sc + STG);
+  }
+}
+
+// All K steps of one tile but the last.  P is k-major for t < bP and in layout
+// PF from then on (bP is 0 or the first step of P's diagonal block, at most
+// nk - 8, so the switch lies in the steady range); Q is in layout QF.
+template <bool PF, bool QF, class OpP, class OpQ>
+__device__ __forceinline__ void kloop(KState& k, int nk, int bP, const OpP& dp, const OpQ& dq,
+                                      const WaveGeo& g, const FragOffsets& fo, int wave,
+                                      uint8_t* lds) {
+  if (bP > 0) kprologue<true, QF>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
+  else kprologue<PF, QF>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
+  k.sc = 0;
+  k.t = 0;
+  if (bP > 0) {
+    ksteps<true, QF, true, QF>(k, bP - 1, dp, dq, g, fo, wave, lds);
+    ksteps<true, QF, PF, QF>(k, bP, dp, dq, g, fo, wave, lds);
+  }
+  ksteps<PF, QF, PF, QF>(k, nk - NS + 1, dp, dq, g, fo, wave, lds);
+  // drain: the Q half of step nk-1 is issued in step nk-NS+1; none after
+  kstep<PF, QF, PF, QF, DMA_PER_STEP * 2, true, false>(
+      k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
+      lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + (NS - 2) * STG), lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep<PF, QF, PF, QF, DMA_PER_STEP, false, false>(
+      k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
+      lds + stage_wrap(k.sc + STG), lds, lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep<PF, QF, PF, QF, 0, false, false>(k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave,
+                                         lds + k.sc, lds + stage_wrap(k.sc + STG), lds, lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+}
+
 // One kernel per stage (and, for apply, per output kind), so that each carries
-// only its own operand layout and epilogue.
+// only its own operand layouts and epilogue.
 template <int STAGE, int OUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_bf16_kernel(GemmParams P) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
-  constexpr bool KM = STAGE != 0;
+  // Gram: P = Q = X rows.  Polynomial: P = Q = A columns (A is stored whole).
+  // Apply: P = B rows, k-major from the mirrored upper tile left of the
+  // diagonal block (B holds its upper tiles only); Q = X columns.
+  constexpr int PK = STAGE == 0 ? OP_RM : STAGE == 1 ? OP_KM : OP_SPLIT;
+  constexpr int QK = STAGE == 0 ? OP_RM : OP_KM;
+  constexpr bool PF = STAGE == 1;   // P layout from the diagonal block on
+  constexpr bool QF = STAGE != 0;   // Q layout
 
   const GemmTile tile = P.tiles[blockIdx.x];
   if (tile.mat < 0) return;   // idle entry padding an XCD stream
@@ -539,22 +615,25 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   const int64_t mp = d.mp, np = d.np;
   const uint16_t* xcur = (const uint16_t*)(P.cur ? d.x[1] : d.x[0]);
   uint16_t* xnext = (uint16_t*)(P.cur ? d.x[0] : d.x[1]);
+  // K is a multiple of 256, so nk >= 8 > NS - 1
+  const int nk = (int)(STAGE == 0 ? np : mp) / BK;
+  // apply: P is k-major for steps t < bP (at most nk - 8)
+  const int bP = STAGE == 2 ? i0 / BK : 0;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  OperandDma<KM> dp, dq;
+  OperandDma<PK> dp;
+  OperandDma<QK> dq;
   if (STAGE == 0) {
-    dp.init(xcur, np, i0, lane);
-    dq.init(xcur, np, j0, lane);
+    dp.init(xcur, np, i0, 0, lane);
+    dq.init(xcur, np, j0, 0, lane);
   } else if (STAGE == 1) {
-    dp.init((const uint16_t*)d.a, mp, i0, lane);
-    dq.init((const uint16_t*)d.a, mp, j0, lane);
+    dp.init((const uint16_t*)d.a, mp, i0, nk, lane);
+    dq.init((const uint16_t*)d.a, mp, j0, nk, lane);
   } else {
-    dp.init((const uint16_t*)d.b, mp, i0, lane);
-    dq.init(xcur, np, j0, lane);
+    dp.init((const uint16_t*)d.b, mp, i0, bP, lane);
+    dq.init(xcur, np, j0, nk, lane);
   }
-  // K is a multiple of 256, so nk >= 8 > NS - 1
-  const int nk = (int)(STAGE == 0 ? np : mp) / BK;
 
   WaveGeo g;
   g.wi0 = (wave >> 1) * 128;   // wave sub-tile origin (rows)
@@ -564,49 +643,23 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   FragOffsets fo;
   fo.init(lane);
 
-  f32x16 acc[4][4];
+  KState k;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
-
-  bf16x8 pa[4], qa[4], pb[4], qb[4];
-  kprologue<KM>(pa, qa, dp, dq, g, fo, wave, lds, lds + STG);
-
-  // Steps 0 .. nk-NS issue both DMA halves; step nk-NS+1 only the Q half of
-  // step nk-1; the last two steps before the final one drain the DMA.
-  uint32_t sc = 0;   // LDS offset of step t's stage
-  constexpr int VM2 = DMA_PER_STEP * 2;
-  int t = 0;
-  for (; t <= nk - NS; ++t) {
-    kstep<KM, VM2, true, true>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
-                               lds + stage_wrap(sc + STG), lds + stage_wrap(sc + (NS - 2) * STG),
-                               lds + stage_wrap(sc + (NS - 1) * STG));
-    sc = stage_wrap(sc + STG);
-  }
-  kstep<KM, VM2, true, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
-                              lds + stage_wrap(sc + STG), lds + stage_wrap(sc + (NS - 2) * STG),
-                              lds);
-  sc = stage_wrap(sc + STG);
-  ++t;
-  kstep<KM, DMA_PER_STEP, false, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
-                                        lds + stage_wrap(sc + STG), lds, lds);
-  sc = stage_wrap(sc + STG);
-  ++t;
-  kstep<KM, 0, false, false>(acc, pa, qa, pb, qb, t, dp, dq, g, fo, wave, lds + sc,
-                             lds + stage_wrap(sc + STG), lds, lds);
-  sc = stage_wrap(sc + STG);
+      for (int r = 0; r < 16; ++r) k.acc[bi][bj][r] = 0.f;
+  kloop<PF, QF>(k, nk, bP, dp, dq, g, fo, wave, lds);
 
   // last K step; the first epilogue stripe is fetched meanwhile
   const int64_t ep_ld = STAGE == 1 ? mp : np;
   const uint16_t* ep_src = STAGE == 1 ? (const uint16_t*)d.a : xcur;
   u32x2 ecur[16];
-  read_frags<KM>(lds + sc, 1, g, fo, pb, qb);
-  mfma16(acc, pa, qa);
+  read_frags<PF, QF>(lds + k.sc, 1, g, fo, k.pb, k.qb);
+  mfma16(k.acc, k.pa, k.qa);
   if (STAGE != 0) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
-  mfma16(acc, pb, qb);
+  mfma16(k.acc, k.pb, k.qb);
   // all fragment reads done (consumed above): the stages become epilogue staging
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   bar_raw();
@@ -614,7 +667,7 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   uint16_t* out = STAGE == 0 ? (uint16_t*)d.a : STAGE == 1 ? (uint16_t*)d.b : xnext;
   const int64_t ld_out = STAGE == 2 ? np : mp;
   const float s_first = P.first ? gload<float>(d.xs) : 1.f;
-  epilogue<STAGE, OUT>(d, P, acc, (float*)(lds + wave * EP_WAVE_BYTES), ep_src, ep_ld, out,
+  epilogue<STAGE, OUT>(d, P, k.acc, (float*)(lds + wave * EP_WAVE_BYTES), ep_src, ep_ld, out,
                        ld_out, i0 + g.wi0, j0 + g.wj0, lane, g.frow, g.fkc, s_first,
                        tile.ti != tile.tj, ecur);
 }
