@@ -4,11 +4,15 @@
 // The three products of one iteration (blog post, appendix Newton-Schulz
 // routine, written in factored form) all reduce to C[i][j] = sum_k P[i][k]Q[j][k]:
 //
-//   stage 0 (Gram)    A = s^2 * X X^T     P = Q = X rows (k contiguous in HBM)
-//   stage 1 (poly)    B = b*A + c*A A     P = Q = A columns (A A = A A^T)
-//   stage 2 (apply)   X' = s*(a*X + B X)  P = B rows, Q = X columns
+//   stage 0 (Gram)    A = s^2 * X X^T          P = Q = X rows (k contiguous in HBM)
+//   stage 1 (poly)    B = a*I + b*A + c*A A    P = Q = A columns (A A = A A^T)
+//   stage 2 (apply)   X' = s * B X             P = B rows, Q = X columns
 //
 // s is the Frobenius scale 1/(||V||+eps) on the first iteration, 1 afterwards.
+// B is the whole polynomial p(A) = aI + bA + cA^2, stored in bf16, so that
+// apply is one product with nothing read back in its epilogue (a X + (bA +
+// cA^2) X = p(A) X; folding a into B's diagonal is as accurate as adding a X
+// in float32, because X' is rounded to bf16 at the same relative precision).
 // A and B are symmetric: only tiles ti <= tj are computed.  The Gram epilogue
 // writes each off-diagonal tile twice, as itself and transposed into the
 // mirror position, so A is stored whole (and bitwise symmetric) and the
@@ -370,8 +374,9 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
 // keeps the kernel small enough for the instruction cache).  Each stripe is
 // staged through the wave's own LDS region (LDS executes one wave's accesses in
 // order, so no workgroup barrier is needed) and written row-wise: 16 chunks of
-// 4 consecutive columns per lane.  The epilogue input of the next stripe (A for
-// the polynomial, X for apply) is prefetched while the current one is written.
+// 4 consecutive columns per lane.  The polynomial's epilogue input (the A tile
+// of the same position) is prefetched one stripe ahead; Gram and apply read
+// nothing back.
 template <int STAGE, int OUT>
 __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          const f32x16 (&acc)[4][4], float* stg,
@@ -379,8 +384,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          int64_t ld_out, int i0, int j0, int lane, int frow,
                                          int fkc, float s_first, bool tile_off_diag,
                                          u32x2 (&ecur)[16]) {
-  constexpr bool EP_IN = STAGE != 0;
-  const int64_t rows = d.rows, cols = d.cols;
+  constexpr bool EP_IN = STAGE == 1;
   const bool out_trans = OUT != OUT_NEXT_X && d.transposed;
   const bool mirror = STAGE == 0 && tile_off_diag;   // A is stored whole
   const float upd = -P.lr * d.upd_scale;
@@ -410,21 +414,19 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
           const float s2 = s_first * s_first;
           val = f32x4{v.x * s2, v.y * s2, v.z * s2, v.w * s2};
         } else {
+          // a*I + b*A + c*(A A): a on the diagonal (global row i == column j + e)
           const u32x2 ain = ecur[p];
-          const float b = P.b, c = P.c;
-          val = f32x4{fmaf(b, lo_bf(ain.x), c * v.x), fmaf(b, hi_bf(ain.x), c * v.y),
-                      fmaf(b, lo_bf(ain.y), c * v.z), fmaf(b, hi_bf(ain.y), c * v.w)};
+          const float a = P.a, b = P.b, c = P.c;
+          const int64_t dg = i - j;
+          val = f32x4{fmaf(b, lo_bf(ain.x), fmaf(c, v.x, dg == 0 ? a : 0.f)),
+                      fmaf(b, hi_bf(ain.x), fmaf(c, v.y, dg == 1 ? a : 0.f)),
+                      fmaf(b, lo_bf(ain.y), fmaf(c, v.z, dg == 2 ? a : 0.f)),
+                      fmaf(b, hi_bf(ain.y), fmaf(c, v.w, dg == 3 ? a : 0.f))};
         }
         gstore<u32x2>(out + i * ld_out + j, u32x2{pack_bf2(val.x, val.y), pack_bf2(val.z, val.w)});
         if (mirror) *(f32x4*)(stg + rr * EP_PITCH + c4) = val;   // mirror pass below
       } else {
-        const u32x2 xin = ecur[p];
-        const float a = P.a;
-        f32x4 val;
-        val.x = s_first * fmaf(a, lo_bf(xin.x), v.x);
-        val.y = s_first * fmaf(a, hi_bf(xin.x), v.y);
-        val.z = s_first * fmaf(a, lo_bf(xin.y), v.z);
-        val.w = s_first * fmaf(a, hi_bf(xin.y), v.w);
+        const f32x4 val = {s_first * v.x, s_first * v.y, s_first * v.z, s_first * v.w};
         if (OUT == OUT_NEXT_X) {
           const u32x2 o = {pack_bf2(val.x, val.y), pack_bf2(val.z, val.w)};
           gstore<u32x2>(out + i * ld_out + j, o);
@@ -653,12 +655,12 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   kloop<PF, QF>(k, nk, bP, dp, dq, g, fo, wave, lds);
 
   // last K step; the first epilogue stripe is fetched meanwhile
-  const int64_t ep_ld = STAGE == 1 ? mp : np;
-  const uint16_t* ep_src = STAGE == 1 ? (const uint16_t*)d.a : xcur;
+  const int64_t ep_ld = mp;
+  const uint16_t* ep_src = (const uint16_t*)d.a;
   u32x2 ecur[16];
   read_frags<PF, QF>(lds + k.sc, 1, g, fo, k.pb, k.qb);
   mfma16(k.acc, k.pa, k.qa);
-  if (STAGE != 0) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
+  if (STAGE == 1) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
   mfma16(k.acc, k.pb, k.qb);
   // all fragment reads done (consumed above): the stages become epilogue staging
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -28,9 +28,10 @@ Readings taken where the pages leave a step open (each is listed in the design
 notes with its reason):
 
 * The iteration is written in the factored form ``A = X X^T``,
-  ``B = b A + c A A``, ``X = a X + B X``.  It equals the page's printed form
-  (``B = A X``, ``X = a X + b B + c A B``) in exact arithmetic; the printed form
-  is kept as ``ns_orthogonalize_page_form`` and the two are pinned together.
+  ``B = p(A) = a I + b A + c A A``, ``X = B X`` -- the quintic polynomial in A,
+  then its product with X.  It equals the page's printed form (``B = A X``,
+  ``X = a X + b B + c A B``) in exact arithmetic; the printed form is kept as
+  ``ns_orthogonalize_page_form`` and the two are pinned together.
 * Scalar parameters are the float32 values a caller passes through the C ABI,
   widened exactly to float64 (``f32_param``).
 * Momentum is rounded once to the storage dtype (the page rounds twice, once per
@@ -38,10 +39,11 @@ notes with its reason):
 * Newton-Schulz consumes the *stored* updated momentum.
 * ``rounding="bf16"`` is the bf16 storage model: the tensors a bf16 engine keeps
   in bf16 between matrix products are rounded to bf16 (round to nearest even) at
-  exactly those points -- A, B and every iterate except the last -- while
-  the Frobenius scale ``1/(||V||+eps)`` is carried as an exact factor into the
-  first iteration's products instead of being rounded into a bf16 copy of V.
-  All accumulation stays float64.  ``rounding="exact"`` rounds nothing.
+  exactly those points -- A, the polynomial B = p(A) (with a on its diagonal)
+  and every iterate except the last -- while the Frobenius scale
+  ``1/(||V||+eps)`` is carried as an exact factor into the first iteration's
+  products instead of being rounded into a bf16 copy of V.  All accumulation
+  stays float64.  ``rounding="exact"`` rounds nothing.
 
 Parity status
 -------------
@@ -123,7 +125,7 @@ def ns_orthogonalize(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
 
     1. ``X0 = x / (||x||_F + eps)``.
     2. If rows > cols (strict), work on the transpose.
-    3. ``steps`` times: ``A = X X^T``; ``B = b A + c A A``; ``X = a X + B X``.
+    3. ``steps`` times: ``A = X X^T``; ``B = a I + b A + c A A``; ``X = B X``.
     4. Transpose back.
 
     ``rounding="bf16"`` applies the bf16 storage model described in the module
@@ -142,14 +144,15 @@ def ns_orthogonalize(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
         s = 1.0
     else:
         s = scale  # carried exactly into the first iteration's products
+    eye = np.eye(X.shape[0])
     for k in range(steps):
         A = (s * s) * (X @ X.T)
         if rounding == "bf16":
             A = round_bf16(A)
-        B = b * A + c * (A @ A)
+        B = a * eye + b * A + c * (A @ A)
         if rounding == "bf16":
             B = round_bf16(B)
-        Xn = s * (a * X + B @ X)
+        Xn = s * (B @ X)
         if rounding == "bf16" and k < steps - 1:
             Xn = round_bf16(Xn)
         X = Xn

@@ -257,21 +257,22 @@ def test_ns_steps_zero_is_normalisation():
 def test_bf16_model_rounds_exactly_a_b_and_iterates():
     # x has orthonormal rows scaled by 1 (4 of 8 unit columns), ||x||_F = 2 and
     # eps = 0, so the Frobenius scale is exactly 1/2 and X X^T = I.  One step:
-    # A = I/4 (bf16-exact), B = b/4 + c/16 times I (rounded to bf16), and the
-    # last iterate 0.5*(a x + B x) is not rounded.
+    # A = I/4 (bf16-exact), B = (a + b/4 + c/16) I (rounded to bf16), and the
+    # last iterate 0.5 * B x is not rounded.
     x = np.zeros((4, 8))
     x[np.arange(4), [1, 3, 5, 7]] = 1.0
     model = ns_orthogonalize(x, steps=1, eps=0.0, rounding="bf16")
-    b_model = round_bf16(B * 0.25 + C * 0.0625)
-    assert b_model != B * 0.25 + C * 0.0625
-    assert np.array_equal(model, 0.5 * (A * x + b_model * x))
+    p1 = A + B * 0.25 + C * 0.0625
+    b_model = round_bf16(p1)
+    assert b_model != p1
+    assert np.array_equal(model, 0.5 * b_model * x)
     exact = ns_orthogonalize(x, steps=1, eps=0.0)
-    assert np.array_equal(exact, 0.5 * (A + B * 0.25 + C * 0.0625) * x)
+    assert np.allclose(exact, 0.5 * p1 * x, rtol=1e-15, atol=0)
     # two steps: the first iterate is rounded to bf16 before the second step
-    x1 = round_bf16(0.5 * (A + b_model))
+    x1 = round_bf16(0.5 * b_model)
     a2 = round_bf16(x1 * x1)
-    b2 = round_bf16(B * a2 + C * a2 * a2)
-    ref2 = (A * x1 + b2 * x1) * x
+    b2 = round_bf16(A + B * a2 + C * a2 * a2)
+    ref2 = (b2 * x1) * x
     assert np.array_equal(ns_orthogonalize(x, steps=2, eps=0.0, rounding="bf16"), ref2)
 
 
