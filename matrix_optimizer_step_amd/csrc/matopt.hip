@@ -201,15 +201,20 @@ struct RmnpGroup {
   size_t off;  // byte offset of its task table in the plan buffer
 };
 
+// A GEMM stage's launch table and its length (the grid size of that stage:
+// the three tables are packed separately and differ in length).
+struct TileTable {
+  const GemmTile* tiles = nullptr;
+  int n = 0;
+};
+
 struct Plan {
   int device = -1;
   void* dbuf = nullptr;
   MatDesc* d_mats = nullptr;
   PrepTile* d_prep = nullptr;
-  GemmTile* d_k3 = nullptr;
-  GemmTile* d_k4 = nullptr;
-  GemmTile* d_k5 = nullptr;
-  int count = 0, n_prep = 0, n_gram = 0, n_apply = 0;
+  TileTable gram, poly, apply;
+  int count = 0, n_prep = 0;
   std::vector<RmnpGroup> rmnp;
   // Evicted plans are freed on their own device after it has drained (a queued
   // launch may still read the tables).  Plans alive at process exit are never
@@ -329,13 +334,11 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
   if (st != MATOPT_OK) return st;
   P.d_mats = at<MatDesc>(P.dbuf, o_mats);
   P.d_prep = at<PrepTile>(P.dbuf, o_prep);
-  P.d_k3 = at<GemmTile>(P.dbuf, o_k3);
-  P.d_k4 = at<GemmTile>(P.dbuf, o_k4);
-  P.d_k5 = at<GemmTile>(P.dbuf, o_k5);
+  P.gram = TileTable{at<GemmTile>(P.dbuf, o_k3), (int)k3.size()};
+  P.poly = TileTable{at<GemmTile>(P.dbuf, o_k4), (int)k4.size()};
+  P.apply = TileTable{at<GemmTile>(P.dbuf, o_k5), (int)k5.size()};
   P.count = count;
   P.n_prep = (int)prep.size();
-  P.n_gram = (int)k3.size();
-  P.n_apply = (int)k5.size();
   (void)kind;
   return MATOPT_OK;
 }
@@ -401,8 +404,10 @@ matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, i
   FinalizeParams fp{P.d_mats, eps};
   e = timed(1, s, [&] { return launch_finalize(fp, P.count, s); });
   if (e != hipSuccess) return hip_fail("finalize launch", e);
-  auto gemm = [&](const GemmParams& g, int n) {
-    return dt == DT_BF16 ? launch_gemm_bf16(g, n, s) : launch_gemm_f32(g, n, s);
+  // every stage launches exactly its own table
+  auto gemm = [&](GemmParams g, const TileTable& t) {
+    g.tiles = t.tiles;
+    return dt == DT_BF16 ? launch_gemm_bf16(g, t.n, s) : launch_gemm_f32(g, t.n, s);
   };
   for (int it = 0; it < ns_steps; ++it) {
     GemmParams g;
@@ -416,18 +421,15 @@ matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, i
     g.c = c;
     g.lr = lr;
     g.stage = 0;
-    g.tiles = P.d_k3;
     g.out_kind = OUT_NEXT_X;
-    e = timed(2, s, [&] { return gemm(g, P.n_gram); });
+    e = timed(2, s, [&] { return gemm(g, P.gram); });
     if (e != hipSuccess) return hip_fail("gram launch", e);
     g.stage = 1;
-    g.tiles = P.d_k4;
-    e = timed(3, s, [&] { return gemm(g, P.n_gram); });
+    e = timed(3, s, [&] { return gemm(g, P.poly); });
     if (e != hipSuccess) return hip_fail("poly launch", e);
     g.stage = 2;
-    g.tiles = P.d_k5;
     g.out_kind = it == ns_steps - 1 ? out_kind : OUT_NEXT_X;
-    e = timed(4, s, [&] { return gemm(g, P.n_apply); });
+    e = timed(4, s, [&] { return gemm(g, P.apply); });
     if (e != hipSuccess) return hip_fail("apply launch", e);
   }
   if (ns_steps == 0) {

@@ -55,6 +55,8 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
   const int stage = P.stage;
   const int i0 = tile.ti * TM, j0 = tile.tj * TM;
   const int64_t mp = d.mp, np = d.np;
+  // memory safety: an entry outside the matrix's output grid does nothing
+  if (i0 < 0 || j0 < 0 || i0 + TM > mp || j0 + TM > (stage == 2 ? np : mp)) return;
   const float* xcur = (const float*)(P.cur ? d.x[1] : d.x[0]);
   float* xnext = (float*)(P.cur ? d.x[0] : d.x[1]);
 

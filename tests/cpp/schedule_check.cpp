@@ -1,10 +1,12 @@
 // Host check of the grouped-launch tile schedule (tile_schedule.hpp).
-// Reads "tm tn k_gram k_apply" lines (one matrix each) from stdin and checks,
-// for the Gram/polynomial (triangle) and apply (full) tables:
+// Reads "tm tn k_gram k_poly" lines (one matrix each; the apply K equals the
+// polynomial's) from stdin and checks, for the Gram and polynomial (triangle)
+// and apply (full) tables:
 //   * every tile (ti <= tj, resp. every ti, tj) appears exactly once,
 //   * all tiles of one unit sit at positions of the same residue mod 8,
 //   * the largest XCD load exceeds the mean by at most one unit's cost.
-// Prints "ok <table sizes>" or the first violation; exit status 0 iff ok.
+// Prints "ok <gram> <poly> <apply table sizes>" or the first violation; exit
+// status 0 iff ok.
 #include <cstdio>
 #include <map>
 #include <set>
@@ -54,17 +56,18 @@ static int check(const std::vector<TileUnit>& units, const std::vector<TileRef>&
 }
 
 int main() {
-  std::vector<TileUnit> tri, full;
+  std::vector<TileUnit> gram, poly, full;
   int tm, tn;
-  long long kg, ka;
+  long long kg, kp;
   int mat = 0;
-  while (std::scanf("%d %d %lld %lld", &tm, &tn, &kg, &ka) == 4) {
-    units_triangle(mat, tm, kg, tri);
-    units_full(mat, tm, tn, ka, full);
+  while (std::scanf("%d %d %lld %lld", &tm, &tn, &kg, &kp) == 4) {
+    units_triangle(mat, tm, kg, gram);
+    units_triangle(mat, tm, kp, poly);
+    units_full(mat, tm, tn, kp, full);
     ++mat;
   }
-  const auto t1 = xcd_schedule(tri), t2 = xcd_schedule(full);
-  if (check(tri, t1, "triangle") || check(full, t2, "full")) return 1;
-  std::printf("ok %zu %zu\n", t1.size(), t2.size());
+  const auto t1 = xcd_schedule(gram), t2 = xcd_schedule(poly), t3 = xcd_schedule(full);
+  if (check(gram, t1, "gram") || check(poly, t2, "poly") || check(full, t3, "full")) return 1;
+  std::printf("ok %zu %zu %zu\n", t1.size(), t2.size(), t3.size());
   return 0;
 }

@@ -38,3 +38,13 @@ def test_schedule_covers_every_tile_once_and_balances(checker, name):
     r = subprocess.run([checker], input=lines, capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.startswith("ok")
+
+
+def test_mixed_batch_has_stage_tables_of_different_lengths(checker):
+    # the GPU parity case for per-stage launch sizes relies on this
+    from tests.test_parity_gpu import MIXED_SHAPES
+    lines = "\n".join("%d %d %d %d" % _grid(s) for s in MIXED_SHAPES)
+    r = subprocess.run([checker], input=lines, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    _, gram, poly, _ = r.stdout.split()
+    assert (int(gram), int(poly)) == (72, 48)

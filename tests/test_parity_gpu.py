@@ -99,6 +99,28 @@ def test_ns_bf16_ragged_batch(mo):
     assert max(big) <= 2e-2
 
 
+# Gram and polynomial tables of this batch differ in length (72 and 48 entries:
+# both are packed longest-unit-first, with K = n and K = m per tile), so it
+# checks that each stage launches exactly its own table.
+MIXED_SHAPES = [(384, 3072), (512, 256), (512, 1024), (512, 128), (512, 2048), (128, 512),
+                (1024, 256), (768, 768), (128, 128), (768, 768), (768, 1536), (2048, 512),
+                (768, 1536), (384, 384), (512, 512)]
+
+
+def test_ns_bf16_mixed_batch_stage_tables_differ(mo):
+    wl = workloads.small_case("mixed", MIXED_SHAPES, seed=21, v_std=1.0)
+    _, V, _ = _inputs(wl)
+    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    errs = [relF(f64(o), oracle.ns_orthogonalize(f64(v), rounding="bf16")) for v, o in zip(V, O)]
+    print("mixed batch relF vs bf16 model", np.round(errs, 5))
+    assert max(errs) <= 2e-2
+    alone = [mo.ns_orthogonalize_batched([v], out_dtype=torch.float32)[0] for v in V]
+    torch.cuda.synchronize()
+    for o, a in zip(O, alone):
+        assert torch.equal(o, a)
+
+
 F32_SHAPES = [(256, 512), (150, 333), (333, 150), (64, 64), (1, 7), (7, 1), (65, 129)]
 
 
