@@ -75,7 +75,9 @@ struct FinalizeParams {
 struct GemmParams {
   const MatDesc* mats;
   const GemmTile* tiles;
-  int32_t stage;      // 0: A = X X^T, 1: B = b A + c A A, 2: X' = a X + B X
+  // 0: A = X X^T;  1: B = aI + bA + cAA (bf16) or bA + cAA (fp32);
+  // 2: X' = B X (bf16) or aX + BX (fp32)
+  int32_t stage;
   int32_t cur;        // index of the current iterate buffer
   int32_t first;      // first iteration: fold the Frobenius scale in
   int32_t out_kind;   // OutKind (stage 2)

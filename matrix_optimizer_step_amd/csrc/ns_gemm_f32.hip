@@ -1,7 +1,10 @@
 // Newton-Schulz matrix products in float32 (the fp32 storage path), grouped over
-// a ragged batch.  Same three stages, operand modes and epilogues as the bf16
-// MFMA kernel (see ns_gemm_bf16.hip), on a simpler engine: 64 x 64 output tiles,
-// 256 threads each owning a 4 x 4 block, K step 16, float32 FMA accumulation.
+// a ragged batch.  The same three stages and tile tables as the bf16 MFMA
+// kernel (ns_gemm_bf16.hip), on a simpler engine: 64 x 64 output tiles, 256
+// threads each owning a 4 x 4 block, K step 16, float32 FMA accumulation.  The
+// polynomial is split between the stages here (B = b A + c A A, then
+// X' = a X + B X): nothing is rounded to bf16 in between, so the split and the
+// folded form (B = aI + bA + cAA, X' = B X) agree to float32 rounding.
 // No reduced-precision products are used anywhere on this path.
 //
 // Roofline: a dense contraction bound by the float32 vector FMA rate; in

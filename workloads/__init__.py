@@ -21,9 +21,9 @@ Workloads (shapes are rows x cols of the stored matrix):
   4096x4096 O, 14336x4096 gate, 14336x4096 up, 4096x14336 down}, bf16.
 * ``ragged_illcond_64``: 64 matrices with power-of-two sides in [128, 8192] and
   aspect ratio within 8:1 either way; each G is ``U diag(s) V^T + 1e-4 noise``
-  with random orthogonal U, V (QR of Gaussians, sign-fixed) and singular values
-  log-uniform in [1e-4, 1]; prior momentum is zero so the momentum keeps that
-  spectrum; bf16.
+  with random orthogonal U, V (columns of randomly signed Hadamard matrices,
+  exactly orthonormal) and singular values log-uniform in [1e-4, 1]; prior
+  momentum is zero so the momentum keeps that spectrum; bf16.
 * ``qwen32b_share_14``: 2 layers x {5120x5120 Q, 1024x5120 K, 1024x5120 V,
   5120x5120 O, 27648x5120 gate, 27648x5120 up, 5120x27648 down}, bf16.
 """
@@ -121,14 +121,27 @@ def _to_storage(a32: np.ndarray, dtype: str):
     return t.to(torch.bfloat16) if dtype == "bf16" else t.clone()
 
 
+def _orthonormal_columns(rng, n: int, k: int) -> np.ndarray:
+    """An n x k float32 matrix with exactly orthonormal columns (n a power of
+    two): k columns, picked at random, of the Sylvester-Hadamard matrix with
+    random row and column signs, scaled by 1/sqrt(n) -- a random orthogonal
+    factor that costs no factorisation."""
+    from scipy.linalg import hadamard
+    cols = rng.permutation(n)[:k]
+    h = hadamard(n, dtype=np.int8)[:, cols].astype(np.float32)
+    rs = rng.choice(np.array([-1.0, 1.0], np.float32), n)
+    cs = rng.choice(np.array([-1.0, 1.0], np.float32), k)
+    return h * (rs[:, None] * cs[None, :] / np.float32(np.sqrt(n)))
+
+
 def _illcond(rng, r, c):
+    """U diag(s) V^T + 1e-4 N(0,1): orthonormal U (r x k), V (c x k),
+    k = min(r, c), singular values log-uniform in [1e-4, 1]."""
     k = min(r, c)
-    qa, ra = np.linalg.qr(rng.standard_normal((r, k)))
-    qa = qa * np.sign(np.diag(ra))[None, :]
-    qb, rb = np.linalg.qr(rng.standard_normal((c, k)))
-    qb = qb * np.sign(np.diag(rb))[None, :]
-    s = np.exp(rng.uniform(np.log(1e-4), 0.0, k))
-    return (qa * s[None, :]) @ qb.T + 1e-4 * rng.standard_normal((r, c))
+    u = _orthonormal_columns(rng, r, k)
+    v = _orthonormal_columns(rng, c, k)
+    s = np.exp(rng.uniform(np.log(1e-4), 0.0, k)).astype(np.float32)
+    return (u * s[None, :]) @ v.T + np.float32(1e-4) * rng.standard_normal((r, c), dtype=np.float32)
 
 
 def matrix_inputs(wl: Workload, i: int):
