@@ -1,7 +1,10 @@
 // Memory-bound kernels that open and (for ns_steps == 0) close the Muon step.
 //
-// prep_kernel      one 64x64 tile of the padded original-orientation matrix:
-//                  momentum V <- mu*V + G (blog post, section 1: heavy ball; one
+// prep_kernel      one tile of 4096 elements: for a matrix that is
+//                  transposed, a 64x64 tile of the padded original-orientation
+//                  matrix; otherwise (X0 has V's layout) a contiguous run of the
+//                  padded X0, so that every access streams whole rows.
+//                  Momentum V <- mu*V + G (blog post, section 1: heavy ball; one
 //                  rounding to storage: see Elem::fma_store), partial sum of squares of the stored V
 //                  (the Frobenius norm that opens the appendix's Newton-Schulz
 //                  routine), and the first iterate X0 written into the workspace
@@ -49,22 +52,49 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams P) {
   const int64_t ldx = d.np;
   T* __restrict__ x0 = (T*)d.x[0];
 
+  // All loads of the tile first, then the arithmetic and the stores: V, G and
+  // the outputs are distinct buffers, but the compiler cannot know that, so
+  // loads written after a store would wait for it.
+  // Element (r, c) of each chunk.  Untransposed: the tile index counts runs of
+  // kThreads * NCH chunks of the padded mp x np X0 (the same count as 64x64
+  // tiles: both cover 4096 elements); np is a multiple of E, so no chunk
+  // straddles a row.
+  bool inb[NCH];
+  int64_t offs[NCH], er[NCH], ec[NCH];
+  u32x4 vraw[NCH], graw[NCH];
+#pragma unroll
+  for (int p = 0; p < NCH; ++p) {
+    const int q = threadIdx.x + kThreads * p;
+    int64_t r = r_base + q / CPR, c = c_base + (q % CPR) * E;
+    if (!transposed) {
+      const int64_t x = ((int64_t)tile.idx * (kThreads * NCH) + q) * E;
+      r = x / ldx;
+      c = x - r * ldx;
+    }
+    er[p] = r;
+    ec[p] = c;
+    inb[p] = r < rows && c < cols;
+    offs[p] = r * cols + c;
+    if (inb[p] && vec) {
+      vraw[p] = gload<u32x4>((const T*)d.v + offs[p]);
+      if (P.momentum) graw[p] = gload<u32x4>((const T*)d.g + offs[p]);
+    }
+  }
+
   float vals[NCH][E];
   float ss = 0.f;
 #pragma unroll
   for (int p = 0; p < NCH; ++p) {
-    const int q = threadIdx.x + kThreads * p;
-    const int rr = q / CPR, cc = (q % CPR) * E;
-    const int64_t r = r_base + rr, c = c_base + cc;
+    const int64_t r = er[p], c = ec[p];
+    const int64_t off = offs[p];
     float vn[E];
-    if (r < rows && c < cols) {
-      const int64_t off = r * cols + c;
+    if (inb[p]) {
       if (vec) {
         float vv[E];
-        Tr::unpack(gload<u32x4>((const T*)d.v + off), vv);
+        Tr::unpack(vraw[p], vv);
         if (P.momentum) {
           float gg[E];
-          Tr::unpack(gload<u32x4>((const T*)d.g + off), gg);
+          Tr::unpack(graw[p], gg);
 #pragma unroll
           for (int e = 0; e < E; ++e) vn[e] = Tr::fma_store(P.mu, vv[e], gg[e]);
           gstore<u32x4>((T*)d.v + off, Tr::pack(vn));

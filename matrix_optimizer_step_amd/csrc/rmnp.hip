@@ -45,19 +45,28 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
   const T* grow = (const T*)d.g + row * cols;
   T* wrow = (T*)d.w + row * cols;
 
-  u32x4 vreg[NCH], wreg[NCH];
+  // All loads of the row first (V, G and W are distinct buffers, but the
+  // compiler cannot know that, so a load written after the V store would wait
+  // for it), then the momentum, its sum of squares and the V stores.
+  u32x4 vreg[NCH], greg[NCH], wreg[NCH];
   float ss = 0.f;
   if (active) {
 #pragma unroll
     for (int p = 0; p < NCH; ++p) {
       const int64_t ch = lr_idx + (int64_t)LPR * p;
       if (ch < nchunks) {
-        const u32x4 vv = gload<u32x4>(vrow + ch * E);
-        const u32x4 gg = gload<u32x4>(grow + ch * E);
+        vreg[p] = gload<u32x4>(vrow + ch * E);
+        greg[p] = gload<u32x4>(grow + ch * E);
         wreg[p] = gload<u32x4>(wrow + ch * E);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < NCH; ++p) {
+      const int64_t ch = lr_idx + (int64_t)LPR * p;
+      if (ch < nchunks) {
         float fv[E], fg[E];
-        Tr::unpack(vv, fv);
-        Tr::unpack(gg, fg);
+        Tr::unpack(vreg[p], fv);
+        Tr::unpack(greg[p], fg);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           fv[e] = Tr::fma_store(P.mu, fv[e], fg[e]);
@@ -133,7 +142,6 @@ hipError_t launch_t(int wpr, int nch, const RmnpParams& p, int n, hipStream_t s)
   MATOPT_RMNP_CASE(1, 2)
   MATOPT_RMNP_CASE(1, 4)
   MATOPT_RMNP_CASE(1, 8)
-  MATOPT_RMNP_CASE(1, 16)
   MATOPT_RMNP_CASE(4, 4)
   MATOPT_RMNP_CASE(4, 8)
   MATOPT_RMNP_CASE(4, 16)
