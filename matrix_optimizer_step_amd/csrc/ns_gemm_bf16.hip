@@ -237,12 +237,13 @@ constexpr int SG_VMEM_RD = 0x020;
 constexpr int SG_DS_RD = 0x100;
 
 __device__ __forceinline__ void prefetch_stripe(const uint16_t* src, int64_t ld, int64_t row0,
-                                                int64_t col0, int lane, u32x2 (&dst)[16]) {
-  // lane q = lane + 64p reads row row0 + q/32, columns col0 + 4(q & 31) .. +3
+                                                int64_t col0, int lane, u32x4 (&dst)[8]) {
+  // lane q = lane + 64p reads row row0 + q/16, columns col0 + 8(q & 15) .. +7;
+  // item p starts 4p rows down (byte offsets)
   const char* base = (const char*)(src + row0 * ld + col0);
-  const uint32_t off = (uint32_t)(((lane >> 5) * ld + (lane & 31) * 4) * 2);
+  const uint32_t off = (uint32_t)(((lane >> 4) * ld + (lane & 15) * 8) * 2);
 #pragma unroll
-  for (int p = 0; p < 16; ++p) dst[p] = gload<u32x2>(base + (int64_t)(4 * p) * ld + off);
+  for (int p = 0; p < 8; ++p) dst[p] = gload<u32x4>(base + (int64_t)(8 * p) * ld + off);
 }
 
 // Stage acc[BI][*] (32 rows of the wave's 128 x 128 sub-tile) into the wave's
@@ -301,70 +302,93 @@ __device__ __forceinline__ void write_out4(const MatDesc& d, const GemmParams& P
 
 // Last-iteration output of one staged stripe (rows ib .. ib+31 of the X
 // orientation, the wave's 128 columns from j0), in the original orientation:
-// item p of lane q = lane + 64p covers 4 consecutive original columns of one
-// original row -- row ib + q/32, columns j0 + 4(q & 31) when not transposed;
-// row j0 + q/8, columns ib + 4(q & 7) when transposed.  Stripes that lie
-// wholly inside a matrix with 16-byte rows take an unrolled path with vector
-// accesses, the stripe's 16 W chunks per lane all read before the first is
-// used; others a rolled per-item path.
+// item p of lane q = lane + 64p covers 8 consecutive original columns of one
+// original row -- row ib + q/16, columns j0 + 8(q & 15) when not transposed;
+// row j0 + q/4, columns ib + 8(q & 3) when transposed.  The staged values are
+// scaled by s (the Frobenius scale when this is also the first iteration, else
+// 1) as they are read.  Stripes that lie wholly inside a matrix with 16-byte
+// rows take an unrolled path with 16-byte accesses, the stripe's 8 W chunks
+// per lane all read before the first is used; others a rolled per-item path.
 template <int OUT, bool TRANS>
 __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P, const float* stg,
-                                           int64_t ib, int64_t j0, int lane, float upd) {
+                                           int64_t ib, int64_t j0, int lane, float upd,
+                                           float s) {
   const int64_t rows = d.rows, cols = d.cols;
   const bool full = d.vec_ok && (TRANS ? (j0 + 128 <= rows && ib + 32 <= cols)
                                        : (ib + 32 <= rows && j0 + 128 <= cols));
-  auto item = [&](int p, int64_t& r, int64_t& c, float (&vv)[4]) {
+  auto item = [&](int p, int64_t& r, int64_t& c, float (&lo)[4], float (&hi)[4]) {
     const int q = lane + 64 * p;
     if (!TRANS) {
-      const int rr = q >> 5, c4 = (q & 31) * 4;
+      // lanes 8-15 of a row read the two halves in the other order (LDS banks)
+      const int rr = q >> 4, c8 = (q & 15) * 8;
       r = ib + rr;
-      c = j0 + c4;
-      const f32x4 v = *(const f32x4*)(stg + rr * EP_PITCH + c4);
-      vv[0] = v.x; vv[1] = v.y; vv[2] = v.z; vv[3] = v.w;
+      c = j0 + c8;
+      const bool hs = (q & 8) != 0;
+      const float* src = stg + rr * EP_PITCH + c8;
+      const f32x4 r0 = *(const f32x4*)(src + (hs ? 4 : 0));
+      const f32x4 r1 = *(const f32x4*)(src + (hs ? 0 : 4));
+      const f32x4 v0 = hs ? r1 : r0, v1 = hs ? r0 : r1;
+      lo[0] = s * v0.x; lo[1] = s * v0.y; lo[2] = s * v0.z; lo[3] = s * v0.w;
+      hi[0] = s * v1.x; hi[1] = s * v1.y; hi[2] = s * v1.z; hi[3] = s * v1.w;
     } else {
-      const int ic = q & 7, jj = q >> 3;
+      const int ic = q & 3, jj = q >> 2;
       r = j0 + jj;
-      c = ib + 4 * ic;
+      c = ib + 8 * ic;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vv[e] = stg[(4 * ic + e) * EP_PITCH + jj];
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = s * stg[(8 * ic + e) * EP_PITCH + jj];
+        hi[e] = s * stg[(8 * ic + 4 + e) * EP_PITCH + jj];
+      }
     }
   };
   if (full) {
-    u32x2 wpre[16];
+    u32x4 wpre[8];
     if (OUT == OUT_W_UPDATE) {
 #pragma unroll
-      for (int p = 0; p < 16; ++p) {
+      for (int p = 0; p < 8; ++p) {
         const int q = lane + 64 * p;
-        const int64_t r = TRANS ? j0 + (q >> 3) : ib + (q >> 5);
-        const int64_t c = TRANS ? ib + 4 * (q & 7) : j0 + (q & 31) * 4;
-        wpre[p] = gload<u32x2>((const uint16_t*)d.w + r * cols + c);
+        const int64_t r = TRANS ? j0 + (q >> 2) : ib + (q >> 4);
+        const int64_t c = TRANS ? ib + 8 * (q & 3) : j0 + (q & 15) * 8;
+        wpre[p] = gload<u32x4>((const uint16_t*)d.w + r * cols + c);
       }
     }
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
+    for (int p = 0; p < 8; ++p) {
       int64_t r, c;
-      float vv[4];
-      item(p, r, c, vv);
+      float lo[4], hi[4];
+      item(p, r, c, lo, hi);
       const int64_t off = r * cols + c;
       if (OUT == OUT_O) {
-        if (P.out_dt == DT_F32) gstore<f32x4>((float*)d.o + off, f32x4{vv[0], vv[1], vv[2], vv[3]});
-        else gstore<u32x2>((uint16_t*)d.o + off, u32x2{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3])});
+        if (P.out_dt == DT_F32) {
+          gstore<f32x4>((float*)d.o + off, f32x4{lo[0], lo[1], lo[2], lo[3]});
+          gstore<f32x4>((float*)d.o + off + 4, f32x4{hi[0], hi[1], hi[2], hi[3]});
+        } else {
+          gstore<u32x4>((uint16_t*)d.o + off, u32x4{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]),
+                                                     pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])});
+        }
       } else {
-        const u32x2 wo = wpre[p];
-        const float w4[4] = {lo_bf(wo.x), hi_bf(wo.x), lo_bf(wo.y), hi_bf(wo.y)};
-        uint32_t h[4];
+        const u32x4 wo = wpre[p];
+        const float w8[8] = {lo_bf(wo.x), hi_bf(wo.x), lo_bf(wo.y), hi_bf(wo.y),
+                             lo_bf(wo.z), hi_bf(wo.z), lo_bf(wo.w), hi_bf(wo.w)};
+        uint32_t h[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = f64_to_bf16(fma((double)upd, (double)vv[e], (double)w4[e]));
-        gstore<u32x2>((uint16_t*)d.w + off, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        for (int e = 0; e < 4; ++e) {
+          h[e] = f64_to_bf16(fma((double)upd, (double)lo[e], (double)w8[e]));
+          h[4 + e] = f64_to_bf16(fma((double)upd, (double)hi[e], (double)w8[4 + e]));
+        }
+        gstore<u32x4>((uint16_t*)d.w + off, u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                                  h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
       }
     }
   } else {
 #pragma unroll 1
-    for (int p = 0; p < 16; ++p) {
+    for (int p = 0; p < 8; ++p) {
       int64_t r, c;
-      float vv[4];
-      item(p, r, c, vv);
-      if (r < rows && c < cols) write_out4<OUT>(d, P, r, c, vv, upd);
+      float lo[4], hi[4];
+      item(p, r, c, lo, hi);
+      if (r >= rows) continue;
+      if (c < cols) write_out4<OUT>(d, P, r, c, lo, upd);
+      if (c + 4 < cols) write_out4<OUT>(d, P, r, c + 4, hi, upd);
     }
   }
 }
@@ -373,8 +397,8 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
 // rolled loop: only the accumulator staging is specialised per stripe, which
 // keeps the kernel small enough for the instruction cache).  Each stripe is
 // staged through the wave's own LDS region (LDS executes one wave's accesses in
-// order, so no workgroup barrier is needed) and written row-wise: 16 chunks of
-// 4 consecutive columns per lane.  The polynomial's epilogue input (the A tile
+// order, so no workgroup barrier is needed) and written row-wise: 8 chunks of
+// 8 consecutive columns (16-byte stores) per lane.  The polynomial's epilogue input (the A tile
 // of the same position) is prefetched one stripe ahead; Gram and apply read
 // nothing back.
 template <int STAGE, int OUT>
@@ -383,12 +407,12 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          const uint16_t* ep_src, int64_t ep_ld, uint16_t* out,
                                          int64_t ld_out, int i0, int j0, int lane, int frow,
                                          int fkc, float s_first, bool tile_off_diag,
-                                         u32x2 (&ecur)[16]) {
+                                         u32x4 (&ecur)[8]) {
   constexpr bool EP_IN = STAGE == 1;
   const bool out_trans = OUT != OUT_NEXT_X && d.transposed;
   const bool mirror = STAGE == 0 && tile_off_diag;   // A is stored whole
   const float upd = -P.lr * d.upd_scale;
-  u32x2 enext[16];
+  u32x4 enext[8];
 #pragma unroll 1
   for (int bi = 0; bi < 4; ++bi) {
     if (EP_IN && bi + 1 < 4) prefetch_stripe(ep_src, ep_ld, i0 + 32 * (bi + 1), j0, lane, enext);
@@ -401,64 +425,73 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
     __builtin_amdgcn_wave_barrier();
 
     const int64_t ib = i0 + 32 * bi;   // first X-orientation row of this stripe
+    if (STAGE != 2 || OUT == OUT_NEXT_X) {
+      // Gram, polynomial and non-final apply: 8 consecutive columns (one
+      // 16-byte store) per lane item.  Lanes 8-15 of a row read their two
+      // float4 halves in the other order so that the 16 lanes of a row meet
+      // distinct LDS banks.
+      const float sc = STAGE == 0 ? s_first * s_first : s_first;
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int q = lane + 64 * p;
-      const int rr = q >> 5, c4 = (q & 31) * 4;
-      const int64_t i = ib + rr;
-      const int64_t j = j0 + c4;
-      const f32x4 v = *(const f32x4*)(stg + rr * EP_PITCH + c4);
-      if (STAGE != 2) {
-        f32x4 val;
-        if (STAGE == 0) {
-          const float s2 = s_first * s_first;
-          val = f32x4{v.x * s2, v.y * s2, v.z * s2, v.w * s2};
-        } else {
-          // a*I + b*A + c*(A A): a on the diagonal (global row i == column j + e)
-          const u32x2 ain = ecur[p];
+      for (int p = 0; p < 8; ++p) {
+        const int q = lane + 64 * p;
+        const int rr = q >> 4, c8 = (q & 15) * 8;
+        const bool hs = (q & 8) != 0;
+        float* src = stg + rr * EP_PITCH + c8;
+        const f32x4 r0 = *(const f32x4*)(src + (hs ? 4 : 0));
+        const f32x4 r1 = *(const f32x4*)(src + (hs ? 0 : 4));
+        const f32x4 v0 = hs ? r1 : r0, v1 = hs ? r0 : r1;
+        f32x4 a0, a1;
+        if (STAGE == 1) {
+          // a*I + b*A + c*(A A): a on the diagonal (global row i == column j)
+          const u32x4 ain = ecur[p];
           const float a = P.a, b = P.b, c = P.c;
-          const int64_t dg = i - j;
-          val = f32x4{fmaf(b, lo_bf(ain.x), fmaf(c, v.x, dg == 0 ? a : 0.f)),
-                      fmaf(b, hi_bf(ain.x), fmaf(c, v.y, dg == 1 ? a : 0.f)),
-                      fmaf(b, lo_bf(ain.y), fmaf(c, v.z, dg == 2 ? a : 0.f)),
-                      fmaf(b, hi_bf(ain.y), fmaf(c, v.w, dg == 3 ? a : 0.f))};
-        }
-        gstore<u32x2>(out + i * ld_out + j, u32x2{pack_bf2(val.x, val.y), pack_bf2(val.z, val.w)});
-        if (mirror) *(f32x4*)(stg + rr * EP_PITCH + c4) = val;   // mirror pass below
-      } else {
-        const f32x4 val = {s_first * v.x, s_first * v.y, s_first * v.z, s_first * v.w};
-        if (OUT == OUT_NEXT_X) {
-          const u32x2 o = {pack_bf2(val.x, val.y), pack_bf2(val.z, val.w)};
-          gstore<u32x2>(out + i * ld_out + j, o);
+          const int64_t dg = (ib + rr) - (j0 + c8);
+          a0 = f32x4{fmaf(b, lo_bf(ain.x), fmaf(c, v0.x, dg == 0 ? a : 0.f)),
+                     fmaf(b, hi_bf(ain.x), fmaf(c, v0.y, dg == 1 ? a : 0.f)),
+                     fmaf(b, lo_bf(ain.y), fmaf(c, v0.z, dg == 2 ? a : 0.f)),
+                     fmaf(b, hi_bf(ain.y), fmaf(c, v0.w, dg == 3 ? a : 0.f))};
+          a1 = f32x4{fmaf(b, lo_bf(ain.z), fmaf(c, v1.x, dg == 4 ? a : 0.f)),
+                     fmaf(b, hi_bf(ain.z), fmaf(c, v1.y, dg == 5 ? a : 0.f)),
+                     fmaf(b, lo_bf(ain.w), fmaf(c, v1.z, dg == 6 ? a : 0.f)),
+                     fmaf(b, hi_bf(ain.w), fmaf(c, v1.w, dg == 7 ? a : 0.f))};
         } else {
-          *(f32x4*)(stg + rr * EP_PITCH + c4) = val;   // final pass below
+          a0 = f32x4{v0.x * sc, v0.y * sc, v0.z * sc, v0.w * sc};
+          a1 = f32x4{v1.x * sc, v1.y * sc, v1.z * sc, v1.w * sc};
+        }
+        gstore<u32x4>(out + (ib + rr) * ld_out + j0 + c8,
+                      u32x4{pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y),
+                            pack_bf2(a1.z, a1.w)});
+        if (mirror) {   // mirror pass below reads the scaled values
+          *(f32x4*)src = a0;
+          *(f32x4*)(src + 4) = a1;
         }
       }
     }
     if (STAGE == 0 && mirror) {
       __builtin_amdgcn_wave_barrier();
       // Mirror tile: row j0+jj of the output holds this stripe's column jj,
-      // i.e. the 32 values of rows ib .. ib+31 (4 per lane item).
+      // i.e. the 32 values of rows ib .. ib+31 (8 per lane item).
 #pragma unroll 4
-      for (int p = 0; p < 16; ++p) {
+      for (int p = 0; p < 8; ++p) {
         const int q = lane + 64 * p;
-        const int ic = q & 7, jj = q >> 3;
-        float vv[4];
+        const int ic = q & 3, jj = q >> 2;
+        float vv[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = stg[(4 * ic + e) * EP_PITCH + jj];
-        gstore<u32x2>(out + (int64_t)(j0 + jj) * ld_out + ib + 4 * ic,
-                      u32x2{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3])});
+        for (int e = 0; e < 8; ++e) vv[e] = stg[(8 * ic + e) * EP_PITCH + jj];
+        gstore<u32x4>(out + (int64_t)(j0 + jj) * ld_out + ib + 8 * ic,
+                      u32x4{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3]), pack_bf2(vv[4], vv[5]),
+                            pack_bf2(vv[6], vv[7])});
       }
     }
     if (OUT != OUT_NEXT_X) {
       __builtin_amdgcn_wave_barrier();
-      if (out_trans) final_pass<OUT, true>(d, P, stg, ib, j0, lane, upd);
-      else final_pass<OUT, false>(d, P, stg, ib, j0, lane, upd);
+      if (out_trans) final_pass<OUT, true>(d, P, stg, ib, j0, lane, upd, s_first);
+      else final_pass<OUT, false>(d, P, stg, ib, j0, lane, upd, s_first);
     }
     __builtin_amdgcn_wave_barrier();
     if (EP_IN) {
 #pragma unroll
-      for (int p = 0; p < 16; ++p) ecur[p] = enext[p];
+      for (int p = 0; p < 8; ++p) ecur[p] = enext[p];
     }
   }
 }
@@ -659,7 +692,7 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   // last K step; the first epilogue stripe is fetched meanwhile
   const int64_t ep_ld = mp;
   const uint16_t* ep_src = (const uint16_t*)d.a;
-  u32x2 ecur[16];
+  u32x4 ecur[8];
   read_frags<PF, QF>(lds + k.sc, 1, g, fo, k.pb, k.qb);
   mfma16(k.acc, k.pa, k.qa);
   if (STAGE == 1) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
