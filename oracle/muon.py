@@ -182,11 +182,15 @@ def ns_orthogonalize_page_form(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
 
 def muon_step(w, g, v, mu: float = MOMENTUM, lr: float = 0.02,
               steps: int = NS_STEPS, coeffs=NS_COEFFS, eps: float = NS_EPS,
-              dtype: str = "bf16", rounding: str = "exact"):
+              dtype: str = "bf16", rounding: str = "exact", wd: float = 0.0):
     """One owner-local Muon step on one whole matrix.
 
     ``V_new = round(mu V + G)``; ``O = NS(V_new)``;
-    ``W_new = round(W - lr * sqrt(max(1, rows/cols)) * O)``.
+    ``W_new = round(W - lr * (wd * W + sqrt(max(1, rows/cols)) * O))``.
+    ``wd`` is decoupled weight decay, 0 in the blog post's step; the MatrixFSDP
+    paper trains with weight decay 1e-2, momentum 0.5 and two Newton-Schulz
+    steps (section 5.1), and decoupled is the reading taken for "weight decay"
+    there (the decay scales W by lr*wd, apart from the orthogonalized direction).
     Returns ``(W_new, V_new, O)`` as float64 arrays.
     """
     w = _f64(w)
@@ -194,7 +198,8 @@ def muon_step(w, g, v, mu: float = MOMENTUM, lr: float = 0.02,
     o = ns_orthogonalize(v_new, steps, coeffs, eps, rounding)
     rows, cols = w.shape
     s = update_scale(rows, cols)
-    w_new = round_storage(w - f32_param(lr) * s * o, dtype)
+    lr64 = f32_param(lr)
+    w_new = round_storage(w - lr64 * (f32_param(wd) * w + s * o), dtype)
     return w_new, v_new, o
 
 

@@ -331,6 +331,36 @@ def test_muon_step_zero_momentum_and_gradient():
     assert np.array_equal(w_new, w)
 
 
+def test_muon_step_weight_decay_alone_scales_weights():
+    # zero momentum and gradient: O = 0, so the step is W (1 - lr wd), one
+    # rounding; lr = wd = 0.5 makes the factor 0.75 exact.  Expected from
+    # torch's own bfloat16 conversion.
+    torch = pytest.importorskip("torch")
+    w = torch.from_numpy(rng(40).standard_normal((7, 12)) * 0.02).to(torch.bfloat16)
+    z = np.zeros((7, 12))
+    w_new, _, o = muon_step(w.double().numpy(), z, z, lr=0.5, wd=0.5, dtype="bf16")
+    assert not o.any()
+    exp = (w.double() * 0.75).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(w_new, exp)
+
+
+@pytest.mark.parametrize("shape,scale", [((8, 2), 2.0), ((2, 8), 1.0)])
+def test_muon_step_weight_decay_is_decoupled(shape, scale):
+    # W_new = W - lr (wd W + s O) with O from the SVD closed form: the decay
+    # multiplies W by lr*wd and is added to the scaled direction, not to it
+    # before orthogonalisation.
+    r = rng(41)
+    w = r.standard_normal(shape) * 0.02
+    v = r.standard_normal(shape)
+    g = r.standard_normal(shape)
+    w_new, v_new, _ = muon_step(w, g, v, mu=0.5, lr=0.25, wd=0.5, steps=2, dtype="f32")
+    o_ref = svd_closed_form(v_new, 2)
+    w_ref = (w - 0.25 * (0.5 * w + scale * o_ref)).astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(w_new, w_ref, rtol=0, atol=1e-6)
+    w0, _, _ = muon_step(w, g, v, mu=0.5, lr=0.25, wd=0.0, steps=2, dtype="f32")
+    np.testing.assert_allclose(w_new - w0, -0.125 * w, rtol=0, atol=1e-6)
+
+
 # --------------------------------------------------------------------------
 # RMNP
 # --------------------------------------------------------------------------
