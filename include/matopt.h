@@ -9,7 +9,7 @@
  *   momentum        V <- mu*V + G                              (heavy ball)
  *   normalisation   X0 = V / (||V||_F + eps)
  *   transpose       work on X0^T when rows > cols (strict)
- *   ns_steps times  A = X X^T ; B = b*A + c*A*A ; X = a*X + B*X
+ *   ns_steps times  A = X X^T ; B = a*I + b*A + c*A*A ; X = B*X
  *   update          W <- W - lr * sqrt(max(1, rows/cols)) * O     (O = last X,
  *                                                                 transposed back)
  *
@@ -109,6 +109,23 @@ matopt_status muon_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The Muon step with decoupled weight decay folded into the update, the
+ * configuration the MatrixFSDP paper trains with (section 5.1: weight decay
+ * 1e-2, momentum 0.5, two Newton-Schulz steps):
+ *   W <- W - lr * (wd * W + sqrt(max(1, rows/cols)) * O)     (one rounding)
+ * Decoupled (the decay scales W by lr*wd and does not pass through the
+ * orthogonalization) is the reading taken for the paper's "weight decay".
+ *   wd          weight decay, finite (MATOPT_ERR_PARAM otherwise); wd = 0 gives
+ *               exactly muon_step_batched's result.
+ * Every other argument, the workspace and the error behaviour are those of
+ * muon_step_batched.
+ */
+matopt_status muon_step_batched_wd(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                   float mu, float lr, float wd, int32_t ns_steps,
+                                   float a, float b, float c, float eps,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One RMNP step on every matrix of `mats` (blog post, section 1 RMNP direction and
  * the appendix's rmnp_local step): V <- mu*V + G (one rounding to storage); row
  * sums of squares of the stored V in float32; W <- W - lr*sqrt(max(1,rows/cols)) *
@@ -146,7 +163,7 @@ int32_t matopt_version(void);
  * bracketed by hipEvents on the stream it is launched on, and per-kernel-class
  * elapsed times are accumulated when matopt_profile_read() is called (which
  * synchronises on those events).  Classes: 0 momentum+norm+X0 build,
- * 1 norm finalize, 2 Gram X X^T, 3 polynomial b*A+c*A*A, 4 apply a*X+B*X
+ * 1 norm finalize, 2 Gram X X^T, 3 polynomial a*I+b*A+c*A*A, 4 apply B*X
  * (incl. fused update on the last step), 5 ns_steps==0 output, 6 RMNP.
  */
 #define MATOPT_PROFILE_CLASSES 7

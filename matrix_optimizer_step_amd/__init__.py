@@ -22,7 +22,7 @@ import threading
 import torch
 
 __all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
-           "rmnp_step_batched", "ns_orthogonalize_batched", "profile_enable",
+           "muon_step_batched_wd", "rmnp_step_batched", "ns_orthogonalize_batched", "profile_enable",
            "profile_read", "PROFILE_CLASSES", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmatopt.so")
@@ -55,6 +55,8 @@ EXPORTS = {
     "matopt_workspace_bytes": (_sz, [ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, _i32]),
     "muon_step_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _i32, _f32,
                                  _f32, _f32, _f32, _vp, _sz, _vp]),
+    "muon_step_batched_wd": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _i32,
+                                    _f32, _f32, _f32, _f32, _vp, _sz, _vp]),
     "rmnp_step_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _vp]),
     "ns_orthogonalize_batched": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                         ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32,
@@ -181,6 +183,21 @@ def muon_step_batched(weights, grads, moms, mu=0.95, lr=0.02, ns_steps=5,
     a, b, c = coeffs
     _check(lib().muon_step_batched(arr, n, _dt(dtype), mu, lr, ns_steps, a, b, c, eps,
                                    wp, wb, _stream_ptr(device, stream)))
+
+
+def muon_step_batched_wd(weights, grads, moms, mu=0.5, lr=1e-3, wd=1e-2, ns_steps=2,
+                         coeffs=NS_COEFFS, eps=1e-7, workspace=None, stream=None):
+    """The Muon step with decoupled weight decay, W <- W - lr*(wd*W + s*O); the
+    defaults are the MatrixFSDP paper's training configuration (section 5.1)."""
+    arr, n, dtype = _mats(weights, grads, moms)
+    if n == 0:
+        return
+    device = weights[0].device
+    shapes = [tuple(w.shape) for w in weights]
+    wp, wb, _keep = _workspace(device, dtype, shapes, workspace)
+    a, b, c = coeffs
+    _check(lib().muon_step_batched_wd(arr, n, _dt(dtype), mu, lr, wd, ns_steps, a, b, c,
+                                      eps, wp, wb, _stream_ptr(device, stream)))
 
 
 def rmnp_step_batched(weights, grads, moms, mu=0.95, lr=0.02, eps=1e-12, stream=None):

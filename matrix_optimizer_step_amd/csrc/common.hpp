@@ -83,6 +83,7 @@ struct GemmParams {
   int32_t out_kind;   // OutKind (stage 2)
   int32_t out_dt;     // dtype of O for OUT_O
   float a, b, c, lr;
+  double wdl;         // lr * weight decay (exact product), 0: no decay
 };
 
 // ns_steps == 0: O = xs * V directly (prep tiles over the original orientation).
@@ -92,6 +93,7 @@ struct ScaleOutParams {
   int32_t out_kind;   // OUT_O or OUT_W_UPDATE
   int32_t out_dt;
   float lr;
+  double wdl;         // lr * weight decay, 0: no decay
 };
 
 // RMNP: a block handles `rows_per_block` consecutive rows of one matrix.

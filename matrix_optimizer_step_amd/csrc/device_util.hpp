@@ -62,6 +62,13 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 __device__ __forceinline__ float lo_bf(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
 
+// The weight update W - lr*wd*W + upd*o in float64, before its one rounding to
+// storage (decoupled weight decay; wdl = lr*wd).  With wdl == 0 it is exactly
+// fma(upd, o, w), so a step without decay is unchanged bit for bit.
+__device__ __forceinline__ double w_update(double w, float upd, float o, double wdl) {
+  return fma((double)upd, (double)o, wdl != 0.0 ? fma(-wdl, w, w) : w);
+}
+
 // Element traits: 16-byte vectors hold E elements of T.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -76,6 +83,8 @@ template <> struct Elem<float> {
   }
   // a*b + c rounded once to storage (float32 fma is exact-then-round)
   __device__ static float fma_store(float a, float b, float c) { return fmaf(a, b, c); }
+  // a float64 value rounded to storage
+  __device__ static float round_store(double x) { return (float)x; }
   __device__ static float load1(const void* p, int64_t i) {
     return gload<float>((const float*)p + i);
   }
@@ -97,6 +106,7 @@ template <> struct Elem<uint16_t> {  // bfloat16
   __device__ static float fma_store(float a, float b, float c) {
     return bf2f(f64_to_bf16(fma((double)a, (double)b, (double)c)));
   }
+  __device__ static float round_store(double x) { return bf2f(f64_to_bf16(x)); }
   __device__ static float load1(const void* p, int64_t i) {
     return bf2f(gload<uint16_t>((const uint16_t*)p + i));
   }

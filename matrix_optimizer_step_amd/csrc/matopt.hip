@@ -396,9 +396,9 @@ matopt_status hip_fail(const char* what, hipError_t e) {
 }
 
 // Enqueue the Newton-Schulz pipeline of a plan.
-matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, int ns_steps,
-                     float a, float b, float c, float eps, int out_kind, int out_dt,
-                     hipStream_t s) {
+matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, double wdl,
+                     int ns_steps, float a, float b, float c, float eps, int out_kind,
+                     int out_dt, hipStream_t s) {
   hipError_t e;
   PrepParams pp{P.d_mats, P.d_prep, mu, momentum ? 1 : 0};
   e = timed(0, s, [&] { return launch_prep(dt, pp, P.n_prep, s); });
@@ -422,6 +422,7 @@ matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, i
     g.b = b;
     g.c = c;
     g.lr = lr;
+    g.wdl = wdl;
     g.stage = 0;
     g.out_kind = OUT_NEXT_X;
     e = timed(2, s, [&] { return gemm(g, P.gram); });
@@ -435,7 +436,7 @@ matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, i
     if (e != hipSuccess) return hip_fail("apply launch", e);
   }
   if (ns_steps == 0) {
-    ScaleOutParams sp{P.d_mats, P.d_prep, out_kind, out_dt, lr};
+    ScaleOutParams sp{P.d_mats, P.d_prep, out_kind, out_dt, lr, wdl};
     e = timed(5, s, [&] { return launch_scale_out(dt, sp, P.n_prep, s); });
     if (e != hipSuccess) return hip_fail("scale_out launch", e);
   }
@@ -493,15 +494,19 @@ size_t matopt_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t 
   return layout(geo, dt).total;
 }
 
-matopt_status muon_step_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt,
-                                float mu, float lr, int32_t ns_steps, float a, float b,
-                                float c, float eps, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+}  // extern "C"
+
+// The Muon step with decoupled weight decay wd (0: the plain step).
+static matopt_status muon_impl(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                               float mu, float lr, float wd, int32_t ns_steps, float a,
+                               float b, float c, float eps, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   matopt_status st = check_common(count, dt);
   if (st != MATOPT_OK) return st;
   if (count == 0) return MATOPT_OK;
   if (!mats) return fail(MATOPT_ERR_NULL, "mats is NULL");
   if (!finite(mu) || !finite(lr)) return fail(MATOPT_ERR_PARAM, "non-finite mu or lr");
+  if (!finite(wd)) return fail(MATOPT_ERR_PARAM, "non-finite weight decay");
   if ((st = check_ns_params(ns_steps, a, b, c, eps)) != MATOPT_OK) return st;
   std::vector<Geo> geo;
   std::vector<Span> spans;
@@ -554,7 +559,26 @@ matopt_status muon_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
       plan_insert(key, plan);
     }
   }
-  return run_ns(*plan, dt, true, mu, lr, ns_steps, a, b, c, eps, OUT_W_UPDATE, dt, s);
+  const double wdl = (double)lr * (double)wd;   // exact: a product of two floats
+  return run_ns(*plan, dt, true, mu, lr, wdl, ns_steps, a, b, c, eps, OUT_W_UPDATE, dt, s);
+}
+
+extern "C" {
+
+matopt_status muon_step_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                float mu, float lr, int32_t ns_steps, float a, float b,
+                                float c, float eps, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return muon_impl(mats, count, dt, mu, lr, 0.f, ns_steps, a, b, c, eps, workspace,
+                   workspace_bytes, stream);
+}
+
+matopt_status muon_step_batched_wd(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                   float mu, float lr, float wd, int32_t ns_steps, float a,
+                                   float b, float c, float eps, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return muon_impl(mats, count, dt, mu, lr, wd, ns_steps, a, b, c, eps, workspace,
+                   workspace_bytes, stream);
 }
 
 matopt_status ns_orthogonalize_batched(const void* const* x, void* const* o, const int64_t* rows,
@@ -616,7 +640,7 @@ matopt_status ns_orthogonalize_batched(const void* const* x, void* const* o, con
       plan_insert(key, plan);
     }
   }
-  return run_ns(*plan, in_dt, false, 0.f, 0.f, ns_steps, a, b, c, eps, OUT_O, out_dt, s);
+  return run_ns(*plan, in_dt, false, 0.f, 0.f, 0.0, ns_steps, a, b, c, eps, OUT_O, out_dt, s);
 }
 
 matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt, float mu,

@@ -152,7 +152,10 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
         store_any(d.o, P.out_dt, off, val[r][c]);
       } else {
         float* w = (float*)d.w + off;
-        gstore<float>(w, fmaf(upd, val[r][c], gload<float>(w)));
+        const float wo = gload<float>(w);
+        // one rounding: float32 fma without decay, float64 then float32 with it
+        gstore<float>(w, P.wdl == 0.0 ? fmaf(upd, val[r][c], wo)
+                                      : (float)w_update(wo, upd, val[r][c], P.wdl));
       }
     }
 }

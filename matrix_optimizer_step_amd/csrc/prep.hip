@@ -196,7 +196,9 @@ __global__ __launch_bounds__(kThreads) void scale_out_kernel(ScaleOutParams P) {
       if (P.out_kind == OUT_O) {
         store_any(d.o, P.out_dt, off, o);
       } else {
-        Tr::store1(d.w, off, Tr::fma_store(step, o, Tr::load1(d.w, off)));
+        const float wo = Tr::load1(d.w, off);
+        Tr::store1(d.w, off, P.wdl == 0.0 ? Tr::fma_store(step, o, wo)
+                                          : Tr::round_store(w_update(wo, step, o, P.wdl)));
       }
     }
   }

@@ -35,13 +35,14 @@ def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
-    keep = [n for n in names if n.startswith("matopt_") or n.endswith("_batched")]
+    keep = [n for n in names if n.startswith("matopt_") or "_batched" in n]
     return sorted(set(keep))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("muon_step_batched", "rmnp_step_batched", "ns_orthogonalize_batched",
+    for n in ("muon_step_batched", "muon_step_batched_wd", "rmnp_step_batched",
+              "ns_orthogonalize_batched",
               "matopt_workspace_bytes", "matopt_status_string", "matopt_last_error_detail"):
         assert n in names
 
@@ -121,6 +122,21 @@ def test_muon_argument_errors(L, mod):
     assert _muon(L, arr, 1, ws=BASE + (2 << 30) - 256 * 4) == ALIAS
     detail = L.matopt_last_error_detail().decode()
     assert "overlaps" in detail
+
+
+def test_muon_wd_argument_errors(L, mod):
+    arr = _mats(mod, [(BASE, BASE + (1 << 30), BASE + (2 << 30), 64, 128)])
+
+    def call(n=1, wd=1e-2, ns=2, ws=BASE * 8):
+        return L.muon_step_batched_wd(arr, n, 1, 0.5, 1e-3, wd, ns, 3.4445, -4.775, 2.0315,
+                                      1e-7, ws, 1 << 40, None)
+    assert call(n=0) == OK
+    assert call(wd=float("nan")) == PARAM
+    assert call(wd=float("-inf")) == PARAM
+    assert call(ns=65) == PARAM
+    assert call(ws=0) == WORKSPACE
+    assert call(wd=float("inf")) == PARAM
+    assert "weight decay" in L.matopt_last_error_detail().decode()
 
 
 def test_rmnp_argument_errors(L, mod):

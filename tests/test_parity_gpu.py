@@ -42,16 +42,17 @@ def _inputs(wl, idx=None):
     return W, V, G
 
 
-def _expect_w(w_old, o_gpu, lr, dtype):
+def _expect_w(w_old, o_gpu, lr, dtype, wd=0.0):
     r, c = w_old.shape
     s = oracle.update_scale(r, c)
-    ref = f64(w_old) - oracle.f32_param(lr) * s * f64(o_gpu)
+    w = f64(w_old)
+    ref = w - oracle.f32_param(lr) * (oracle.f32_param(wd) * w + s * f64(o_gpu))
     st = "bf16" if dtype == torch.bfloat16 else "f32"
     return oracle.round_storage(ref, st)
 
 
-def _check_w(w_new, w_old, o_gpu, lr):
-    exp = _expect_w(w_old, o_gpu, lr, w_new.dtype)
+def _check_w(w_new, w_old, o_gpu, lr, wd=0.0):
+    exp = _expect_w(w_old, o_gpu, lr, w_new.dtype, wd)
     got = f64(w_new)
     exp_t = torch.from_numpy(exp).to(w_new.dtype)
     d = ulp_distance(w_new.cpu(), exp_t)
@@ -239,6 +240,63 @@ def test_muon_step_ns_steps_zero_and_lr_zero(mo):
     torch.cuda.synchronize()
     for w, w1 in zip(W, W1):
         assert torch.equal(w, w1)
+
+
+# MatrixFSDP section 5.1 trains with momentum 0.5, two Newton-Schulz steps and
+# weight decay 1e-2 at lr 1e-3; the second case makes the decay large enough to
+# move most bf16 weights.
+@pytest.mark.parametrize("lr,wd", [(1e-3, 1e-2), (0.05, 0.5)])
+def test_muon_wd_training_config_bf16(mo, lr, wd):
+    shapes = [(700, 1300), (1300, 700), (256, 256), (37, 45), (1, 300), (300, 1)]
+    wl = workloads.small_case("muon_wd", shapes, seed=23)
+    W, V, G = _inputs(wl)
+    W0, V0 = [w.clone() for w in W], [v.clone() for v in V]
+    mo.muon_step_batched_wd(W, G, V, mu=0.5, lr=lr, wd=wd, ns_steps=2)
+    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, ns_steps=2)
+    torch.cuda.synchronize()
+    moved = 0
+    for w, w0, v, v0, g, o in zip(W, W0, V, V0, G, O):
+        _check_v(v, v0, g, 0.5)
+        _check_w(w, w0, o, lr, wd)
+        ref = oracle.ns_orthogonalize(f64(v), steps=2, rounding="bf16")
+        assert relF(f64(o), ref) <= 2e-2
+        moved += int((w != w0).sum())
+    assert moved > 0
+
+
+def test_muon_wd_zero_is_the_plain_step(mo):
+    for dtype, shapes in (("bf16", [(512, 1280), (1280, 512), (37, 45)]),
+                          ("f32", [(256, 512), (65, 129)])):
+        wl = workloads.small_case("wd0", shapes, dtype=dtype, seed=24)
+        W1, V1, G = _inputs(wl)
+        W2, V2 = [w.clone() for w in W1], [v.clone() for v in V1]
+        mo.muon_step_batched(W1, G, V1, mu=0.9, lr=0.03, ns_steps=3)
+        mo.muon_step_batched_wd(W2, G, V2, mu=0.9, lr=0.03, wd=0.0, ns_steps=3)
+        torch.cuda.synchronize()
+        for a, b in zip(W1 + V1, W2 + V2):
+            assert torch.equal(a, b)
+
+
+def test_muon_wd_f32_and_ns_steps_zero(mo):
+    # float32 storage (vector and ragged-width rows), then the ns_steps == 0 path
+    wl = workloads.small_case("wd_f32", [(256, 512), (65, 129)], dtype="f32", seed=25)
+    W, V, G = _inputs(wl)
+    W0, V0 = [w.clone() for w in W], [v.clone() for v in V]
+    mo.muon_step_batched_wd(W, G, V, mu=0.5, lr=0.05, wd=0.5, ns_steps=2)
+    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, ns_steps=2)
+    torch.cuda.synchronize()
+    for w, w0, v, v0, g, o in zip(W, W0, V, V0, G, O):
+        _check_v(v, v0, g, 0.5)
+        _check_w(w, w0, o, 0.05, 0.5)
+        assert relF(f64(o), oracle.ns_orthogonalize(f64(v), steps=2)) <= 1e-4
+    wl = workloads.small_case("wd_ns0", [(128, 640), (640, 128), (33, 70)], seed=26)
+    W, V, G = _inputs(wl)
+    W0 = [w.clone() for w in W]
+    mo.muon_step_batched_wd(W, G, V, mu=0.5, lr=0.05, wd=0.5, ns_steps=0)
+    O = mo.ns_orthogonalize_batched(V, ns_steps=0)
+    torch.cuda.synchronize()
+    for w, w0, o in zip(W, W0, O):
+        _check_w(w, w0, o, 0.05, 0.5)
 
 
 def test_muon_step_zero_inputs(mo):
