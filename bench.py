@@ -105,6 +105,52 @@ def cpu_baseline(wl, budget_s=15.0):
                       f"{t_total:.1f} s measured, scaled by NS flop share"}
 
 
+def square_sweep(args):
+    """One s x s bf16 matrix per size (the blog post's single-matrix size sweep,
+    without the gather that its distributed setting adds): the whole Muon step,
+    Newton-Schulz alone, and the RMNP step, each timed like the main bench."""
+    import torch
+    import matrix_optimizer_step_amd as mo
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    rows = []
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1337)
+    for sz in (1024, 2048, 4096, 8192):
+        W = [(torch.randn(sz, sz, device="cuda", generator=g) * 0.02).bfloat16()]
+        V = [(torch.randn(sz, sz, device="cuda", generator=g) * 1e-3).bfloat16()]
+        G = [(torch.randn(sz, sz, device="cuda", generator=g) * 1e-3).bfloat16()]
+        O = [torch.empty(sz, sz, dtype=torch.bfloat16, device="cuda")]
+        muon = timed(lambda: mo.muon_step_batched(W, G, V, mu=0.95, lr=0.02, ns_steps=5))
+        ns = timed(lambda: mo.ns_orthogonalize_batched(V, out_dtype=torch.bfloat16, outs=O))
+        rmnp = timed(lambda: mo.rmnp_step_batched(W, G, V, mu=0.95, lr=0.02))
+        fl = ns_alg_flops([(sz, sz)], 5)
+        rows.append({"s": sz, "muon_step_ms": round(muon, 4), "ns_ms": round(ns, 4),
+                     "rmnp_step_ms": round(rmnp, 4), "muon_over_rmnp": round(muon / rmnp, 1),
+                     "ns_tflops": round(fl / (ns * 1e-3) / 1e12, 1),
+                     "rmnp_GB_s": round(10 * sz * sz / (rmnp * 1e-3) / 1e9, 1)})
+        log(f"[sweep] {sz}x{sz}: muon {muon:.3f} ms, NS {ns:.3f} ms, rmnp {rmnp:.3f} ms")
+        del W, V, G, O
+    return {"metric": "single s x s bf16 matrix: Muon step vs RMNP step (ms)", "unit": "ms",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+            "data": "synthetic (torch.randn, W 0.02, V and G 1e-3)",
+            "config": {"workload": "square_sweep", "sizes": [1024, 2048, 4096, 8192],
+                       "ns_steps": 5}, "sweep": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +160,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rmnp", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step benchmark: one s x s bf16 matrix for s in "
+                         "1024..8192, Muon step vs Newton-Schulz alone vs RMNP step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (float32), the "
                          "known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
@@ -131,6 +180,9 @@ def main():
     import workloads
 
     mo.lib()
+    if args.sweep:
+        print(json.dumps(square_sweep(args)), flush=True)
+        return
     wl = workloads.get(args.workload)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     log(f"[bench] workload {wl.name}: {len(wl.shapes)} matrices, {wl.numel / 1e6:.1f}M elements")
@@ -248,6 +300,25 @@ def main():
                           "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                           "muon_over_rmnp": round(ms / rms, 1)}
         log(f"[bench] rmnp step {rms:.3f} ms ({gbs:.0f} GB/s)")
+
+    # MatrixFSDP's training configuration (section 5.1) on the same matrices:
+    # momentum 0.5, 2 Newton-Schulz steps, decoupled weight decay 1e-2, lr 1e-3
+    def step_wd():
+        mo.muon_step_batched_wd(W, G, V, mu=0.5, lr=1e-3, wd=1e-2, ns_steps=2)
+
+    for _ in range(args.warmup):
+        step_wd()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step_wd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wms = e0.elapsed_time(e1) / args.steps
+    result["training_config"] = {"ms_per_step": round(wms, 4), "mu": 0.5, "lr": 1e-3,
+                                 "wd": 1e-2, "ns_steps": 2,
+                                 "ns_alg_tflop_per_step": round(ns_alg_flops(wl.shapes, 2) / 1e12, 4)}
+    log(f"[bench] training-config muon step {wms:.3f} ms")
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
