@@ -14,11 +14,14 @@ Sources (cited by page title and section):
 
 * "Optimizers In A Sharded World: Muon's O(mn) Vs RMNP's Zero" (blog post):
   section 1 (heavy-ball momentum, the Muon target direction, the RMNP row
-  direction), section 8 (summary), and the appendix "The Code That Ran"
-  (the five-step Newton-Schulz routine, the ``rmnp_local`` and ``muon_sc``
-  steps with their update scale).
+  direction), section 3 (the column-cut layout's row sums), section 8
+  (summary), and the appendix "The Code That Ran" (the five-step Newton-Schulz
+  routine, the ``rmnp_local``, ``rmnp_colcut`` and ``muon_sc`` steps with their
+  update scale).
 * "MatrixFSDP" (arXiv 2607.05895), section 3 and section 4.4: the owner runs
-  the whole-matrix Newton-Schulz update locally on each matrix it owns.
+  the whole-matrix Newton-Schulz update locally on each matrix it owns;
+  section 5.1: the training configuration (weight decay, momentum 0.5, two
+  Newton-Schulz steps).
 
 Parity status of every function is listed in ``oracle/muon.py``'s header.
 """
@@ -29,6 +32,7 @@ from .muon import (  # noqa: F401
     NS_EPS,
     MOMENTUM,
     RMNP_EPS,
+    RMNP_COLCUT_EPS,
     f32_param,
     round_bf16,
     round_storage,
@@ -40,4 +44,6 @@ from .muon import (  # noqa: F401
     muon_step,
     rmnp_direction,
     rmnp_step,
+    rmnp_colcut_partial,
+    rmnp_colcut_apply,
 )

@@ -19,10 +19,20 @@ Blog post "Optimizers In A Sharded World: Muon's O(mn) Vs RMNP's Zero":
   fp32 row normalisation with the library default ``max(||v||, 1e-12)``
   clamp, the same update scale).
 
+* Section 3, the column-cut layout, and the appendix's ``rmnp_colcut``: each
+  rank holds a column slice of every matrix, computes one partial sum of
+  squares per row of its updated momentum slice, the partials of all matrices
+  are summed over the ranks, and each slice is divided by the clamped root
+  (``max(sqrt(.), 1e-7)``).  ``rmnp_colcut_partial`` and ``rmnp_colcut_apply``
+  are the two local halves on one slice; the sum over ranks happens between
+  them.
+
 MatrixFSDP (arXiv 2607.05895), section 3 and section 4.4: each owner applies
 this update to the whole 2D matrices it owns, independently per matrix; there
 is no cross-matrix coupling, which is why every function below works on one
-matrix at a time.
+matrix at a time.  Section 5.1: the training configuration adds weight decay
+1e-2 (with momentum 0.5 and two Newton-Schulz steps); ``muon_step`` takes it
+as decoupled decay, ``W - lr (wd W + s O)``.
 
 Readings taken where the pages leave a step open (each is listed in the design
 notes with its reason):
@@ -66,6 +76,8 @@ NS_EPS = 1e-7
 MOMENTUM = 0.95
 # The row normalisation in the appendix calls the library default clamp.
 RMNP_EPS = 1e-12
+# The column-cut RMNP listing clamps the all-reduced norm at 1e-7.
+RMNP_COLCUT_EPS = 1e-7
 
 
 def f32_param(p: float) -> float:
@@ -223,3 +235,26 @@ def rmnp_step(w, g, v, mu: float = MOMENTUM, lr: float = 0.02,
     s = update_scale(rows, cols)
     w_new = round_storage(w - f32_param(lr) * s * u, dtype)
     return w_new, v_new, u
+
+
+def rmnp_colcut_partial(v, g, mu: float = MOMENTUM, dtype: str = "bf16"):
+    """Column-cut RMNP, the local half on one column slice (blog post, section 3,
+    the column-cut layout; appendix ``rmnp_colcut``): momentum on the slice, then
+    one partial sum of squares per row of the stored slice.  The row's squared
+    norm is the sum of these partials over the slices of the row.
+    Returns ``(V_new, rowsq)``."""
+    v_new = momentum(v, g, mu, dtype)
+    return v_new, np.sum(v_new * v_new, axis=1)
+
+
+def rmnp_colcut_apply(w, v_new, rowsq, lr: float = 0.02, eps: float = RMNP_COLCUT_EPS,
+                      full_cols: int | None = None, dtype: str = "bf16") -> np.ndarray:
+    """The update of one column slice once the row sums of squares are summed
+    over all slices: ``W - lr sqrt(max(1, rows/full_cols)) V / max(sqrt(rowsq), eps)``
+    with the whole matrix's shape in the scale (rows x full_cols) and one
+    rounding.  The column-cut listing clamps the norm at 1e-7."""
+    w = _f64(w)
+    rows, cols = w.shape
+    s = update_scale(rows, cols if full_cols is None else full_cols)
+    u = _f64(v_new) / np.maximum(np.sqrt(_f64(rowsq)), f32_param(eps))[:, None]
+    return round_storage(w - f32_param(lr) * s * u, dtype)

@@ -404,3 +404,39 @@ def test_rmnp_step_scale_tall():
     w_new, v_new, u = rmnp_step(w, g, v, mu=0.95, lr=0.1, dtype="f32")
     ref = (w - 0.1 * 2.0 * v_new / np.linalg.norm(v_new, axis=1, keepdims=True))
     np.testing.assert_allclose(w_new, ref.astype(np.float32), rtol=0, atol=1e-7)
+
+
+# --------------------------------------------------------------------------
+# Column-cut RMNP (local halves)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,cuts", [((12, 40), [0, 7, 20, 40]), ((40, 12), [0, 5, 12]),
+                                        ((9, 9), [0, 9])])
+def test_rmnp_colcut_slices_reproduce_the_row_local_step(shape, cuts):
+    # A row's squared norm is the sum of its slices' squared norms: partials
+    # summed over the slices, then each slice updated with the whole matrix's
+    # scale, give the row-local RMNP step (pinned against torch's normalize).
+    r = rng(50)
+    w = r.standard_normal(shape) * 0.02
+    v = r.standard_normal(shape)
+    g = r.standard_normal(shape)
+    parts = [oracle.rmnp_colcut_partial(v[:, a:b], g[:, a:b], mu=0.9, dtype="f32")
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    rowsq = sum(pp[1] for pp in parts)
+    w_cut = np.concatenate([oracle.rmnp_colcut_apply(w[:, a:b], pp[0], rowsq, lr=0.3,
+                                                     eps=1e-7, full_cols=shape[1], dtype="f32")
+                            for (a, b), pp in zip(zip(cuts[:-1], cuts[1:]), parts)], axis=1)
+    w_ref, v_ref, _ = oracle.rmnp_step(w, g, v, mu=0.9, lr=0.3, eps=1e-7, dtype="f32")
+    assert np.array_equal(np.concatenate([pp[0] for pp in parts], axis=1), v_ref)
+    np.testing.assert_allclose(w_cut, w_ref, rtol=0, atol=1e-7)
+
+
+def test_rmnp_colcut_clamp_and_zero_row():
+    # rowsq = 0 leaves W; a norm below the 1e-7 clamp divides by 1e-7 exactly
+    w = np.array([[0.5, -0.25], [0.125, 1.0]])
+    v = np.array([[0.0, 0.0], [3e-9, 4e-9]])   # second row norm 5e-9 < 1e-7
+    rowsq = np.array([0.0, 25e-18])
+    out = oracle.rmnp_colcut_apply(w, v, rowsq, lr=0.5, eps=1e-7, dtype="f32")
+    eps = float(np.float32(1e-7))
+    exp = np.array([[0.5, -0.25], [0.125 - 0.5 * 3e-9 / eps, 1.0 - 0.5 * 4e-9 / eps]])
+    np.testing.assert_allclose(out, exp.astype(np.float32), rtol=0, atol=1e-7)
