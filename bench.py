@@ -301,6 +301,36 @@ def main():
                           "muon_over_rmnp": round(ms / rms, 1)}
         log(f"[bench] rmnp step {rms:.3f} ms ({gbs:.0f} GB/s)")
 
+    # Column-cut RMNP, both local halves on whole-width slices (one rank: the
+    # sum over ranks between them is the identity)
+    if not args.no_rmnp:
+        rowsq = torch.empty(sum(r for r, _ in wl.shapes), dtype=torch.float32, device="cuda")
+
+        def colcut():
+            mo.rmnp_colcut_partial_batched(G, V, rowsq=rowsq, mu=wl.mu)
+            mo.rmnp_colcut_apply_batched(W, V, rowsq, lr=wl.lr)
+
+        for _ in range(args.warmup):
+            colcut()
+        torch.cuda.synchronize()
+        mo.profile_read()
+        mo.profile_enable(True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            colcut()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mo.profile_enable(False)
+        cms = e0.elapsed_time(e1) / args.steps
+        cp = mo.profile_read()
+        cgbs = 12 * esz / 2 * numel / (cms * 1e-3) / 1e9
+        result["rmnp_colcut"] = {
+            "ms_per_step": round(cms, 4), "bytes_per_elem": 6 * esz, "GB_s": round(cgbs, 1),
+            "frac_hbm": round(cgbs / PEAK_HBM_GBS, 4),
+            "partial_ms": round(cp["colcut_partial"][0] / args.steps, 4),
+            "apply_ms": round(cp["colcut_apply"][0] / args.steps, 4)}
+        log(f"[bench] column-cut rmnp {cms:.3f} ms ({cgbs:.0f} GB/s)")
+
     # MatrixFSDP's training configuration (section 5.1) on the same matrices:
     # momentum 0.5, 2 Newton-Schulz steps, decoupled weight decay 1e-2, lr 1e-3
     def step_wd():

@@ -136,6 +136,34 @@ matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
                                 float mu, float lr, float eps, void* stream);
 
 /*
+ * Column-cut RMNP, the two local halves on one rank (blog post, section 3, the
+ * column-cut layout; appendix rmnp_colcut).  Each matrix of `mats` is this
+ * rank's column slice (rows x cols) of a whole matrix (rows x full_cols[i]).
+ * The row sums of squares of all matrices form one float32 vector `rowsq` of
+ * sum(rows) entries, matrix i's rows starting after those of matrices 0..i-1.
+ * Between the two calls the caller sums `rowsq` over the ranks that hold the
+ * other slices (one all-reduce); on a single rank nothing happens in between.
+ *
+ * rmnp_colcut_partial_batched: V <- mu*V + G (one rounding to storage), then
+ *   rowsq[row] = sum over this slice of the stored V[row, :]^2, in float32 in a
+ *   fixed order (deterministic).  mats[i].w is not used (may be NULL).
+ *   rowsq: DEVICE pointer, 4-byte aligned, overwritten.
+ * rmnp_colcut_apply_batched: W <- W - lr*sqrt(max(1, rows/full_cols[i])) *
+ *   V / max(sqrt(rowsq[row]), eps)   (one rounding).  mats[i].g is not used
+ *   (may be NULL); V and rowsq are read only.  eps: 1e-7 in the column-cut
+ *   listing, >= 0.  full_cols: HOST array of count entries, each >= the slice's
+ *   cols (MATOPT_ERR_SHAPE otherwise), or NULL for full_cols[i] = cols.
+ * Both need no workspace; rowsq must not overlap any matrix (MATOPT_ERR_ALIAS).
+ */
+matopt_status rmnp_colcut_partial_batched(const matopt_mat* mats, int32_t count,
+                                          matopt_dtype dt, float mu, float* rowsq,
+                                          void* stream);
+matopt_status rmnp_colcut_apply_batched(const matopt_mat* mats, int32_t count,
+                                        matopt_dtype dt, float lr, float eps,
+                                        const float* rowsq, const int64_t* full_cols,
+                                        void* stream);
+
+/*
  * Newton-Schulz only (the appendix's routine): o[i] = NS(x[i]) for each matrix,
  * in the original orientation.  x[i]: rows[i] x cols[i] in `in_dt` (selects the
  * compute path as `dt` does above); o[i]: same shape in `out_dt` (F32 or BF16).
@@ -164,9 +192,10 @@ int32_t matopt_version(void);
  * elapsed times are accumulated when matopt_profile_read() is called (which
  * synchronises on those events).  Classes: 0 momentum+norm+X0 build,
  * 1 norm finalize, 2 Gram X X^T, 3 polynomial a*I+b*A+c*A*A, 4 apply B*X
- * (incl. fused update on the last step), 5 ns_steps==0 output, 6 RMNP.
+ * (incl. fused update on the last step), 5 ns_steps==0 output, 6 RMNP,
+ * 7 column-cut RMNP partial, 8 column-cut RMNP apply.
  */
-#define MATOPT_PROFILE_CLASSES 7
+#define MATOPT_PROFILE_CLASSES 9
 matopt_status matopt_profile_enable(int32_t on);
 /* ms[k], launches[k] for k < MATOPT_PROFILE_CLASSES; resets the accumulators. */
 matopt_status matopt_profile_read(double* ms, int64_t* launches);

@@ -22,13 +22,15 @@ import threading
 import torch
 
 __all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
-           "muon_step_batched_wd", "rmnp_step_batched", "ns_orthogonalize_batched", "profile_enable",
+           "muon_step_batched_wd", "rmnp_step_batched", "rmnp_colcut_partial_batched",
+           "rmnp_colcut_apply_batched", "ns_orthogonalize_batched", "profile_enable",
            "profile_read", "PROFILE_CLASSES", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmatopt.so")
 
 F32, BF16 = 0, 1
-PROFILE_CLASSES = ("prep", "finalize", "gram", "poly", "apply", "scale_out", "rmnp")
+PROFILE_CLASSES = ("prep", "finalize", "gram", "poly", "apply", "scale_out", "rmnp",
+                   "colcut_partial", "colcut_apply")
 
 # Defaults printed on the pages (blog post appendix).
 NS_COEFFS = (3.4445, -4.7750, 2.0315)
@@ -58,6 +60,9 @@ EXPORTS = {
     "muon_step_batched_wd": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _i32,
                                     _f32, _f32, _f32, _f32, _vp, _sz, _vp]),
     "rmnp_step_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _vp]),
+    "rmnp_colcut_partial_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _vp, _vp]),
+    "rmnp_colcut_apply_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _vp,
+                                         ctypes.POINTER(_i64), _vp]),
     "ns_orthogonalize_batched": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                         ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32,
                                         _i32, _i32, _i32, _f32, _f32, _f32, _f32, _vp, _sz,
@@ -208,6 +213,60 @@ def rmnp_step_batched(weights, grads, moms, mu=0.95, lr=0.02, eps=1e-12, stream=
     device = weights[0].device
     _check(lib().rmnp_step_batched(arr, n, _dt(dtype), mu, lr, eps,
                                    _stream_ptr(device, stream)))
+
+
+def _colcut_mats(weights, moms, others, what):
+    n = len(moms)
+    if n == 0:
+        return None, 0, None
+    dtype = moms[0].dtype
+    arr = (_Mat * n)()
+    for i, v in enumerate(moms):
+        _check_mat(v, f"moms[{i}]", dtype)
+        o = others[i]
+        _check_mat(o, f"{what}[{i}]", dtype)
+        if o.shape != v.shape:
+            raise ValueError(f"{what}[{i}] shape differs from moms[{i}]")
+        w = o.data_ptr() if what == "weights" else None
+        g = o.data_ptr() if what == "grads" else None
+        arr[i] = _Mat(w, g, v.data_ptr(), v.shape[0], v.shape[1])
+    return arr, n, dtype
+
+
+def rmnp_colcut_partial_batched(grads, moms, rowsq=None, mu=0.95, stream=None):
+    """Column-cut RMNP, first local half: V <- mu V + G on each column slice and
+    the float32 row sums of squares of the stored slices, concatenated over the
+    matrices into ``rowsq`` (allocated if not given).  Returns ``rowsq``; sum it
+    over the ranks holding the other slices before the apply half."""
+    arr, n, dtype = _colcut_mats(None, moms, grads, "grads")
+    if n == 0:
+        return rowsq
+    device = moms[0].device
+    total = sum(v.shape[0] for v in moms)
+    if rowsq is None:
+        rowsq = torch.empty(total, dtype=torch.float32, device=device)
+    if rowsq.dtype != torch.float32 or rowsq.numel() < total or not rowsq.is_contiguous():
+        raise ValueError("rowsq must be a contiguous float32 tensor of sum(rows) entries")
+    _check(lib().rmnp_colcut_partial_batched(arr, n, _dt(dtype), mu, rowsq.data_ptr(),
+                                             _stream_ptr(device, stream)))
+    return rowsq
+
+
+def rmnp_colcut_apply_batched(weights, moms, rowsq, full_cols=None, lr=0.02, eps=1e-7,
+                              stream=None):
+    """Column-cut RMNP, second local half: W <- W - lr s V / max(sqrt(rowsq), eps)
+    on each column slice, with s from the whole matrix's shape (rows x
+    full_cols[i]; default: the slice's own width)."""
+    arr, n, dtype = _colcut_mats(weights, moms, weights, "weights")
+    if n == 0:
+        return
+    device = moms[0].device
+    total = sum(v.shape[0] for v in moms)
+    if rowsq.dtype != torch.float32 or rowsq.numel() < total or not rowsq.is_contiguous():
+        raise ValueError("rowsq must be a contiguous float32 tensor of sum(rows) entries")
+    fc = None if full_cols is None else (_i64 * n)(*full_cols)
+    _check(lib().rmnp_colcut_apply_batched(arr, n, _dt(dtype), lr, eps, rowsq.data_ptr(), fc,
+                                           _stream_ptr(device, stream)))
 
 
 def ns_orthogonalize_batched(xs, out_dtype=torch.float32, ns_steps=5, coeffs=NS_COEFFS,

@@ -107,6 +107,13 @@ struct RmnpParams {
   float mu, lr, eps;
 };
 
+// Column-cut RMNP halves: a block handles 4 consecutive rows (one per wave).
+struct ColcutParams {
+  const MatDesc* mats;   // partials: this matrix's row-sum entries
+  const RmnpTask* tasks;
+  float mu, lr, eps;
+};
+
 // Tile geometry.
 constexpr int kPrepTile = 64;
 constexpr int kTileBf16 = 256;
@@ -123,5 +130,7 @@ hipError_t launch_gemm_f32(const GemmParams& p, int n_tiles, hipStream_t s);
 // streaming two-pass variant (any width, scalar loads).
 hipError_t launch_rmnp(int dt, int wpr, int nch, const RmnpParams& p, int n_tasks,
                        hipStream_t s);
+// Column-cut RMNP: apply == false launches the partial half, true the update.
+hipError_t launch_colcut(int dt, bool apply, const ColcutParams& p, int n_tasks, hipStream_t s);
 
 }  // namespace matopt

@@ -194,7 +194,7 @@ hipError_t timed(int cls, hipStream_t s, F&& launch) {
 }
 
 // ---------------------------------------------------------------- plans
-enum PlanKind { PK_MUON = 1, PK_NS = 2, PK_RMNP = 3 };
+enum PlanKind { PK_MUON = 1, PK_NS = 2, PK_RMNP = 3, PK_COLCUT_PARTIAL = 4, PK_COLCUT_APPLY = 5 };
 
 struct RmnpGroup {
   int wpr, nch, n;
@@ -456,6 +456,109 @@ matopt_status check_ns_params(int32_t ns_steps, float a, float b, float c, float
   return MATOPT_OK;
 }
 
+// Column-cut RMNP plan: descriptors whose `partials` point into the caller's
+// row-sum vector (matrix i starts at the sum of the rows before it) and one
+// task per 4 rows.  full_cols (NULL: the slice's own width) sets the update
+// scale from the whole matrix's shape.
+matopt_status build_colcut_plan(Plan& P, int dt, const matopt_mat* mats, int count,
+                                const float* rowsq, const int64_t* full_cols, hipStream_t s) {
+  const int E = 16 / esize(dt);
+  std::vector<MatDesc> descs(count);
+  std::vector<RmnpTask> tasks;
+  int64_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    MatDesc& d = descs[i];
+    std::memset(&d, 0, sizeof(d));
+    d.w = mats[i].w;
+    d.g = mats[i].g;
+    d.v = mats[i].v;
+    d.rows = mats[i].rows;
+    d.cols = mats[i].cols;
+    const int64_t fc = full_cols ? full_cols[i] : d.cols;
+    d.upd_scale = (float)std::sqrt(std::max(1.0, (double)d.rows / (double)fc));
+    d.vec_ok = d.cols % E == 0 ? 1 : 0;
+    d.partials = const_cast<float*>(rowsq) + off;
+    off += d.rows;
+    for (int64_t r = 0; r < d.rows; r += 4) tasks.push_back({i, (int32_t)r});
+  }
+  HostBuf hb;
+  const size_t o_mats = hb.put(descs);
+  RmnpGroup g;
+  g.wpr = 1;
+  g.nch = 0;
+  g.n = (int)tasks.size();
+  g.off = hb.put(tasks);
+  P.rmnp.push_back(g);
+  matopt_status st = upload(P, hb, s);
+  if (st != MATOPT_OK) return st;
+  P.d_mats = at<MatDesc>(P.dbuf, o_mats);
+  P.count = count;
+  return MATOPT_OK;
+}
+
+// Shared by both column-cut halves: validation, plan lookup, one launch.
+matopt_status colcut_run(bool apply, const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                         float mu, float lr, float eps, const float* rowsq,
+                         const int64_t* full_cols, void* stream) {
+  matopt_status st = check_common(count, dt);
+  if (st != MATOPT_OK) return st;
+  if (count == 0) return MATOPT_OK;
+  if (!mats) return fail(MATOPT_ERR_NULL, "mats is NULL");
+  if (!rowsq) return fail(MATOPT_ERR_NULL, "rowsq is NULL");
+  if (((uintptr_t)rowsq & 3) != 0) return fail(MATOPT_ERR_ALIGN, "rowsq not 4-byte aligned");
+  if (!finite(mu) || !finite(lr) || !finite(eps) || eps < 0.f)
+    return fail(MATOPT_ERR_PARAM, "non-finite mu/lr/eps or eps < 0");
+  std::vector<Span> spans;
+  const size_t es = esize(dt);
+  int64_t total_rows = 0;
+  for (int i = 0; i < count; ++i) {
+    const matopt_mat& m = mats[i];
+    const std::string tag = "matrix " + std::to_string(i);
+    void* a = apply ? m.w : const_cast<void*>(m.g);   // the other operand of this half
+    if (!a || !m.v) return fail(MATOPT_ERR_NULL, tag + ": NULL pointer");
+    if ((st = check_shape(m.rows, m.cols, i)) != MATOPT_OK) return st;
+    if (apply && full_cols && (full_cols[i] < m.cols || full_cols[i] > kMaxSide))
+      return fail(MATOPT_ERR_SHAPE, tag + ": full_cols smaller than the slice or too large");
+    if (!aligned16(a) || !aligned16(m.v)) return fail(MATOPT_ERR_ALIGN, tag + ": pointer not 16-byte aligned");
+    const size_t bytes = (size_t)m.rows * m.cols * es;
+    spans.push_back({(uintptr_t)a, (uintptr_t)a + bytes, tag + (apply ? " W" : " G")});
+    spans.push_back({(uintptr_t)m.v, (uintptr_t)m.v + bytes, tag + " V"});
+    total_rows += m.rows;
+  }
+  spans.push_back({(uintptr_t)rowsq, (uintptr_t)rowsq + (size_t)total_rows * 4, "rowsq"});
+  if ((st = check_overlap(spans)) != MATOPT_OK) return st;
+  int dev;
+  if ((st = check_device(&dev)) != MATOPT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  PlanKey key{(uint64_t)(apply ? PK_COLCUT_APPLY : PK_COLCUT_PARTIAL), (uint64_t)dt, (uint64_t)dev,
+              (uint64_t)count, (uint64_t)(uintptr_t)rowsq};
+  for (int i = 0; i < count; ++i) {
+    key.push_back((uint64_t)mats[i].rows);
+    key.push_back((uint64_t)mats[i].cols);
+    key.push_back((uint64_t)(uintptr_t)(apply ? mats[i].w : mats[i].g));
+    key.push_back((uint64_t)(uintptr_t)mats[i].v);
+    key.push_back((uint64_t)(apply && full_cols ? full_cols[i] : mats[i].cols));
+  }
+  std::shared_ptr<Plan> plan;
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    plan = plan_lookup(key);
+    if (!plan) {
+      plan = std::make_shared<Plan>();
+      plan->device = dev;
+      if ((st = build_colcut_plan(*plan, dt, mats, count, rowsq, apply ? full_cols : nullptr, s)) !=
+          MATOPT_OK)
+        return st;
+      plan_insert(key, plan);
+    }
+  }
+  const RmnpGroup& g = plan->rmnp[0];
+  ColcutParams cp{plan->d_mats, at<RmnpTask>(plan->dbuf, g.off), mu, lr, eps};
+  hipError_t e = timed(apply ? 8 : 7, s, [&] { return launch_colcut(dt, apply, cp, g.n, s); });
+  if (e != hipSuccess) return hip_fail(apply ? "colcut apply launch" : "colcut partial launch", e);
+  return MATOPT_OK;
+}
+
 }  // namespace
 
 // ==================================================================== C ABI
@@ -695,6 +798,17 @@ matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
     if (e != hipSuccess) return hip_fail("rmnp launch", e);
   }
   return MATOPT_OK;
+}
+
+matopt_status rmnp_colcut_partial_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                          float mu, float* rowsq, void* stream) {
+  return colcut_run(false, mats, count, dt, mu, 0.f, 0.f, rowsq, nullptr, stream);
+}
+
+matopt_status rmnp_colcut_apply_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                        float lr, float eps, const float* rowsq,
+                                        const int64_t* full_cols, void* stream) {
+  return colcut_run(true, mats, count, dt, 0.f, lr, eps, rowsq, full_cols, stream);
 }
 
 matopt_status matopt_profile_enable(int32_t on) {

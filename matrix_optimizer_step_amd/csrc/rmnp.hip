@@ -130,6 +130,118 @@ __global__ __launch_bounds__(kThreads) void rmnp_stream_kernel(RmnpParams P) {
   }
 }
 
+// Column-cut RMNP, the two local halves on a column slice of each matrix (blog
+// post, section 3, the column-cut layout; appendix rmnp_colcut).  One wave per
+// row, four rows per workgroup, any width.  d.partials points at the matrix's
+// first entry of the [sum of rows] row-sum vector; d.upd_scale uses the whole
+// matrix's shape.
+//   partial: V <- mu*V + G (one rounding, stored); rowsq[r] = sum of the stored
+//            V[r, :]^2 over this slice in float32 -- per lane over its chunks in
+//            order, then a fixed wave tree (deterministic, batch independent).
+//   apply:   W <- W - lr*s * V / max(sqrt(rowsq[r]), eps)   (one rounding),
+//            after the row sums were summed over all slices.
+// Each lane handles chunks lane, lane + 64, ...; four chunks' loads are issued
+// before their stores.  Algorithmic bytes per element (bf16): partial 6 (read
+// G, V; write V), apply 6 (read V, W; write W).
+constexpr int kColcutUnroll = 4;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void colcut_partial_kernel(ColcutParams P) {
+  using Tr = Elem<T>;
+  constexpr int E = Tr::E;
+  const RmnpTask task = P.tasks[blockIdx.x];
+  const MatDesc& d = P.mats[task.mat];
+  const int64_t row = task.row0 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= d.rows) return;
+  const int64_t cols = d.cols;
+  T* vrow = (T*)d.v + row * cols;
+  const T* grow = (const T*)d.g + row * cols;
+  float ss = 0.f;
+  if (d.vec_ok) {
+    const int64_t nch = cols / E;
+    for (int64_t base = lane; base < nch; base += 64 * kColcutUnroll) {
+      u32x4 vv[kColcutUnroll], gg[kColcutUnroll];
+#pragma unroll
+      for (int u = 0; u < kColcutUnroll; ++u) {
+        const int64_t ch = base + 64 * u;
+        if (ch < nch) {
+          vv[u] = gload<u32x4>(vrow + ch * E);
+          gg[u] = gload<u32x4>(grow + ch * E);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kColcutUnroll; ++u) {
+        const int64_t ch = base + 64 * u;
+        if (ch < nch) {
+          float fv[E], fg[E];
+          Tr::unpack(vv[u], fv);
+          Tr::unpack(gg[u], fg);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            fv[e] = Tr::fma_store(P.mu, fv[e], fg[e]);
+            ss = fmaf(fv[e], fv[e], ss);
+          }
+          gstore<u32x4>(vrow + ch * E, Tr::pack(fv));
+        }
+      }
+    }
+  } else {
+    for (int64_t c = lane; c < cols; c += 64) {
+      const float v = Tr::fma_store(P.mu, Tr::load1(vrow, c), Tr::load1(grow, c));
+      Tr::store1(vrow, c, v);
+      ss = fmaf(v, v, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) gstore<float>(d.partials + row, ss);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void colcut_apply_kernel(ColcutParams P) {
+  using Tr = Elem<T>;
+  constexpr int E = Tr::E;
+  const RmnpTask task = P.tasks[blockIdx.x];
+  const MatDesc& d = P.mats[task.mat];
+  const int64_t row = task.row0 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= d.rows) return;
+  const int64_t cols = d.cols;
+  const T* vrow = (const T*)d.v + row * cols;
+  T* wrow = (T*)d.w + row * cols;
+  const float inv = 1.f / fmaxf(sqrtf(gload<float>(d.partials + row)), P.eps);
+  const float step = -P.lr * d.upd_scale * inv;
+  if (d.vec_ok) {
+    const int64_t nch = cols / E;
+    for (int64_t base = lane; base < nch; base += 64 * kColcutUnroll) {
+      u32x4 vv[kColcutUnroll], ww[kColcutUnroll];
+#pragma unroll
+      for (int u = 0; u < kColcutUnroll; ++u) {
+        const int64_t ch = base + 64 * u;
+        if (ch < nch) {
+          vv[u] = gload<u32x4>(vrow + ch * E);
+          ww[u] = gload<u32x4>(wrow + ch * E);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kColcutUnroll; ++u) {
+        const int64_t ch = base + 64 * u;
+        if (ch < nch) {
+          float fv[E], fw[E];
+          Tr::unpack(vv[u], fv);
+          Tr::unpack(ww[u], fw);
+#pragma unroll
+          for (int e = 0; e < E; ++e) fw[e] = Tr::fma_store(step, fv[e], fw[e]);
+          gstore<u32x4>(wrow + ch * E, Tr::pack(fw));
+        }
+      }
+    }
+  } else {
+    for (int64_t c = lane; c < cols; c += 64)
+      Tr::store1(wrow, c, Tr::fma_store(step, Tr::load1(vrow, c), Tr::load1(wrow, c)));
+  }
+}
+
 template <typename T>
 hipError_t launch_t(int wpr, int nch, const RmnpParams& p, int n, hipStream_t s) {
   dim3 g(n), b(kThreads);
@@ -160,6 +272,19 @@ hipError_t launch_rmnp(int dt, int wpr, int nch, const RmnpParams& p, int n_task
   if (n_tasks <= 0) return hipSuccess;
   return dt == DT_BF16 ? launch_t<uint16_t>(wpr, nch, p, n_tasks, s)
                        : launch_t<float>(wpr, nch, p, n_tasks, s);
+}
+
+hipError_t launch_colcut(int dt, bool apply, const ColcutParams& p, int n_tasks, hipStream_t s) {
+  if (n_tasks <= 0) return hipSuccess;
+  dim3 g(n_tasks), b(kThreads);
+  if (dt == DT_BF16) {
+    if (apply) hipLaunchKernelGGL(colcut_apply_kernel<uint16_t>, g, b, 0, s, p);
+    else hipLaunchKernelGGL(colcut_partial_kernel<uint16_t>, g, b, 0, s, p);
+  } else {
+    if (apply) hipLaunchKernelGGL(colcut_apply_kernel<float>, g, b, 0, s, p);
+    else hipLaunchKernelGGL(colcut_partial_kernel<float>, g, b, 0, s, p);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace matopt

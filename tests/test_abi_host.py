@@ -139,6 +139,23 @@ def test_muon_wd_argument_errors(L, mod):
     assert "weight decay" in L.matopt_last_error_detail().decode()
 
 
+def test_rmnp_colcut_argument_errors(L, mod):
+    # partial: G and V used, W may be NULL; apply: W and V used, G may be NULL
+    part = _mats(mod, [(0, BASE + (1 << 30), BASE + (2 << 30), 64, 128)])
+    rowsq = BASE + (5 << 30)
+    assert L.rmnp_colcut_partial_batched(part, 0, 1, 0.9, rowsq, None) == OK
+    assert L.rmnp_colcut_partial_batched(part, 1, 1, 0.9, None, None) == NULL
+    assert L.rmnp_colcut_partial_batched(part, 1, 1, 0.9, rowsq + 2, None) == ALIGN
+    assert L.rmnp_colcut_partial_batched(part, 1, 1, float("nan"), rowsq, None) == PARAM
+    # rowsq overlapping V
+    assert L.rmnp_colcut_partial_batched(part, 1, 1, 0.9, BASE + (2 << 30) + 64, None) == ALIAS
+    app = _mats(mod, [(BASE, 0, BASE + (2 << 30), 64, 128)])
+    fc = (ctypes.c_int64 * 1)(100)   # narrower than the slice
+    assert L.rmnp_colcut_apply_batched(app, 1, 1, 0.02, 1e-7, rowsq, fc, None) == SHAPE
+    assert L.rmnp_colcut_apply_batched(app, 1, 1, 0.02, -1.0, rowsq, None, None) == PARAM
+    assert L.rmnp_colcut_apply_batched(part, 1, 1, 0.02, 1e-7, rowsq, None, None) == NULL
+
+
 def test_rmnp_argument_errors(L, mod):
     arr = _mats(mod, [(BASE, BASE + (1 << 30), BASE + (2 << 30), 64, 128)])
     assert L.rmnp_step_batched(arr, 0, 1, 0.95, 0.02, 1e-12, None) == OK

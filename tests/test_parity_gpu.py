@@ -61,6 +61,22 @@ def _check_w(w_new, w_old, o_gpu, lr, wd=0.0):
     return float(np.abs(got - exp).max())
 
 
+def _check_w_rmnp(w, exp, upd):
+    """RMNP weights against the oracle: bf16 within 1 ulp (99% exact).  float32:
+    the row norm is summed in float32 (relative error ~1e-7 of the update);
+    where W - lr*s*u cancels towards zero an ulp of the result is far smaller
+    than that, so the bound is one ulp of the result plus 1e-6 of the update."""
+    if w.dtype == torch.bfloat16:
+        d = ulp_distance(w.cpu(), torch.from_numpy(exp).to(w.dtype))
+        assert d.max() <= 1, (w.shape, d.max())
+        assert (d == 0).mean() >= 0.99
+    else:
+        err = np.abs(f64(w) - exp)
+        allowed = (np.spacing(np.abs(exp).astype(np.float32)).astype(np.float64)
+                   + 1e-6 * np.abs(upd))
+        assert (err <= allowed).all(), (w.shape, float((err / allowed).max()))
+
+
 def _check_v(v_new, v_old, g, mu):
     st = "bf16" if v_new.dtype == torch.bfloat16 else "f32"
     exp = oracle.momentum(f64(v_old), f64(g), mu, st)
@@ -370,19 +386,7 @@ def test_rmnp_step(mo, dtype):
         r, c = w.shape
         exp = oracle.round_storage(f64(w0) - oracle.f32_param(0.02) * oracle.update_scale(r, c) * u,
                                    dtype)
-        if dtype == "bf16":
-            d = ulp_distance(w.cpu(), torch.from_numpy(exp).to(w.dtype))
-            assert d.max() <= 1, (w.shape, d.max())
-            assert (d == 0).mean() >= 0.99
-        else:
-            # float32: the row norm is summed in float32 (relative error ~1e-7
-            # of the update); where W - lr*s*u cancels towards zero an ulp of
-            # the result is far smaller than that, so bound the error by one
-            # ulp of the result plus 1e-6 of the update.
-            upd = np.abs(oracle.f32_param(0.02) * oracle.update_scale(r, c) * u)
-            err = np.abs(f64(w) - exp)
-            allowed = np.spacing(np.abs(exp).astype(np.float32)).astype(np.float64) + 1e-6 * upd
-            assert (err <= allowed).all(), (w.shape, float((err / allowed).max()))
+        _check_w_rmnp(w, exp, oracle.f32_param(0.02) * oracle.update_scale(r, c) * u)
 
 
 def test_rmnp_row_split_invariance_bitwise(mo):
@@ -409,3 +413,70 @@ def test_rmnp_zero_row(mo):
     torch.cuda.synchronize()
     assert torch.equal(w[3], w0[3])
     assert not torch.equal(w[2], w0[2])
+
+
+# --------------------------------------------------------------------------
+# Column-cut RMNP (local halves); two ranks simulated on one GPU
+# --------------------------------------------------------------------------
+
+COLCUT = [((300, 1000), [0, 400, 1000]), ((1280, 640), [0, 320, 640]), ((37, 45), [0, 13, 45]),
+          ((64, 8), [0, 8, 8]), ((5, 3000), [0, 1496, 3000])]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rmnp_colcut_two_slices(mo, dtype):
+    shapes = [sh for sh, _ in COLCUT]
+    wl = workloads.small_case("colcut", shapes, dtype=dtype, seed=31, v_std=1.0, g_std=1.0)
+    W, V, G = _inputs(wl)
+    tdt = W[0].dtype
+    ranks = []
+    for k in range(2):
+        sl = [(a[k], a[k + 1]) for _, a in COLCUT]
+        ranks.append({
+            # copies (a slice spanning every column would otherwise alias the whole)
+            "W": [w[:, a:b].clone() for w, (a, b) in zip(W, sl) if b > a],
+            "V": [v[:, a:b].clone() for v, (a, b) in zip(V, sl) if b > a],
+            "G": [g[:, a:b].clone() for g, (a, b) in zip(G, sl) if b > a],
+            "full": [sh[1] for (sh, _), (a, b) in zip(COLCUT, sl) if b > a],
+            "idx": [i for i, (a, b) in enumerate(sl) if b > a]})
+    for r in ranks:
+        r["W0"] = [w.clone() for w in r["W"]]
+        r["V0"] = [v.clone() for v in r["V"]]
+        r["rowsq"] = mo.rmnp_colcut_partial_batched(r["G"], r["V"], mu=0.9)
+    torch.cuda.synchronize()
+    # the all-reduce over the ranks, as a host-side sum of each row's partials
+    total = {}
+    for r in ranks:
+        off = 0
+        for i, v in zip(r["idx"], r["V"]):
+            part = r["rowsq"][off:off + v.shape[0]]
+            total[i] = part.clone() if i not in total else total[i] + part
+            off += v.shape[0]
+    for r in ranks:
+        r["sum"] = torch.cat([total[i] for i in r["idx"]])
+        mo.rmnp_colcut_apply_batched(r["W"], r["V"], r["sum"], full_cols=r["full"], lr=0.3,
+                                     eps=1e-7)
+    torch.cuda.synchronize()
+    st = "bf16" if dtype == "bf16" else "f32"
+    for r in ranks:
+        off = 0
+        for w, w0, v, v0, g, fc in zip(r["W"], r["W0"], r["V"], r["V0"], r["G"], r["full"]):
+            rows = v.shape[0]
+            _check_v(v, v0, g, 0.9)
+            v_new, rowsq = oracle.rmnp_colcut_partial(f64(v0), f64(g), mu=0.9, dtype=st)
+            got = r["rowsq"][off:off + rows].double().cpu().numpy()
+            np.testing.assert_allclose(got, rowsq, rtol=2e-6, atol=0)
+            tot = r["sum"][off:off + rows].double().cpu().numpy()
+            exp = oracle.rmnp_colcut_apply(f64(w0), v_new, tot, lr=0.3, eps=1e-7, full_cols=fc,
+                                           dtype=st)
+            upd = (oracle.f32_param(0.3) * oracle.update_scale(rows, fc) * v_new
+                   / np.maximum(np.sqrt(tot), oracle.f32_param(1e-7))[:, None])
+            _check_w_rmnp(w, exp, upd)
+            off += rows
+    # recombined slices against the row-local step on the whole matrices
+    for i, (sh, _) in enumerate(COLCUT):
+        parts = [r["W"][r["idx"].index(i)] for r in ranks if i in r["idx"]]
+        w_full = torch.cat(parts, dim=1).cpu()
+        w_ref, _, u = oracle.rmnp_step(f64(W[i]), f64(G[i]), f64(V[i]), mu=0.9, lr=0.3, eps=1e-7,
+                                       dtype=st)
+        _check_w_rmnp(w_full, w_ref, oracle.f32_param(0.3) * oracle.update_scale(*sh) * u)
