@@ -46,4 +46,5 @@ from .muon import (  # noqa: F401
     rmnp_step,
     rmnp_colcut_partial,
     rmnp_colcut_apply,
+    adamw_step,
 )

@@ -32,7 +32,9 @@ this update to the whole 2D matrices it owns, independently per matrix; there
 is no cross-matrix coupling, which is why every function below works on one
 matrix at a time.  Section 5.1: the training configuration adds weight decay
 1e-2 (with momentum 0.5 and two Newton-Schulz steps); ``muon_step`` takes it
-as decoupled decay, ``W - lr (wd W + s O)``.
+as decoupled decay, ``W - lr (wd W + s O)``.  The same section puts the
+non-2D tail on AdamW (``adamw_step``, the standard form; its formula is not on
+the pages).
 
 Readings taken where the pages leave a step open (each is listed in the design
 notes with its reason):
@@ -258,3 +260,36 @@ def rmnp_colcut_apply(w, v_new, rowsq, lr: float = 0.02, eps: float = RMNP_COLCU
     s = update_scale(rows, cols if full_cols is None else full_cols)
     u = _f64(v_new) / np.maximum(np.sqrt(_f64(rowsq)), f32_param(eps))[:, None]
     return round_storage(w - f32_param(lr) * s * u, dtype)
+
+
+def adamw_step(p, g, m, v, step: int, lr: float = 1e-3, beta1: float = 0.9,
+               beta2: float = 0.999, eps: float = 1e-8, wd: float = 1e-2,
+               dtype: str = "bf16"):
+    """AdamW on one non-2D tensor of the owner's tail.  MatrixFSDP section 5.1
+    puts LayerNorm weights and other non-2D tensors on AdamW with lr 1e-3,
+    weight decay 1e-2, betas (0.9, 0.999), eps 1e-8 and no schedule; the update
+    itself is not written on the pages, so this is the standard decoupled form
+    (Loshchilov and Hutter's AdamW, as torch.optim.AdamW computes it):
+
+        m = beta1 m + (1 - beta1) g            (stored as float32)
+        v = beta2 v + (1 - beta2) g^2          (stored as float32)
+        p = p - lr wd p - lr/(1 - beta1^t) m / (sqrt(v)/sqrt(1 - beta2^t) + eps)
+
+    using the stored m and v in the last line, rounded once to ``dtype``
+    ('bf16', 'f32', or 'f64' for no rounding).  ``step`` is t >= 1, the count
+    of steps including this one.  Returns ``(p_new, m_new, v_new)``."""
+    p, g, m, v = _f64(p), _f64(g), _f64(m), _f64(v)
+    b1, b2 = f32_param(beta1), f32_param(beta2)
+    m_new = b1 * m + (1.0 - b1) * g
+    v_new = b2 * v + (1.0 - b2) * g * g
+    if dtype != "f64":
+        m_new = round_storage(m_new, "f32")
+        v_new = round_storage(v_new, "f32")
+    lr64 = f32_param(lr)
+    bc1 = 1.0 - b1 ** step
+    bc2 = 1.0 - b2 ** step
+    denom = np.sqrt(v_new) / np.sqrt(bc2) + f32_param(eps)
+    p_new = p - lr64 * f32_param(wd) * p - (lr64 / bc1) * m_new / denom
+    if dtype != "f64":
+        p_new = round_storage(p_new, dtype)
+    return p_new, m_new, v_new

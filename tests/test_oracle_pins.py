@@ -440,3 +440,46 @@ def test_rmnp_colcut_clamp_and_zero_row():
     eps = float(np.float32(1e-7))
     exp = np.array([[0.5, -0.25], [0.125 - 0.5 * 3e-9 / eps, 1.0 - 0.5 * 4e-9 / eps]])
     np.testing.assert_allclose(out, exp.astype(np.float32), rtol=0, atol=1e-7)
+
+
+# --------------------------------------------------------------------------
+# AdamW for the non-2D tail
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("step", [1, 7])
+def test_adamw_matches_torch_adamw_in_float64(step):
+    # the standard form as torch.optim.AdamW computes it (single-tensor path),
+    # with the same float32 hyperparameters, mid-run state for step > 1
+    torch = pytest.importorskip("torch")
+    r = rng(60)
+    p0 = r.standard_normal(257)
+    g = r.standard_normal(257) * 0.1
+    m0 = r.standard_normal(257) * 0.01 if step > 1 else np.zeros(257)
+    v0 = np.abs(r.standard_normal(257)) * 1e-3 if step > 1 else np.zeros(257)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, wd=1e-2)
+    f = {k: f32_param(x) for k, x in hp.items()}
+    prm = torch.nn.Parameter(torch.tensor(p0, dtype=torch.float64))
+    prm.grad = torch.tensor(g, dtype=torch.float64)
+    opt = torch.optim.AdamW([prm], lr=f["lr"], betas=(f["beta1"], f["beta2"]), eps=f["eps"],
+                            weight_decay=f["wd"], foreach=False)
+    opt.state[prm] = {"step": torch.tensor(float(step - 1)),
+                      "exp_avg": torch.tensor(m0, dtype=torch.float64),
+                      "exp_avg_sq": torch.tensor(v0, dtype=torch.float64)}
+    opt.step()
+    p_new, m_new, v_new = oracle.adamw_step(p0, g, m0, v0, step, dtype="f64", **hp)
+    np.testing.assert_allclose(m_new, opt.state[prm]["exp_avg"].numpy(), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(v_new, opt.state[prm]["exp_avg_sq"].numpy(), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(p_new, prm.detach().numpy(), rtol=1e-13, atol=0)
+
+
+def test_adamw_first_step_is_a_signed_step():
+    # t = 1 from zero state and no decay: m_hat = g, v_hat = g^2, so the
+    # update is lr g / (|g| + eps)
+    g = np.array([3.0, -0.5, 1e-9, 0.0])
+    p0 = np.array([1.0, 2.0, -3.0, 4.0])
+    p_new, m_new, v_new = oracle.adamw_step(p0, g, np.zeros(4), np.zeros(4), 1, lr=0.5, wd=0.0,
+                                            eps=1e-8, dtype="f64")
+    eps = f32_param(1e-8)
+    b1 = f32_param(0.9)
+    np.testing.assert_allclose(m_new, (1 - b1) * g, rtol=1e-15)
+    np.testing.assert_allclose(p0 - p_new, 0.5 * g / (np.abs(g) + eps), rtol=1e-12, atol=1e-300)
