@@ -331,6 +331,51 @@ def main():
             "apply_ms": round(cp["colcut_apply"][0] / args.steps, 4)}
         log(f"[bench] column-cut rmnp {cms:.3f} ms ({cgbs:.0f} GB/s)")
 
+    # AdamW on the non-2D tail: GPT-2 Large's LayerNorm weights and biases and
+    # its linear biases (36 layers x {1280 x 6, 3840, 5120} + the final
+    # LayerNorm's 2 x 1280: 290 tensors, 601,600 elements; bf16 parameters,
+    # float32 moments) as 290 tensors and as one flat tensor (the tail kept as
+    # one owner role), then a 64M-element tail for the HBM rate.  kernel_us is
+    # the library's own per-launch HIP-event time; wall_us also holds the
+    # Python marshalling of the tensor list.
+    if not args.no_rmnp:
+        tail = [1280, 1280, 3840, 1280, 1280, 1280, 5120, 1280] * 36 + [1280, 1280]
+        result["adamw"] = {}
+        for name, lens in (("gpt2_large_tail_290", tail), ("gpt2_large_tail_flat", [sum(tail)]),
+                           ("tail_64M", [1 << 24] * 4)):
+            tp = [torch.randn(n, device="cuda").bfloat16() for n in lens]
+            tg = [(torch.randn(n, device="cuda") * 0.1).bfloat16() for n in lens]
+            tm = [torch.zeros(n, device="cuda") for n in lens]
+            tv = [torch.zeros(n, device="cuda") for n in lens]
+            st = [0]
+
+            def adamw():
+                st[0] += 1
+                mo.adamw_step_batched(tp, tg, tm, tv, st[0])
+
+            for _ in range(args.warmup):
+                adamw()
+            torch.cuda.synchronize()
+            mo.profile_read()
+            mo.profile_enable(True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                adamw()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mo.profile_enable(False)
+            wall = e0.elapsed_time(e1) / args.steps
+            kms = mo.profile_read()["adamw"][0] / args.steps
+            nel = sum(lens)
+            agbs = 22 * nel / (kms * 1e-3) / 1e9
+            result["adamw"][name] = {"tensors": len(lens), "elements": nel,
+                                     "kernel_us": round(kms * 1e3, 2),
+                                     "wall_us": round(wall * 1e3, 2), "bytes_per_elem": 22,
+                                     "GB_s": round(agbs, 1), "frac_hbm": round(agbs / PEAK_HBM_GBS, 4)}
+            log(f"[bench] adamw {name}: kernel {kms * 1e3:.1f} us ({agbs:.0f} GB/s), "
+                f"wall {wall * 1e3:.1f} us")
+            del tp, tg, tm, tv
+
     # MatrixFSDP's training configuration (section 5.1) on the same matrices:
     # momentum 0.5, 2 Newton-Schulz steps, decoupled weight decay 1e-2, lr 1e-3
     def step_wd():

@@ -163,6 +163,34 @@ matopt_status rmnp_colcut_apply_batched(const matopt_mat* mats, int32_t count,
                                         const float* rowsq, const int64_t* full_cols,
                                         void* stream);
 
+/* One flat tensor of the AdamW tail: p (in/out) and g (in) in the storage
+ * dtype, m and v (in/out) float32, n elements each, 16-byte aligned. */
+typedef struct {
+    void* p;
+    const void* g;
+    float* m;
+    float* v;
+    int64_t n;
+} matopt_vec;
+
+/*
+ * One AdamW step on every tensor of `vecs`: the non-2D tail of an owner's
+ * parameters (LayerNorm weights, biases), which MatrixFSDP section 5.1 updates
+ * with AdamW (lr 1e-3, weight decay 1e-2, betas (0.9, 0.999), eps 1e-8).  The
+ * pages do not write the update out; it is the standard decoupled form:
+ *   m <- beta1*m + (1-beta1)*g ;  v <- beta2*v + (1-beta2)*g^2   (float32)
+ *   p <- p - lr*wd*p - lr/(1-beta1^step) * m / (sqrt(v)/sqrt(1-beta2^step) + eps)
+ * computed in float64 from the stored m, v, p rounded once to `dt`.
+ *   dt      storage dtype of p and g (BF16 or F32); m, v are always float32.
+ *   step    1-based count of steps including this one (>= 1).
+ *   beta1, beta2 in [0, 1); lr, wd finite; eps finite and >= 0.
+ * All pointers are DEVICE pointers; buffers must not overlap (MATOPT_ERR_ALIAS).
+ * Needs no workspace.
+ */
+matopt_status adamw_step_batched(const matopt_vec* vecs, int32_t count, matopt_dtype dt,
+                                 float lr, float beta1, float beta2, float eps, float wd,
+                                 int32_t step, void* stream);
+
 /*
  * Newton-Schulz only (the appendix's routine): o[i] = NS(x[i]) for each matrix,
  * in the original orientation.  x[i]: rows[i] x cols[i] in `in_dt` (selects the
@@ -193,9 +221,9 @@ int32_t matopt_version(void);
  * synchronises on those events).  Classes: 0 momentum+norm+X0 build,
  * 1 norm finalize, 2 Gram X X^T, 3 polynomial a*I+b*A+c*A*A, 4 apply B*X
  * (incl. fused update on the last step), 5 ns_steps==0 output, 6 RMNP,
- * 7 column-cut RMNP partial, 8 column-cut RMNP apply.
+ * 7 column-cut RMNP partial, 8 column-cut RMNP apply, 9 AdamW.
  */
-#define MATOPT_PROFILE_CLASSES 9
+#define MATOPT_PROFILE_CLASSES 10
 matopt_status matopt_profile_enable(int32_t on);
 /* ms[k], launches[k] for k < MATOPT_PROFILE_CLASSES; resets the accumulators. */
 matopt_status matopt_profile_read(double* ms, int64_t* launches);

@@ -23,14 +23,14 @@ import torch
 
 __all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
            "muon_step_batched_wd", "rmnp_step_batched", "rmnp_colcut_partial_batched",
-           "rmnp_colcut_apply_batched", "ns_orthogonalize_batched", "profile_enable",
+           "rmnp_colcut_apply_batched", "adamw_step_batched", "ns_orthogonalize_batched", "profile_enable",
            "profile_read", "PROFILE_CLASSES", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmatopt.so")
 
 F32, BF16 = 0, 1
 PROFILE_CLASSES = ("prep", "finalize", "gram", "poly", "apply", "scale_out", "rmnp",
-                   "colcut_partial", "colcut_apply")
+                   "colcut_partial", "colcut_apply", "adamw")
 
 # Defaults printed on the pages (blog post appendix).
 NS_COEFFS = (3.4445, -4.7750, 2.0315)
@@ -42,6 +42,11 @@ class MatoptError(RuntimeError):
         self.status = status
         self.name = name
         self.detail = detail
+
+
+class _Vec(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_void_p), ("g", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class _Mat(ctypes.Structure):
@@ -60,6 +65,8 @@ EXPORTS = {
     "muon_step_batched_wd": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _i32,
                                     _f32, _f32, _f32, _f32, _vp, _sz, _vp]),
     "rmnp_step_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _vp]),
+    "adamw_step_batched": (_i32, [ctypes.POINTER(_Vec), _i32, _i32, _f32, _f32, _f32, _f32, _f32,
+                                  _i32, _vp]),
     "rmnp_colcut_partial_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _vp, _vp]),
     "rmnp_colcut_apply_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _vp,
                                          ctypes.POINTER(_i64), _vp]),
@@ -267,6 +274,33 @@ def rmnp_colcut_apply_batched(weights, moms, rowsq, full_cols=None, lr=0.02, eps
     fc = None if full_cols is None else (_i64 * n)(*full_cols)
     _check(lib().rmnp_colcut_apply_batched(arr, n, _dt(dtype), lr, eps, rowsq.data_ptr(), fc,
                                            _stream_ptr(device, stream)))
+
+
+def adamw_step_batched(params, grads, exp_avgs, exp_avg_sqs, step, lr=1e-3, betas=(0.9, 0.999),
+                       eps=1e-8, wd=1e-2, stream=None):
+    """One AdamW step on every (p, g, m, v) of the non-2D tail (contiguous tensors
+    of any shape, treated as flat): p and g in bf16 or float32, m and v float32,
+    all updated in place but g.  ``step`` counts steps including this one.  The
+    defaults are the MatrixFSDP paper's AdamW settings (section 5.1)."""
+    n = len(params)
+    if n == 0:
+        return
+    dtype = params[0].dtype
+    device = params[0].device
+    arr = (_Vec * n)()
+    for i, (p, g, m, v) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs)):
+        for t, what, dt in ((p, "params", dtype), (g, "grads", dtype),
+                            (m, "exp_avgs", torch.float32), (v, "exp_avg_sqs", torch.float32)):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda:
+                raise ValueError(f"{what}[{i}] must be a CUDA tensor")
+            if t.dtype != dt or not t.is_contiguous():
+                raise ValueError(f"{what}[{i}] must be a contiguous {dt} tensor")
+            if t.numel() != p.numel():
+                raise ValueError(f"{what}[{i}] has {t.numel()} elements, params[{i}] {p.numel()}")
+        arr[i] = _Vec(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), p.numel())
+    b1, b2 = betas
+    _check(lib().adamw_step_batched(arr, n, _dt(dtype), lr, b1, b2, eps, wd, int(step),
+                                    _stream_ptr(device, stream)))
 
 
 def ns_orthogonalize_batched(xs, out_dtype=torch.float32, ns_steps=5, coeffs=NS_COEFFS,

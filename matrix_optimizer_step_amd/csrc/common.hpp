@@ -114,6 +114,32 @@ struct ColcutParams {
   float mu, lr, eps;
 };
 
+// AdamW over flat tensors: one descriptor per tensor, one task per 2048
+// consecutive elements of a tensor (256 threads x 8).
+struct VecDesc {
+  void* p;          // parameters (storage dtype)
+  const void* g;    // gradient (storage dtype)
+  float* m;         // first moment, float32
+  float* v;         // second moment, float32
+  int64_t n;        // elements
+};
+
+struct VecTask {
+  int32_t t, pad_;
+  int64_t start;
+};
+
+struct AdamwParams {
+  const VecDesc* vecs;
+  const VecTask* tasks;
+  double b1, omb1, b2, omb2;   // betas and 1 - betas
+  double step_size;            // lr / (1 - beta1^t)
+  double inv_sqrt_bc2;         // 1 / sqrt(1 - beta2^t)
+  double eps, wdl;             // eps; lr * weight decay
+};
+
+constexpr int kAdamwTask = 2048;
+
 // Tile geometry.
 constexpr int kPrepTile = 64;
 constexpr int kTileBf16 = 256;
@@ -130,6 +156,7 @@ hipError_t launch_gemm_f32(const GemmParams& p, int n_tiles, hipStream_t s);
 // streaming two-pass variant (any width, scalar loads).
 hipError_t launch_rmnp(int dt, int wpr, int nch, const RmnpParams& p, int n_tasks,
                        hipStream_t s);
+hipError_t launch_adamw(int dt, const AdamwParams& p, int n_tasks, hipStream_t s);
 // Column-cut RMNP: apply == false launches the partial half, true the update.
 hipError_t launch_colcut(int dt, bool apply, const ColcutParams& p, int n_tasks, hipStream_t s);
 

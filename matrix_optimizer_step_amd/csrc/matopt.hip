@@ -194,7 +194,9 @@ hipError_t timed(int cls, hipStream_t s, F&& launch) {
 }
 
 // ---------------------------------------------------------------- plans
-enum PlanKind { PK_MUON = 1, PK_NS = 2, PK_RMNP = 3, PK_COLCUT_PARTIAL = 4, PK_COLCUT_APPLY = 5 };
+enum PlanKind {
+  PK_MUON = 1, PK_NS = 2, PK_RMNP = 3, PK_COLCUT_PARTIAL = 4, PK_COLCUT_APPLY = 5, PK_ADAMW = 6
+};
 
 struct RmnpGroup {
   int wpr, nch, n;
@@ -213,6 +215,7 @@ struct Plan {
   void* dbuf = nullptr;
   MatDesc* d_mats = nullptr;
   PrepTile* d_prep = nullptr;
+  VecDesc* d_vecs = nullptr;   // AdamW plans
   TileTable gram, poly, apply;
   int count = 0, n_prep = 0;
   std::vector<RmnpGroup> rmnp;
@@ -559,6 +562,29 @@ matopt_status colcut_run(bool apply, const matopt_mat* mats, int32_t count, mato
   return MATOPT_OK;
 }
 
+// AdamW plan: one descriptor per tensor and one task per kAdamwTask elements.
+matopt_status build_adamw_plan(Plan& P, const matopt_vec* vecs, int count, hipStream_t s) {
+  std::vector<VecDesc> descs(count);
+  std::vector<VecTask> tasks;
+  for (int i = 0; i < count; ++i) {
+    descs[i] = VecDesc{vecs[i].p, vecs[i].g, vecs[i].m, vecs[i].v, vecs[i].n};
+    for (int64_t e = 0; e < vecs[i].n; e += kAdamwTask) tasks.push_back({i, 0, e});
+  }
+  HostBuf hb;
+  const size_t o_vecs = hb.put(descs);
+  RmnpGroup g;
+  g.wpr = 0;
+  g.nch = 0;
+  g.n = (int)tasks.size();
+  g.off = hb.put(tasks);
+  P.rmnp.push_back(g);
+  matopt_status st = upload(P, hb, s);
+  if (st != MATOPT_OK) return st;
+  P.d_vecs = at<VecDesc>(P.dbuf, o_vecs);
+  P.count = count;
+  return MATOPT_OK;
+}
+
 }  // namespace
 
 // ==================================================================== C ABI
@@ -809,6 +835,72 @@ matopt_status rmnp_colcut_apply_batched(const matopt_mat* mats, int32_t count, m
                                         float lr, float eps, const float* rowsq,
                                         const int64_t* full_cols, void* stream) {
   return colcut_run(true, mats, count, dt, 0.f, lr, eps, rowsq, full_cols, stream);
+}
+
+matopt_status adamw_step_batched(const matopt_vec* vecs, int32_t count, matopt_dtype dt, float lr,
+                                 float beta1, float beta2, float eps, float wd, int32_t step,
+                                 void* stream) {
+  matopt_status st = check_common(count, dt);
+  if (st != MATOPT_OK) return st;
+  if (count == 0) return MATOPT_OK;
+  if (!vecs) return fail(MATOPT_ERR_NULL, "vecs is NULL");
+  if (!finite(lr) || !finite(wd) || !finite(eps) || eps < 0.f)
+    return fail(MATOPT_ERR_PARAM, "non-finite lr/wd/eps or eps < 0");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+    return fail(MATOPT_ERR_PARAM, "betas must lie in [0, 1)");
+  if (step < 1) return fail(MATOPT_ERR_PARAM, "step must be >= 1");
+  std::vector<Span> spans;
+  const size_t es = esize(dt);
+  for (int i = 0; i < count; ++i) {
+    const matopt_vec& t = vecs[i];
+    const std::string tag = "tensor " + std::to_string(i);
+    if (!t.p || !t.g || !t.m || !t.v) return fail(MATOPT_ERR_NULL, tag + ": NULL pointer");
+    if (t.n < 1 || t.n > kMaxElems) return fail(MATOPT_ERR_SHAPE, tag + ": invalid length");
+    if (!aligned16(t.p) || !aligned16(t.g) || !aligned16(t.m) || !aligned16(t.v))
+      return fail(MATOPT_ERR_ALIGN, tag + ": pointer not 16-byte aligned");
+    spans.push_back({(uintptr_t)t.p, (uintptr_t)t.p + (size_t)t.n * es, tag + " p"});
+    spans.push_back({(uintptr_t)t.g, (uintptr_t)t.g + (size_t)t.n * es, tag + " g"});
+    spans.push_back({(uintptr_t)t.m, (uintptr_t)t.m + (size_t)t.n * 4, tag + " m"});
+    spans.push_back({(uintptr_t)t.v, (uintptr_t)t.v + (size_t)t.n * 4, tag + " v"});
+  }
+  if ((st = check_overlap(spans)) != MATOPT_OK) return st;
+  int dev;
+  if ((st = check_device(&dev)) != MATOPT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  PlanKey key{PK_ADAMW, (uint64_t)dt, (uint64_t)dev, (uint64_t)count};
+  for (int i = 0; i < count; ++i) {
+    key.push_back((uint64_t)vecs[i].n);
+    key.push_back((uint64_t)(uintptr_t)vecs[i].p);
+    key.push_back((uint64_t)(uintptr_t)vecs[i].g);
+    key.push_back((uint64_t)(uintptr_t)vecs[i].m);
+    key.push_back((uint64_t)(uintptr_t)vecs[i].v);
+  }
+  std::shared_ptr<Plan> plan;
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    plan = plan_lookup(key);
+    if (!plan) {
+      plan = std::make_shared<Plan>();
+      plan->device = dev;
+      if ((st = build_adamw_plan(*plan, vecs, count, s)) != MATOPT_OK) return st;
+      plan_insert(key, plan);
+    }
+  }
+  const double b1 = beta1, b2 = beta2;
+  AdamwParams ap;
+  ap.vecs = plan->d_vecs;
+  ap.tasks = at<VecTask>(plan->dbuf, plan->rmnp[0].off);
+  ap.b1 = b1;
+  ap.omb1 = 1.0 - b1;
+  ap.b2 = b2;
+  ap.omb2 = 1.0 - b2;
+  ap.step_size = (double)lr / (1.0 - std::pow(b1, (double)step));
+  ap.inv_sqrt_bc2 = 1.0 / std::sqrt(1.0 - std::pow(b2, (double)step));
+  ap.eps = eps;
+  ap.wdl = (double)lr * (double)wd;
+  hipError_t e = timed(9, s, [&] { return launch_adamw(dt, ap, plan->rmnp[0].n, s); });
+  if (e != hipSuccess) return hip_fail("adamw launch", e);
+  return MATOPT_OK;
 }
 
 matopt_status matopt_profile_enable(int32_t on) {

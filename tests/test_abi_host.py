@@ -156,6 +156,24 @@ def test_rmnp_colcut_argument_errors(L, mod):
     assert L.rmnp_colcut_apply_batched(part, 1, 1, 0.02, 1e-7, rowsq, None, None) == NULL
 
 
+def test_adamw_argument_errors(L, mod):
+    arr = (mod._Vec * 1)(mod._Vec(BASE, BASE + (1 << 30), BASE + (2 << 30), BASE + (3 << 30), 1000))
+
+    def call(n=1, b1=0.9, b2=0.999, eps=1e-8, step=1, a=arr):
+        return L.adamw_step_batched(a, n, 1, 1e-3, b1, b2, eps, 1e-2, step, None)
+    assert call(n=0) == OK
+    assert call(step=0) == PARAM
+    assert call(b1=1.0) == PARAM
+    assert call(b2=-0.1) == PARAM
+    assert call(eps=float("nan")) == PARAM
+    bad = (mod._Vec * 1)(mod._Vec(BASE, BASE + 8, BASE + (2 << 30), BASE + (3 << 30), 1000))
+    assert call(a=bad) == ALIGN
+    ali = (mod._Vec * 1)(mod._Vec(BASE, BASE + 512, BASE + (2 << 30), BASE + (3 << 30), 1000))
+    assert call(a=ali) == ALIAS   # g starts inside p (1000 bf16 = 2000 bytes)
+    zero = (mod._Vec * 1)(mod._Vec(BASE, BASE + (1 << 30), BASE + (2 << 30), BASE + (3 << 30), 0))
+    assert call(a=zero) == SHAPE
+
+
 def test_rmnp_argument_errors(L, mod):
     arr = _mats(mod, [(BASE, BASE + (1 << 30), BASE + (2 << 30), 64, 128)])
     assert L.rmnp_step_batched(arr, 0, 1, 0.95, 0.02, 1e-12, None) == OK

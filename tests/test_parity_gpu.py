@@ -480,3 +480,42 @@ def test_rmnp_colcut_two_slices(mo, dtype):
         w_ref, _, u = oracle.rmnp_step(f64(W[i]), f64(G[i]), f64(V[i]), mu=0.9, lr=0.3, eps=1e-7,
                                        dtype=st)
         _check_w_rmnp(w_full, w_ref, oracle.f32_param(0.3) * oracle.update_scale(*sh) * u)
+
+
+# --------------------------------------------------------------------------
+# AdamW for the non-2D tail
+# --------------------------------------------------------------------------
+
+ADAMW_LENS = [1280, 1280, 3840, 1280, 5120, 1280, 7, 1, 1000, 4099, 2048, 2049]
+
+
+@pytest.mark.parametrize("dtype,step", [("bf16", 1), ("bf16", 7), ("f32", 7)])
+def test_adamw_ragged_tail(mo, dtype, step):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(40 + step)
+    P = [torch.randn(n, generator=gen).to(tdt) for n in ADAMW_LENS]
+    G = [(torch.randn(n, generator=gen) * 0.1).to(tdt) for n in ADAMW_LENS]
+    if step == 1:
+        M = [torch.zeros(n) for n in ADAMW_LENS]
+        Vs = [torch.zeros(n) for n in ADAMW_LENS]
+    else:
+        M = [torch.randn(n, generator=gen) * 0.01 for n in ADAMW_LENS]
+        Vs = [torch.rand(n, generator=gen) * 1e-3 for n in ADAMW_LENS]
+    dP, dG, dM, dV = ([t.cuda() for t in L] for L in (P, G, M, Vs))
+    mo.adamw_step_batched(dP, dG, dM, dV, step, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, wd=1e-2)
+    torch.cuda.synchronize()
+    for p0, g, m0, v0, p1, m1, v1 in zip(P, G, M, Vs, dP, dM, dV):
+        pe, me, ve = oracle.adamw_step(f64(p0), f64(g), f64(m0), f64(v0), step, lr=1e-3,
+                                       beta1=0.9, beta2=0.999, eps=1e-8, wd=1e-2, dtype=dtype)
+        # the moments: one float64 expression in the same order, one rounding
+        assert torch.equal(m1.cpu(), torch.from_numpy(me).float())
+        assert torch.equal(v1.cpu(), torch.from_numpy(ve).float())
+        if dtype == "bf16":
+            d = ulp_distance(p1.cpu(), torch.from_numpy(pe).to(tdt))
+            assert d.max() <= 1 and (d == 0).mean() >= 0.99
+        else:
+            upd = np.abs(f64(p0) - oracle.adamw_step(f64(p0), f64(g), f64(m0), f64(v0), step,
+                                                      dtype="f64")[0])
+            err = np.abs(f64(p1) - pe)
+            allowed = np.spacing(np.abs(pe).astype(np.float32)).astype(np.float64) + 1e-9 * upd
+            assert (err <= allowed).all()
