@@ -159,6 +159,9 @@ def main():
     ap.add_argument("--workload", default="gpt2_large_144")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rmnp", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the Muon step only (no RMNP, column-cut RMNP, AdamW or "
+                         "training-configuration lines), e.g. for a profiler run")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step benchmark: one s x s bf16 matrix for s in "
@@ -167,6 +170,8 @@ def main():
                     help="first run one plain device copy of this many MiB (float32), the "
                          "known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
     args = ap.parse_args()
+    if args.step_only:
+        args.no_rmnp = True
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -378,6 +383,12 @@ def main():
 
     # MatrixFSDP's training configuration (section 5.1) on the same matrices:
     # momentum 0.5, 2 Newton-Schulz steps, decoupled weight decay 1e-2, lr 1e-3
+    if args.step_only:
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        print(json.dumps(result), flush=True)
+        return
+
     def step_wd():
         mo.muon_step_batched_wd(W, G, V, mu=0.5, lr=1e-3, wd=1e-2, ns_steps=2)
 
