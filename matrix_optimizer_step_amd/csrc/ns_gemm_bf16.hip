@@ -393,6 +393,44 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
   }
 }
 
+// Apply before the last iteration: the wave's 128 x 128 sub-tile goes straight
+// from the accumulators to HBM, without LDS staging.  Register group g of
+// acc[bi][bj] holds, for row 32bi + (lane & 31), columns 32bj + 8g + 4(lane>>5)
+// + 0..3.  After packing to bf16, one v_permlane32_swap per packed register
+// trades group 1 of the low half-wave for group 0 of the high half (and group 3
+// for group 2): lane l then holds columns 32bj + 8(lane>>5) + 16h + 0..7 for
+// h = 0, 1 -- two 16-byte stores per block and lane, each instruction writing
+// 32 bytes of 32 rows.
+__device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][4], uint16_t* out,
+                                                 int64_t ld, int64_t i0, int64_t j0, int lane,
+                                                 float s) {
+  uint16_t* base = out + (i0 + (lane & 31)) * ld + j0 + 8 * (lane >> 5);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const f32x16& a = acc[bi][bj];
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        pk[g][0] = pack_bf2(s * a[4 * g], s * a[4 * g + 1]);
+        pk[g][1] = pack_bf2(s * a[4 * g + 2], s * a[4 * g + 3]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * h][k], pk[2 * h + 1][k], false,
+                                                          false);
+          pk[2 * h][k] = r[0];
+          pk[2 * h + 1][k] = r[1];
+        }
+      uint16_t* row = base + (int64_t)(32 * bi) * ld + 32 * bj;
+      gstore<u32x4>(row, u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
+      gstore<u32x4>(row + 16, u32x4{pk[2][0], pk[2][1], pk[3][0], pk[3][1]});
+    }
+}
+
 // Epilogue of one wave's 128 x 128 sub-tile, one 32-row stripe at a time (a
 // rolled loop: only the accumulator staging is specialised per stripe, which
 // keeps the kernel small enough for the instruction cache).  Each stripe is
@@ -697,6 +735,11 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   mfma16(k.acc, k.pa, k.qa);
   if (STAGE == 1) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
   mfma16(k.acc, k.pb, k.qb);
+  if (STAGE == 2 && OUT == OUT_NEXT_X) {
+    const float s_first = P.first ? gload<float>(d.xs) : 1.f;
+    store_acc_direct(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first);
+    return;
+  }
   // all fragment reads done (consumed above): the stages become epilogue staging
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   bar_raw();
