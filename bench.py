@@ -49,6 +49,19 @@ def ns_alg_flops(shapes, steps):
     return tot * steps
 
 
+def prep_alg_bytes(shapes, dtype):
+    """Algorithmic HBM bytes of the prep kernel: read G and V, write V, and
+    write X0 -- except where X0 would be a copy of V in the same layout (bf16,
+    not transposed, both sides multiples of the 256 GEMM tile), which the
+    first iteration reads in place."""
+    esz = 2 if dtype == "bf16" else 4
+    tot = 0
+    for r, c in shapes:
+        in_place = dtype == "bf16" and r <= c and r % 256 == 0 and c % 256 == 0
+        tot += (3 if in_place else 4) * esz * r * c
+    return tot
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -247,8 +260,9 @@ def main():
     numel = wl.numel
     esz = 2 if wl.dtype == "bf16" else 4
     prep_gbs = None
+    prep_bytes = prep_alg_bytes(wl.shapes, wl.dtype)
     if "prep" in per:
-        prep_gbs = 4 * esz * numel / (per["prep"]["ms_per_step"] * 1e-3) / 1e9
+        prep_gbs = prep_bytes / (per["prep"]["ms_per_step"] * 1e-3) / 1e9
     traffic = load_traffic(wl.name)
 
     result = {
@@ -285,7 +299,8 @@ def main():
                         "launches_per_step": v["launches_per_step"]} for k, v in per.items()},
         "ms_per_step_profiled": round(ms_prof, 4),
         "hbm_kernels": {
-            "prep": {"bytes_per_elem": 4 * esz, "GB_s": round(prep_gbs, 1) if prep_gbs else None,
+            "prep": {"bytes_per_elem": round(prep_bytes / numel, 3),
+                     "GB_s": round(prep_gbs, 1) if prep_gbs else None,
                      "frac_hbm": round(prep_gbs / PEAK_HBM_GBS, 4) if prep_gbs else None},
         },
     }

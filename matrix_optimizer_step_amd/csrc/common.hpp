@@ -42,12 +42,15 @@ struct MatDesc {
   float upd_scale;      // sqrt(max(1, rows/cols))
   int32_t prep_tiles_c; // prep tiles along the padded original columns
   void* x[2];           // iterates, mp x np, leading dimension np
+  const void* x0in;     // the first iteration's input: V itself when x0_is_v,
+                        // else x[0] (filled by the prep kernel)
   void* a;              // Gram,       mp x mp, leading dimension mp
   void* b;              // polynomial, mp x mp, leading dimension mp
   float* xs;            // this matrix's Frobenius scale
   float* partials;      // this matrix's first prep-tile partial
   int32_t n_prep;       // prep tiles of this matrix
-  int32_t pad_;
+  int32_t x0_is_v;      // bf16, not transposed, no padding: X0 would be a copy
+                        // of the stored V in the same layout, so it is not written
 };
 
 // Prep tile: 64 x 64 block of the padded original-orientation matrix.

@@ -311,6 +311,10 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
     d.prep_tiles_c = g.prep_tc;
     d.x[0] = at<void>(ws, L.x0[i]);
     d.x[1] = at<void>(ws, L.x1[i]);
+    // X0 is the stored V; when V has X0's layout the first iteration reads it
+    // in place and the prep kernel skips the copy
+    d.x0_is_v = (dt == DT_BF16 && !g.transposed && g.rows == g.mp && g.cols == g.np) ? 1 : 0;
+    d.x0in = d.x0_is_v ? vv[i] : d.x[0];
     d.a = at<void>(ws, L.a[i]);
     d.b = at<void>(ws, L.b[i]);
     d.xs = at<float>(ws, L.xs) + i;

@@ -688,7 +688,7 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   const int64_t mp = d.mp, np = d.np;
   // memory safety: an entry outside the matrix's output grid does nothing
   if (i0 < 0 || j0 < 0 || i0 + BM > mp || j0 + BM > (STAGE == 2 ? np : mp)) return;
-  const uint16_t* xcur = (const uint16_t*)(P.cur ? d.x[1] : d.x[0]);
+  const uint16_t* xcur = (const uint16_t*)(P.first ? d.x0in : P.cur ? d.x[1] : d.x[0]);
   uint16_t* xnext = (uint16_t*)(P.cur ? d.x[0] : d.x[1]);
   // K is a multiple of 256, so nk >= 8 > NS - 1
   const int nk = (int)(STAGE == 0 ? np : mp) / BK;

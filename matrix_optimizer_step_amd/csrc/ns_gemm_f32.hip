@@ -60,7 +60,7 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
   const int64_t mp = d.mp, np = d.np;
   // memory safety: an entry outside the matrix's output grid does nothing
   if (i0 < 0 || j0 < 0 || i0 + TM > mp || j0 + TM > (stage == 2 ? np : mp)) return;
-  const float* xcur = (const float*)(P.cur ? d.x[1] : d.x[0]);
+  const float* xcur = (const float*)(P.first ? d.x0in : P.cur ? d.x[1] : d.x[0]);
   float* xnext = (float*)(P.cur ? d.x[0] : d.x[1]);
 
   OpSrc sp, sq;

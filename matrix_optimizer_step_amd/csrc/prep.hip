@@ -12,6 +12,9 @@
 //                  the routine's transpose), zero in the padding.  X0 is the
 //                  stored V itself: the scale 1/(||V||+eps) is applied in float32
 //                  inside the first iteration's products, not rounded into X0.
+//                  When V already has X0's layout (bf16, not transposed, sides
+//                  multiples of the GEMM tile) X0 is not written at all: the
+//                  first iteration reads V (the descriptor's x0in).
 //                  Algorithmic HBM bytes per element: bf16 read G,V + write V,X0
 //                  = 8 (fp32: 16).
 // finalize_kernel  xs = 1/(sqrt(sum partials) + eps), one block per matrix, fixed
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams P) {
       ss = fmaf(vn[e], vn[e], ss);
       vals[p][e] = vn[e];
     }
-    if (!transposed) {
+    if (!transposed && !d.x0_is_v) {
       gstore<u32x4>(x0 + r * ldx + c, Tr::pack(vn));
     }
   }
