@@ -72,7 +72,6 @@ constexpr int NTHR = 256;
 constexpr int OPB = BM * BK * 2;      // bytes of one operand tile (16 KB)
 constexpr int STG = 2 * OPB;          // one stage: P then Q (32 KB)
 constexpr int LDS_BYTES = NS * STG;   // 160 KB
-constexpr int DMA_PER_STEP = 8;       // DMA instructions per wave per step (4 P + 4 Q)
 constexpr int EP_PITCH = 132;         // float pitch of the epilogue staging rows
 constexpr int EP_WAVE_BYTES = 32 * EP_PITCH * 4;
 static_assert(4 * EP_WAVE_BYTES <= LDS_BYTES, "epilogue staging must fit");
@@ -128,9 +127,9 @@ struct OperandDma {
     off_km1 = lo + 64u * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
   }
 
-  template <int Q>
+  template <int Q, int BPW>
   __device__ __forceinline__ void block(bool km, int t, uint8_t* tile, int wave) const {
-    const int b = 4 * wave + Q;
+    const int b = BPW * wave + Q;   // parity of b is that of Q (BPW is even)
     const char* base = km ? org_km + (int64_t)(t * BK + 2 * b) * ldb
                           : org_rm + (int64_t)(16 * b) * ldb + t * BK * 2;   // wave-uniform
     const uint32_t kmoff = (Q & 1) ? off_km1 : off_km0;
@@ -140,12 +139,16 @@ struct OperandDma {
                                      (MATOPT_LDS void*)(tile + 1024 * b), 16, 0, 0);
   }
 
+  // BPW blocks per wave (4 with four waves, 2 with eight): block b = BPW*wave + q
+  template <int BPW = 4>
   __device__ __forceinline__ void issue(int t, uint8_t* tile, int wave) const {
     const bool km = KIND == OP_KM || (KIND == OP_SPLIT && t < t_km);
-    block<0>(km, t, tile, wave);
-    block<1>(km, t, tile, wave);
-    block<2>(km, t, tile, wave);
-    block<3>(km, t, tile, wave);
+    block<0, BPW>(km, t, tile, wave);
+    block<1, BPW>(km, t, tile, wave);
+    if (BPW == 4) {
+      block<2, BPW>(km, t, tile, wave);
+      block<3, BPW>(km, t, tile, wave);
+    }
   }
 };
 
@@ -164,6 +167,7 @@ struct OperandDma {
 struct FragOffsets {
   uint32_t rm[2];   // by kk
   uint32_t km[4];   // by block bb (kk = 0, first read)
+  uint32_t kmq[2];  // eight-wave layout: Q blocks of the wave, origin included
   __device__ void init(int lane) {
     const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -173,6 +177,16 @@ struct FragOffsets {
     const int col = 16 * (G & 1) + 4 * h;
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) km[bb] = kr * 512 + ((bb ^ e) << 6) + 2 * col;
+  }
+  // Q columns from wq0 (a multiple of 64): block BB = wq0/32 + bb of the tile,
+  // whose unit swizzle (BB ^ e) & 7 can carry into bit 2 of BB
+  __device__ void init_q64(int lane, int wq0) {
+    const int G = lane >> 4, c = lane & 15, e = c >> 2, h = c & 3;
+    const int kr = 8 * (G >> 1) + e;
+    const int col = 16 * (G & 1) + 4 * h;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+      kmq[bb] = kr * 512 + ((((wq0 >> 5) + bb) ^ e) & 7) * 64 + 2 * col;
   }
 };
 
@@ -195,24 +209,34 @@ struct WaveGeo {
   int wi0, wj0, frow, fkc;
 };
 
-template <bool PKM, bool QKM>
+template <bool PKM, bool QKM, int NBJ>
 __device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, const WaveGeo& g,
                                            const FragOffsets& fo, bf16x8 (&p)[4],
-                                           bf16x8 (&q)[4]) {
+                                           bf16x8 (&q)[NBJ]) {
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi) p[bi] = frag<PKM>(stage, g.wi0, bi, kk, fo);
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) q[bj] = frag<QKM>(stage + OPB, g.wj0, bj, kk, fo);
+  for (int bj = 0; bj < NBJ; ++bj) {
+    if (NBJ == 4 || !QKM) {
+      q[bj] = frag<QKM>(stage + OPB, g.wj0, bj, kk, fo);
+    } else {   // eight-wave layout, k-major Q
+      const uint8_t* base = stage + OPB + fo.kmq[bj] + 8192 * kk;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base + 2048));
+      q[bj] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
 }
 
 // 16 MFMAs of one k16 sub-step (operands swapped: acc[bi][bj] holds C^T blocks,
 // i.e. 4 consecutive output columns per register group).
-__device__ __forceinline__ void mfma16(f32x16 (&acc)[4][4], const bf16x8 (&p)[4],
-                                       const bf16x8 (&q)[4]) {
+template <int NBJ>
+__device__ __forceinline__ void mfma16(f32x16 (&acc)[4][NBJ], const bf16x8 (&p)[4],
+                                       const bf16x8 (&q)[NBJ]) {
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int bj = 0; bj < NBJ; ++bj)
       acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[bj], p[bi], acc[bi][bj], 0, 0, 0);
 }
 
@@ -401,14 +425,15 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
 // for group 2): lane l then holds columns 32bj + 8(lane>>5) + 16h + 0..7 for
 // h = 0, 1 -- two 16-byte stores per block and lane, each instruction writing
 // 32 bytes of 32 rows.
-__device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][4], uint16_t* out,
+template <int NBJ>
+__device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][NBJ], uint16_t* out,
                                                  int64_t ld, int64_t i0, int64_t j0, int lane,
                                                  float s) {
   uint16_t* base = out + (i0 + (lane & 31)) * ld + j0 + 8 * (lane >> 5);
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
+    for (int bj = 0; bj < NBJ; ++bj) {
       const f32x16& a = acc[bi][bj];
       uint32_t pk[4][2];
 #pragma unroll
@@ -550,83 +575,90 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
 // here, so it adds no wait of its own for the DMA before an LDS read.  No
 // LDS-read wait is needed before the barrier either: every read of step t-1's
 // stage was consumed by an MFMA of step t-1, before this point.
-template <bool P0, bool Q0, bool P1, bool Q1, int VMW, bool DQ, bool DP, class OpP, class OpQ>
-__device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], bf16x8 (&pa)[4], bf16x8 (&qa)[4],
-                                      bf16x8 (&pb)[4], bf16x8 (&qb)[4], int t, const OpP& dp,
+template <bool P0, bool Q0, bool P1, bool Q1, int VMW, bool DQ, bool DP, int NBJ, int BPW,
+          class OpP, class OpQ>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[4][NBJ], bf16x8 (&pa)[4], bf16x8 (&qa)[NBJ],
+                                      bf16x8 (&pb)[4], bf16x8 (&qb)[NBJ], int t, const OpP& dp,
                                       const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
                                       int wave, const uint8_t* __restrict__ cur,
                                       const uint8_t* __restrict__ nxt,
                                       uint8_t* __restrict__ dst_q, uint8_t* __restrict__ dst_p) {
-  constexpr int RD0 = (P0 ? 8 : 4) + (Q0 ? 8 : 4);   // LDS reads of a k16 sub-step
-  constexpr int RD1 = (P1 ? 8 : 4) + (Q1 ? 8 : 4);
-  read_frags<P0, Q0>(cur, 1, g, fo, pb, qb);
-  if (DQ) dq.issue(t + NS - 2, dst_q + OPB, wave);
-  mfma16(acc, pa, qa);
+  constexpr int NM = 4 * NBJ;                                // MFMAs of a k16 sub-step
+  constexpr int RD0 = (P0 ? 8 : 4) + (Q0 ? 2 : 1) * NBJ;    // LDS reads of a k16 sub-step
+  constexpr int RD1 = (P1 ? 8 : 4) + (Q1 ? 2 : 1) * NBJ;
+  constexpr int VEV = 8 / BPW;   // one DMA instruction per VEV interleaved MFMAs
+  read_frags<P0, Q0, NBJ>(cur, 1, g, fo, pb, qb);
+  if (DQ) dq.template issue<BPW>(t + NS - 2, dst_q + OPB, wave);
+  mfma16<NBJ>(acc, pa, qa);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD0 / 8, 0);
-    if (DQ && (i & 1)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+    if (DQ && i % VEV == VEV - 1) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
+  if (NM > 8) __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM - 8, 0);
   __builtin_amdgcn_sched_barrier(0);
 
   wait_vm<VMW>();
   bar_raw();
-  if (DP) dp.issue(t + NS - 1, dst_p, wave);
-  read_frags<P1, Q1>(nxt, 0, g, fo, pa, qa);
-  mfma16(acc, pb, qb);
+  if (DP) dp.template issue<BPW>(t + NS - 1, dst_p, wave);
+  read_frags<P1, Q1, NBJ>(nxt, 0, g, fo, pa, qa);
+  mfma16<NBJ>(acc, pb, qb);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD1 / 8, 0);
-    if (DP && (i & 1)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+    if (DP && i % VEV == VEV - 1) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
+  if (NM > 8) __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM - 8, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Prologue: DMA of steps 0 .. NS-3 and the P half of step NS-2, wait for step
 // 0, first fragments (layouts P0, Q0 of step 0).  The reads alias only the DMA
 // of step 0 (s0); the compiler's own wait for it is the same vmcnt as the
-// explicit one.
-template <bool P0, bool Q0, class OpP, class OpQ>
-__device__ __forceinline__ void kprologue(bf16x8 (&pa)[4], bf16x8 (&qa)[4], const OpP& dp,
+// explicit one.  A wave issues 2*BPW DMA instructions per step.
+template <bool P0, bool Q0, int NBJ, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void kprologue(bf16x8 (&pa)[4], bf16x8 (&qa)[NBJ], const OpP& dp,
                                           const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
                                           int wave, uint8_t* __restrict__ s0,
                                           uint8_t* __restrict__ rest) {
-  dp.issue(0, s0, wave);
-  dq.issue(0, s0 + OPB, wave);
+  constexpr int DPS = 2 * BPW;
+  dp.template issue<BPW>(0, s0, wave);
+  dq.template issue<BPW>(0, s0 + OPB, wave);
 #pragma unroll
   for (int t = 1; t < NS - 2; ++t) {
-    dp.issue(t, rest + (t - 1) * STG, wave);
-    dq.issue(t, rest + (t - 1) * STG + OPB, wave);
+    dp.template issue<BPW>(t, rest + (t - 1) * STG, wave);
+    dq.template issue<BPW>(t, rest + (t - 1) * STG + OPB, wave);
   }
-  dp.issue(NS - 2, rest + (NS - 3) * STG, wave);
-  wait_vm<DMA_PER_STEP * (NS - 3) + DMA_PER_STEP / 2>();
+  dp.template issue<BPW>(NS - 2, rest + (NS - 3) * STG, wave);
+  wait_vm<DPS * (NS - 3) + DPS / 2>();
   bar_raw();
-  read_frags<P0, Q0>(s0, 0, g, fo, pa, qa);
+  read_frags<P0, Q0, NBJ>(s0, 0, g, fo, pa, qa);
 }
 
 __device__ __forceinline__ uint32_t stage_wrap(uint32_t x) {
   return x >= (uint32_t)LDS_BYTES ? x - (uint32_t)LDS_BYTES : x;
 }
 
-// Register state of one tile's K loop and the stage of its current step.
+// Register state of one tile's K loop and the stage of its current step: the
+// wave's 4 x NBJ accumulator blocks (NBJ = 4: 128 x 128 with four waves; 2:
+// 128 x 64 with eight).
+template <int NBJ>
 struct KState {
-  f32x16 acc[4][4];
-  bf16x8 pa[4], qa[4], pb[4], qb[4];
+  f32x16 acc[4][NBJ];
+  bf16x8 pa[4], qa[NBJ], pb[4], qb[NBJ];
   uint32_t sc;   // LDS offset of step t's stage
   int t;
 };
 
 // Steady steps t < t_end with both DMA halves and layouts (P0, Q0) -> (P1, Q1).
-template <bool P0, bool Q0, bool P1, bool Q1, class OpP, class OpQ>
-__device__ __forceinline__ void ksteps(KState& k, int t_end, const OpP& dp, const OpQ& dq,
+template <bool P0, bool Q0, bool P1, bool Q1, int NBJ, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void ksteps(KState<NBJ>& k, int t_end, const OpP& dp, const OpQ& dq,
                                        const WaveGeo& g, const FragOffsets& fo, int wave,
                                        uint8_t* lds) {
   for (; k.t < t_end; ++k.t) {
-    kstep<P0, Q0, P1, Q1, DMA_PER_STEP * 2, true, true>(
+    kstep<P0, Q0, P1, Q1, 4 * BPW, true, true, NBJ, BPW>(
         k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
         lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + (NS - 2) * STG),
         lds + stage_wrap(k.sc + (NS - 1) * STG));
@@ -637,41 +669,51 @@ __device__ __forceinline__ void ksteps(KState& k, int t_end, const OpP& dp, cons
 // All K steps of one tile but the last.  P is k-major for t < bP and in layout
 // PF from then on (bP is 0 or the first step of P's diagonal block, at most
 // nk - 8, so the switch lies in the steady range); Q is in layout QF.
-template <bool PF, bool QF, class OpP, class OpQ>
-__device__ __forceinline__ void kloop(KState& k, int nk, int bP, const OpP& dp, const OpQ& dq,
-                                      const WaveGeo& g, const FragOffsets& fo, int wave,
-                                      uint8_t* lds) {
-  if (bP > 0) kprologue<true, QF>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
-  else kprologue<PF, QF>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
+template <bool PF, bool QF, int NBJ, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void kloop(KState<NBJ>& k, int nk, int bP, const OpP& dp,
+                                      const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
+                                      int wave, uint8_t* lds) {
+  constexpr int DPS = 2 * BPW;   // DMA instructions per wave and step
+  if (bP > 0) kprologue<true, QF, NBJ, BPW>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
+  else kprologue<PF, QF, NBJ, BPW>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
   k.sc = 0;
   k.t = 0;
   if (bP > 0) {
-    ksteps<true, QF, true, QF>(k, bP - 1, dp, dq, g, fo, wave, lds);
-    ksteps<true, QF, PF, QF>(k, bP, dp, dq, g, fo, wave, lds);
+    ksteps<true, QF, true, QF, NBJ, BPW>(k, bP - 1, dp, dq, g, fo, wave, lds);
+    ksteps<true, QF, PF, QF, NBJ, BPW>(k, bP, dp, dq, g, fo, wave, lds);
   }
-  ksteps<PF, QF, PF, QF>(k, nk - NS + 1, dp, dq, g, fo, wave, lds);
+  ksteps<PF, QF, PF, QF, NBJ, BPW>(k, nk - NS + 1, dp, dq, g, fo, wave, lds);
   // drain: the Q half of step nk-1 is issued in step nk-NS+1; none after
-  kstep<PF, QF, PF, QF, DMA_PER_STEP * 2, true, false>(
+  kstep<PF, QF, PF, QF, DPS * 2, true, false, NBJ, BPW>(
       k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
       lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + (NS - 2) * STG), lds);
   k.sc = stage_wrap(k.sc + STG);
   ++k.t;
-  kstep<PF, QF, PF, QF, DMA_PER_STEP, false, false>(
+  kstep<PF, QF, PF, QF, DPS, false, false, NBJ, BPW>(
       k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
       lds + stage_wrap(k.sc + STG), lds, lds);
   k.sc = stage_wrap(k.sc + STG);
   ++k.t;
-  kstep<PF, QF, PF, QF, 0, false, false>(k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave,
-                                         lds + k.sc, lds + stage_wrap(k.sc + STG), lds, lds);
+  kstep<PF, QF, PF, QF, 0, false, false, NBJ, BPW>(k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g,
+                                                   fo, wave, lds + k.sc,
+                                                   lds + stage_wrap(k.sc + STG), lds, lds);
   k.sc = stage_wrap(k.sc + STG);
   ++k.t;
 }
 
 // One kernel per stage (and, for apply, per output kind), so that each carries
 // only its own operand layouts and epilogue.
-template <int STAGE, int OUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(1, 1)))
+// NW = 4: four waves of 128 x 128 (one per SIMD).  NW = 8 (apply before the last
+// iteration only): eight waves of 128 x 64, two per SIMD, so that one wave's
+// MFMAs run while the other waits on LDS, DMA or the barrier; the DMA of a step
+// is spread over all eight waves (two 1 KB blocks per operand each).
+template <int STAGE, int OUT, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
+                          amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void ns_gemm_bf16_kernel(GemmParams P) {
+  static_assert(NW == 4 || (NW == 8 && STAGE == 2 && OUT == OUT_NEXT_X), "layout");
+  constexpr int NBJ = NW == 4 ? 4 : 2;   // 32-column blocks per wave
+  constexpr int BPW = NW == 4 ? 4 : 2;   // DMA blocks per wave and operand
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
   // Gram: P = Q = X rows.  Polynomial: P = Q = A columns (A is stored whole).
   // Apply: P = B rows, k-major from the mirrored upper tile left of the
@@ -711,35 +753,37 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   }
 
   WaveGeo g;
-  g.wi0 = (wave >> 1) * 128;   // wave sub-tile origin (rows)
-  g.wj0 = (wave & 1) * 128;    // wave sub-tile origin (cols)
+  g.wi0 = NW == 4 ? (wave >> 1) * 128 : (wave >> 2) * 128;   // wave sub-tile origin (rows)
+  g.wj0 = NW == 4 ? (wave & 1) * 128 : (wave & 3) * 64;      // wave sub-tile origin (cols)
   g.frow = lane & 31;
   g.fkc = lane >> 5;
   FragOffsets fo;
   fo.init(lane);
+  if (NW == 8) fo.init_q64(lane, g.wj0);
 
-  KState k;
+  KState<NBJ> k;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int bj = 0; bj < NBJ; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) k.acc[bi][bj][r] = 0.f;
-  kloop<PF, QF>(k, nk, bP, dp, dq, g, fo, wave, lds);
+  kloop<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
 
   // last K step; the first epilogue stripe is fetched meanwhile
   const int64_t ep_ld = mp;
   const uint16_t* ep_src = (const uint16_t*)d.a;
   u32x4 ecur[8];
-  read_frags<PF, QF>(lds + k.sc, 1, g, fo, k.pb, k.qb);
-  mfma16(k.acc, k.pa, k.qa);
+  read_frags<PF, QF, NBJ>(lds + k.sc, 1, g, fo, k.pb, k.qb);
+  mfma16<NBJ>(k.acc, k.pa, k.qa);
   if (STAGE == 1) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
-  mfma16(k.acc, k.pb, k.qb);
+  mfma16<NBJ>(k.acc, k.pb, k.qb);
   if (STAGE == 2 && OUT == OUT_NEXT_X) {
     const float s_first = P.first ? gload<float>(d.xs) : 1.f;
-    store_acc_direct(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first);
+    store_acc_direct<NBJ>(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first);
     return;
   }
+  if constexpr (NW == 4) {
   // all fragment reads done (consumed above): the stages become epilogue staging
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   bar_raw();
@@ -750,23 +794,29 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   epilogue<STAGE, OUT>(d, P, k.acc, (float*)(lds + wave * EP_WAVE_BYTES), ep_src, ep_ld, out,
                        ld_out, i0 + g.wi0, j0 + g.wj0, lane, g.frow, g.fkc, s_first,
                        tile.ti != tile.tj, ecur);
+  }
 }
 
 }  // namespace
 
+#ifndef MATOPT_APPLY_WAVES
+#define MATOPT_APPLY_WAVES 8
+#endif
+
 hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
+  constexpr int AW = MATOPT_APPLY_WAVES;   // waves of the apply before the last iteration
   const dim3 grid(n_tiles), block(NTHR);
   if (p.stage == 0)
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<0, OUT_NEXT_X>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<0, OUT_NEXT_X, 4>), grid, block, 0, s, p);
   else if (p.stage == 1)
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<1, OUT_NEXT_X>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<1, OUT_NEXT_X, 4>), grid, block, 0, s, p);
   else if (p.out_kind == OUT_NEXT_X)
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_NEXT_X>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_NEXT_X, AW>), grid, dim3(64 * AW), 0, s, p);
   else if (p.out_kind == OUT_O)
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_O>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_O, 4>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_W_UPDATE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_W_UPDATE, 4>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
