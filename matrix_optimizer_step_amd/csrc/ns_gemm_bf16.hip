@@ -24,8 +24,10 @@
 // step) from there on.  X is read row-major by the Gram and k-major (through
 // its columns) by apply.
 //
-// Engine.  A 256 x 256 output tile per workgroup of 4 waves (each wave 128 x
-// 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, accumulators in AGPRs).  The
+// Engine.  A 256 x 256 output tile per workgroup of 8 waves, two per SIMD
+// (each wave 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16, accumulators
+// in AGPRs; while one wave of a SIMD waits on LDS the other issues MFMAs).  A
+// 4-wave variant (128 x 128 per wave) is kept behind MATOPT_*_WAVES.  The
 // K loop runs in steps of 32 through NS = 5 LDS stages of 32 KB (one 256 x 32
 // tile per operand), filled by global_load_lds_dwordx4 (HBM -> LDS without
 // registers) three steps ahead of use, in the layout the tile has in HBM.
@@ -45,8 +47,9 @@
 //
 // Epilogue: each wave stages its accumulators through its own LDS region
 // (float32) so that every global store is a contiguous row segment; the
-// epilogue inputs (A for the polynomial, X for apply) are prefetched during
-// the last K step and one stripe ahead.  On the last iteration the result is
+// polynomial's epilogue input (A) is prefetched during the last K step and one
+// stripe ahead.  A non-final apply skips the staging: its accumulators go
+// straight to X' with cross-half-wave lane swaps.  On the last iteration the result is
 // written in the original orientation as O, or folded straight into
 // W <- W - lr*sqrt(max(1,rows/cols))*O (so O never round-trips through HBM).
 //
@@ -68,13 +71,22 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int BM = 256;               // tile rows == tile cols == symmetric block
 constexpr int BK = 32;                // K step
 constexpr int NS = 5;                 // LDS stages
-constexpr int NTHR = 256;
 constexpr int OPB = BM * BK * 2;      // bytes of one operand tile (16 KB)
 constexpr int STG = 2 * OPB;          // one stage: P then Q (32 KB)
 constexpr int LDS_BYTES = NS * STG;   // 160 KB
-constexpr int EP_PITCH = 132;         // float pitch of the epilogue staging rows
-constexpr int EP_WAVE_BYTES = 32 * EP_PITCH * 4;
-static_assert(4 * EP_WAVE_BYTES <= LDS_BYTES, "epilogue staging must fit");
+// Epilogue geometry of a wave whose sub-tile is 128 rows x WN columns (WN =
+// 128 with four waves, 64 with eight): staging rows of WN + 4 floats, LPR
+// lanes per staged row, IPL 8-column items per lane and 32-row stripe.
+template <int WN>
+struct Ep {
+  static constexpr int PITCH = WN + 4;
+  static constexpr int LPR = WN / 8;
+  static constexpr int IPL = WN / 16;
+  static constexpr int RPI = 64 / LPR;   // rows between a lane's items
+  static constexpr int WAVE_BYTES = 32 * PITCH * 4;
+};
+static_assert(4 * Ep<128>::WAVE_BYTES <= LDS_BYTES && 8 * Ep<64>::WAVE_BYTES <= LDS_BYTES,
+              "epilogue staging must fit");
 
 // ---------------------------------------------------------------- LDS layouts
 // Row-major tile: 256 rows x 32 k = 64-byte rows of four 16-byte chunks; the
@@ -260,30 +272,35 @@ constexpr int SG_MFMA = 0x008;
 constexpr int SG_VMEM_RD = 0x020;
 constexpr int SG_DS_RD = 0x100;
 
+template <int WN>
 __device__ __forceinline__ void prefetch_stripe(const uint16_t* src, int64_t ld, int64_t row0,
-                                                int64_t col0, int lane, u32x4 (&dst)[8]) {
-  // lane q = lane + 64p reads row row0 + q/16, columns col0 + 8(q & 15) .. +7;
-  // item p starts 4p rows down (byte offsets)
+                                                int64_t col0, int lane,
+                                                u32x4 (&dst)[Ep<WN>::IPL]) {
+  // lane q = lane + 64p reads row row0 + q/LPR, columns col0 + 8(q % LPR) .. +7;
+  // item p starts RPI*p rows down (byte offsets)
+  using G = Ep<WN>;
   const char* base = (const char*)(src + row0 * ld + col0);
-  const uint32_t off = (uint32_t)(((lane >> 4) * ld + (lane & 15) * 8) * 2);
+  const uint32_t off = (uint32_t)(((lane / G::LPR) * ld + (lane % G::LPR) * 8) * 2);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) dst[p] = gload<u32x4>(base + (int64_t)(8 * p) * ld + off);
+  for (int p = 0; p < G::IPL; ++p)
+    dst[p] = gload<u32x4>(base + (int64_t)(2 * G::RPI * p) * ld + off);
 }
 
 // Stage acc[BI][*] (32 rows of the wave's 128 x 128 sub-tile) into the wave's
 // LDS region as float32 rows.  acc[BI][bj][r] holds
 //   C[32BI + (lane & 31)][32bj + 8(r>>2) + 4(lane>>5) + (r&3)]   (wave-local)
 // (operands swapped in the MFMA, so 4 consecutive columns per register group).
-template <int BI>
-__device__ __forceinline__ void stage_stripe(const f32x16 (&acc)[4][4], float* stg, int frow,
+template <int BI, int NBJ>
+__device__ __forceinline__ void stage_stripe(const f32x16 (&acc)[4][NBJ], float* stg, int frow,
                                              int fkc) {
+  constexpr int PITCH = Ep<32 * NBJ>::PITCH;
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj)
+  for (int bj = 0; bj < NBJ; ++bj)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 v = {acc[BI][bj][4 * g], acc[BI][bj][4 * g + 1], acc[BI][bj][4 * g + 2],
                        acc[BI][bj][4 * g + 3]};
-      *(f32x4*)(stg + frow * EP_PITCH + 32 * bj + 8 * g + 4 * fkc) = v;
+      *(f32x4*)(stg + frow * PITCH + 32 * bj + 8 * g + 4 * fkc) = v;
     }
 }
 
@@ -325,29 +342,32 @@ __device__ __forceinline__ void write_out4(const MatDesc& d, const GemmParams& P
 }
 
 // Last-iteration output of one staged stripe (rows ib .. ib+31 of the X
-// orientation, the wave's 128 columns from j0), in the original orientation:
+// orientation, the wave's WN columns from j0), in the original orientation:
 // item p of lane q = lane + 64p covers 8 consecutive original columns of one
-// original row -- row ib + q/16, columns j0 + 8(q & 15) when not transposed;
+// original row -- row ib + q/LPR, columns j0 + 8(q % LPR) when not transposed;
 // row j0 + q/4, columns ib + 8(q & 3) when transposed.  The staged values are
 // scaled by s (the Frobenius scale when this is also the first iteration, else
 // 1) as they are read.  Stripes that lie wholly inside a matrix with 16-byte
-// rows take an unrolled path with 16-byte accesses, the stripe's 8 W chunks
+// rows take an unrolled path with 16-byte accesses, the stripe's W chunks
 // per lane all read before the first is used; others a rolled per-item path.
-template <int OUT, bool TRANS>
+template <int OUT, bool TRANS, int WN>
 __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P, const float* stg,
                                            int64_t ib, int64_t j0, int lane, float upd,
                                            float s) {
+  using G = Ep<WN>;
+  constexpr int EP_PITCH = G::PITCH;
   const int64_t rows = d.rows, cols = d.cols;
-  const bool full = d.vec_ok && (TRANS ? (j0 + 128 <= rows && ib + 32 <= cols)
-                                       : (ib + 32 <= rows && j0 + 128 <= cols));
+  const bool full = d.vec_ok && (TRANS ? (j0 + WN <= rows && ib + 32 <= cols)
+                                       : (ib + 32 <= rows && j0 + WN <= cols));
   auto item = [&](int p, int64_t& r, int64_t& c, float (&lo)[4], float (&hi)[4]) {
     const int q = lane + 64 * p;
     if (!TRANS) {
-      // lanes 8-15 of a row read the two halves in the other order (LDS banks)
-      const int rr = q >> 4, c8 = (q & 15) * 8;
+      // with 16 lanes per row, lanes 8-15 read the two halves in the other
+      // order (LDS banks); with 8, consecutive rows already meet other banks
+      const int rr = q / G::LPR, c8 = (q % G::LPR) * 8;
       r = ib + rr;
       c = j0 + c8;
-      const bool hs = (q & 8) != 0;
+      const bool hs = G::LPR == 16 && (q & 8) != 0;
       const float* src = stg + rr * EP_PITCH + c8;
       const f32x4 r0 = *(const f32x4*)(src + (hs ? 4 : 0));
       const f32x4 r1 = *(const f32x4*)(src + (hs ? 0 : 4));
@@ -366,18 +386,18 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
     }
   };
   if (full) {
-    u32x4 wpre[8];
+    u32x4 wpre[G::IPL];
     if (OUT == OUT_W_UPDATE) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < G::IPL; ++p) {
         const int q = lane + 64 * p;
-        const int64_t r = TRANS ? j0 + (q >> 2) : ib + (q >> 4);
-        const int64_t c = TRANS ? ib + 8 * (q & 3) : j0 + (q & 15) * 8;
+        const int64_t r = TRANS ? j0 + (q >> 2) : ib + q / G::LPR;
+        const int64_t c = TRANS ? ib + 8 * (q & 3) : j0 + (q % G::LPR) * 8;
         wpre[p] = gload<u32x4>((const uint16_t*)d.w + r * cols + c);
       }
     }
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < G::IPL; ++p) {
       int64_t r, c;
       float lo[4], hi[4];
       item(p, r, c, lo, hi);
@@ -406,7 +426,7 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
     }
   } else {
 #pragma unroll 1
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < G::IPL; ++p) {
       int64_t r, c;
       float lo[4], hi[4];
       item(p, r, c, lo, hi);
@@ -456,49 +476,53 @@ __device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][NBJ], ui
     }
 }
 
-// Epilogue of one wave's 128 x 128 sub-tile, one 32-row stripe at a time (a
+// Epilogue of one wave's 128 x WN sub-tile, one 32-row stripe at a time (a
 // rolled loop: only the accumulator staging is specialised per stripe, which
 // keeps the kernel small enough for the instruction cache).  Each stripe is
 // staged through the wave's own LDS region (LDS executes one wave's accesses in
-// order, so no workgroup barrier is needed) and written row-wise: 8 chunks of
-// 8 consecutive columns (16-byte stores) per lane.  The polynomial's epilogue input (the A tile
+// order, so no workgroup barrier is needed) and written row-wise: WN/16 chunks
+// of 8 consecutive columns (16-byte stores) per lane.  The polynomial's epilogue input (the A tile
 // of the same position) is prefetched one stripe ahead; Gram and apply read
 // nothing back.
-template <int STAGE, int OUT>
+template <int STAGE, int OUT, int NBJ>
 __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
-                                         const f32x16 (&acc)[4][4], float* stg,
+                                         const f32x16 (&acc)[4][NBJ], float* stg,
                                          const uint16_t* ep_src, int64_t ep_ld, uint16_t* out,
                                          int64_t ld_out, int i0, int j0, int lane, int frow,
                                          int fkc, float s_first, bool tile_off_diag,
-                                         u32x4 (&ecur)[8]) {
+                                         u32x4 (&ecur)[Ep<32 * NBJ>::IPL]) {
+  constexpr int WN = 32 * NBJ;
+  using G = Ep<WN>;
+  constexpr int EP_PITCH = G::PITCH;
   constexpr bool EP_IN = STAGE == 1;
   const bool out_trans = OUT != OUT_NEXT_X && d.transposed;
   const bool mirror = STAGE == 0 && tile_off_diag;   // A is stored whole
   const float upd = -P.lr * d.upd_scale;
-  u32x4 enext[8];
+  u32x4 enext[G::IPL];
 #pragma unroll 1
   for (int bi = 0; bi < 4; ++bi) {
-    if (EP_IN && bi + 1 < 4) prefetch_stripe(ep_src, ep_ld, i0 + 32 * (bi + 1), j0, lane, enext);
+    if (EP_IN && bi + 1 < 4)
+      prefetch_stripe<WN>(ep_src, ep_ld, i0 + 32 * (bi + 1), j0, lane, enext);
     switch (bi) {
-      case 0: stage_stripe<0>(acc, stg, frow, fkc); break;
-      case 1: stage_stripe<1>(acc, stg, frow, fkc); break;
-      case 2: stage_stripe<2>(acc, stg, frow, fkc); break;
-      default: stage_stripe<3>(acc, stg, frow, fkc); break;
+      case 0: stage_stripe<0, NBJ>(acc, stg, frow, fkc); break;
+      case 1: stage_stripe<1, NBJ>(acc, stg, frow, fkc); break;
+      case 2: stage_stripe<2, NBJ>(acc, stg, frow, fkc); break;
+      default: stage_stripe<3, NBJ>(acc, stg, frow, fkc); break;
     }
     __builtin_amdgcn_wave_barrier();
 
     const int64_t ib = i0 + 32 * bi;   // first X-orientation row of this stripe
     if (STAGE != 2 || OUT == OUT_NEXT_X) {
       // Gram, polynomial and non-final apply: 8 consecutive columns (one
-      // 16-byte store) per lane item.  Lanes 8-15 of a row read their two
-      // float4 halves in the other order so that the 16 lanes of a row meet
-      // distinct LDS banks.
+      // 16-byte store) per lane item.  With 16 lanes per row, lanes 8-15 read
+      // their two float4 halves in the other order so that the 16 lanes of a
+      // row meet distinct LDS banks.
       const float sc = STAGE == 0 ? s_first * s_first : s_first;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < G::IPL; ++p) {
         const int q = lane + 64 * p;
-        const int rr = q >> 4, c8 = (q & 15) * 8;
-        const bool hs = (q & 8) != 0;
+        const int rr = q / G::LPR, c8 = (q % G::LPR) * 8;
+        const bool hs = G::LPR == 16 && (q & 8) != 0;
         float* src = stg + rr * EP_PITCH + c8;
         const f32x4 r0 = *(const f32x4*)(src + (hs ? 4 : 0));
         const f32x4 r1 = *(const f32x4*)(src + (hs ? 0 : 4));
@@ -535,7 +559,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
       // Mirror tile: row j0+jj of the output holds this stripe's column jj,
       // i.e. the 32 values of rows ib .. ib+31 (8 per lane item).
 #pragma unroll 4
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < G::IPL; ++p) {
         const int q = lane + 64 * p;
         const int ic = q & 3, jj = q >> 2;
         float vv[8];
@@ -548,13 +572,13 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
     }
     if (OUT != OUT_NEXT_X) {
       __builtin_amdgcn_wave_barrier();
-      if (out_trans) final_pass<OUT, true>(d, P, stg, ib, j0, lane, upd, s_first);
-      else final_pass<OUT, false>(d, P, stg, ib, j0, lane, upd, s_first);
+      if (out_trans) final_pass<OUT, true, WN>(d, P, stg, ib, j0, lane, upd, s_first);
+      else final_pass<OUT, false, WN>(d, P, stg, ib, j0, lane, upd, s_first);
     }
     __builtin_amdgcn_wave_barrier();
     if (EP_IN) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) ecur[p] = enext[p];
+      for (int p = 0; p < G::IPL; ++p) ecur[p] = enext[p];
     }
   }
 }
@@ -711,8 +735,9 @@ template <int STAGE, int OUT, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void ns_gemm_bf16_kernel(GemmParams P) {
-  static_assert(NW == 4 || (NW == 8 && STAGE == 2 && OUT == OUT_NEXT_X), "layout");
+  static_assert(NW == 4 || NW == 8, "layout");
   constexpr int NBJ = NW == 4 ? 4 : 2;   // 32-column blocks per wave
+  constexpr int WN = 32 * NBJ;           // columns per wave
   constexpr int BPW = NW == 4 ? 4 : 2;   // DMA blocks per wave and operand
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
   // Gram: P = Q = X rows.  Polynomial: P = Q = A columns (A is stored whole).
@@ -773,17 +798,17 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   // last K step; the first epilogue stripe is fetched meanwhile
   const int64_t ep_ld = mp;
   const uint16_t* ep_src = (const uint16_t*)d.a;
-  u32x4 ecur[8];
+  u32x4 ecur[Ep<WN>::IPL];
   read_frags<PF, QF, NBJ>(lds + k.sc, 1, g, fo, k.pb, k.qb);
   mfma16<NBJ>(k.acc, k.pa, k.qa);
-  if (STAGE == 1) prefetch_stripe(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
+  if (STAGE == 1) prefetch_stripe<WN>(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
   mfma16<NBJ>(k.acc, k.pb, k.qb);
   if (STAGE == 2 && OUT == OUT_NEXT_X) {
     const float s_first = P.first ? gload<float>(d.xs) : 1.f;
     store_acc_direct<NBJ>(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first);
     return;
   }
-  if constexpr (NW == 4) {
+  {
   // all fragment reads done (consumed above): the stages become epilogue staging
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   bar_raw();
@@ -791,7 +816,7 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   uint16_t* out = STAGE == 0 ? (uint16_t*)d.a : STAGE == 1 ? (uint16_t*)d.b : xnext;
   const int64_t ld_out = STAGE == 2 ? np : mp;
   const float s_first = P.first ? gload<float>(d.xs) : 1.f;
-  epilogue<STAGE, OUT>(d, P, k.acc, (float*)(lds + wave * EP_WAVE_BYTES), ep_src, ep_ld, out,
+  epilogue<STAGE, OUT, NBJ>(d, P, k.acc, (float*)(lds + wave * Ep<WN>::WAVE_BYTES), ep_src, ep_ld, out,
                        ld_out, i0 + g.wi0, j0 + g.wj0, lane, g.frow, g.fkc, s_first,
                        tile.ti != tile.tj, ecur);
   }
@@ -802,21 +827,31 @@ void ns_gemm_bf16_kernel(GemmParams P) {
 #ifndef MATOPT_APPLY_WAVES
 #define MATOPT_APPLY_WAVES 8
 #endif
+#ifndef MATOPT_GRAM_WAVES
+#define MATOPT_GRAM_WAVES 8
+#endif
+#ifndef MATOPT_POLY_WAVES
+#define MATOPT_POLY_WAVES 8
+#endif
+#ifndef MATOPT_FINAL_WAVES
+#define MATOPT_FINAL_WAVES 8
+#endif
 
 hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  constexpr int AW = MATOPT_APPLY_WAVES;   // waves of the apply before the last iteration
-  const dim3 grid(n_tiles), block(NTHR);
+  constexpr int GW = MATOPT_GRAM_WAVES, PW = MATOPT_POLY_WAVES;
+  constexpr int AW = MATOPT_APPLY_WAVES, FW = MATOPT_FINAL_WAVES;
+  const dim3 grid(n_tiles);
   if (p.stage == 0)
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<0, OUT_NEXT_X, 4>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<0, OUT_NEXT_X, GW>), grid, dim3(64 * GW), 0, s, p);
   else if (p.stage == 1)
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<1, OUT_NEXT_X, 4>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<1, OUT_NEXT_X, PW>), grid, dim3(64 * PW), 0, s, p);
   else if (p.out_kind == OUT_NEXT_X)
     hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_NEXT_X, AW>), grid, dim3(64 * AW), 0, s, p);
   else if (p.out_kind == OUT_O)
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_O, 4>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_O, FW>), grid, dim3(64 * FW), 0, s, p);
   else
-    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_W_UPDATE, 4>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<2, OUT_W_UPDATE, FW>), grid, dim3(64 * FW), 0, s, p);
   return hipGetLastError();
 }
 
