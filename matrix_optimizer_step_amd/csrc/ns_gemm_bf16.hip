@@ -58,6 +58,21 @@
 #include "common.hpp"
 #include "device_util.hpp"
 
+// K loop DMA schedule per stage: 1 pairs the loads of consecutive K steps
+// (kloop2), 0 spreads each step's DMA over two steps (kloop).  Pairing halves
+// the L1 -> L2 line requests of a row-major operand but shortens some
+// prefetch distances: on the GPT-2 Large set it makes apply 2% faster (its B
+// rows are row-major right of the diagonal) and the Gram 9% slower.
+#ifndef MATOPT_PAIR_GRAM
+#define MATOPT_PAIR_GRAM 0
+#endif
+#ifndef MATOPT_PAIR_POLY
+#define MATOPT_PAIR_POLY 0
+#endif
+#ifndef MATOPT_PAIR_APPLY
+#define MATOPT_PAIR_APPLY 1
+#endif
+
 namespace matopt {
 
 namespace {
@@ -139,6 +154,10 @@ struct OperandDma {
     off_km1 = lo + 64u * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
   }
 
+  __device__ __forceinline__ bool is_km(int t) const {
+    return KIND == OP_KM || (KIND == OP_SPLIT && t < t_km);
+  }
+
   template <int Q, int BPW>
   __device__ __forceinline__ void block(bool km, int t, uint8_t* tile, int wave) const {
     const int b = BPW * wave + Q;   // parity of b is that of Q (BPW is even)
@@ -154,7 +173,7 @@ struct OperandDma {
   // BPW blocks per wave (4 with four waves, 2 with eight): block b = BPW*wave + q
   template <int BPW = 4>
   __device__ __forceinline__ void issue(int t, uint8_t* tile, int wave) const {
-    const bool km = KIND == OP_KM || (KIND == OP_SPLIT && t < t_km);
+    const bool km = is_km(t);
     block<0, BPW>(km, t, tile, wave);
     block<1, BPW>(km, t, tile, wave);
     if (BPW == 4) {
@@ -725,6 +744,128 @@ __device__ __forceinline__ void kloop(KState<NBJ>& k, int nk, int bP, const OpP&
   ++k.t;
 }
 
+// Paired DMA schedule.  A row-major operand uses 64 bytes of each 128-byte
+// line per K step and the other 64 bytes in the next step; the vector L1
+// fetches whole lines, so issuing the two steps' loads of a line far apart
+// fetches it from L2 twice.  Here the DMA of steps s and s+1 (s even) is
+// issued back to back (the same line BPW loads apart), so the second load of a
+// line finds it in (or on its way into) the L1: P(s), P(s+1) after the barrier of step s-3
+// (odd) into the stages of s-5 and s-4, Q(s), Q(s+1) before the barrier of step
+// s-2 (even) into the same two stages, both free by then.  The wait before the
+// barrier of step t (for step t+1) leaves in flight P(t+2), P(t+3), Q(t+2),
+// Q(t+3) when t is even and Q(t+2) when t is odd.  d0, d1 are the stages of
+// steps t+2, t+3 (even t) or t+3, t+4 (odd t).
+template <class Op, int BPW>
+__device__ __forceinline__ void issue_pair(const Op& op, int s, uint8_t* a, uint8_t* b, int wave) {
+  // step s first, then s+1: a wait that leaves BPW loads in flight covers step s
+  op.template issue<BPW>(s, a, wave);
+  op.template issue<BPW>(s + 1, b, wave);
+}
+
+template <bool P0, bool Q0, bool P1, bool Q1, int VMW, bool QPAIR, bool PPAIR, int NBJ, int BPW,
+          class OpP, class OpQ>
+__device__ __forceinline__ void kstep2(f32x16 (&acc)[4][NBJ], bf16x8 (&pa)[4], bf16x8 (&qa)[NBJ],
+                                       bf16x8 (&pb)[4], bf16x8 (&qb)[NBJ], int t, const OpP& dp,
+                                       const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
+                                       int wave, const uint8_t* __restrict__ cur,
+                                       const uint8_t* __restrict__ nxt, uint8_t* __restrict__ d0,
+                                       uint8_t* __restrict__ d1) {
+  constexpr int NM = 4 * NBJ;
+  constexpr int RD0 = (P0 ? 8 : 4) + (Q0 ? 2 : 1) * NBJ;
+  constexpr int RD1 = (P1 ? 8 : 4) + (Q1 ? 2 : 1) * NBJ;
+  constexpr int ND0 = QPAIR ? 2 * BPW : 0, ND1 = PPAIR ? 2 * BPW : 0;
+  read_frags<P0, Q0, NBJ>(cur, 1, g, fo, pb, qb);
+  if (QPAIR) issue_pair<OpQ, BPW>(dq, t + 2, d0 + OPB, d1 + OPB, wave);
+  mfma16<NBJ>(acc, pa, qa);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD0 / 8, 0);
+    if ((i + 1) * ND0 / 8 > i * ND0 / 8) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+  }
+  if (NM > 8) __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM - 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  wait_vm<VMW>();
+  bar_raw();
+  if (PPAIR) issue_pair<OpP, BPW>(dp, t + 3, d0, d1, wave);
+  read_frags<P1, Q1, NBJ>(nxt, 0, g, fo, pa, qa);
+  mfma16<NBJ>(acc, pb, qb);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD1 / 8, 0);
+    if ((i + 1) * ND1 / 8 > i * ND1 / 8) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+  }
+  if (NM > 8) __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM - 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One even and one odd step with the paired DMA: layouts (PE, Q) -> (PM, Q)
+// -> (PO, Q) for steps t, t+1, t+2.
+template <bool PE, bool PM, bool PO, bool QF, int NBJ, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void kpair(KState<NBJ>& k, const OpP& dp, const OpQ& dq,
+                                      const WaveGeo& g, const FragOffsets& fo, int wave,
+                                      uint8_t* lds) {
+  constexpr int DPS = 2 * BPW;
+  kstep2<PE, QF, PM, QF, 2 * DPS, true, false, NBJ, BPW>(
+      k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
+      lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + 2 * STG),
+      lds + stage_wrap(k.sc + 3 * STG));
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep2<PM, QF, PO, QF, BPW, false, true, NBJ, BPW>(
+      k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
+      lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + 3 * STG),
+      lds + stage_wrap(k.sc + 4 * STG));
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+}
+
+// All K steps of one tile but the last, paired DMA (same contract as kloop;
+// nk and bP are even).  Prologue: P(0), Q(0), P(1), Q(1), P(2), P(3).
+template <bool PF, bool QF, int NBJ, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP& dp,
+                                       const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
+                                       int wave, uint8_t* lds) {
+  constexpr int DPS = 2 * BPW;
+  {
+    dp.template issue<BPW>(0, lds, wave);
+    dq.template issue<BPW>(0, lds + OPB, wave);
+    dp.template issue<BPW>(1, lds + STG, wave);
+    dq.template issue<BPW>(1, lds + STG + OPB, wave);
+    issue_pair<OpP, BPW>(dp, 2, lds + 2 * STG, lds + 3 * STG, wave);
+    wait_vm<2 * DPS>();
+    bar_raw();
+    if (bP > 0) read_frags<true, QF, NBJ>(lds, 0, g, fo, k.pa, k.qa);
+    else read_frags<PF, QF, NBJ>(lds, 0, g, fo, k.pa, k.qa);
+  }
+  k.sc = 0;
+  k.t = 0;
+  if (bP > 0) {
+    for (; k.t < bP - 2;) kpair<true, true, true, QF, NBJ, BPW>(k, dp, dq, g, fo, wave, lds);
+    kpair<true, true, PF, QF, NBJ, BPW>(k, dp, dq, g, fo, wave, lds);
+  }
+  for (; k.t < nk - 4;) kpair<PF, PF, PF, QF, NBJ, BPW>(k, dp, dq, g, fo, wave, lds);
+  // step nk-4 issues Q(nk-2), Q(nk-1), the last DMA; nk-3 and nk-2 issue none
+  kstep2<PF, QF, PF, QF, 2 * DPS, true, false, NBJ, BPW>(
+      k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
+      lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + 2 * STG),
+      lds + stage_wrap(k.sc + 3 * STG));
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep2<PF, QF, PF, QF, BPW, false, false, NBJ, BPW>(
+      k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
+      lds + stage_wrap(k.sc + STG), lds, lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep2<PF, QF, PF, QF, 0, false, false, NBJ, BPW>(
+      k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
+      lds + stage_wrap(k.sc + STG), lds, lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+}
+
 // One kernel per stage (and, for apply, per output kind), so that each carries
 // only its own operand layouts and epilogue.
 // NW = 4: four waves of 128 x 128 (one per SIMD).  NW = 8 (apply before the last
@@ -793,7 +934,10 @@ void ns_gemm_bf16_kernel(GemmParams P) {
     for (int bj = 0; bj < NBJ; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) k.acc[bi][bj][r] = 0.f;
-  kloop<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
+  constexpr bool PAIRED = STAGE == 0 ? MATOPT_PAIR_GRAM : STAGE == 1 ? MATOPT_PAIR_POLY
+                                                                     : MATOPT_PAIR_APPLY;
+  if (PAIRED) kloop2<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
+  else kloop<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
 
   // last K step; the first epilogue stripe is fetched meanwhile
   const int64_t ep_ld = mp;
