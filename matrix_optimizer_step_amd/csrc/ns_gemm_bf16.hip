@@ -72,6 +72,10 @@
 #ifndef MATOPT_PAIR_APPLY
 #define MATOPT_PAIR_APPLY 1
 #endif
+// Diagonal Gram and polynomial tiles compute only their upper 36 of 64 blocks.
+#ifndef MATOPT_DIAG_TILES
+#define MATOPT_DIAG_TILES 1
+#endif
 
 namespace matopt {
 
@@ -866,6 +870,277 @@ __device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP
   ++k.t;
 }
 
+// ------------------------------------------------------- diagonal tiles
+// A Gram or polynomial tile on the diagonal (ti == tj) has P = Q (the same 256
+// operand rows) and a symmetric output, so only the 36 blocks on and above
+// the diagonal of its 8 x 8 grid of 32 x 32 blocks are computed, from one
+// operand panel (half the DMA of an ordinary tile).  In 64 x 64 super-blocks
+// (a 4 x 4 grid): waves 0-3 (type A) each take diagonal super-block (d, d),
+// d = wave (blocks (2d,2d), (2d,2d+1), (2d+1,2d+1)), and one half of
+// super-block (1,3) or (2,3) (blocks (2+d, 6), (2+d, 7)); waves 4-7 (type B)
+// each take one off-diagonal super-block, (0,1), (0,2), (0,3) or (1,2).  A
+// SIMD runs one wave of each type: 5 + 4 = 9 MFMAs per k16 sub-step instead of
+// 16.  Each wave reads 5 (A) or 4 (B) fragments per sub-step ("slots", any
+// of the panel's eight 32-row fragments).  Every block off the 32-block
+// diagonal is also written transposed, so the stored tile is whole and
+// exactly symmetric.
+template <bool TA>
+struct DiagGeo {
+  static constexpr int NSL = TA ? 5 : 4;   // fragment slots
+  static constexpr int NB = TA ? 5 : 4;    // accumulator blocks
+  int f[NSL];                              // fragment (32-row block) of each slot
+  int br[NB], bc[NB];                      // block row / column of each accumulator
+  __device__ void init(int wave) {
+    if (TA) {
+      const int dd = wave;                 // 0..3
+      f[0] = 2 * dd; f[1] = 2 * dd + 1; f[2] = 2 + dd; f[3] = 6; f[4] = 7;
+      br[0] = 2 * dd;     bc[0] = 2 * dd;
+      br[1] = 2 * dd;     bc[1] = 2 * dd + 1;
+      br[2] = 2 * dd + 1; bc[2] = 2 * dd + 1;
+      br[3] = 2 + dd;     bc[3] = 6;
+      br[4] = 2 + dd;     bc[4] = 7;
+    } else {
+      const int u = wave - 4;              // super-blocks (0,1) (0,2) (0,3) (1,2)
+      const int I = u == 3 ? 1 : 0, J = u == 3 ? 2 : u + 1;
+      f[0] = 2 * I; f[1] = 2 * I + 1; f[2] = 2 * J; f[3] = 2 * J + 1;
+      br[0] = 2 * I;     bc[0] = 2 * J;
+      br[1] = 2 * I;     bc[1] = 2 * J + 1;
+      br[2] = 2 * I + 1; bc[2] = 2 * J;
+      br[3] = 2 * I + 1; bc[3] = 2 * J + 1;
+    }
+  }
+};
+
+// LDS offsets of the slots' fragments (kk = 0, first read): row-major 2048 f
+// (fo.rm[kk] added at the read); k-major as FragOffsets::km for 32-row block f.
+template <bool PKM, int NSL>
+__device__ __forceinline__ void slot_offsets(const int (&f)[NSL], int lane, uint32_t (&so)[NSL]) {
+  const int G = lane >> 4, c = lane & 15, e = c >> 2, h = c & 3;
+  const int kr = 8 * (G >> 1) + e;
+  const int col = 16 * (G & 1) + 4 * h;
+#pragma unroll
+  for (int j = 0; j < NSL; ++j)
+    so[j] = PKM ? (uint32_t)(kr * 512 + ((f[j] ^ e) << 6) + 2 * col) : (uint32_t)(2048 * f[j]);
+}
+
+template <bool PKM, int NSL>
+__device__ __forceinline__ void read_slots(const uint8_t* stage, int kk, const uint32_t (&so)[NSL],
+                                           const FragOffsets& fo, bf16x8 (&fr)[NSL]) {
+#pragma unroll
+  for (int j = 0; j < NSL; ++j) {
+    if (!PKM) {
+      fr[j] = *(const bf16x8*)(stage + so[j] + fo.rm[kk]);
+    } else {
+      const uint8_t* base = stage + so[j] + 8192 * kk;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base + 2048));
+      fr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+}
+
+// MFMAs of one k16 sub-step (first operand: the column fragment, second: the
+// row fragment, so that acc holds the block transposed as in mfma16).
+//   type A slots: f2d, f2d+1, f2+d, f6, f7
+//   type B slots: f2I, f2I+1, f2J, f2J+1
+template <bool TA>
+__device__ __forceinline__ void mfma_diag(f32x16 (&acc)[DiagGeo<TA>::NB],
+                                          const bf16x8 (&fr)[DiagGeo<TA>::NSL]) {
+  if (TA) {
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[0], fr[0], acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[1], fr[0], acc[1], 0, 0, 0);
+    acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[1], fr[1], acc[2], 0, 0, 0);
+    acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[3], fr[2], acc[3], 0, 0, 0);
+    acc[4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[DiagGeo<TA>::NSL - 1], fr[2],
+                                                     acc[DiagGeo<TA>::NB - 1], 0, 0, 0);
+  } else {
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2], fr[0], acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[3], fr[0], acc[1], 0, 0, 0);
+    acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2], fr[1], acc[2], 0, 0, 0);
+    acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[3], fr[1], acc[3], 0, 0, 0);
+  }
+}
+
+// One K step t of a diagonal tile (as kstep, P panel only): sub-step 0 on
+// fragments read earlier while those of sub-step 1 are read; wait for the DMA
+// of step t+1; barrier; (DP) the DMA of step t+4 into the stage of step t-1;
+// sub-step 1 while the sub-step-0 fragments of step t+1 are read.
+template <bool PKM, bool TA, int VMW, bool DP, class OpP>
+__device__ __forceinline__ void kstep_diag(f32x16 (&acc)[DiagGeo<TA>::NB],
+                                           bf16x8 (&fa)[DiagGeo<TA>::NSL],
+                                           bf16x8 (&fb)[DiagGeo<TA>::NSL], int t, const OpP& dp,
+                                           const uint32_t (&so)[DiagGeo<TA>::NSL],
+                                           const FragOffsets& fo, int wave,
+                                           const uint8_t* __restrict__ cur,
+                                           const uint8_t* __restrict__ nxt,
+                                           uint8_t* __restrict__ dst_p) {
+  constexpr int NSL = DiagGeo<TA>::NSL, NB = DiagGeo<TA>::NB;
+  static_assert(NSL == NB, "one fragment slot per accumulator block");
+  constexpr int RDS = PKM ? 2 : 1;   // LDS instructions per fragment
+  read_slots<PKM, NSL>(cur, 1, so, fo, fb);
+  mfma_diag<TA>(acc, fa);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {   // NB == NSL: one fragment per MFMA
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RDS, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<VMW>();
+  bar_raw();
+  if (DP) dp.template issue<2>(t + NS - 1, dst_p, wave);
+  read_slots<PKM, NSL>(nxt, 0, so, fo, fa);
+  mfma_diag<TA>(acc, fb);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RDS, 0);
+    if (DP && i < 2) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Epilogue of one block of a diagonal tile: staged through the wave's LDS
+// region (32 rows of 36 floats), written row-wise (two 16-byte items per
+// lane), then (off the 32-block diagonal) transposed into the mirror block.
+// Gram: value s^2 * acc.  Polynomial: a*I + b*A + c*acc with the A block
+// read first (ain: this lane's two items).
+template <int STAGE>
+__device__ __forceinline__ void diag_block_out(const f32x16& acc, float* stg, uint16_t* out,
+                                               int64_t ld, int64_t r0, int64_t c0, bool mirror,
+                                               int lane, float sc, const GemmParams& P,
+                                               const u32x4 (&ain)[2]) {
+  constexpr int PITCH = 36;
+  const int frow = lane & 31, fkc = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *(f32x4*)(stg + frow * PITCH + 8 * g + 4 * fkc) =
+        f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = lane + 64 * p;
+    const int rr = q >> 2, c8 = (q & 3) * 8;
+    float* src = stg + rr * PITCH + c8;
+    const f32x4 v0 = *(const f32x4*)src, v1 = *(const f32x4*)(src + 4);
+    f32x4 a0, a1;
+    if (STAGE == 0) {
+      a0 = f32x4{v0.x * sc, v0.y * sc, v0.z * sc, v0.w * sc};
+      a1 = f32x4{v1.x * sc, v1.y * sc, v1.z * sc, v1.w * sc};
+    } else {
+      const u32x4 ai = ain[p];
+      const float a = P.a, b = P.b, c = P.c;
+      const int64_t dg = (r0 + rr) - (c0 + c8);   // 0..7 on the matrix diagonal
+      a0 = f32x4{fmaf(b, lo_bf(ai.x), fmaf(c, v0.x, dg == 0 ? a : 0.f)),
+                 fmaf(b, hi_bf(ai.x), fmaf(c, v0.y, dg == 1 ? a : 0.f)),
+                 fmaf(b, lo_bf(ai.y), fmaf(c, v0.z, dg == 2 ? a : 0.f)),
+                 fmaf(b, hi_bf(ai.y), fmaf(c, v0.w, dg == 3 ? a : 0.f))};
+      a1 = f32x4{fmaf(b, lo_bf(ai.z), fmaf(c, v1.x, dg == 4 ? a : 0.f)),
+                 fmaf(b, hi_bf(ai.z), fmaf(c, v1.y, dg == 5 ? a : 0.f)),
+                 fmaf(b, lo_bf(ai.w), fmaf(c, v1.z, dg == 6 ? a : 0.f)),
+                 fmaf(b, hi_bf(ai.w), fmaf(c, v1.w, dg == 7 ? a : 0.f))};
+    }
+    gstore<u32x4>(out + (r0 + rr) * ld + c0 + c8,
+                  u32x4{pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y),
+                        pack_bf2(a1.z, a1.w)});
+    if (mirror) {   // the transposed pass reads the final values
+      *(f32x4*)src = a0;
+      *(f32x4*)(src + 4) = a1;
+    }
+  }
+  if (mirror) {
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int q = lane + 64 * p;
+      const int ic = q & 3, jj = q >> 2;
+      float vv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vv[e] = stg[(8 * ic + e) * PITCH + jj];
+      gstore<u32x4>(out + (c0 + jj) * ld + r0 + 8 * ic,
+                    u32x4{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3]), pack_bf2(vv[4], vv[5]),
+                          pack_bf2(vv[6], vv[7])});
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// K loop and epilogue of a diagonal tile for one wave type.  Stage 0: P = X
+// rows (row-major), out A.  Stage 1: P = A columns (k-major), out B.
+template <int STAGE, bool TA, class OpP>
+__device__ __forceinline__ void diag_tile(const MatDesc& d, const GemmParams& P, const OpP& dp,
+                                          int nk, int i0, int wave, int lane, uint8_t* lds) {
+  constexpr bool PKM = STAGE == 1;
+  constexpr int NSL = DiagGeo<TA>::NSL, NB = DiagGeo<TA>::NB;
+  constexpr int BPW = 2;   // 16 one-KB blocks of the panel over 8 waves
+  DiagGeo<TA> geo;
+  geo.init(wave);
+  FragOffsets fo;
+  fo.init(lane);
+  uint32_t so[NSL];
+  slot_offsets<PKM, NSL>(geo.f, lane, so);
+  f32x16 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+  bf16x8 fa[NSL], fb[NSL];
+
+  // prologue: panel DMA of steps 0..3, wait for step 0
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) dp.template issue<BPW>(t, lds + t * STG, wave);
+  wait_vm<BPW * (NS - 2)>();
+  bar_raw();
+  read_slots<PKM, NSL>(lds, 0, so, fo, fa);
+  uint32_t sc = 0;
+  int t = 0;
+  for (; t < nk - NS + 1; ++t) {   // steady: DMA of step t+4; in flight after t+1's: t+2, t+3
+    kstep_diag<PKM, TA, 2 * BPW, true>(acc, fa, fb, t, dp, so, fo, wave, lds + sc,
+                                       lds + stage_wrap(sc + STG),
+                                       lds + stage_wrap(sc + (NS - 1) * STG));
+    sc = stage_wrap(sc + STG);
+  }
+  kstep_diag<PKM, TA, 2 * BPW, false>(acc, fa, fb, t, dp, so, fo, wave, lds + sc,
+                                      lds + stage_wrap(sc + STG), lds);
+  sc = stage_wrap(sc + STG);
+  ++t;
+  kstep_diag<PKM, TA, BPW, false>(acc, fa, fb, t, dp, so, fo, wave, lds + sc,
+                                  lds + stage_wrap(sc + STG), lds);
+  sc = stage_wrap(sc + STG);
+  ++t;
+  kstep_diag<PKM, TA, 0, false>(acc, fa, fb, t, dp, so, fo, wave, lds + sc,
+                                lds + stage_wrap(sc + STG), lds);
+  sc = stage_wrap(sc + STG);
+  // last step (nk-1)
+  read_slots<PKM, NSL>(lds + sc, 1, so, fo, fb);
+  mfma_diag<TA>(acc, fa);
+  mfma_diag<TA>(acc, fb);
+
+  // epilogue inputs (polynomial: the A blocks at the output positions)
+  const int64_t ld = d.mp;
+  u32x4 ain[NB][2];
+  if (STAGE == 1) {
+    const uint16_t* A = (const uint16_t*)d.a;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int q = lane + 64 * p;
+        ain[b][p] = gload<u32x4>(A + (i0 + 32 * geo.br[b] + (q >> 2)) * ld + i0 +
+                                 32 * geo.bc[b] + (q & 3) * 8);
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  bar_raw();
+  float* stg = (float*)(lds + wave * (32 * 36 * 4));
+  uint16_t* out = STAGE == 0 ? (uint16_t*)d.a : (uint16_t*)d.b;
+  const float s_first = P.first ? gload<float>(d.xs) : 1.f;
+  const float sc2 = s_first * s_first;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    diag_block_out<STAGE>(acc[b], stg, out, ld, i0 + 32 * geo.br[b], i0 + 32 * geo.bc[b],
+                          geo.br[b] != geo.bc[b], lane, sc2, P, ain[b]);
+}
+
 // One kernel per stage (and, for apply, per output kind), so that each carries
 // only its own operand layouts and epilogue.
 // NW = 4: four waves of 128 x 128 (one per SIMD).  NW = 8 (apply before the last
@@ -916,6 +1191,14 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   } else {
     dp.init((const uint16_t*)d.b, mp, i0, bP, lane);
     dq.init(xcur, np, j0, nk, lane);
+  }
+
+  if constexpr ((STAGE == 0 || STAGE == 1) && NW == 8 && MATOPT_DIAG_TILES) {
+    if (tile.ti == tile.tj) {   // wave-uniform (one tile per workgroup)
+      if (wave < 4) diag_tile<STAGE, true>(d, P, dp, nk, i0, wave, lane, lds);
+      else diag_tile<STAGE, false>(d, P, dp, nk, i0, wave, lane, lds);
+      return;
+    }
   }
 
   WaveGeo g;
