@@ -324,8 +324,10 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
     for (int tr = 0; tr < g.prep_tr; ++tr)
       for (int tc = 0; tc < g.prep_tc; ++tc) prep.push_back({i, tr, tc, idx++});
     const int tm = g.mp / tile, tn = g.np / tile;
-    units_triangle(i, tm, g.np, u3);
-    units_triangle(i, tm, g.mp, u4);
+    // bf16 diagonal tiles compute 36 of their 64 blocks
+    const int diag16 = dt == DT_BF16 ? 9 : 16;
+    units_triangle(i, tm, g.np, u3, diag16);
+    units_triangle(i, tm, g.mp, u4, diag16);
     units_full(i, tm, tn, g.mp, u5);
   }
   static_assert(sizeof(TileRef) == sizeof(GemmTile), "tile record layout");

@@ -25,7 +25,7 @@ struct TileRef {
 
 struct TileUnit {
   std::vector<TileRef> tiles;
-  int64_t cost = 0;     // sum over tiles of the K extent
+  int64_t cost = 0;     // sum over tiles of the K extent (diagonal tiles scaled)
   int32_t mat = 0, seq = 0;
 };
 
@@ -33,15 +33,18 @@ constexpr int kXcds = 8;
 constexpr int kUnitTiles = 64;
 
 // Symmetric-output stage (Gram or polynomial): tiles ti <= tj of a tm x tm
-// block grid, row-major, cut into units of at most kUnitTiles.
-inline void units_triangle(int mat, int tm, int64_t k_extent, std::vector<TileUnit>& out) {
+// block grid, row-major, cut into units of at most kUnitTiles.  A diagonal
+// tile costs diag16/16 of an off-diagonal one (9/16 where the kernel computes
+// only its upper 36 of 64 blocks).
+inline void units_triangle(int mat, int tm, int64_t k_extent, std::vector<TileUnit>& out,
+                           int diag16 = 16) {
   TileUnit u;
   u.mat = mat;
   int seq = 0;
   for (int ti = 0; ti < tm; ++ti)
     for (int tj = ti; tj < tm; ++tj) {
       u.tiles.push_back({mat, ti, tj, 0});
-      u.cost += k_extent;
+      u.cost += ti == tj ? k_extent * diag16 / 16 : k_extent;
       if ((int)u.tiles.size() == kUnitTiles) {
         u.seq = seq++;
         out.push_back(u);

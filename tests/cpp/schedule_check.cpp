@@ -8,6 +8,7 @@
 // Prints "ok <gram> <poly> <apply table sizes>" or the first violation; exit
 // status 0 iff ok.
 #include <cstdio>
+#include <cstdlib>
 #include <map>
 #include <set>
 #include <tuple>
@@ -55,14 +56,16 @@ static int check(const std::vector<TileUnit>& units, const std::vector<TileRef>&
   return 0;
 }
 
-int main() {
+int main(int argc, char** argv) {
+  // optional argument: cost of a diagonal tile in 16ths (9 for bf16, 16 for fp32)
+  const int diag16 = argc > 1 ? std::atoi(argv[1]) : 16;
   std::vector<TileUnit> gram, poly, full;
   int tm, tn;
   long long kg, kp;
   int mat = 0;
   while (std::scanf("%d %d %lld %lld", &tm, &tn, &kg, &kp) == 4) {
-    units_triangle(mat, tm, kg, gram);
-    units_triangle(mat, tm, kp, poly);
+    units_triangle(mat, tm, kg, gram, diag16);
+    units_triangle(mat, tm, kp, poly, diag16);
     units_full(mat, tm, tn, kp, full);
     ++mat;
   }
