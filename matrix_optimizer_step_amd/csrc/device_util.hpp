@@ -69,6 +69,28 @@ __device__ __forceinline__ double w_update(double w, float upd, float o, double 
   return fma((double)upd, (double)o, wdl != 0.0 ? fma(-wdl, w, w) : w);
 }
 
+// bfloat16 of the weight update of a bfloat16 weight w, rounded once: the same
+// bits as f64_to_bf16(w_update(w, upd, o, wdl)).  Without decay the float32 fma
+// fma(upd, o, w) is the exact value rounded once; rounding that float32 to
+// bfloat16 can differ from rounding the exact value only when it lands on a
+// bfloat16 midpoint (low 16 bits 0x8000) -- every midpoint is a float32, so
+// an exact value strictly between two midpoints rounds to a float32 in the
+// same interval -- and there the float64 value decides the side (the
+// float32 is moved one unit toward it, as rounding to odd does).  With decay
+// the float64 path is used throughout.
+__device__ __forceinline__ uint32_t w_update_bf16(float w, float upd, float o, double wdl) {
+  if (wdl != 0.0) return f64_to_bf16(w_update(w, upd, o, wdl));
+  float s = fmaf(upd, o, w);
+  uint32_t u = __float_as_uint(s);
+  if ((u & 0xffffu) == 0x8000u) {
+    const double x = fma((double)upd, (double)o, (double)w);
+    const double sd = (double)s;
+    if (x != sd) u += ((x > sd) == (s > 0.f)) ? 1u : 0xffffffffu;
+    s = __uint_as_float(u);
+  }
+  return f2bf(s);
+}
+
 // Element traits: 16-byte vectors hold E elements of T.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -346,7 +346,7 @@ __device__ __forceinline__ void write_out4(const MatDesc& d, const GemmParams& P
       const float w4[4] = {lo_bf(wo.x), hi_bf(wo.x), lo_bf(wo.y), hi_bf(wo.y)};
       uint32_t h[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = f64_to_bf16(w_update(w4[e], upd, v[e], P.wdl));
+      for (int e = 0; e < 4; ++e) h[e] = w_update_bf16(w4[e], upd, v[e], P.wdl);
       gstore<u32x2>(w, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
     }
     return;
@@ -359,7 +359,7 @@ __device__ __forceinline__ void write_out4(const MatDesc& d, const GemmParams& P
     } else {
       uint16_t* w = (uint16_t*)d.w + off + e;
       const float wo = bf2f(gload<uint16_t>(w));
-      gstore<uint16_t>(w, (uint16_t)f64_to_bf16(w_update(wo, upd, v[e], P.wdl)));
+      gstore<uint16_t>(w, (uint16_t)w_update_bf16(wo, upd, v[e], P.wdl));
     }
   }
 }
@@ -440,8 +440,8 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
         uint32_t h[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          h[e] = f64_to_bf16(w_update(w8[e], upd, lo[e], P.wdl));
-          h[4 + e] = f64_to_bf16(w_update(w8[4 + e], upd, hi[e], P.wdl));
+          h[e] = w_update_bf16(w8[e], upd, lo[e], P.wdl);
+          h[4 + e] = w_update_bf16(w8[4 + e], upd, hi[e], P.wdl);
         }
         gstore<u32x4>((uint16_t*)d.w + off, u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
                                                   h[4] | (h[5] << 16), h[6] | (h[7] << 16)});

@@ -8,7 +8,8 @@ Tolerances (relative Frobenius error per matrix, max over matrices):
 * stored momentum: bit-identical to the oracle's single rounding of mu*V+G.
 * stored weights: within 1 ulp of round(W - lr*sqrt(max(1,r/c))*O_gpu), where
   O_gpu is the GPU's own float32 direction for the GPU's own V (the kernels are
-  deterministic, so this isolates the update).
+  deterministic, so this isolates the update); bit-identical to the single
+  rounding of W + upd*O_gpu when upd is formed in float32 as the kernel does.
 """
 import numpy as np
 import pytest
@@ -238,6 +239,36 @@ def test_muon_step_bf16_ragged(mo):
         _check_w(w, w0, o, 0.02)
         ref = oracle.ns_orthogonalize(f64(v), rounding="bf16")
         assert relF(f64(o), ref) <= 2e-2
+
+
+def test_muon_fused_update_rounds_once_bitwise(mo):
+    """The fused bf16 weight update stores the single nearest-even rounding of
+    W + upd*O bit for bit, where upd = -lr*sqrt(max(1, r/c)) is formed in
+    float32 as the kernel forms it and O is the GPU's own float32 direction
+    for the updated V.  The shapes (full and ragged tiles, both orientations)
+    hold millions of weights, so float32 sums that fall exactly on a bfloat16
+    midpoint -- the case that needs the float64 tie-break -- occur and are
+    counted."""
+    shapes = [(1280, 5120), (5120, 1280), (1000, 3000)]
+    wl = workloads.small_case("muon_fused_round", shapes, seed=23)
+    W, V, G = _inputs(wl)
+    W0 = [w.clone() for w in W]
+    lr = 0.02
+    mo.muon_step_batched(W, G, V, mu=0.95, lr=lr, ns_steps=5)
+    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    midpoints = 0
+    for w, w0, o in zip(W, W0, O):
+        r, c = w.shape
+        upd = np.float32(-(np.float32(lr) * np.float32(np.sqrt(max(1.0, r / c)))))
+        exact = f64(w0) + float(upd) * f64(o)
+        s32 = exact.astype(np.float32)
+        midpoints += int(((s32.view(np.uint32) & 0xFFFF) == 0x8000).sum())
+        got = f64(w)
+        exp = oracle.round_bf16(exact)
+        bad = int((got != exp).sum())
+        assert bad == 0, f"{w.shape}: {bad} weights differ from the single rounding"
+    assert midpoints > 0, "no float32 result fell on a bfloat16 midpoint"
 
 
 def test_muon_step_ns_steps_zero_and_lr_zero(mo):
