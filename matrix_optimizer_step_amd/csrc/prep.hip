@@ -79,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams P) {
     inb[p] = r < rows && c < cols;
     offs[p] = r * cols + c;
     if (inb[p] && vec) {
-      vraw[p] = gload<u32x4>((const T*)d.v + offs[p]);
-      if (P.momentum) graw[p] = gload<u32x4>((const T*)d.g + offs[p]);
+      vraw[p] = gload_nt<u32x4>((const T*)d.v + offs[p]);
+      if (P.momentum) graw[p] = gload_nt<u32x4>((const T*)d.g + offs[p]);
     }
   }
 
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams P) {
           Tr::unpack(graw[p], gg);
 #pragma unroll
           for (int e = 0; e < E; ++e) vn[e] = Tr::fma_store(P.mu, vv[e], gg[e]);
-          gstore<u32x4>((T*)d.v + off, Tr::pack(vn));
+          gstore_nt<u32x4>((T*)d.v + off, Tr::pack(vn));
         } else {
 #pragma unroll
           for (int e = 0; e < E; ++e) vn[e] = vv[e];

@@ -55,9 +55,9 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
     for (int p = 0; p < NCH; ++p) {
       const int64_t ch = lr_idx + (int64_t)LPR * p;
       if (ch < nchunks) {
-        vreg[p] = gload<u32x4>(vrow + ch * E);
-        greg[p] = gload<u32x4>(grow + ch * E);
-        wreg[p] = gload<u32x4>(wrow + ch * E);
+        vreg[p] = gload_nt<u32x4>(vrow + ch * E);
+        greg[p] = gload_nt<u32x4>(grow + ch * E);
+        wreg[p] = gload_nt<u32x4>(wrow + ch * E);
       }
     }
 #pragma unroll
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
           ss = fmaf(fv[e], fv[e], ss);
         }
         vreg[p] = Tr::pack(fv);
-        gstore<u32x4>(vrow + ch * E, vreg[p]);
+        gstore_nt<u32x4>(vrow + ch * E, vreg[p]);
       }
     }
   }
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
       Tr::unpack(wreg[p], fw);
 #pragma unroll
       for (int e = 0; e < E; ++e) fw[e] = Tr::fma_store(step, fv[e], fw[e]);
-      gstore<u32x4>(wrow + ch * E, Tr::pack(fw));
+      gstore_nt<u32x4>(wrow + ch * E, Tr::pack(fw));
     }
   }
 }
@@ -166,8 +166,8 @@ __global__ __launch_bounds__(kThreads) void colcut_partial_kernel(ColcutParams P
       for (int u = 0; u < kColcutUnroll; ++u) {
         const int64_t ch = base + 64 * u;
         if (ch < nch) {
-          vv[u] = gload<u32x4>(vrow + ch * E);
-          gg[u] = gload<u32x4>(grow + ch * E);
+          vv[u] = gload_nt<u32x4>(vrow + ch * E);
+          gg[u] = gload_nt<u32x4>(grow + ch * E);
         }
       }
 #pragma unroll
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void colcut_partial_kernel(ColcutParams P
             fv[e] = Tr::fma_store(P.mu, fv[e], fg[e]);
             ss = fmaf(fv[e], fv[e], ss);
           }
-          gstore<u32x4>(vrow + ch * E, Tr::pack(fv));
+          gstore_nt<u32x4>(vrow + ch * E, Tr::pack(fv));
         }
       }
     }
@@ -219,8 +219,8 @@ __global__ __launch_bounds__(kThreads) void colcut_apply_kernel(ColcutParams P) 
       for (int u = 0; u < kColcutUnroll; ++u) {
         const int64_t ch = base + 64 * u;
         if (ch < nch) {
-          vv[u] = gload<u32x4>(vrow + ch * E);
-          ww[u] = gload<u32x4>(wrow + ch * E);
+          vv[u] = gload_nt<u32x4>(vrow + ch * E);
+          ww[u] = gload_nt<u32x4>(wrow + ch * E);
         }
       }
 #pragma unroll
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void colcut_apply_kernel(ColcutParams P) 
           Tr::unpack(ww[u], fw);
 #pragma unroll
           for (int e = 0; e < E; ++e) fw[e] = Tr::fma_store(step, fv[e], fw[e]);
-          gstore<u32x4>(wrow + ch * E, Tr::pack(fw));
+          gstore_nt<u32x4>(wrow + ch * E, Tr::pack(fw));
         }
       }
     }
