@@ -43,7 +43,14 @@
 // wave waits for its own DMA of the next step (explicit vmcnt), after it the
 // DMA of a step three ahead is issued into the stage everyone has finished
 // with.  The fragment reads of the next sub-step are interleaved with the
-// MFMAs of the current one (explicit scheduling groups).
+// MFMAs of the current one (explicit scheduling groups).  Apply pairs the DMA
+// of consecutive K steps (kloop2) so that the two 64-byte halves of each
+// 128-byte line of its row-major B rows are fetched from L2 once.
+//
+// Diagonal tiles (ti == tj) of the Gram and the polynomial compute only the 36
+// of their 64 32 x 32 blocks on and above the diagonal, from one operand
+// panel, 9 MFMAs per SIMD and k16 sub-step instead of 16, and write the blocks
+// above the diagonal twice (diag_tile).
 //
 // Epilogue: each wave stages its accumulators through its own LDS region
 // (float32) so that every global store is a contiguous row segment; the
@@ -1143,10 +1150,11 @@ __device__ __forceinline__ void diag_tile(const MatDesc& d, const GemmParams& P,
 
 // One kernel per stage (and, for apply, per output kind), so that each carries
 // only its own operand layouts and epilogue.
-// NW = 4: four waves of 128 x 128 (one per SIMD).  NW = 8 (apply before the last
-// iteration only): eight waves of 128 x 64, two per SIMD, so that one wave's
-// MFMAs run while the other waits on LDS, DMA or the barrier; the DMA of a step
-// is spread over all eight waves (two 1 KB blocks per operand each).
+// NW = 8 (every stage, by default): eight waves of 128 x 64, two per SIMD, so
+// that one wave's MFMAs run while the other waits on LDS, DMA or the barrier;
+// the DMA of a step is spread over all eight waves (two 1 KB blocks per
+// operand each).  NW = 4 (four waves of 128 x 128, one per SIMD) remains a
+// build-time alternative (MATOPT_*_WAVES).
 template <int STAGE, int OUT, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(NW / 4, NW / 4)))
