@@ -1148,6 +1148,167 @@ __device__ __forceinline__ void diag_tile(const MatDesc& d, const GemmParams& P,
                           geo.br[b] != geo.bc[b], lane, sc2, P, ain[b]);
 }
 
+// Two diagonal tiles of one matrix in one workgroup (a "diagonal pair"): the
+// first tile's operand panel fills the P slot of every stage, the second's
+// the Q slot, with the ordinary DMA schedule.  Each wave takes both pieces of
+// index d = wave & 3 of its tile (the type-A piece, 5 blocks, and the type-B
+// piece, 4 blocks, as in DiagGeo): waves 0-3 the first tile, waves 4-7 the
+// second.  That is 9 MFMAs per wave and k16 sub-step, 18 per SIMD, about 1.125
+// ordinary tiles, so the pair keeps pace with the other tiles of the matrix,
+// which read the same operand panels through L2 at the same time (a single
+// diagonal tile runs ahead of them and fetches its panel on its own).
+struct PairGeo {
+  static constexpr int NSL = 9, NB = 9;
+  int f[NSL];              // fragment (32-row block of the wave's panel) per slot
+  int br[NB], bc[NB];      // block row / column per accumulator
+  __device__ void init(int d) {
+    DiagGeo<true> a;
+    a.init(d);
+    DiagGeo<false> b;
+    b.init(d + 4);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) { f[j] = a.f[j]; br[j] = a.br[j]; bc[j] = a.bc[j]; }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f[5 + j] = b.f[j]; br[5 + j] = b.br[j]; bc[5 + j] = b.bc[j]; }
+  }
+};
+
+// The type-A MFMAs on slots 0-4 (accumulators 0-4), the type-B ones on slots
+// 5-8 (accumulators 5-8); operand order as in mfma_diag.
+__device__ __forceinline__ void mfma_pair(f32x16 (&acc)[9], const bf16x8 (&fr)[9]) {
+  acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[0], fr[0], acc[0], 0, 0, 0);
+  acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[1], fr[0], acc[1], 0, 0, 0);
+  acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[1], fr[1], acc[2], 0, 0, 0);
+  acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[3], fr[2], acc[3], 0, 0, 0);
+  acc[4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[4], fr[2], acc[4], 0, 0, 0);
+  acc[5] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[7], fr[5], acc[5], 0, 0, 0);
+  acc[6] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[8], fr[5], acc[6], 0, 0, 0);
+  acc[7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[7], fr[6], acc[7], 0, 0, 0);
+  acc[8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[8], fr[6], acc[8], 0, 0, 0);
+}
+
+// One K step of a diagonal pair: the DMA of kstep (both operands), the
+// fragment reads and MFMAs of the wave's 9 slots.
+template <bool PKM, int VMW, bool DQ, bool DP, class OpP, class OpQ>
+__device__ __forceinline__ void kstep_pair(f32x16 (&acc)[9], bf16x8 (&fa)[9], bf16x8 (&fb)[9],
+                                           int t, const OpP& dp, const OpQ& dq,
+                                           const uint32_t (&so)[9], const FragOffsets& fo,
+                                           int wave, const uint8_t* __restrict__ cur,
+                                           const uint8_t* __restrict__ nxt,
+                                           uint8_t* __restrict__ dst_q,
+                                           uint8_t* __restrict__ dst_p) {
+  constexpr int RDS = PKM ? 2 : 1;
+  read_slots<PKM, 9>(cur, 1, so, fo, fb);
+  if (DQ) dq.template issue<2>(t + NS - 2, dst_q + OPB, wave);
+  mfma_pair(acc, fa);
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RDS, 0);
+    if (DQ && (i == 3 || i == 7)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<VMW>();
+  bar_raw();
+  if (DP) dp.template issue<2>(t + NS - 1, dst_p, wave);
+  read_slots<PKM, 9>(nxt, 0, so, fo, fa);
+  mfma_pair(acc, fb);
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RDS, 0);
+    if (DP && (i == 3 || i == 7)) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// K loop (the schedule of kloop with bP = 0) and epilogue of a diagonal pair
+// with tiles at block rows i0 (P slot) and i1 (Q slot).
+template <int STAGE, class OpP, class OpQ>
+__device__ __forceinline__ void diag_pair(const MatDesc& d, const GemmParams& P, const OpP& dp,
+                                          const OpQ& dq, int nk, int i0, int i1, int wave,
+                                          int lane, uint8_t* lds) {
+  constexpr bool PKM = STAGE == 1;
+  constexpr int BPW = 2, DPS = 2 * BPW;
+  PairGeo geo;
+  geo.init(wave & 3);
+  FragOffsets fo;
+  fo.init(lane);
+  uint32_t so[9];
+  slot_offsets<PKM, 9>(geo.f, lane, so);
+  const uint32_t panel = wave < 4 ? 0u : (uint32_t)OPB;
+#pragma unroll
+  for (int j = 0; j < 9; ++j) so[j] += panel;
+  f32x16 acc[9];
+#pragma unroll
+  for (int b = 0; b < 9; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+  bf16x8 fa[9], fb[9];
+
+  // prologue (as kprologue): steps 0 .. NS-3 and the P half of step NS-2
+  dp.template issue<BPW>(0, lds, wave);
+  dq.template issue<BPW>(0, lds + OPB, wave);
+#pragma unroll
+  for (int t = 1; t < NS - 2; ++t) {
+    dp.template issue<BPW>(t, lds + t * STG, wave);
+    dq.template issue<BPW>(t, lds + t * STG + OPB, wave);
+  }
+  dp.template issue<BPW>(NS - 2, lds + (NS - 2) * STG, wave);
+  wait_vm<DPS * (NS - 3) + BPW>();
+  bar_raw();
+  read_slots<PKM, 9>(lds, 0, so, fo, fa);
+  uint32_t sc = 0;
+  int t = 0;
+  for (; t < nk - NS + 1; ++t) {
+    kstep_pair<PKM, 2 * DPS, true, true>(acc, fa, fb, t, dp, dq, so, fo, wave, lds + sc,
+                                         lds + stage_wrap(sc + STG),
+                                         lds + stage_wrap(sc + (NS - 2) * STG),
+                                         lds + stage_wrap(sc + (NS - 1) * STG));
+    sc = stage_wrap(sc + STG);
+  }
+  kstep_pair<PKM, 2 * DPS, true, false>(acc, fa, fb, t, dp, dq, so, fo, wave, lds + sc,
+                                        lds + stage_wrap(sc + STG),
+                                        lds + stage_wrap(sc + (NS - 2) * STG), lds);
+  sc = stage_wrap(sc + STG);
+  ++t;
+  kstep_pair<PKM, DPS, false, false>(acc, fa, fb, t, dp, dq, so, fo, wave, lds + sc,
+                                     lds + stage_wrap(sc + STG), lds, lds);
+  sc = stage_wrap(sc + STG);
+  ++t;
+  kstep_pair<PKM, 0, false, false>(acc, fa, fb, t, dp, dq, so, fo, wave, lds + sc,
+                                   lds + stage_wrap(sc + STG), lds, lds);
+  sc = stage_wrap(sc + STG);
+  read_slots<PKM, 9>(lds + sc, 1, so, fo, fb);
+  mfma_pair(acc, fa);
+  mfma_pair(acc, fb);
+
+  const int64_t ld = d.mp;
+  const int r0 = wave < 4 ? i0 : i1;   // this wave's tile
+  u32x4 ain[9][2];
+  if (STAGE == 1) {
+    const uint16_t* A = (const uint16_t*)d.a;
+#pragma unroll
+    for (int b = 0; b < 9; ++b)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int q = lane + 64 * p;
+        ain[b][p] = gload<u32x4>(A + (r0 + 32 * geo.br[b] + (q >> 2)) * ld + r0 +
+                                 32 * geo.bc[b] + (q & 3) * 8);
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  bar_raw();
+  float* stg = (float*)(lds + wave * (32 * 36 * 4));
+  uint16_t* out = STAGE == 0 ? (uint16_t*)d.a : (uint16_t*)d.b;
+  const float s_first = P.first ? gload<float>(d.xs) : 1.f;
+  const float sc2 = s_first * s_first;
+#pragma unroll
+  for (int b = 0; b < 9; ++b)
+    diag_block_out<STAGE>(acc[b], stg, out, ld, r0 + 32 * geo.br[b], r0 + 32 * geo.bc[b],
+                          geo.br[b] != geo.bc[b], lane, sc2, P, ain[b]);
+}
+
 // One kernel per stage (and, for apply, per output kind), so that each carries
 // only its own operand layouts and epilogue.
 // NW = 8 (every stage, by default): eight waves of 128 x 64, two per SIMD, so
@@ -1175,10 +1336,13 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   const GemmTile tile = P.tiles[blockIdx.x];
   if (tile.mat < 0) return;   // idle entry padding an XCD stream
   const MatDesc d = P.mats[tile.mat];
-  const int i0 = tile.ti * BM, j0 = tile.tj * BM;
+  // tj < 0 marks a diagonal pair (Gram and polynomial tables only): block rows
+  // ti and -tj-1
+  const bool pair = tile.tj < 0;
+  const int i0 = tile.ti * BM, j0 = pair ? i0 : tile.tj * BM;
   const int64_t mp = d.mp, np = d.np;
   // memory safety: an entry outside the matrix's output grid does nothing
-  if (i0 < 0 || j0 < 0 || i0 + BM > mp || j0 + BM > (STAGE == 2 ? np : mp)) return;
+  if (i0 < 0 || i0 + BM > mp || j0 + BM > (STAGE == 2 ? np : mp) || (pair && STAGE == 2)) return;
   const uint16_t* xcur = (const uint16_t*)(P.first ? d.x0in : P.cur ? d.x[1] : d.x[0]);
   uint16_t* xnext = (uint16_t*)(P.cur ? d.x[0] : d.x[1]);
   // K is a multiple of 256, so nk >= 8 > NS - 1
@@ -1202,6 +1366,15 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   }
 
   if constexpr ((STAGE == 0 || STAGE == 1) && NW == 8 && MATOPT_DIAG_TILES) {
+    if (pair) {
+      const int i1 = (-tile.tj - 1) * BM;
+      if (i1 < 0 || i1 + BM > mp) return;
+      OperandDma<PK> dq1;
+      if (STAGE == 0) dq1.init(xcur, np, i1, 0, lane);
+      else dq1.init((const uint16_t*)d.a, mp, i1, nk, lane);
+      diag_pair<STAGE>(d, P, dp, dq1, nk, i0, i1, wave, lane, lds);
+      return;
+    }
     if (tile.ti == tile.tj) {   // wave-uniform (one tile per workgroup)
       if (wave < 4) diag_tile<STAGE, true>(d, P, dp, nk, i0, wave, lane, lds);
       else diag_tile<STAGE, false>(d, P, dp, nk, i0, wave, lane, lds);

@@ -19,6 +19,7 @@
 
 namespace matopt {
 
+// tj < 0: a diagonal pair, the diagonal tiles of block rows ti and -tj-1
 struct TileRef {
   int32_t mat, ti, tj, pad_;
 };
@@ -35,16 +36,25 @@ constexpr int kUnitTiles = 64;
 // Symmetric-output stage (Gram or polynomial): tiles ti <= tj of a tm x tm
 // block grid, row-major, cut into units of at most kUnitTiles.  A diagonal
 // tile costs diag16/16 of an off-diagonal one (9/16 where the kernel computes
-// only its upper 36 of 64 blocks).
+// only its upper 36 of 64 blocks).  With pair_diag the diagonal tiles of block
+// rows 2p and 2p+1 form one entry {mat, 2p, -(2p+1)-1} (a diagonal pair, in
+// place of tile (2p, 2p)); a last diagonal tile stays alone when tm is odd.
 inline void units_triangle(int mat, int tm, int64_t k_extent, std::vector<TileUnit>& out,
-                           int diag16 = 16) {
+                           int diag16 = 16, bool pair_diag = false) {
   TileUnit u;
   u.mat = mat;
   int seq = 0;
+  const int64_t kd = k_extent * diag16 / 16;
   for (int ti = 0; ti < tm; ++ti)
     for (int tj = ti; tj < tm; ++tj) {
-      u.tiles.push_back({mat, ti, tj, 0});
-      u.cost += ti == tj ? k_extent * diag16 / 16 : k_extent;
+      if (ti == tj && pair_diag && ti % 2 == 1) continue;   // in the pair of ti-1
+      if (ti == tj && pair_diag && ti + 1 < tm) {
+        u.tiles.push_back({mat, ti, -(ti + 1) - 1, 0});
+        u.cost += 2 * kd;
+      } else {
+        u.tiles.push_back({mat, ti, tj, 0});
+        u.cost += ti == tj ? kd : k_extent;
+      }
       if ((int)u.tiles.size() == kUnitTiles) {
         u.seq = seq++;
         out.push_back(u);

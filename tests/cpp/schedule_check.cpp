@@ -20,26 +20,40 @@ using namespace matopt;
 
 static int check(const std::vector<TileUnit>& units, const std::vector<TileRef>& table,
                  const char* what) {
+  // a diagonal pair (tj < 0) stands for tiles (ti, ti) and (-tj-1, -tj-1)
+  auto keys = [](const TileRef& t) {
+    std::vector<std::tuple<int, int, int>> k;
+    if (t.tj < 0) {
+      k.push_back(std::make_tuple(t.mat, t.ti, t.ti));
+      k.push_back(std::make_tuple(t.mat, -t.tj - 1, -t.tj - 1));
+    } else {
+      k.push_back(std::make_tuple(t.mat, t.ti, t.tj));
+    }
+    return k;
+  };
   std::map<std::tuple<int, int, int>, int> pos;
   for (size_t p = 0; p < table.size(); ++p) {
     const TileRef& t = table[p];
     if (t.mat < 0) continue;
-    auto key = std::make_tuple(t.mat, t.ti, t.tj);
-    if (pos.count(key)) { std::printf("%s: duplicate tile\n", what); return 1; }
-    pos[key] = (int)p;
+    for (const auto& key : keys(t)) {
+      if (pos.count(key)) { std::printf("%s: duplicate tile\n", what); return 1; }
+      pos[key] = (int)p;
+    }
   }
   size_t n = 0;
   int64_t total = 0, maxunit = 0;
   std::vector<int64_t> load(kXcds, 0);
   for (const TileUnit& u : units) {
-    n += u.tiles.size();
     total += u.cost;
     maxunit = std::max(maxunit, u.cost);
     std::set<int> res;
     for (const TileRef& t : u.tiles) {
-      auto it = pos.find(std::make_tuple(t.mat, t.ti, t.tj));
-      if (it == pos.end()) { std::printf("%s: missing tile\n", what); return 1; }
-      res.insert(it->second % kXcds);
+      for (const auto& key : keys(t)) {
+        ++n;
+        auto it = pos.find(key);
+        if (it == pos.end()) { std::printf("%s: missing tile\n", what); return 1; }
+        res.insert(it->second % kXcds);
+      }
     }
     if (res.size() != 1) { std::printf("%s: unit split across XCDs\n", what); return 1; }
     load[*res.begin()] += u.cost;
@@ -57,15 +71,17 @@ static int check(const std::vector<TileUnit>& units, const std::vector<TileRef>&
 }
 
 int main(int argc, char** argv) {
-  // optional argument: cost of a diagonal tile in 16ths (9 for bf16, 16 for fp32)
+  // optional arguments: cost of a diagonal tile in 16ths (9 for bf16, 16 for
+  // fp32); 1 to pair the diagonal tiles (bf16)
   const int diag16 = argc > 1 ? std::atoi(argv[1]) : 16;
+  const bool pairs = argc > 2 && std::atoi(argv[2]) != 0;
   std::vector<TileUnit> gram, poly, full;
   int tm, tn;
   long long kg, kp;
   int mat = 0;
   while (std::scanf("%d %d %lld %lld", &tm, &tn, &kg, &kp) == 4) {
-    units_triangle(mat, tm, kg, gram, diag16);
-    units_triangle(mat, tm, kp, poly, diag16);
+    units_triangle(mat, tm, kg, gram, diag16, pairs);
+    units_triangle(mat, tm, kp, poly, diag16, pairs);
     units_full(mat, tm, tn, kp, full);
     ++mat;
   }

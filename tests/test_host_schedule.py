@@ -30,14 +30,16 @@ def _grid(shape, tile=256):
     return mp // tile, np_ // tile, np_, mp
 
 
-@pytest.mark.parametrize("diag16", [16, 9])
+@pytest.mark.parametrize("diag16,pairs", [(16, 0), (9, 1)])
 @pytest.mark.parametrize("name", ["gpt2_large_144", "llama3_8b_share_28", "qwen32b_share_14",
                                   "ragged_illcond_64"])
-def test_schedule_covers_every_tile_once_and_balances(checker, name, diag16):
-    # diag16 = 9: diagonal tiles cost 9/16 (bf16 computes 36 of their 64 blocks)
+def test_schedule_covers_every_tile_once_and_balances(checker, name, diag16, pairs):
+    # bf16 (9, 1): diagonal tiles cost 9/16 (36 of their 64 blocks) and go in
+    # pairs of block rows 2p, 2p+1 (one table entry covers both)
     wl = workloads.get(name)
     lines = "\n".join("%d %d %d %d" % _grid(s) for s in wl.shapes)
-    r = subprocess.run([checker, str(diag16)], input=lines, capture_output=True, text=True)
+    r = subprocess.run([checker, str(diag16), str(pairs)], input=lines, capture_output=True,
+                       text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.startswith("ok")
 
