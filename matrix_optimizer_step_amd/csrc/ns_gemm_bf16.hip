@@ -5,7 +5,7 @@
 // routine, written in factored form) all reduce to C[i][j] = sum_k P[i][k]Q[j][k]:
 //
 //   stage 0 (Gram)    A = s^2 * X X^T          P = Q = X rows (k contiguous in HBM)
-//   stage 1 (poly)    B = a*I + b*A + c*A A    P = Q = A columns (A A = A A^T)
+//   stage 1 (poly)    B = a*I + b*A + c*A A    P = A rows, Q = A columns (A A = A A^T)
 //   stage 2 (apply)   X' = s * B X             P = B rows, Q = X columns
 //
 // s is the Frobenius scale 1/(||V||+eps) on the first iteration, 1 afterwards.
@@ -16,8 +16,9 @@
 // A and B are symmetric: only tiles ti <= tj are computed.  The Gram epilogue
 // writes each off-diagonal tile twice, as itself and transposed into the
 // mirror position, so A is stored whole (and bitwise symmetric) and the
-// polynomial reads it through its columns in one fixed layout (k-major: each
-// k row of an operand tile is 512 contiguous bytes).  B keeps its upper tiles
+// polynomial reads it as apply reads its operands: P through A's rows
+// (row-major, 64 contiguous bytes per row and K step), Q through its columns
+// (k-major: each k row of an operand tile is 512 contiguous bytes).  B keeps its upper tiles
 // only (the mirror writes cost more in the polynomial than they save): apply
 // reads a B row block k-major from the mirrored upper tile for the k-blocks
 // left of its diagonal block and row-major (64 contiguous bytes per row and K
@@ -69,12 +70,13 @@
 // (kloop2), 0 spreads each step's DMA over two steps (kloop).  Pairing halves
 // the L1 -> L2 line requests of a row-major operand but shortens some
 // prefetch distances: on the GPT-2 Large set it makes apply 2% faster (its B
-// rows are row-major right of the diagonal) and the Gram 9% slower.
+// rows are row-major right of the diagonal) and the polynomial 1.5% faster
+// (its A rows), but the Gram 9% slower.
 #ifndef MATOPT_PAIR_GRAM
 #define MATOPT_PAIR_GRAM 0
 #endif
 #ifndef MATOPT_PAIR_POLY
-#define MATOPT_PAIR_POLY 0
+#define MATOPT_PAIR_POLY 1
 #endif
 #ifndef MATOPT_PAIR_APPLY
 #define MATOPT_PAIR_APPLY 1
@@ -1072,11 +1074,11 @@ __device__ __forceinline__ void diag_block_out(const f32x16& acc, float* stg, ui
 }
 
 // K loop and epilogue of a diagonal tile for one wave type.  Stage 0: P = X
-// rows (row-major), out A.  Stage 1: P = A columns (k-major), out B.
+// rows, out A.  Stage 1: P = A rows, out B.  Both panels are row-major.
 template <int STAGE, bool TA, class OpP>
 __device__ __forceinline__ void diag_tile(const MatDesc& d, const GemmParams& P, const OpP& dp,
                                           int nk, int i0, int wave, int lane, uint8_t* lds) {
-  constexpr bool PKM = STAGE == 1;
+  constexpr bool PKM = false;   // the P panel is row-major in both stages
   constexpr int NSL = DiagGeo<TA>::NSL, NB = DiagGeo<TA>::NB;
   constexpr int BPW = 2;   // 16 one-KB blocks of the panel over 8 waves
   DiagGeo<TA> geo;
@@ -1228,7 +1230,7 @@ template <int STAGE, class OpP, class OpQ>
 __device__ __forceinline__ void diag_pair(const MatDesc& d, const GemmParams& P, const OpP& dp,
                                           const OpQ& dq, int nk, int i0, int i1, int wave,
                                           int lane, uint8_t* lds) {
-  constexpr bool PKM = STAGE == 1;
+  constexpr bool PKM = false;   // the panels are row-major in both stages
   constexpr int BPW = 2, DPS = 2 * BPW;
   PairGeo geo;
   geo.init(wave & 3);
@@ -1325,12 +1327,13 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   constexpr int WN = 32 * NBJ;           // columns per wave
   constexpr int BPW = NW == 4 ? 4 : 2;   // DMA blocks per wave and operand
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
-  // Gram: P = Q = X rows.  Polynomial: P = Q = A columns (A is stored whole).
+  // Gram: P = Q = X rows.  Polynomial: P = A rows, Q = A columns (A is stored
+  // whole and symmetric).
   // Apply: P = B rows, k-major from the mirrored upper tile left of the
   // diagonal block (B holds its upper tiles only); Q = X columns.
-  constexpr int PK = STAGE == 0 ? OP_RM : STAGE == 1 ? OP_KM : OP_SPLIT;
+  constexpr int PK = STAGE == 2 ? OP_SPLIT : OP_RM;
   constexpr int QK = STAGE == 0 ? OP_RM : OP_KM;
-  constexpr bool PF = STAGE == 1;   // P layout from the diagonal block on
+  constexpr bool PF = false;   // P layout (from the diagonal block on, for apply)
   constexpr bool QF = STAGE != 0;   // Q layout
 
   const GemmTile tile = P.tiles[blockIdx.x];
