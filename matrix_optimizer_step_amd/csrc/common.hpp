@@ -153,6 +153,9 @@ hipError_t launch_prep(int dt, const PrepParams& p, int n_tiles, hipStream_t s);
 hipError_t launch_finalize(const FinalizeParams& p, int count, hipStream_t s);
 hipError_t launch_scale_out(int dt, const ScaleOutParams& p, int n_tiles, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s);
+// Diagonal tiles of the bf16 Gram (stage 0) / polynomial (stage 1): 0 whole,
+// 1 upper 36 of 64 blocks, 2 the same two per workgroup (entries with tj < 0).
+int gemm_bf16_diag_mode(int stage);
 hipError_t launch_gemm_f32(const GemmParams& p, int n_tiles, hipStream_t s);
 // RMNP kernel variants: rows of one wave (wpr=1) or of a whole block (wpr=4),
 // holding `nch` 16-byte chunks per lane in registers; nch == 0 selects the

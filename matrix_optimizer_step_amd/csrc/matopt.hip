@@ -324,13 +324,13 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
     for (int tr = 0; tr < g.prep_tr; ++tr)
       for (int tc = 0; tc < g.prep_tc; ++tc) prep.push_back({i, tr, tc, idx++});
     const int tm = g.mp / tile, tn = g.np / tile;
-    // bf16 diagonal tiles compute 36 of their 64 blocks; the Gram's go two per
-    // workgroup (in step with the matrix's other tiles, which share their
-    // operand panels through L2; the polynomial's k-major fragment reads make
-    // a pair LDS-bound there)
-    const int diag16 = dt == DT_BF16 ? 9 : 16;
-    units_triangle(i, tm, g.np, u3, diag16, dt == DT_BF16);
-    units_triangle(i, tm, g.mp, u4, diag16, false);
+    // diagonal tiles as the GEMM build treats them (bf16: 36 of their 64
+    // blocks; the Gram's two per workgroup, in step with the matrix's other
+    // tiles, which share their operand panels through L2)
+    const int dm3 = dt == DT_BF16 ? gemm_bf16_diag_mode(0) : 0;
+    const int dm4 = dt == DT_BF16 ? gemm_bf16_diag_mode(1) : 0;
+    units_triangle(i, tm, g.np, u3, dm3 ? 9 : 16, dm3 == 2);
+    units_triangle(i, tm, g.mp, u4, dm4 ? 9 : 16, dm4 == 2);
     units_full(i, tm, tn, g.mp, u5);
   }
   static_assert(sizeof(TileRef) == sizeof(GemmTile), "tile record layout");

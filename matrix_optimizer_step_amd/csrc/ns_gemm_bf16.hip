@@ -1448,6 +1448,17 @@ void ns_gemm_bf16_kernel(GemmParams P) {
 #define MATOPT_FINAL_WAVES 8
 #endif
 
+// How the bf16 Gram (stage 0) and polynomial (stage 1) launches treat the
+// diagonal tiles of their tables: 0 computes them whole, 1 computes their
+// upper 36 of 64 blocks, 2 does so with two tiles per workgroup (table entries
+// with tj < 0).  The host builds the tables to match.
+int gemm_bf16_diag_mode(int stage) {
+  if (!MATOPT_DIAG_TILES) return 0;
+  if (stage == 0) return MATOPT_GRAM_WAVES == 8 ? 2 : 0;
+  if (stage == 1) return MATOPT_POLY_WAVES == 8 ? 1 : 0;
+  return 0;
+}
+
 hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
   constexpr int GW = MATOPT_GRAM_WAVES, PW = MATOPT_POLY_WAVES;
