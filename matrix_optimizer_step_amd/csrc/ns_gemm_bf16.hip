@@ -147,24 +147,50 @@ enum OpKind { OP_RM = 0, OP_KM = 1, OP_SPLIT = 2 };
 
 template <int KIND>
 struct OperandDma {
-  const char* org_rm;   // byte address of element (r0, 0)
-  const char* org_km;   // byte address of stored element (0, r0)
-  uint32_t ldb;         // row pitch in bytes
+  const char* org_rm;   // byte address of the row-major origin (row r0)
+  const char* org_km;   // byte address of the k-major origin (column r0)
+  uint32_t rs;          // bytes between consecutive rows (k rows) as addressed
+  uint32_t us;          // bytes between 32-column units (k-major)
+  int64_t rm_b2, rm_b1; // row-major block b: (b >> 1) * rm_b2 + (b & 1) * rm_b1
+  int64_t rm_t, km_t;   // bytes per K step, row-major / k-major
   uint32_t off_rm;      // lane offset of row-major blocks
   uint32_t off_km0;     // lane offset of k-major blocks with b even
   uint32_t off_km1;     // lane offset of k-major blocks with b odd
   int t_km;             // steps t < t_km are k-major
 
-  __device__ void init(const uint16_t* src, int64_t ld, int r0, int tkm, int lane) {
-    ldb = (uint32_t)(ld * 2);
-    org_rm = (const char*)(src + (int64_t)r0 * ld);
-    org_km = (const char*)(src + r0);
+  // Plain: src is a row-major matrix with ld elements per row.  Blocked: src
+  // is an iterate X stored in 32 x 32 blocks (2 KB each, row-major inside,
+  // ld/32 blocks per block row), so that a row-major block (16 rows x 64 B)
+  // is 1 KB of one block and a k-major block (2 k rows x 8 units) is eight
+  // whole 128-byte lines (the two 64-byte rows of each unit are adjacent).
+  __device__ void init(const uint16_t* src, int64_t ld, int r0, int tkm, int lane,
+                       bool blocked = false) {
     t_km = tkm;
-    off_rm = (uint32_t)(lane >> 2) * ldb + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    if (!blocked) {
+      rs = (uint32_t)(ld * 2);
+      us = 64u;
+      rm_b2 = 32 * (int64_t)rs;
+      rm_b1 = 16 * (int64_t)rs;
+      rm_t = BK * 2;
+      km_t = BK * (int64_t)rs;
+      org_rm = (const char*)(src + (int64_t)r0 * ld);
+      org_km = (const char*)(src + r0);
+    } else {
+      const int64_t blkrow = (ld / 32) * 2048;   // bytes per block row
+      rs = 64u;
+      us = 2048u;
+      rm_b2 = blkrow;
+      rm_b1 = 1024;
+      rm_t = 2048;
+      km_t = blkrow;
+      org_rm = (const char*)src + (int64_t)(r0 / 32) * blkrow;
+      org_km = (const char*)src + (int64_t)(r0 / 32) * 2048;
+    }
+    off_rm = (uint32_t)(lane >> 2) * rs + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     // (2b + L/32) & 3 is L/32 for even b and 2 + L/32 for odd b
-    const uint32_t lo = (uint32_t)(lane >> 5) * ldb + 16u * (lane & 3);
-    off_km0 = lo + 64u * (((lane & 31) >> 2) ^ (lane >> 5));
-    off_km1 = lo + 64u * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
+    const uint32_t lo = (uint32_t)(lane >> 5) * rs + 16u * (lane & 3);
+    off_km0 = lo + us * (((lane & 31) >> 2) ^ (lane >> 5));
+    off_km1 = lo + us * (((lane & 31) >> 2) ^ (2 + (lane >> 5)));
   }
 
   __device__ __forceinline__ bool is_km(int t) const {
@@ -174,8 +200,8 @@ struct OperandDma {
   template <int Q, int BPW>
   __device__ __forceinline__ void block(bool km, int t, uint8_t* tile, int wave) const {
     const int b = BPW * wave + Q;   // parity of b is that of Q (BPW is even)
-    const char* base = km ? org_km + (int64_t)(t * BK + 2 * b) * ldb
-                          : org_rm + (int64_t)(16 * b) * ldb + t * BK * 2;   // wave-uniform
+    const char* base = km ? org_km + t * km_t + 2 * b * (int64_t)rs
+                          : org_rm + (b >> 1) * rm_b2 + (b & 1) * rm_b1 + t * rm_t;   // uniform
     const uint32_t kmoff = (Q & 1) ? off_km1 : off_km0;
     // per-lane offset chosen arithmetically (km is uniform)
     const uint32_t off = off_rm ^ ((off_rm ^ kmoff) & (km ? 0xffffffffu : 0u));
@@ -469,19 +495,23 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
   }
 }
 
-// Apply before the last iteration: the wave's 128 x 128 sub-tile goes straight
-// from the accumulators to HBM, without LDS staging.  Register group g of
+// Apply before the last iteration: the wave's sub-tile goes straight from the
+// accumulators to the next iterate in HBM, without LDS staging; each 32 x 32
+// block is one 2 KB block of the iterate's blocked layout.  Register group g of
 // acc[bi][bj] holds, for row 32bi + (lane & 31), columns 32bj + 8g + 4(lane>>5)
 // + 0..3.  After packing to bf16, one v_permlane32_swap per packed register
 // trades group 1 of the low half-wave for group 0 of the high half (and group 3
 // for group 2): lane l then holds columns 32bj + 8(lane>>5) + 16h + 0..7 for
-// h = 0, 1 -- two 16-byte stores per block and lane, each instruction writing
-// 32 bytes of 32 rows.
+// h = 0, 1 -- two 16-byte stores per block and lane, the pair of instructions
+// writing the whole 2 KB block.
 template <int NBJ>
 __device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][NBJ], uint16_t* out,
                                                  int64_t ld, int64_t i0, int64_t j0, int lane,
                                                  float s) {
-  uint16_t* base = out + (i0 + (lane & 31)) * ld + j0 + 8 * (lane >> 5);
+  // out is stored in 32 x 32 blocks (see OperandDma): block (bi, bj) of the
+  // wave is the 2 KB block ((i0 >> 5) + bi, (j0 >> 5) + bj), row-major inside
+  const int64_t nb = ld / 32;
+  uint16_t* base = out + ((i0 >> 5) * nb + (j0 >> 5)) * 1024 + (lane & 31) * 32 + 8 * (lane >> 5);
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -502,7 +532,7 @@ __device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][NBJ], ui
           pk[2 * h][k] = r[0];
           pk[2 * h + 1][k] = r[1];
         }
-      uint16_t* row = base + (int64_t)(32 * bi) * ld + 32 * bj;
+      uint16_t* row = base + (bi * nb + bj) * 1024;
       gstore<u32x4>(row, u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
       gstore<u32x4>(row + 16, u32x4{pk[2][0], pk[2][1], pk[3][0], pk[3][1]});
     }
@@ -1357,15 +1387,18 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   OperandDma<PK> dp;
   OperandDma<QK> dq;
+  // the first iteration reads X0 (V itself or the prep copy) in the plain
+  // layout; later ones read the iterate the previous apply stored in blocks
+  const bool xblk = !P.first;
   if (STAGE == 0) {
-    dp.init(xcur, np, i0, 0, lane);
-    dq.init(xcur, np, j0, 0, lane);
+    dp.init(xcur, np, i0, 0, lane, xblk);
+    dq.init(xcur, np, j0, 0, lane, xblk);
   } else if (STAGE == 1) {
     dp.init((const uint16_t*)d.a, mp, i0, nk, lane);
     dq.init((const uint16_t*)d.a, mp, j0, nk, lane);
   } else {
     dp.init((const uint16_t*)d.b, mp, i0, bP, lane);
-    dq.init(xcur, np, j0, nk, lane);
+    dq.init(xcur, np, j0, nk, lane, xblk);
   }
 
   if constexpr ((STAGE == 0 || STAGE == 1) && NW == 8 && MATOPT_DIAG_TILES) {
@@ -1373,7 +1406,7 @@ void ns_gemm_bf16_kernel(GemmParams P) {
       const int i1 = (-tile.tj - 1) * BM;
       if (i1 < 0 || i1 + BM > mp) return;
       OperandDma<PK> dq1;
-      if (STAGE == 0) dq1.init(xcur, np, i1, 0, lane);
+      if (STAGE == 0) dq1.init(xcur, np, i1, 0, lane, xblk);
       else dq1.init((const uint16_t*)d.a, mp, i1, nk, lane);
       diag_pair<STAGE>(d, P, dp, dq1, nk, i0, i1, wave, lane, lds);
       return;
