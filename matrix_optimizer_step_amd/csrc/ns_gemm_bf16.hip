@@ -145,6 +145,18 @@ __device__ __forceinline__ uint32_t km_off(uint32_t k, uint32_t col) {
 // from the mirrored upper tile of a symmetric matrix) and row-major after.
 enum OpKind { OP_RM = 0, OP_KM = 1, OP_SPLIT = 2 };
 
+// The workspace matrices -- the iterates X after the first iteration, A and B
+// -- are stored in 32 x 32 blocks of 2 KB, row-major inside and in the block
+// grid, so that every operand load of a K step (16 rows x 64 B, or 2 k rows
+// of 8 column units) and every 16-byte epilogue item stays within whole
+// 128-byte lines of one block.  Address of element (r, c) of such a matrix
+// with ld columns (r, c, ld multiples of 32 where blocks start).
+template <class Ptr>
+__device__ __forceinline__ Ptr blk_at(Ptr base, int64_t r, int64_t c, int64_t ld) {
+  const int64_t off = (((r >> 5) * (ld >> 5) + (c >> 5)) << 11) + ((r & 31) << 6) + ((c & 31) << 1);
+  return reinterpret_cast<Ptr>(reinterpret_cast<uintptr_t>(base) + off);
+}
+
 template <int KIND>
 struct OperandDma {
   const char* org_rm;   // byte address of the row-major origin (row r0)
@@ -336,12 +348,12 @@ __device__ __forceinline__ void prefetch_stripe(const uint16_t* src, int64_t ld,
                                                 u32x4 (&dst)[Ep<WN>::IPL]) {
   // lane q = lane + 64p reads row row0 + q/LPR, columns col0 + 8(q % LPR) .. +7;
   // item p starts RPI*p rows down (byte offsets)
+  // (src in 32 x 32 blocks)
   using G = Ep<WN>;
-  const char* base = (const char*)(src + row0 * ld + col0);
-  const uint32_t off = (uint32_t)(((lane / G::LPR) * ld + (lane % G::LPR) * 8) * 2);
 #pragma unroll
   for (int p = 0; p < G::IPL; ++p)
-    dst[p] = gload<u32x4>(base + (int64_t)(2 * G::RPI * p) * ld + off);
+    dst[p] = gload<u32x4>(blk_at(src, row0 + lane / G::LPR + G::RPI * p,
+                                 col0 + (lane % G::LPR) * 8, ld));
 }
 
 // Stage acc[BI][*] (32 rows of the wave's 128 x 128 sub-tile) into the wave's
@@ -607,7 +619,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
           a0 = f32x4{v0.x * sc, v0.y * sc, v0.z * sc, v0.w * sc};
           a1 = f32x4{v1.x * sc, v1.y * sc, v1.z * sc, v1.w * sc};
         }
-        gstore<u32x4>(out + (ib + rr) * ld_out + j0 + c8,
+        gstore<u32x4>(blk_at(out, ib + rr, j0 + c8, ld_out),
                       u32x4{pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y),
                             pack_bf2(a1.z, a1.w)});
         if (mirror) {   // mirror pass below reads the scaled values
@@ -627,7 +639,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
         float vv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vv[e] = stg[(8 * ic + e) * EP_PITCH + jj];
-        gstore<u32x4>(out + (int64_t)(j0 + jj) * ld_out + ib + 8 * ic,
+        gstore<u32x4>(blk_at(out, j0 + jj, ib + 8 * ic, ld_out),
                       u32x4{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3]), pack_bf2(vv[4], vv[5]),
                             pack_bf2(vv[6], vv[7])});
       }
@@ -1078,7 +1090,7 @@ __device__ __forceinline__ void diag_block_out(const f32x16& acc, float* stg, ui
                  fmaf(b, lo_bf(ai.w), fmaf(c, v1.z, dg == 6 ? a : 0.f)),
                  fmaf(b, hi_bf(ai.w), fmaf(c, v1.w, dg == 7 ? a : 0.f))};
     }
-    gstore<u32x4>(out + (r0 + rr) * ld + c0 + c8,
+    gstore<u32x4>(blk_at(out, r0 + rr, c0 + c8, ld),
                   u32x4{pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y),
                         pack_bf2(a1.z, a1.w)});
     if (mirror) {   // the transposed pass reads the final values
@@ -1095,7 +1107,7 @@ __device__ __forceinline__ void diag_block_out(const f32x16& acc, float* stg, ui
       float vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) vv[e] = stg[(8 * ic + e) * PITCH + jj];
-      gstore<u32x4>(out + (c0 + jj) * ld + r0 + 8 * ic,
+      gstore<u32x4>(blk_at(out, c0 + jj, r0 + 8 * ic, ld),
                     u32x4{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3]), pack_bf2(vv[4], vv[5]),
                           pack_bf2(vv[6], vv[7])});
     }
@@ -1164,8 +1176,8 @@ __device__ __forceinline__ void diag_tile(const MatDesc& d, const GemmParams& P,
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int q = lane + 64 * p;
-        ain[b][p] = gload<u32x4>(A + (i0 + 32 * geo.br[b] + (q >> 2)) * ld + i0 +
-                                 32 * geo.bc[b] + (q & 3) * 8);
+        ain[b][p] = gload<u32x4>(blk_at(A, i0 + 32 * geo.br[b] + (q >> 2),
+                                        i0 + 32 * geo.bc[b] + (q & 3) * 8, ld));
       }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1325,8 +1337,8 @@ __device__ __forceinline__ void diag_pair(const MatDesc& d, const GemmParams& P,
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int q = lane + 64 * p;
-        ain[b][p] = gload<u32x4>(A + (r0 + 32 * geo.br[b] + (q >> 2)) * ld + r0 +
-                                 32 * geo.bc[b] + (q & 3) * 8);
+        ain[b][p] = gload<u32x4>(blk_at(A, r0 + 32 * geo.br[b] + (q >> 2),
+                                        r0 + 32 * geo.bc[b] + (q & 3) * 8, ld));
       }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1394,10 +1406,10 @@ void ns_gemm_bf16_kernel(GemmParams P) {
     dp.init(xcur, np, i0, 0, lane, xblk);
     dq.init(xcur, np, j0, 0, lane, xblk);
   } else if (STAGE == 1) {
-    dp.init((const uint16_t*)d.a, mp, i0, nk, lane);
-    dq.init((const uint16_t*)d.a, mp, j0, nk, lane);
+    dp.init((const uint16_t*)d.a, mp, i0, nk, lane, true);
+    dq.init((const uint16_t*)d.a, mp, j0, nk, lane, true);
   } else {
-    dp.init((const uint16_t*)d.b, mp, i0, bP, lane);
+    dp.init((const uint16_t*)d.b, mp, i0, bP, lane, true);
     dq.init(xcur, np, j0, nk, lane, xblk);
   }
 
@@ -1407,7 +1419,7 @@ void ns_gemm_bf16_kernel(GemmParams P) {
       if (i1 < 0 || i1 + BM > mp) return;
       OperandDma<PK> dq1;
       if (STAGE == 0) dq1.init(xcur, np, i1, 0, lane, xblk);
-      else dq1.init((const uint16_t*)d.a, mp, i1, nk, lane);
+      else dq1.init((const uint16_t*)d.a, mp, i1, nk, lane, true);
       diag_pair<STAGE>(d, P, dp, dq1, nk, i0, i1, wave, lane, lds);
       return;
     }
