@@ -145,6 +145,15 @@ __device__ __forceinline__ uint32_t km_off(uint32_t k, uint32_t col) {
 // from the mirrored upper tile of a symmetric matrix) and row-major after.
 enum OpKind { OP_RM = 0, OP_KM = 1, OP_SPLIT = 2 };
 
+// Item q of a mirror (transposed) read of a staged stripe (32 rows, pitch 4
+// mod 64 floats) whose result goes to a blocked workspace matrix: staged
+// column jj = tr_jj(q), rows 8 ic .. 8 ic + 7 with ic = tr_ic(q).  The 16
+// lanes of a quarter-wave take one ic and 16 consecutive columns, so each of
+// their 4-byte reads meets a distinct bank (with ic = q & 3, lanes with ic and
+// ic+2 share one); a store instruction still writes whole 64-byte block rows.
+__device__ __forceinline__ int tr_ic(int q) { return (q >> 4) & 3; }
+__device__ __forceinline__ int tr_jj(int q) { return (q & 15) + 16 * (q >> 6); }
+
 // The workspace matrices -- the iterates X after the first iteration, A and B
 // -- are stored in 32 x 32 blocks of 2 KB, row-major inside and in the block
 // grid, so that every operand load of a K step (16 rows x 64 B, or 2 k rows
@@ -445,6 +454,9 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
       lo[0] = s * v0.x; lo[1] = s * v0.y; lo[2] = s * v0.z; lo[3] = s * v0.w;
       hi[0] = s * v1.x; hi[1] = s * v1.y; hi[2] = s * v1.z; hi[3] = s * v1.w;
     } else {
+      // four consecutive lanes per output row: each quarter-wave reads or
+      // writes four 64-byte row segments of the caller's W / O (the 2-way LDS
+      // bank conflict of this mapping costs less than 16 segments would)
       const int ic = q & 3, jj = q >> 2;
       r = j0 + jj;
       c = ib + 8 * ic;
@@ -635,7 +647,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
 #pragma unroll 4
       for (int p = 0; p < G::IPL; ++p) {
         const int q = lane + 64 * p;
-        const int ic = q & 3, jj = q >> 2;
+        const int ic = tr_ic(q), jj = tr_jj(q);
         float vv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vv[e] = stg[(8 * ic + e) * EP_PITCH + jj];
@@ -1103,7 +1115,7 @@ __device__ __forceinline__ void diag_block_out(const f32x16& acc, float* stg, ui
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int q = lane + 64 * p;
-      const int ic = q & 3, jj = q >> 2;
+      const int ic = tr_ic(q), jj = tr_jj(q);
       float vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) vv[e] = stg[(8 * ic + e) * PITCH + jj];
