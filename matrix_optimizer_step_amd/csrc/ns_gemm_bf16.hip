@@ -53,11 +53,13 @@
 // panel, 9 MFMAs per SIMD and k16 sub-step instead of 16, and write the blocks
 // above the diagonal twice (diag_tile).
 //
-// Epilogue: each wave stages its accumulators through its own LDS region
-// (float32) so that every global store is a contiguous row segment; the
-// polynomial's epilogue input (A) is prefetched during the last K step and one
-// stripe ahead.  A non-final apply skips the staging: its accumulators go
-// straight to X' with cross-half-wave lane swaps.  On the last iteration the result is
+// Epilogue: the Gram (which also writes the mirror tile) and the last apply
+// (which writes the caller's orientation) stage each wave's accumulators
+// through its own LDS region (float32) so that every global store is a
+// contiguous row segment.  The polynomial and a non-final apply skip the
+// staging: their accumulators go straight to whole 2 KB blocks of B or X'
+// with cross-half-wave lane swaps, the polynomial reading A at the lanes' own
+// accumulator positions one 32-row stripe ahead.  On the last iteration the result is
 // written in the original orientation as O, or folded straight into
 // W <- W - lr*sqrt(max(1,rows/cols))*O (so O never round-trips through HBM).
 //
@@ -528,6 +530,29 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
 // for group 2): lane l then holds columns 32bj + 8(lane>>5) + 16h + 0..7 for
 // h = 0, 1 -- two 16-byte stores per block and lane, the pair of instructions
 // writing the whole 2 KB block.
+// The 16 values v of one accumulator block of a lane (v[4g + e] at row
+// (lane & 31), column 8g + 4(lane >> 5) + e of the block), packed to bf16 and
+// stored through the lane swaps above into the 2 KB block at blk (row-major
+// inside, this lane's row and column offset already added).
+__device__ __forceinline__ void store_block_direct(const float (&v)[16], uint16_t* blk) {
+  uint32_t pk[4][2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    pk[g][0] = pack_bf2(v[4 * g], v[4 * g + 1]);
+    pk[g][1] = pack_bf2(v[4 * g + 2], v[4 * g + 3]);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * h][k], pk[2 * h + 1][k], false, false);
+      pk[2 * h][k] = r[0];
+      pk[2 * h + 1][k] = r[1];
+    }
+  gstore<u32x4>(blk, u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
+  gstore<u32x4>(blk + 16, u32x4{pk[2][0], pk[2][1], pk[3][0], pk[3][1]});
+}
+
 template <int NBJ>
 __device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][NBJ], uint16_t* out,
                                                  int64_t ld, int64_t i0, int64_t j0, int lane,
@@ -540,26 +565,64 @@ __device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][NBJ], ui
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj) {
-      const f32x16& a = acc[bi][bj];
-      uint32_t pk[4][2];
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = s * acc[bi][bj][r];
+      store_block_direct(v, base + (bi * nb + bj) * 1024);
+    }
+}
+
+// The polynomial's epilogue, straight from the accumulators as well (B has no
+// mirror): B = a I + b A + c (A A) with the A values read at the lanes' own
+// accumulator positions (8 bytes per register group), one 32-row stripe of
+// blocks ahead; a_first holds stripe 0, read during the last K step.
+template <int NBJ>
+__device__ __forceinline__ void poly_a_stripe(const uint16_t* A, int64_t ld, int64_t r0,
+                                              int64_t j0, int lane, u32x2 (&dst)[NBJ][4]) {
+#pragma unroll
+  for (int bj = 0; bj < NBJ; ++bj)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      dst[bj][g] = gload<u32x2>(blk_at(A, r0 + (lane & 31), j0 + 32 * bj + 8 * g + 4 * (lane >> 5), ld));
+}
+
+template <int NBJ>
+__device__ __forceinline__ void poly_store_direct(const f32x16 (&acc)[4][NBJ], uint16_t* out,
+                                                  const uint16_t* A, int64_t ld, int64_t i0,
+                                                  int64_t j0, int lane, float a, float b, float c,
+                                                  const u32x2 (&a_first)[NBJ][4]) {
+  const int64_t nb = ld / 32;
+  uint16_t* base = out + ((i0 >> 5) * nb + (j0 >> 5)) * 1024 + (lane & 31) * 32 + 8 * (lane >> 5);
+  u32x2 ac[NBJ][4], an[NBJ][4];
+#pragma unroll
+  for (int bj = 0; bj < NBJ; ++bj)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) ac[bj][g] = a_first[bj][g];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) {
+    if (bi + 1 < 4) poly_a_stripe<NBJ>(A, ld, i0 + 32 * (bi + 1), j0, lane, an);
+    const int64_t row = i0 + 32 * bi + (lane & 31);
+#pragma unroll
+    for (int bj = 0; bj < NBJ; ++bj) {
+      float v[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        pk[g][0] = pack_bf2(s * a[4 * g], s * a[4 * g + 1]);
-        pk[g][1] = pack_bf2(s * a[4 * g + 2], s * a[4 * g + 3]);
+        const int64_t col = j0 + 32 * bj + 8 * g + 4 * (lane >> 5);
+        const float av[4] = {lo_bf(ac[bj][g].x), hi_bf(ac[bj][g].x), lo_bf(ac[bj][g].y),
+                             hi_bf(ac[bj][g].y)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[4 * g + e] = fmaf(b, av[e], fmaf(c, acc[bi][bj][4 * g + e], row == col + e ? a : 0.f));
       }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * h][k], pk[2 * h + 1][k], false,
-                                                          false);
-          pk[2 * h][k] = r[0];
-          pk[2 * h + 1][k] = r[1];
-        }
-      uint16_t* row = base + (bi * nb + bj) * 1024;
-      gstore<u32x4>(row, u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
-      gstore<u32x4>(row + 16, u32x4{pk[2][0], pk[2][1], pk[3][0], pk[3][1]});
+      store_block_direct(v, base + (bi * nb + bj) * 1024);
     }
+    if (bi + 1 < 4) {
+#pragma unroll
+      for (int bj = 0; bj < NBJ; ++bj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) ac[bj][g] = an[bj][g];
+    }
+  }
 }
 
 // Epilogue of one wave's 128 x WN sub-tile, one 32-row stripe at a time (a
@@ -1426,13 +1489,14 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   }
 
   if constexpr ((STAGE == 0 || STAGE == 1) && NW == 8 && MATOPT_DIAG_TILES) {
-    if (pair) {
-      const int i1 = (-tile.tj - 1) * BM;
-      if (i1 < 0 || i1 + BM > mp) return;
-      OperandDma<PK> dq1;
-      if (STAGE == 0) dq1.init(xcur, np, i1, 0, lane, xblk);
-      else dq1.init((const uint16_t*)d.a, mp, i1, nk, lane, true);
-      diag_pair<STAGE>(d, P, dp, dq1, nk, i0, i1, wave, lane, lds);
+    if (pair) {   // only the Gram's tables hold diagonal pairs
+      if constexpr (STAGE == 0) {
+        const int i1 = (-tile.tj - 1) * BM;
+        if (i1 < 0 || i1 + BM > mp) return;
+        OperandDma<PK> dq1;
+        dq1.init(xcur, np, i1, 0, lane, xblk);
+        diag_pair<STAGE>(d, P, dp, dq1, nk, i0, i1, wave, lane, lds);
+      }
       return;
     }
     if (tile.ti == tile.tj) {   // wave-uniform (one tile per workgroup)
@@ -1467,10 +1531,19 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   const int64_t ep_ld = mp;
   const uint16_t* ep_src = (const uint16_t*)d.a;
   u32x4 ecur[Ep<WN>::IPL];
+  u32x2 afirst[NBJ][4];
   read_frags<PF, QF, NBJ>(lds + k.sc, 1, g, fo, k.pb, k.qb);
   mfma16<NBJ>(k.acc, k.pa, k.qa);
-  if (STAGE == 1) prefetch_stripe<WN>(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
+  if (STAGE == 1 && NW == 8)
+    poly_a_stripe<NBJ>((const uint16_t*)d.a, mp, i0 + g.wi0, j0 + g.wj0, lane, afirst);
+  else if (STAGE == 1)
+    prefetch_stripe<WN>(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
   mfma16<NBJ>(k.acc, k.pb, k.qb);
+  if (STAGE == 1 && NW == 8) {
+    poly_store_direct<NBJ>(k.acc, (uint16_t*)d.b, (const uint16_t*)d.a, mp, i0 + g.wi0, j0 + g.wj0,
+                           lane, P.a, P.b, P.c, afirst);
+    return;
+  }
   if (STAGE == 2 && OUT == OUT_NEXT_X) {
     const float s_first = P.first ? gload<float>(d.xs) : 1.f;
     store_acc_direct<NBJ>(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first);
