@@ -113,7 +113,11 @@ struct Ep {
   static constexpr int LPR = WN / 8;
   static constexpr int IPL = WN / 16;
   static constexpr int RPI = 64 / LPR;   // rows between a lane's items
-  static constexpr int WAVE_BYTES = 32 * PITCH * 4;
+  // float offset of staged row r: rows 16-31 sit 16 floats (banks) further on,
+  // so that the eight rows of a transposed read (rows 8i + e, i = 0..3) that
+  // 32 lanes touch together spread over all 64 banks
+  __device__ static constexpr int row(int r) { return r * PITCH + 16 * (r >> 4); }
+  static constexpr int WAVE_BYTES = (32 * PITCH + 16) * 4;
 };
 static_assert(4 * Ep<128>::WAVE_BYTES <= LDS_BYTES && 8 * Ep<64>::WAVE_BYTES <= LDS_BYTES,
               "epilogue staging must fit");
@@ -374,14 +378,14 @@ __device__ __forceinline__ void prefetch_stripe(const uint16_t* src, int64_t ld,
 template <int BI, int NBJ>
 __device__ __forceinline__ void stage_stripe(const f32x16 (&acc)[4][NBJ], float* stg, int frow,
                                              int fkc) {
-  constexpr int PITCH = Ep<32 * NBJ>::PITCH;
+  using G = Ep<32 * NBJ>;
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 v = {acc[BI][bj][4 * g], acc[BI][bj][4 * g + 1], acc[BI][bj][4 * g + 2],
                        acc[BI][bj][4 * g + 3]};
-      *(f32x4*)(stg + frow * PITCH + 32 * bj + 8 * g + 4 * fkc) = v;
+      *(f32x4*)(stg + G::row(frow) + 32 * bj + 8 * g + 4 * fkc) = v;
     }
 }
 
@@ -436,7 +440,6 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
                                            int64_t ib, int64_t j0, int lane, float upd,
                                            float s) {
   using G = Ep<WN>;
-  constexpr int EP_PITCH = G::PITCH;
   const int64_t rows = d.rows, cols = d.cols;
   const bool full = d.vec_ok && (TRANS ? (j0 + WN <= rows && ib + 32 <= cols)
                                        : (ib + 32 <= rows && j0 + WN <= cols));
@@ -449,7 +452,7 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
       r = ib + rr;
       c = j0 + c8;
       const bool hs = G::LPR == 16 && (q & 8) != 0;
-      const float* src = stg + rr * EP_PITCH + c8;
+      const float* src = stg + G::row(rr) + c8;
       const f32x4 r0 = *(const f32x4*)(src + (hs ? 4 : 0));
       const f32x4 r1 = *(const f32x4*)(src + (hs ? 0 : 4));
       const f32x4 v0 = hs ? r1 : r0, v1 = hs ? r0 : r1;
@@ -457,15 +460,15 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
       hi[0] = s * v1.x; hi[1] = s * v1.y; hi[2] = s * v1.z; hi[3] = s * v1.w;
     } else {
       // four consecutive lanes per output row: each quarter-wave reads or
-      // writes four 64-byte row segments of the caller's W / O (the 2-way LDS
-      // bank conflict of this mapping costs less than 16 segments would)
+      // writes four 64-byte row segments of the caller's W / O (the row skew
+      // of the staging keeps these column reads free of bank conflicts)
       const int ic = q & 3, jj = q >> 2;
       r = j0 + jj;
       c = ib + 8 * ic;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        lo[e] = s * stg[(8 * ic + e) * EP_PITCH + jj];
-        hi[e] = s * stg[(8 * ic + 4 + e) * EP_PITCH + jj];
+        lo[e] = s * stg[G::row(8 * ic + e) + jj];
+        hi[e] = s * stg[G::row(8 * ic + 4 + e) + jj];
       }
     }
   };
@@ -642,7 +645,6 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          u32x4 (&ecur)[Ep<32 * NBJ>::IPL]) {
   constexpr int WN = 32 * NBJ;
   using G = Ep<WN>;
-  constexpr int EP_PITCH = G::PITCH;
   constexpr bool EP_IN = STAGE == 1;
   const bool out_trans = OUT != OUT_NEXT_X && d.transposed;
   const bool mirror = STAGE == 0 && tile_off_diag;   // A is stored whole
@@ -672,7 +674,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
         const int q = lane + 64 * p;
         const int rr = q / G::LPR, c8 = (q % G::LPR) * 8;
         const bool hs = G::LPR == 16 && (q & 8) != 0;
-        float* src = stg + rr * EP_PITCH + c8;
+        float* src = stg + G::row(rr) + c8;
         const f32x4 r0 = *(const f32x4*)(src + (hs ? 4 : 0));
         const f32x4 r1 = *(const f32x4*)(src + (hs ? 0 : 4));
         const f32x4 v0 = hs ? r1 : r0, v1 = hs ? r0 : r1;
@@ -713,7 +715,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
         const int ic = tr_ic(q), jj = tr_jj(q);
         float vv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vv[e] = stg[(8 * ic + e) * EP_PITCH + jj];
+        for (int e = 0; e < 8; ++e) vv[e] = stg[G::row(8 * ic + e) + jj];
         gstore<u32x4>(blk_at(out, j0 + jj, ib + 8 * ic, ld_out),
                       u32x4{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3]), pack_bf2(vv[4], vv[5]),
                             pack_bf2(vv[6], vv[7])});
