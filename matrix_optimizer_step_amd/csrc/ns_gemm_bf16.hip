@@ -70,15 +70,16 @@
 
 // K loop DMA schedule per stage: 1 pairs the loads of consecutive K steps
 // (kloop2), 0 spreads each step's DMA over two steps (kloop).  Pairing halves
-// the L1 -> L2 line requests of a row-major operand but shortens some
-// prefetch distances: on the GPT-2 Large set it makes apply 2% faster (its B
-// rows are row-major right of the diagonal) and the polynomial 1.5% faster
-// (its A rows), but the Gram 9% slower.
+// the L1 -> L2 line requests of an operand read row-major from a plain
+// row-major matrix but shortens some prefetch distances.  On the GPT-2 Large
+// set the Gram (whose first iteration reads X0 plain) is 9% slower with it;
+// with A and B stored in 32 x 32 blocks every load covers whole lines anyway,
+// and the polynomial runs 2.4% faster spread, apply 0.7% faster paired.
 #ifndef MATOPT_PAIR_GRAM
 #define MATOPT_PAIR_GRAM 0
 #endif
 #ifndef MATOPT_PAIR_POLY
-#define MATOPT_PAIR_POLY 1
+#define MATOPT_PAIR_POLY 0
 #endif
 #ifndef MATOPT_PAIR_APPLY
 #define MATOPT_PAIR_APPLY 1
