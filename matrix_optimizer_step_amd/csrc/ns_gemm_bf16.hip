@@ -13,17 +13,13 @@
 // apply is one product with nothing read back in its epilogue (a X + (bA +
 // cA^2) X = p(A) X; folding a into B's diagonal is as accurate as adding a X
 // in float32, because X' is rounded to bf16 at the same relative precision).
-// A and B are symmetric: only tiles ti <= tj are computed.  The Gram epilogue
-// writes each off-diagonal tile twice, as itself and transposed into the
-// mirror position, so A is stored whole (and bitwise symmetric) and the
-// polynomial reads it as apply reads its operands: P through A's rows
-// (row-major, 64 contiguous bytes per row and K step), Q through its columns
-// (k-major: each k row of an operand tile is 512 contiguous bytes).  B keeps its upper tiles
-// only (the mirror writes cost more in the polynomial than they save): apply
-// reads a B row block k-major from the mirrored upper tile for the k-blocks
-// left of its diagonal block and row-major (64 contiguous bytes per row and K
-// step) from there on.  X is read row-major by the Gram and k-major (through
-// its columns) by apply.
+// A and B are symmetric: only tiles ti <= tj are computed and stored (a
+// diagonal tile whole).  A row block of A or B is read k-major from the upper
+// tiles above it for the k-blocks left of its diagonal block (each k row of an
+// operand tile is 512 contiguous bytes) and row-major (64 contiguous bytes per
+// row and K step) from there on: apply reads B's rows so, the polynomial A's
+// rows i0.. as P and, A being symmetric, A's rows j0.. as Q (its columns).  X
+// is read row-major by the Gram and k-major (through its columns) by apply.
 //
 // Engine.  A 256 x 256 output tile per workgroup of 8 waves, two per SIMD
 // (each wave 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16, accumulators
@@ -53,13 +49,12 @@
 // panel, 9 MFMAs per SIMD and k16 sub-step instead of 16, and write the blocks
 // above the diagonal twice (diag_tile).
 //
-// Epilogue: the Gram (which also writes the mirror tile) and the last apply
-// (which writes the caller's orientation) stage each wave's accumulators
-// through its own LDS region (float32) so that every global store is a
-// contiguous row segment.  The polynomial and a non-final apply skip the
-// staging: their accumulators go straight to whole 2 KB blocks of B or X'
-// with cross-half-wave lane swaps, the polynomial reading A at the lanes' own
-// accumulator positions one 32-row stripe ahead.  On the last iteration the result is
+// Epilogue: the last apply (which writes the caller's orientation) stages
+// each wave's accumulators through its own LDS region (float32) so that every
+// global store is a contiguous row segment.  The Gram, the polynomial and a
+// non-final apply skip the staging: their accumulators go straight to whole
+// 2 KB blocks of A, B or X' with cross-half-wave lane swaps, the polynomial
+// reading A at the lanes' own accumulator positions one 32-row stripe ahead.  On the last iteration the result is
 // written in the original orientation as O, or folded straight into
 // W <- W - lr*sqrt(max(1,rows/cols))*O (so O never round-trips through HBM).
 //
@@ -152,8 +147,9 @@ __device__ __forceinline__ uint32_t km_off(uint32_t k, uint32_t col) {
 // from the mirrored upper tile of a symmetric matrix) and row-major after.
 enum OpKind { OP_RM = 0, OP_KM = 1, OP_SPLIT = 2 };
 
-// Item q of a mirror (transposed) read of a staged stripe (32 rows, pitch 4
-// mod 64 floats) whose result goes to a blocked workspace matrix: staged
+// Item q of a mirror (transposed) read of a staged block (32 rows, pitch 36
+// floats: eight rows span 32 banks) whose result goes to a blocked workspace
+// matrix (the diagonal tiles' blocks above the diagonal): staged
 // column jj = tr_jj(q), rows 8 ic .. 8 ic + 7 with ic = tr_ic(q).  The 16
 // lanes of a quarter-wave take one ic and 16 consecutive columns, so each of
 // their 4-byte reads meets a distinct bank (with ic = q & 3, lanes with ic and
@@ -642,13 +638,13 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          const f32x16 (&acc)[4][NBJ], float* stg,
                                          const uint16_t* ep_src, int64_t ep_ld, uint16_t* out,
                                          int64_t ld_out, int i0, int j0, int lane, int frow,
-                                         int fkc, float s_first, bool tile_off_diag,
+                                         int fkc, float s_first,
                                          u32x4 (&ecur)[Ep<32 * NBJ>::IPL]) {
   constexpr int WN = 32 * NBJ;
   using G = Ep<WN>;
+  static_assert(STAGE != 0, "the Gram stores its tiles from the accumulators");
   constexpr bool EP_IN = STAGE == 1;
   const bool out_trans = OUT != OUT_NEXT_X && d.transposed;
-  const bool mirror = STAGE == 0 && tile_off_diag;   // A is stored whole
   const float upd = -P.lr * d.upd_scale;
   u32x4 enext[G::IPL];
 #pragma unroll 1
@@ -665,11 +661,11 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
 
     const int64_t ib = i0 + 32 * bi;   // first X-orientation row of this stripe
     if (STAGE != 2 || OUT == OUT_NEXT_X) {
-      // Gram, polynomial and non-final apply: 8 consecutive columns (one
+      // Polynomial and non-final apply (four-wave builds): 8 consecutive columns (one
       // 16-byte store) per lane item.  With 16 lanes per row, lanes 8-15 read
       // their two float4 halves in the other order so that the 16 lanes of a
       // row meet distinct LDS banks.
-      const float sc = STAGE == 0 ? s_first * s_first : s_first;
+      const float sc = s_first;
 #pragma unroll
       for (int p = 0; p < G::IPL; ++p) {
         const int q = lane + 64 * p;
@@ -700,26 +696,6 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
         gstore<u32x4>(blk_at(out, ib + rr, j0 + c8, ld_out),
                       u32x4{pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y),
                             pack_bf2(a1.z, a1.w)});
-        if (mirror) {   // mirror pass below reads the scaled values
-          *(f32x4*)src = a0;
-          *(f32x4*)(src + 4) = a1;
-        }
-      }
-    }
-    if (STAGE == 0 && mirror) {
-      __builtin_amdgcn_wave_barrier();
-      // Mirror tile: row j0+jj of the output holds this stripe's column jj,
-      // i.e. the 32 values of rows ib .. ib+31 (8 per lane item).
-#pragma unroll 4
-      for (int p = 0; p < G::IPL; ++p) {
-        const int q = lane + 64 * p;
-        const int ic = tr_ic(q), jj = tr_jj(q);
-        float vv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vv[e] = stg[G::row(8 * ic + e) + jj];
-        gstore<u32x4>(blk_at(out, j0 + jj, ib + 8 * ic, ld_out),
-                      u32x4{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3]), pack_bf2(vv[4], vv[5]),
-                            pack_bf2(vv[6], vv[7])});
       }
     }
     if (OUT != OUT_NEXT_X) {
@@ -842,24 +818,13 @@ __device__ __forceinline__ void ksteps(KState<NBJ>& k, int t_end, const OpP& dp,
   }
 }
 
-// All K steps of one tile but the last.  P is k-major for t < bP and in layout
-// PF from then on (bP is 0 or the first step of P's diagonal block, at most
-// nk - 8, so the switch lies in the steady range); Q is in layout QF.
+// Steps nk-4 .. nk-2 (no DMA after the Q half of step nk-1, issued in step
+// nk-4) and the sub-step-1 fragments of the last step, layouts (PF, QF).
 template <bool PF, bool QF, int NBJ, int BPW, class OpP, class OpQ>
-__device__ __forceinline__ void kloop(KState<NBJ>& k, int nk, int bP, const OpP& dp,
-                                      const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
-                                      int wave, uint8_t* lds) {
+__device__ __forceinline__ void kdrain(KState<NBJ>& k, const OpP& dp, const OpQ& dq,
+                                       const WaveGeo& g, const FragOffsets& fo, int wave,
+                                       uint8_t* lds) {
   constexpr int DPS = 2 * BPW;   // DMA instructions per wave and step
-  if (bP > 0) kprologue<true, QF, NBJ, BPW>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
-  else kprologue<PF, QF, NBJ, BPW>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
-  k.sc = 0;
-  k.t = 0;
-  if (bP > 0) {
-    ksteps<true, QF, true, QF, NBJ, BPW>(k, bP - 1, dp, dq, g, fo, wave, lds);
-    ksteps<true, QF, PF, QF, NBJ, BPW>(k, bP, dp, dq, g, fo, wave, lds);
-  }
-  ksteps<PF, QF, PF, QF, NBJ, BPW>(k, nk - NS + 1, dp, dq, g, fo, wave, lds);
-  // drain: the Q half of step nk-1 is issued in step nk-NS+1; none after
   kstep<PF, QF, PF, QF, DPS * 2, true, false, NBJ, BPW>(
       k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
       lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + (NS - 2) * STG), lds);
@@ -875,6 +840,42 @@ __device__ __forceinline__ void kloop(KState<NBJ>& k, int nk, int bP, const OpP&
                                                    lds + stage_wrap(k.sc + STG), lds, lds);
   k.sc = stage_wrap(k.sc + STG);
   ++k.t;
+  read_frags<PF, QF, NBJ>(lds + k.sc, 1, g, fo, k.pb, k.qb);
+}
+
+// All K steps of one tile but the last, and the last step's sub-step-1
+// fragments (in k.pb, k.qb).  P is k-major for t < bP and in layout PF from
+// then on (bP is 0 or the first step of P's diagonal block, at most nk - 8, so
+// the switch lies in the steady range).  Q is in layout QF, or with QS
+// k-major for t < bQ and in layout QF from then on (a multiple of 8, at most
+// nk - 8; bQ > bP, or with QEQ bQ >= bP: a diagonal tile in this loop).  The
+// step that switches both layouts at once is left out of builds that never
+// need it (it costs the register allocator dearly).
+template <bool PF, bool QF, bool QS, bool QEQ, int NBJ, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void kloop(KState<NBJ>& k, int nk, int bP, int bQ, const OpP& dp,
+                                      const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
+                                      int wave, uint8_t* lds) {
+  constexpr bool QA = QS ? true : QF;   // Q layout before bQ
+  if (bP > 0) kprologue<true, QA, NBJ, BPW>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
+  else if (QS && bQ > 0) kprologue<PF, QA, NBJ, BPW>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
+  else kprologue<PF, QF, NBJ, BPW>(k.pa, k.qa, dp, dq, g, fo, wave, lds, lds + STG);
+  k.sc = 0;
+  k.t = 0;
+  if (bP > 0) {
+    ksteps<true, QA, true, QA, NBJ, BPW>(k, bP - 1, dp, dq, g, fo, wave, lds);
+    if constexpr (QS && QEQ) {
+      if (bQ == bP) ksteps<true, QA, PF, QF, NBJ, BPW>(k, bP, dp, dq, g, fo, wave, lds);
+      else ksteps<true, QA, PF, QA, NBJ, BPW>(k, bP, dp, dq, g, fo, wave, lds);
+    } else {
+      ksteps<true, QA, PF, QA, NBJ, BPW>(k, bP, dp, dq, g, fo, wave, lds);
+    }
+  }
+  if (QS && bQ > bP) {
+    ksteps<PF, QA, PF, QA, NBJ, BPW>(k, bQ - 1, dp, dq, g, fo, wave, lds);
+    ksteps<PF, QA, PF, QF, NBJ, BPW>(k, bQ, dp, dq, g, fo, wave, lds);
+  }
+  ksteps<PF, QF, PF, QF, NBJ, BPW>(k, nk - NS + 1, dp, dq, g, fo, wave, lds);
+  kdrain<PF, QF, NBJ, BPW>(k, dp, dq, g, fo, wave, lds);
 }
 
 // Paired DMA schedule.  A row-major operand uses 64 bytes of each 128-byte
@@ -955,8 +956,8 @@ __device__ __forceinline__ void kpair(KState<NBJ>& k, const OpP& dp, const OpQ& 
   ++k.t;
 }
 
-// All K steps of one tile but the last, paired DMA (same contract as kloop;
-// nk and bP are even).  Prologue: P(0), Q(0), P(1), Q(1), P(2), P(3).
+// All K steps of one tile but the last, paired DMA (same contract as kloop
+// without QS; nk and bP are even).  Prologue: P(0), Q(0), P(1), Q(1), P(2), P(3).
 template <bool PF, bool QF, int NBJ, int BPW, class OpP, class OpQ>
 __device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP& dp,
                                        const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
@@ -997,6 +998,7 @@ __device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP
       lds + stage_wrap(k.sc + STG), lds, lds);
   k.sc = stage_wrap(k.sc + STG);
   ++k.t;
+  read_frags<PF, QF, NBJ>(lds + k.sc, 1, g, fo, k.pb, k.qb);
 }
 
 // ------------------------------------------------------- diagonal tiles
@@ -1093,12 +1095,14 @@ __device__ __forceinline__ void mfma_diag(f32x16 (&acc)[DiagGeo<TA>::NB],
 // One K step t of a diagonal tile (as kstep, P panel only): sub-step 0 on
 // fragments read earlier while those of sub-step 1 are read; wait for the DMA
 // of step t+1; barrier; (DP) the DMA of step t+4 into the stage of step t-1;
-// sub-step 1 while the sub-step-0 fragments of step t+1 are read.
-template <bool PKM, bool TA, int VMW, bool DP, class OpP>
+// sub-step 1 while the sub-step-0 fragments of step t+1 are read.  PKM / PKM1:
+// the panel layout of step t / t+1 (true: k-major), with slot offsets so / so1.
+template <bool PKM, bool PKM1, bool TA, int VMW, bool DP, class OpP>
 __device__ __forceinline__ void kstep_diag(f32x16 (&acc)[DiagGeo<TA>::NB],
                                            bf16x8 (&fa)[DiagGeo<TA>::NSL],
                                            bf16x8 (&fb)[DiagGeo<TA>::NSL], int t, const OpP& dp,
                                            const uint32_t (&so)[DiagGeo<TA>::NSL],
+                                           const uint32_t (&so1)[DiagGeo<TA>::NSL],
                                            const FragOffsets& fo, int wave,
                                            const uint8_t* __restrict__ cur,
                                            const uint8_t* __restrict__ nxt,
@@ -1106,6 +1110,7 @@ __device__ __forceinline__ void kstep_diag(f32x16 (&acc)[DiagGeo<TA>::NB],
   constexpr int NSL = DiagGeo<TA>::NSL, NB = DiagGeo<TA>::NB;
   static_assert(NSL == NB, "one fragment slot per accumulator block");
   constexpr int RDS = PKM ? 2 : 1;   // LDS instructions per fragment
+  constexpr int RDS1 = PKM1 ? 2 : 1;
   read_slots<PKM, NSL>(cur, 1, so, fo, fb);
   mfma_diag<TA>(acc, fa);
 #pragma unroll
@@ -1117,12 +1122,12 @@ __device__ __forceinline__ void kstep_diag(f32x16 (&acc)[DiagGeo<TA>::NB],
   wait_vm<VMW>();
   bar_raw();
   if (DP) dp.template issue<2>(t + NS - 1, dst_p, wave);
-  read_slots<PKM, NSL>(nxt, 0, so, fo, fa);
+  read_slots<PKM1, NSL>(nxt, 0, so1, fo, fa);
   mfma_diag<TA>(acc, fb);
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RDS, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RDS1, 0);
     if (DP && i < 2) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1197,16 +1202,19 @@ __device__ __forceinline__ void diag_block_out(const f32x16& acc, float* stg, ui
 // rows, out A.  Stage 1: P = A rows, out B.  Both panels are row-major.
 template <int STAGE, bool TA, class OpP>
 __device__ __forceinline__ void diag_tile(const MatDesc& d, const GemmParams& P, const OpP& dp,
-                                          int nk, int i0, int wave, int lane, uint8_t* lds) {
-  constexpr bool PKM = false;   // the P panel is row-major in both stages
+                                          int nk, int bP, int i0, int wave, int lane,
+                                          uint8_t* lds) {
   constexpr int NSL = DiagGeo<TA>::NSL, NB = DiagGeo<TA>::NB;
   constexpr int BPW = 2;   // 16 one-KB blocks of the panel over 8 waves
   DiagGeo<TA> geo;
   geo.init(wave);
   FragOffsets fo;
   fo.init(lane);
-  uint32_t so[NSL];
-  slot_offsets<PKM, NSL>(geo.f, lane, so);
+  // the panel is row-major from step bP on; before it (polynomial: the k
+  // blocks left of the diagonal, read through the upper tiles) k-major
+  uint32_t so[NSL], sok[NSL];
+  slot_offsets<false, NSL>(geo.f, lane, so);
+  slot_offsets<true, NSL>(geo.f, lane, sok);
   f32x16 acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -1219,28 +1227,44 @@ __device__ __forceinline__ void diag_tile(const MatDesc& d, const GemmParams& P,
   for (int t = 0; t < NS - 1; ++t) dp.template issue<BPW>(t, lds + t * STG, wave);
   wait_vm<BPW * (NS - 2)>();
   bar_raw();
-  read_slots<PKM, NSL>(lds, 0, so, fo, fa);
+  if (bP > 0) read_slots<true, NSL>(lds, 0, sok, fo, fa);
+  else read_slots<false, NSL>(lds, 0, so, fo, fa);
   uint32_t sc = 0;
   int t = 0;
-  for (; t < nk - NS + 1; ++t) {   // steady: DMA of step t+4; in flight after t+1's: t+2, t+3
-    kstep_diag<PKM, TA, 2 * BPW, true>(acc, fa, fb, t, dp, so, fo, wave, lds + sc,
-                                       lds + stage_wrap(sc + STG),
-                                       lds + stage_wrap(sc + (NS - 1) * STG));
+  // steady: DMA of step t+4; in flight after t+1's: t+2, t+3.  bP (a multiple
+  // of 8, at most nk - 8) lies in the steady range.
+  for (; t < bP - 1; ++t) {
+    kstep_diag<true, true, TA, 2 * BPW, true>(acc, fa, fb, t, dp, sok, sok, fo, wave, lds + sc,
+                                              lds + stage_wrap(sc + STG),
+                                              lds + stage_wrap(sc + (NS - 1) * STG));
     sc = stage_wrap(sc + STG);
   }
-  kstep_diag<PKM, TA, 2 * BPW, false>(acc, fa, fb, t, dp, so, fo, wave, lds + sc,
-                                      lds + stage_wrap(sc + STG), lds);
+  if (bP > 0) {
+    kstep_diag<true, false, TA, 2 * BPW, true>(acc, fa, fb, t, dp, sok, so, fo, wave, lds + sc,
+                                               lds + stage_wrap(sc + STG),
+                                               lds + stage_wrap(sc + (NS - 1) * STG));
+    sc = stage_wrap(sc + STG);
+    ++t;
+  }
+  for (; t < nk - NS + 1; ++t) {
+    kstep_diag<false, false, TA, 2 * BPW, true>(acc, fa, fb, t, dp, so, so, fo, wave, lds + sc,
+                                                lds + stage_wrap(sc + STG),
+                                                lds + stage_wrap(sc + (NS - 1) * STG));
+    sc = stage_wrap(sc + STG);
+  }
+  kstep_diag<false, false, TA, 2 * BPW, false>(acc, fa, fb, t, dp, so, so, fo, wave, lds + sc,
+                                               lds + stage_wrap(sc + STG), lds);
   sc = stage_wrap(sc + STG);
   ++t;
-  kstep_diag<PKM, TA, BPW, false>(acc, fa, fb, t, dp, so, fo, wave, lds + sc,
-                                  lds + stage_wrap(sc + STG), lds);
+  kstep_diag<false, false, TA, BPW, false>(acc, fa, fb, t, dp, so, so, fo, wave, lds + sc,
+                                           lds + stage_wrap(sc + STG), lds);
   sc = stage_wrap(sc + STG);
   ++t;
-  kstep_diag<PKM, TA, 0, false>(acc, fa, fb, t, dp, so, fo, wave, lds + sc,
-                                lds + stage_wrap(sc + STG), lds);
+  kstep_diag<false, false, TA, 0, false>(acc, fa, fb, t, dp, so, so, fo, wave, lds + sc,
+                                         lds + stage_wrap(sc + STG), lds);
   sc = stage_wrap(sc + STG);
   // last step (nk-1)
-  read_slots<PKM, NSL>(lds + sc, 1, so, fo, fb);
+  read_slots<false, NSL>(lds + sc, 1, so, fo, fb);
   mfma_diag<TA>(acc, fa);
   mfma_diag<TA>(acc, fb);
 
@@ -1447,14 +1471,18 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   constexpr int WN = 32 * NBJ;           // columns per wave
   constexpr int BPW = NW == 4 ? 4 : 2;   // DMA blocks per wave and operand
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
-  // Gram: P = Q = X rows.  Polynomial: P = A rows, Q = A columns (A is stored
-  // whole and symmetric).
-  // Apply: P = B rows, k-major from the mirrored upper tile left of the
-  // diagonal block (B holds its upper tiles only); Q = X columns.
-  constexpr int PK = STAGE == 2 ? OP_SPLIT : OP_RM;
-  constexpr int QK = STAGE == 0 ? OP_RM : OP_KM;
-  constexpr bool PF = false;   // P layout (from the diagonal block on, for apply)
-  constexpr bool QF = STAGE != 0;   // Q layout
+  // Gram: P = Q = X rows.  A and B hold their upper tiles only (diagonal
+  // tiles whole), so a row block of either is read k-major, through the upper
+  // tiles above it, for the k blocks left of its diagonal block, and
+  // row-major from there on.  Polynomial: P = rows i0.. of A, Q = rows j0.. of
+  // A (A's columns j0.., A being symmetric), both read that way; every tile
+  // ends its K loop with both operands row-major.  Apply: P = B rows; Q = X
+  // columns (k-major).
+  constexpr int PK = STAGE == 0 ? OP_RM : OP_SPLIT;
+  constexpr int QK = STAGE == 0 ? OP_RM : STAGE == 1 ? OP_SPLIT : OP_KM;
+  constexpr bool PF = false;        // P layout (from its diagonal block on)
+  constexpr bool QF = STAGE == 2;   // Q layout (polynomial: from its diagonal block on)
+  constexpr bool QS = STAGE == 1;   // Q k-major before step bQ
 
   const GemmTile tile = P.tiles[blockIdx.x];
   if (tile.mat < 0) return;   // idle entry padding an XCD stream
@@ -1470,8 +1498,10 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   uint16_t* xnext = (uint16_t*)(P.cur ? d.x[0] : d.x[1]);
   // K is a multiple of 256, so nk >= 8 > NS - 1
   const int nk = (int)(STAGE == 0 ? np : mp) / BK;
-  // apply: P is k-major for steps t < bP (at most nk - 8)
-  const int bP = STAGE == 2 ? i0 / BK : 0;
+  // polynomial and apply: P is k-major for steps t < bP; polynomial: Q for
+  // steps t < bQ (bP <= bQ <= nk - 8)
+  const int bP = STAGE == 0 ? 0 : i0 / BK;
+  const int bQ = STAGE == 1 ? j0 / BK : 0;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1484,8 +1514,8 @@ void ns_gemm_bf16_kernel(GemmParams P) {
     dp.init(xcur, np, i0, 0, lane, xblk);
     dq.init(xcur, np, j0, 0, lane, xblk);
   } else if (STAGE == 1) {
-    dp.init((const uint16_t*)d.a, mp, i0, nk, lane, true);
-    dq.init((const uint16_t*)d.a, mp, j0, nk, lane, true);
+    dp.init((const uint16_t*)d.a, mp, i0, bP, lane, true);
+    dq.init((const uint16_t*)d.a, mp, j0, bQ, lane, true);
   } else {
     dp.init((const uint16_t*)d.b, mp, i0, bP, lane, true);
     dq.init(xcur, np, j0, nk, lane, xblk);
@@ -1503,8 +1533,8 @@ void ns_gemm_bf16_kernel(GemmParams P) {
       return;
     }
     if (tile.ti == tile.tj) {   // wave-uniform (one tile per workgroup)
-      if (wave < 4) diag_tile<STAGE, true>(d, P, dp, nk, i0, wave, lane, lds);
-      else diag_tile<STAGE, false>(d, P, dp, nk, i0, wave, lane, lds);
+      if (wave < 4) diag_tile<STAGE, true>(d, P, dp, nk, bP, i0, wave, lane, lds);
+      else diag_tile<STAGE, false>(d, P, dp, nk, bP, i0, wave, lane, lds);
       return;
     }
   }
@@ -1527,15 +1557,18 @@ void ns_gemm_bf16_kernel(GemmParams P) {
       for (int r = 0; r < 16; ++r) k.acc[bi][bj][r] = 0.f;
   constexpr bool PAIRED = STAGE == 0 ? MATOPT_PAIR_GRAM : STAGE == 1 ? MATOPT_PAIR_POLY
                                                                      : MATOPT_PAIR_APPLY;
-  if (PAIRED) kloop2<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
-  else kloop<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
+  static_assert(!(PAIRED && QS), "the paired schedule keeps one Q layout");
+  // diagonal polynomial tiles take this path unless diag_tile handles them
+  constexpr bool QEQ = !(NW == 8 && MATOPT_DIAG_TILES);
+  if constexpr (PAIRED) kloop2<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
+  else kloop<PF, QF, QS, QEQ, NBJ, BPW>(k, nk, bP, bQ, dp, dq, g, fo, wave, lds);
 
-  // last K step; the first epilogue stripe is fetched meanwhile
+  // last K step (its fragments are read); the first epilogue stripe is
+  // fetched meanwhile
   const int64_t ep_ld = mp;
   const uint16_t* ep_src = (const uint16_t*)d.a;
   u32x4 ecur[Ep<WN>::IPL];
   u32x2 afirst[NBJ][4];
-  read_frags<PF, QF, NBJ>(lds + k.sc, 1, g, fo, k.pb, k.qb);
   mfma16<NBJ>(k.acc, k.pa, k.qa);
   if (STAGE == 1 && NW == 8)
     poly_a_stripe<NBJ>((const uint16_t*)d.a, mp, i0 + g.wi0, j0 + g.wj0, lane, afirst);
@@ -1552,17 +1585,23 @@ void ns_gemm_bf16_kernel(GemmParams P) {
     store_acc_direct<NBJ>(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first);
     return;
   }
-  {
+  if (STAGE == 0) {   // an upper tile of A, scaled by s^2 on the first iteration
+    const float s_first = P.first ? gload<float>(d.xs) : 1.f;
+    store_acc_direct<NBJ>(k.acc, (uint16_t*)d.a, mp, i0 + g.wi0, j0 + g.wj0, lane,
+                          s_first * s_first);
+    return;
+  }
+  if constexpr (STAGE != 0) {
   // all fragment reads done (consumed above): the stages become epilogue staging
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   bar_raw();
 
-  uint16_t* out = STAGE == 0 ? (uint16_t*)d.a : STAGE == 1 ? (uint16_t*)d.b : xnext;
+  uint16_t* out = STAGE == 1 ? (uint16_t*)d.b : xnext;
   const int64_t ld_out = STAGE == 2 ? np : mp;
   const float s_first = P.first ? gload<float>(d.xs) : 1.f;
   epilogue<STAGE, OUT, NBJ>(d, P, k.acc, (float*)(lds + wave * Ep<WN>::WAVE_BYTES), ep_src, ep_ld, out,
                        ld_out, i0 + g.wi0, j0 + g.wj0, lane, g.frow, g.fkc, s_first,
-                       tile.ti != tile.tj, ecur);
+                       ecur);
   }
 }
 
