@@ -36,10 +36,20 @@
  * - count == 0 is a no-op returning MATOPT_OK.
  * - Calls on one stream are ordered.  Calls that share a workspace must not run
  *   concurrently on different streams.
- * - The first call with a given (shapes, pointers, workspace) list builds a small
- *   device-side plan (matrix descriptors and tile tables), which allocates device
- *   memory and synchronises `stream` once; later calls with the same list reuse
- *   it and allocate nothing.
+ * - Plans.  The first call of an entry point with a given list of shapes (and
+ *   dtype; for the column-cut apply also full_cols) builds a plan: descriptor
+ *   templates and the tile and task tables of every launch, which depend on
+ *   the shapes only.  Building it allocates one device buffer (stream-ordered,
+ *   on `stream`) and copies the tables into it on `stream`.  Every later call
+ *   with the same shapes reuses it whatever its pointers: it allocates nothing,
+ *   frees nothing, copies nothing from host memory and never synchronises the
+ *   host -- this call's pointers reach the device as kernel arguments of a
+ *   small bind launch that writes the descriptors (into the workspace for the
+ *   Newton-Schulz entry points, into the plan for the others).  Calls that use
+ *   one plan are therefore chained: a call on another stream than the previous
+ *   call of the same plan first waits (on the device) for that call's work.
+ *   At most 64 plans are cached; an evicted plan is freed, stream-ordered,
+ *   once the device has finished every call that used it.
  */
 #ifndef MATOPT_H
 #define MATOPT_H
@@ -221,12 +231,22 @@ int32_t matopt_version(void);
  * synchronises on those events).  Classes: 0 momentum+norm+X0 build,
  * 1 norm finalize, 2 Gram X X^T, 3 polynomial a*I+b*A+c*A*A, 4 apply B*X
  * (incl. fused update on the last step), 5 ns_steps==0 output, 6 RMNP,
- * 7 column-cut RMNP partial, 8 column-cut RMNP apply, 9 AdamW.
+ * 7 column-cut RMNP partial, 8 column-cut RMNP apply, 9 AdamW, 10 descriptor
+ * bind.
  */
-#define MATOPT_PROFILE_CLASSES 10
+#define MATOPT_PROFILE_CLASSES 11
 matopt_status matopt_profile_enable(int32_t on);
 /* ms[k], launches[k] for k < MATOPT_PROFILE_CLASSES; resets the accumulators. */
 matopt_status matopt_profile_read(double* ms, int64_t* launches);
+
+/*
+ * Diagnostics of the plan cache, cumulative since the library was loaded:
+ * out[0] plans built, out[1] device allocations, out[2] device frees, out[3]
+ * bind launches (one per 112 descriptors of a call).  Writes the first n <=
+ * MATOPT_COUNTERS values to the HOST array out; MATOPT_ERR_PARAM otherwise.
+ */
+#define MATOPT_COUNTERS 4
+matopt_status matopt_counters(int64_t* out, int32_t n);
 
 #ifdef __cplusplus
 }

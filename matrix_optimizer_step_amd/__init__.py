@@ -11,10 +11,12 @@ Entry points mirror the C ABI (``include/matopt.h``):
 * ``muon_step_batched(weights, grads, moms, mu, lr, ns_steps, coeffs, eps)``
 * ``rmnp_step_batched(weights, grads, moms, mu, lr, eps)``
 * ``ns_orthogonalize_batched(xs, out_dtype, ns_steps, coeffs, eps)``
-* ``workspace_bytes(shapes, dtype)``, ``profile_enable``, ``profile_read``
+* ``workspace_bytes(shapes, dtype)``, ``profile_enable``, ``profile_read``,
+  ``counters``
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
 import threading
@@ -24,13 +26,14 @@ import torch
 __all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
            "muon_step_batched_wd", "rmnp_step_batched", "rmnp_colcut_partial_batched",
            "rmnp_colcut_apply_batched", "adamw_step_batched", "ns_orthogonalize_batched", "profile_enable",
-           "profile_read", "PROFILE_CLASSES", "LIB_PATH", "EXPORTS"]
+           "profile_read", "counters", "PROFILE_CLASSES", "COUNTERS", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmatopt.so")
 
 F32, BF16 = 0, 1
 PROFILE_CLASSES = ("prep", "finalize", "gram", "poly", "apply", "scale_out", "rmnp",
-                   "colcut_partial", "colcut_apply", "adamw")
+                   "colcut_partial", "colcut_apply", "adamw", "bind")
+COUNTERS = ("plan_builds", "device_allocs", "device_frees", "bind_launches")
 
 # Defaults printed on the pages (blog post appendix).
 NS_COEFFS = (3.4445, -4.7750, 2.0315)
@@ -79,6 +82,7 @@ EXPORTS = {
     "matopt_version": (_i32, []),
     "matopt_profile_enable": (_i32, [_i32]),
     "matopt_profile_read": (_i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "matopt_counters": (_i32, [ctypes.POINTER(_i64), _i32]),
 }
 
 _lib = None
@@ -121,9 +125,17 @@ def _dt(dtype) -> int:
     raise TypeError(f"unsupported dtype {dtype} (bfloat16 or float32)")
 
 
-def _check_mat(t: torch.Tensor, what: str, dtype=None):
+def _check_dev(t, what: str, device=None):
+    """A CUDA (HIP) tensor, on ``device`` when given: a host pointer must never
+    reach a kernel."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{what} must be a CUDA (HIP) tensor")
+    if device is not None and t.device != torch.device(device):
+        raise TypeError(f"{what} is on {t.device}, expected {device}")
+
+
+def _check_mat(t: torch.Tensor, what: str, dtype=None):
+    _check_dev(t, what)
     if t.dim() != 2:
         raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
@@ -144,20 +156,29 @@ def workspace_bytes(shapes, dtype) -> int:
     return int(lib().matopt_workspace_bytes(rows, cols, n, _dt(dtype)))
 
 
-_ws_cache: dict = {}
+# Workspaces allocated by the binding, most recently used last; at most
+# _WS_CACHE_CAP of them are kept (an evicted one goes back to torch's caching
+# allocator once the last call that used it is no longer referenced).
+_WS_CACHE_CAP = 4
+_ws_cache: "collections.OrderedDict" = collections.OrderedDict()
 
 
 def _workspace(device, dtype, shapes, workspace):
     need = workspace_bytes(shapes, dtype)
     if workspace is not None:
+        _check_dev(workspace, "workspace", device)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
         if workspace.numel() * workspace.element_size() < need:
             raise ValueError(f"workspace too small: need {need} bytes")
         return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
     key = (str(device), _dt(dtype), tuple(shapes))
-    ws = _ws_cache.get(key)
+    ws = _ws_cache.pop(key, None)
     if ws is None:
         ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
-        _ws_cache[key] = ws
+    _ws_cache[key] = ws
+    while len(_ws_cache) > _WS_CACHE_CAP:
+        _ws_cache.popitem(last=False)
     base = ws.data_ptr()
     off = (-base) % 256
     return base + off, need, ws
@@ -252,6 +273,7 @@ def rmnp_colcut_partial_batched(grads, moms, rowsq=None, mu=0.95, stream=None):
     total = sum(v.shape[0] for v in moms)
     if rowsq is None:
         rowsq = torch.empty(total, dtype=torch.float32, device=device)
+    _check_dev(rowsq, "rowsq", device)
     if rowsq.dtype != torch.float32 or rowsq.numel() < total or not rowsq.is_contiguous():
         raise ValueError("rowsq must be a contiguous float32 tensor of sum(rows) entries")
     _check(lib().rmnp_colcut_partial_batched(arr, n, _dt(dtype), mu, rowsq.data_ptr(),
@@ -269,6 +291,7 @@ def rmnp_colcut_apply_batched(weights, moms, rowsq, full_cols=None, lr=0.02, eps
         return
     device = moms[0].device
     total = sum(v.shape[0] for v in moms)
+    _check_dev(rowsq, "rowsq", device)
     if rowsq.dtype != torch.float32 or rowsq.numel() < total or not rowsq.is_contiguous():
         raise ValueError("rowsq must be a contiguous float32 tensor of sum(rows) entries")
     fc = None if full_cols is None else (_i64 * n)(*full_cols)
@@ -343,3 +366,11 @@ def profile_read() -> dict:
     n = (_i64 * k)()
     _check(lib().matopt_profile_read(ms, n))
     return {name: (ms[i], n[i]) for i, name in enumerate(PROFILE_CLASSES)}
+
+
+def counters() -> dict:
+    """The library's cumulative plan-cache diagnostics (see matopt_counters)."""
+    k = len(COUNTERS)
+    out = (_i64 * k)()
+    _check(lib().matopt_counters(out, k))
+    return {name: int(out[i]) for i, name in enumerate(COUNTERS)}

@@ -143,6 +143,32 @@ struct AdamwParams {
 
 constexpr int kAdamwTask = 2048;
 
+// Per-call binding of the caller's pointers into the descriptors a launch
+// reads.  A plan (built once per list of shapes) holds descriptor templates;
+// every call launches bind_kernel, whose by-value arguments carry up to
+// kBindMax pointer sets, to write the descriptors of this call:
+//   BIND_NS      MatDesc; p = {w, g, v, o}; x[], a, b, xs, partials of the
+//                template are byte offsets from `base` (the workspace);
+//                x0in = v when x0_is_v, else x[0]
+//   BIND_ROWS    MatDesc; p = {w, g, v, -}; nothing relocated (RMNP)
+//   BIND_COLCUT  MatDesc; p = {w, g, v, -}; partials is a byte offset from
+//                `base` (the caller's row-sum vector)
+//   BIND_VEC     VecDesc; p = {p, g, m, v} (AdamW)
+enum BindMode : int32_t { BIND_NS = 0, BIND_ROWS = 1, BIND_COLCUT = 2, BIND_VEC = 3 };
+constexpr int kBindMax = 112;
+struct BindPtrs {
+  const void* p[4];
+};
+struct BindArgs {
+  void* dst;           // descriptor array (device)
+  const void* tmpl;    // template array (device, plan memory)
+  const char* base;    // relocation base (see BindMode)
+  int32_t first, n;    // descriptors first .. first+n-1 (n <= kBindMax)
+  int32_t mode, pad_;
+  BindPtrs ptr[kBindMax];
+};
+static_assert(sizeof(BindArgs) <= 3712, "bind arguments must stay well inside the kernarg limit");
+
 // Tile geometry.
 constexpr int kPrepTile = 64;
 constexpr int kTileBf16 = 256;
@@ -165,5 +191,7 @@ hipError_t launch_rmnp(int dt, int wpr, int nch, const RmnpParams& p, int n_task
 hipError_t launch_adamw(int dt, const AdamwParams& p, int n_tasks, hipStream_t s);
 // Column-cut RMNP: apply == false launches the partial half, true the update.
 hipError_t launch_colcut(int dt, bool apply, const ColcutParams& p, int n_tasks, hipStream_t s);
+// One bind launch (a.n <= kBindMax descriptors).
+hipError_t launch_bind(const BindArgs& a, hipStream_t s);
 
 }  // namespace matopt

@@ -1,16 +1,26 @@
 // Host side of libmatopt: the C ABI declared in include/matopt.h.
 //
 // Each entry point validates its arguments synchronously, looks up (or builds
-// once) a device-side plan for the exact list of shapes and pointers -- matrix
-// descriptors plus the tile tables of every launch -- and enqueues the whole
-// step on the caller's stream as a fixed sequence of grouped launches (every
-// launch covers every matrix of the batch):
+// once) a plan for its list of shapes -- descriptor templates plus the tile
+// and task tables of every launch, in one device buffer the library owns --
+// binds this call's pointers into the descriptors (bind_kernel: the pointers
+// travel as kernel arguments), and enqueues the whole step on the caller's
+// stream as a fixed sequence of grouped launches (every launch covers every
+// matrix of the batch):
 //
-//   muon_step_batched        prep (momentum, norm partials, X0) -> finalize ->
-//                            ns_steps x {Gram, polynomial, apply} (the last apply
-//                            folds the update into W) | scale_out if ns_steps==0
+//   muon_step_batched        bind -> prep (momentum, norm partials, X0) ->
+//                            finalize -> ns_steps x {Gram, polynomial, apply}
+//                            (the last apply folds the update into W) |
+//                            scale_out if ns_steps == 0
 //   ns_orthogonalize_batched same with no momentum; the last apply writes O
-//   rmnp_step_batched        one fused row kernel launch per width class
+//   rmnp_step_batched        bind -> one fused row kernel launch per width class
+//
+// A plan depends on the shapes only, so a caller whose tensors move between
+// calls (gradients reallocated every step) reuses it: after the first call
+// with a list of shapes nothing is allocated, copied from the host or
+// synchronised.  Descriptors of the Newton-Schulz calls live in the caller's
+// workspace; those of the calls without a workspace in a slot of the plan,
+// which is why the calls that use one plan are chained across streams.
 //
 // Tile tables are ordered longest-K first (largest work first, the greedy the
 // MatrixFSDP owner planner uses for roles, section 4.1, Algorithm 1), so that
@@ -99,7 +109,7 @@ Geo geometry(int64_t rows, int64_t cols, int dt) {
 
 struct Layout {
   std::vector<size_t> x0, x1, a, b;
-  size_t partials = 0, xs = 0, total = 0;
+  size_t partials = 0, xs = 0, desc = 0, total = 0;
   int n_prep = 0;
   std::vector<int> prep_off;
 };
@@ -125,6 +135,8 @@ Layout layout(const std::vector<Geo>& geo, int dt) {
   off += align256((size_t)L.n_prep * 4);
   L.xs = off;
   off += align256(geo.size() * 4);
+  L.desc = off;   // this call's descriptors (written by bind_kernel)
+  off += align256(geo.size() * sizeof(MatDesc));
   L.total = off;
   return L;
 }
@@ -193,9 +205,17 @@ hipError_t timed(int cls, hipStream_t s, F&& launch) {
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------- counters
+// Cumulative diagnostics (matopt_counters): plans built, device allocations
+// and frees, bind launches.
+enum { CNT_PLAN_BUILDS = 0, CNT_DEV_ALLOCS = 1, CNT_DEV_FREES = 2, CNT_BIND_LAUNCHES = 3 };
+std::atomic<int64_t> g_counters[MATOPT_COUNTERS];
+
+void bump(int k) { g_counters[k].fetch_add(1, std::memory_order_relaxed); }
+
 // ---------------------------------------------------------------- plans
 enum PlanKind {
-  PK_MUON = 1, PK_NS = 2, PK_RMNP = 3, PK_COLCUT_PARTIAL = 4, PK_COLCUT_APPLY = 5, PK_ADAMW = 6
+  PK_NS = 2, PK_RMNP = 3, PK_COLCUT_PARTIAL = 4, PK_COLCUT_APPLY = 5, PK_ADAMW = 6
 };
 
 struct RmnpGroup {
@@ -206,52 +226,67 @@ struct RmnpGroup {
 // A GEMM stage's launch table and its length (the grid size of that stage:
 // the three tables are packed separately and differ in length).
 struct TileTable {
-  const GemmTile* tiles = nullptr;
+  size_t off = 0;   // byte offset in the plan buffer
   int n = 0;
 };
 
+// Everything a call's launches need that depends on the list of shapes only:
+// descriptor templates (pointer fields empty, or byte offsets from the
+// workspace / row-sum vector where BindMode says so) and the tile and task
+// tables, in one device buffer, uploaded once.  No caller pointer is kept.
 struct Plan {
   int device = -1;
+  bool pooled = false;               // dbuf from the stream-ordered allocator
   void* dbuf = nullptr;
-  MatDesc* d_mats = nullptr;
-  PrepTile* d_prep = nullptr;
-  VecDesc* d_vecs = nullptr;   // AdamW plans
+  std::vector<uint8_t> host;         // the uploaded bytes, kept until the plan is freed
+  size_t o_tmpl = 0;                 // templates (MatDesc, or VecDesc for AdamW)
+  size_t o_slot = 0;                 // descriptors of calls without a workspace
+  size_t ws_desc = 0;                // Newton-Schulz plans: descriptor offset in the workspace
+  size_t o_prep = 0;
+  int n_prep = 0;
   TileTable gram, poly, apply;
-  int count = 0, n_prep = 0;
+  int count = 0;
   std::vector<RmnpGroup> rmnp;
-  // Evicted plans are freed on their own device after it has drained (a queued
-  // launch may still read the tables).  Plans alive at process exit are never
-  // destroyed: the cache is a leaked singleton, so no HIP call runs during
-  // static destruction.
-  ~Plan() {
-    if (!dbuf) return;
-    int cur = -1;
-    (void)hipGetDevice(&cur);
-    if (device >= 0 && device != cur) (void)hipSetDevice(device);
-    (void)hipDeviceSynchronize();
-    (void)hipFree(dbuf);
-    if (device >= 0 && device != cur) (void)hipSetDevice(cur);
-  }
+  // Calls that use this plan are enqueued one at a time and chained across
+  // streams (a call on another stream than the previous one first waits, on
+  // the device, for ev_last), so the descriptor slot is never rewritten under
+  // a launch that still reads it and ev_last covers every use so far.
+  std::mutex mu;
+  hipEvent_t ev_last = nullptr;
+  hipStream_t last_stream = nullptr;
+
+  template <class T>
+  T* dev(size_t off) const { return (T*)((uint8_t*)dbuf + off); }
 };
 
 using PlanKey = std::vector<uint64_t>;
 constexpr size_t kPlanCap = 64;
 std::mutex g_plan_mu;
 using PlanList = std::list<std::pair<PlanKey, std::shared_ptr<Plan>>>;
-PlanList& g_plans = *new PlanList();  // front = most recent; never destroyed
+// Leaked singletons: no HIP call runs during static destruction.
+PlanList& g_plans = *new PlanList();   // front = most recently used
+std::vector<std::shared_ptr<Plan>>& g_retired = *new std::vector<std::shared_ptr<Plan>>();
 
-std::shared_ptr<Plan> plan_lookup(const PlanKey& key) {
-  for (auto it = g_plans.begin(); it != g_plans.end(); ++it)
-    if (it->first == key) {
-      g_plans.splice(g_plans.begin(), g_plans, it);
-      return g_plans.front().second;
+// Frees evicted plans whose last use has completed on the device (polled,
+// never waited for) and that no call still holds, stream-ordered on the
+// caller's stream of the same device.
+void sweep_retired(int dev, hipStream_t s) {
+  for (size_t i = 0; i < g_retired.size();) {
+    Plan& p = *g_retired[i];
+    const bool idle = g_retired[i].use_count() == 1 &&
+                      (!p.ev_last || hipEventQuery(p.ev_last) == hipSuccess);
+    if (!idle || p.device != dev) {
+      ++i;
+      continue;
     }
-  return nullptr;
-}
-
-void plan_insert(const PlanKey& key, std::shared_ptr<Plan> p) {
-  g_plans.emplace_front(key, std::move(p));
-  while (g_plans.size() > kPlanCap) g_plans.pop_back();
+    if (p.dbuf) {
+      if (p.pooled) (void)hipFreeAsync(p.dbuf, s);
+      else (void)hipFree(p.dbuf);
+      bump(CNT_DEV_FREES);
+    }
+    if (p.ev_last) (void)hipEventDestroy(p.ev_last);
+    g_retired.erase(g_retired.begin() + (long)i);
+  }
 }
 
 struct HostBuf {
@@ -263,27 +298,124 @@ struct HostBuf {
     if (!v.empty()) std::memcpy(bytes.data() + off, v.data(), v.size() * sizeof(T));
     return off;
   }
+  size_t reserve(size_t n) {
+    size_t off = align256(bytes.size());
+    bytes.resize(off + align256(n + 1));
+    return off;
+  }
 };
 
-matopt_status upload(Plan& p, HostBuf& hb, hipStream_t s) {
-  hipError_t e = hipMalloc(&p.dbuf, hb.bytes.size());
-  if (e != hipSuccess) return fail(MATOPT_ERR_HIP, std::string("plan hipMalloc: ") + hipGetErrorString(e));
-  e = hipMemcpyAsync(p.dbuf, hb.bytes.data(), hb.bytes.size(), hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return fail(MATOPT_ERR_HIP, std::string("plan upload: ") + hipGetErrorString(e));
+matopt_status hip_fail(const char* what, hipError_t e) {
+  return fail(MATOPT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// One device buffer per plan from the stream-ordered allocator (the plain
+// allocator if the device has no memory pools), filled from the plan's own
+// host copy on `s`; ev_last marks the upload for calls on other streams.
+matopt_status upload(Plan& p, hipStream_t s) {
+  hipError_t e = hipEventCreateWithFlags(&p.ev_last, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_fail("plan event", e);
+  e = hipMallocAsync(&p.dbuf, p.host.size(), s);
+  p.pooled = e == hipSuccess;
+  if (e == hipErrorNotSupported) {
+    (void)hipGetLastError();
+    e = hipMalloc(&p.dbuf, p.host.size());
+  }
+  if (e != hipSuccess) {
+    p.dbuf = nullptr;
+    return hip_fail("plan allocation", e);
+  }
+  bump(CNT_DEV_ALLOCS);
+  e = hipMemcpyAsync(p.dbuf, p.host.data(), p.host.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipEventRecord(p.ev_last, s);
+  if (e != hipSuccess) return hip_fail("plan upload", e);
+  p.last_stream = s;
   return MATOPT_OK;
 }
 
-template <typename T>
-T* at(void* base, size_t off) {
-  return (T*)((uint8_t*)base + off);
+// The plan for `key`, built and uploaded on `s` if it is not cached.  Plans
+// evicted beyond kPlanCap are retired and freed once idle (sweep_retired).
+template <class Build>
+matopt_status get_plan(const PlanKey& key, int dev, hipStream_t s, Build&& build,
+                       std::shared_ptr<Plan>& out) {
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  sweep_retired(dev, s);
+  for (auto it = g_plans.begin(); it != g_plans.end(); ++it)
+    if (it->first == key) {
+      g_plans.splice(g_plans.begin(), g_plans, it);
+      out = g_plans.front().second;
+      return MATOPT_OK;
+    }
+  auto p = std::make_shared<Plan>();
+  p->device = dev;
+  matopt_status st = build(*p);
+  if (st != MATOPT_OK) return st;
+  st = upload(*p, s);
+  if (st != MATOPT_OK) {
+    g_retired.push_back(p);   // whatever was allocated is freed once idle
+    return st;
+  }
+  bump(CNT_PLAN_BUILDS);
+  g_plans.emplace_front(key, p);
+  while (g_plans.size() > kPlanCap) {
+    g_retired.push_back(g_plans.back().second);
+    g_plans.pop_back();
+  }
+  out = p;
+  return MATOPT_OK;
 }
 
-// Builds the descriptors and tile tables of a Newton-Schulz plan (muon / ns).
-matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& geo,
-                            const std::vector<const void*>& wv, const std::vector<const void*>& gv,
-                            const std::vector<const void*>& vv, const std::vector<const void*>& ov,
-                            void* ws, hipStream_t s) {
+// Holds a plan for one call's enqueue (see Plan::mu).
+class PlanUse {
+ public:
+  PlanUse(Plan& p, hipStream_t s) : p_(p), s_(s) {
+    p_.mu.lock();
+    if (p_.last_stream != s_) err_ = hipStreamWaitEvent(s_, p_.ev_last, 0);
+  }
+  ~PlanUse() {
+    (void)hipEventRecord(p_.ev_last, s_);
+    p_.last_stream = s_;
+    p_.mu.unlock();
+  }
+  hipError_t error() const { return err_; }
+
+ private:
+  Plan& p_;
+  hipStream_t s_;
+  hipError_t err_ = hipSuccess;
+};
+
+// Writes descriptors [0, ptrs.size()) of `dst` from the templates and this
+// call's pointers, kBindMax per launch.
+matopt_status bind_descs(const void* tmpl, void* dst, const char* base, int mode,
+                   const std::vector<BindPtrs>& ptrs, hipStream_t s) {
+  BindArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.dst = dst;
+  a.tmpl = tmpl;
+  a.base = base;
+  a.mode = mode;
+  const int n = (int)ptrs.size();
+  for (int first = 0; first < n; first += kBindMax) {
+    a.first = first;
+    a.n = std::min(kBindMax, n - first);
+    for (int i = 0; i < a.n; ++i) a.ptr[i] = ptrs[first + i];
+    hipError_t e = timed(10, s, [&] { return launch_bind(a, s); });
+    if (e != hipSuccess) return hip_fail("bind launch", e);
+    bump(CNT_BIND_LAUNCHES);
+  }
+  return MATOPT_OK;
+}
+
+template <class P>
+P as_off(size_t off) {
+  return (P)(uintptr_t)off;
+}
+
+// Templates and tile tables of a Newton-Schulz plan (muon step and NS only).
+// The workspace-resident fields of the templates are byte offsets from the
+// workspace (BIND_NS).
+matopt_status build_ns_plan(Plan& P, int dt, const std::vector<Geo>& geo) {
   const int count = (int)geo.size();
   const Layout L = layout(geo, dt);
   const int tile = gemm_tile(dt);
@@ -295,10 +427,6 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
     const Geo& g = geo[i];
     MatDesc& d = mats[i];
     std::memset(&d, 0, sizeof(d));
-    d.w = (void*)wv[i];
-    d.g = gv[i];
-    d.v = (void*)vv[i];
-    d.o = (void*)ov[i];
     d.rows = g.rows;
     d.cols = g.cols;
     d.m = g.m;
@@ -309,16 +437,15 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
     d.vec_ok = (g.cols % (16 / esize(dt))) == 0 ? 1 : 0;
     d.upd_scale = (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
     d.prep_tiles_c = g.prep_tc;
-    d.x[0] = at<void>(ws, L.x0[i]);
-    d.x[1] = at<void>(ws, L.x1[i]);
+    d.x[0] = as_off<void*>(L.x0[i]);
+    d.x[1] = as_off<void*>(L.x1[i]);
     // X0 is the stored V; when V has X0's layout the first iteration reads it
-    // in place and the prep kernel skips the copy
+    // in place and the prep kernel skips the copy (bind sets x0in)
     d.x0_is_v = (dt == DT_BF16 && !g.transposed && g.rows == g.mp && g.cols == g.np) ? 1 : 0;
-    d.x0in = d.x0_is_v ? vv[i] : d.x[0];
-    d.a = at<void>(ws, L.a[i]);
-    d.b = at<void>(ws, L.b[i]);
-    d.xs = at<float>(ws, L.xs) + i;
-    d.partials = at<float>(ws, L.partials) + L.prep_off[i];
+    d.a = as_off<void*>(L.a[i]);
+    d.b = as_off<void*>(L.b[i]);
+    d.xs = as_off<float*>(L.xs + 4 * (size_t)i);
+    d.partials = as_off<float*>(L.partials + 4 * (size_t)L.prep_off[i]);
     d.n_prep = g.prep_tr * g.prep_tc;
     int idx = 0;
     for (int tr = 0; tr < g.prep_tr; ++tr)
@@ -337,36 +464,32 @@ matopt_status build_ns_plan(Plan& P, int kind, int dt, const std::vector<Geo>& g
   const std::vector<TileRef> k3 = xcd_schedule(u3), k4 = xcd_schedule(u4), k5 = xcd_schedule(u5);
 
   HostBuf hb;
-  const size_t o_mats = hb.put(mats);
+  P.o_tmpl = hb.put(mats);
   const size_t o_prep = hb.put(prep);
   const size_t o_k3 = hb.put(k3);
   const size_t o_k4 = hb.put(k4);
   const size_t o_k5 = hb.put(k5);
-  matopt_status st = upload(P, hb, s);
-  if (st != MATOPT_OK) return st;
-  P.d_mats = at<MatDesc>(P.dbuf, o_mats);
-  P.d_prep = at<PrepTile>(P.dbuf, o_prep);
-  P.gram = TileTable{at<GemmTile>(P.dbuf, o_k3), (int)k3.size()};
-  P.poly = TileTable{at<GemmTile>(P.dbuf, o_k4), (int)k4.size()};
-  P.apply = TileTable{at<GemmTile>(P.dbuf, o_k5), (int)k5.size()};
+  P.host = std::move(hb.bytes);
   P.count = count;
   P.n_prep = (int)prep.size();
-  (void)kind;
+  P.ws_desc = L.desc;
+  P.o_prep = o_prep;
+  P.gram = TileTable{o_k3, (int)k3.size()};
+  P.poly = TileTable{o_k4, (int)k4.size()};
+  P.apply = TileTable{o_k5, (int)k5.size()};
   return MATOPT_OK;
 }
 
-matopt_status build_rmnp_plan(Plan& P, int dt, const matopt_mat* mats, int count, hipStream_t s) {
+matopt_status build_rmnp_plan(Plan& P, int dt, const std::vector<std::pair<int64_t, int64_t>>& shp) {
+  const int count = (int)shp.size();
   const int E = 16 / esize(dt);
   std::vector<MatDesc> descs(count);
   std::map<std::pair<int, int>, std::vector<RmnpTask>> groups;
   for (int i = 0; i < count; ++i) {
     MatDesc& d = descs[i];
     std::memset(&d, 0, sizeof(d));
-    d.w = mats[i].w;
-    d.g = mats[i].g;
-    d.v = mats[i].v;
-    d.rows = mats[i].rows;
-    d.cols = mats[i].cols;
+    d.rows = shp[i].first;
+    d.cols = shp[i].second;
     d.upd_scale = (float)std::sqrt(std::max(1.0, (double)d.rows / (double)d.cols));
     const bool vec = d.cols % E == 0;
     const int64_t nchunks = d.cols / E;
@@ -387,7 +510,8 @@ matopt_status build_rmnp_plan(Plan& P, int dt, const matopt_mat* mats, int count
     for (int64_t r = 0; r < d.rows; r += step) tasks.push_back({i, (int32_t)r});
   }
   HostBuf hb;
-  const size_t o_mats = hb.put(descs);
+  P.o_tmpl = hb.put(descs);
+  P.o_slot = hb.reserve(descs.size() * sizeof(MatDesc));
   for (auto& kv : groups) {
     RmnpGroup g;
     g.wpr = kv.first.first;
@@ -396,37 +520,33 @@ matopt_status build_rmnp_plan(Plan& P, int dt, const matopt_mat* mats, int count
     g.off = hb.put(kv.second);
     P.rmnp.push_back(g);
   }
-  matopt_status st = upload(P, hb, s);
-  if (st != MATOPT_OK) return st;
-  P.d_mats = at<MatDesc>(P.dbuf, o_mats);
+  P.host = std::move(hb.bytes);
   P.count = count;
   return MATOPT_OK;
 }
 
-matopt_status hip_fail(const char* what, hipError_t e) {
-  return fail(MATOPT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
-}
-
-// Enqueue the Newton-Schulz pipeline of a plan.
-matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, double wdl,
-                     int ns_steps, float a, float b, float c, float eps, int out_kind,
-                     int out_dt, hipStream_t s) {
+// Enqueue the Newton-Schulz pipeline of a plan on descriptors `mats` (this
+// call's, already bound).
+matopt_status run_ns(const Plan& P, const MatDesc* mats, int dt, bool momentum, float mu,
+                     float lr, double wdl, int ns_steps, float a, float b, float c, float eps,
+                     int out_kind, int out_dt, hipStream_t s) {
   hipError_t e;
-  PrepParams pp{P.d_mats, P.d_prep, mu, momentum ? 1 : 0};
+  const PrepTile* prep = P.dev<const PrepTile>(P.o_prep);
+  PrepParams pp{mats, prep, mu, momentum ? 1 : 0};
   e = timed(0, s, [&] { return launch_prep(dt, pp, P.n_prep, s); });
   if (e != hipSuccess) return hip_fail("prep launch", e);
-  FinalizeParams fp{P.d_mats, eps};
+  FinalizeParams fp{mats, eps};
   e = timed(1, s, [&] { return launch_finalize(fp, P.count, s); });
   if (e != hipSuccess) return hip_fail("finalize launch", e);
   // every stage launches exactly its own table
   auto gemm = [&](GemmParams g, const TileTable& t) {
-    g.tiles = t.tiles;
+    g.tiles = P.dev<const GemmTile>(t.off);
     return dt == DT_BF16 ? launch_gemm_bf16(g, t.n, s) : launch_gemm_f32(g, t.n, s);
   };
   for (int it = 0; it < ns_steps; ++it) {
     GemmParams g;
     std::memset(&g, 0, sizeof(g));
-    g.mats = P.d_mats;
+    g.mats = mats;
     g.cur = it & 1;
     g.first = it == 0 ? 1 : 0;
     g.out_dt = out_dt;
@@ -448,11 +568,36 @@ matopt_status run_ns(const Plan& P, int dt, bool momentum, float mu, float lr, d
     if (e != hipSuccess) return hip_fail("apply launch", e);
   }
   if (ns_steps == 0) {
-    ScaleOutParams sp{P.d_mats, P.d_prep, out_kind, out_dt, lr, wdl};
+    ScaleOutParams sp{mats, prep, out_kind, out_dt, lr, wdl};
     e = timed(5, s, [&] { return launch_scale_out(dt, sp, P.n_prep, s); });
     if (e != hipSuccess) return hip_fail("scale_out launch", e);
   }
   return MATOPT_OK;
+}
+
+// Plan lookup, binding and the Newton-Schulz pipeline of one muon / NS call
+// (arguments already validated).
+matopt_status ns_call(int dt, const std::vector<Geo>& geo, const std::vector<BindPtrs>& ptrs,
+                      void* workspace, int dev, hipStream_t s, bool momentum, float mu, float lr,
+                      double wdl, int ns_steps, float a, float b, float c, float eps,
+                      int out_kind, int out_dt) {
+  PlanKey key{PK_NS, (uint64_t)dt, (uint64_t)dev, (uint64_t)geo.size()};
+  for (const Geo& g : geo) {
+    key.push_back((uint64_t)g.rows);
+    key.push_back((uint64_t)g.cols);
+  }
+  std::shared_ptr<Plan> plan;
+  matopt_status st =
+      get_plan(key, dev, s, [&](Plan& p) { return build_ns_plan(p, dt, geo); }, plan);
+  if (st != MATOPT_OK) return st;
+  PlanUse use(*plan, s);
+  if (use.error() != hipSuccess) return hip_fail("plan stream wait", use.error());
+  MatDesc* mats = (MatDesc*)((uint8_t*)workspace + plan->ws_desc);
+  if ((st = bind_descs(plan->dev<MatDesc>(plan->o_tmpl), mats, (const char*)workspace, BIND_NS, ptrs,
+                 s)) != MATOPT_OK)
+    return st;
+  return run_ns(*plan, mats, dt, momentum, mu, lr, wdl, ns_steps, a, b, c, eps, out_kind, out_dt,
+                s);
 }
 
 matopt_status check_common(int32_t count, int dt) {
@@ -468,12 +613,12 @@ matopt_status check_ns_params(int32_t ns_steps, float a, float b, float c, float
   return MATOPT_OK;
 }
 
-// Column-cut RMNP plan: descriptors whose `partials` point into the caller's
-// row-sum vector (matrix i starts at the sum of the rows before it) and one
+// Column-cut RMNP plan: templates whose `partials` are byte offsets into the
+// caller's row-sum vector (matrix i starts after the rows before it) and one
 // task per 4 rows.  full_cols (NULL: the slice's own width) sets the update
 // scale from the whole matrix's shape.
 matopt_status build_colcut_plan(Plan& P, int dt, const matopt_mat* mats, int count,
-                                const float* rowsq, const int64_t* full_cols, hipStream_t s) {
+                                const int64_t* full_cols) {
   const int E = 16 / esize(dt);
   std::vector<MatDesc> descs(count);
   std::vector<RmnpTask> tasks;
@@ -481,34 +626,30 @@ matopt_status build_colcut_plan(Plan& P, int dt, const matopt_mat* mats, int cou
   for (int i = 0; i < count; ++i) {
     MatDesc& d = descs[i];
     std::memset(&d, 0, sizeof(d));
-    d.w = mats[i].w;
-    d.g = mats[i].g;
-    d.v = mats[i].v;
     d.rows = mats[i].rows;
     d.cols = mats[i].cols;
     const int64_t fc = full_cols ? full_cols[i] : d.cols;
     d.upd_scale = (float)std::sqrt(std::max(1.0, (double)d.rows / (double)fc));
     d.vec_ok = d.cols % E == 0 ? 1 : 0;
-    d.partials = const_cast<float*>(rowsq) + off;
+    d.partials = as_off<float*>((size_t)off * 4);
     off += d.rows;
     for (int64_t r = 0; r < d.rows; r += 4) tasks.push_back({i, (int32_t)r});
   }
   HostBuf hb;
-  const size_t o_mats = hb.put(descs);
+  P.o_tmpl = hb.put(descs);
+  P.o_slot = hb.reserve(descs.size() * sizeof(MatDesc));
   RmnpGroup g;
   g.wpr = 1;
   g.nch = 0;
   g.n = (int)tasks.size();
   g.off = hb.put(tasks);
   P.rmnp.push_back(g);
-  matopt_status st = upload(P, hb, s);
-  if (st != MATOPT_OK) return st;
-  P.d_mats = at<MatDesc>(P.dbuf, o_mats);
+  P.host = std::move(hb.bytes);
   P.count = count;
   return MATOPT_OK;
 }
 
-// Shared by both column-cut halves: validation, plan lookup, one launch.
+// Shared by both column-cut halves: validation, plan lookup, bind, one launch.
 matopt_status colcut_run(bool apply, const matopt_mat* mats, int32_t count, matopt_dtype dt,
                          float mu, float lr, float eps, const float* rowsq,
                          const int64_t* full_cols, void* stream) {
@@ -523,6 +664,7 @@ matopt_status colcut_run(bool apply, const matopt_mat* mats, int32_t count, mato
   std::vector<Span> spans;
   const size_t es = esize(dt);
   int64_t total_rows = 0;
+  std::vector<BindPtrs> ptrs(count);
   for (int i = 0; i < count; ++i) {
     const matopt_mat& m = mats[i];
     const std::string tag = "matrix " + std::to_string(i);
@@ -536,6 +678,7 @@ matopt_status colcut_run(bool apply, const matopt_mat* mats, int32_t count, mato
     spans.push_back({(uintptr_t)a, (uintptr_t)a + bytes, tag + (apply ? " W" : " G")});
     spans.push_back({(uintptr_t)m.v, (uintptr_t)m.v + bytes, tag + " V"});
     total_rows += m.rows;
+    ptrs[i] = BindPtrs{{apply ? m.w : nullptr, apply ? nullptr : m.g, m.v, nullptr}};
   }
   spans.push_back({(uintptr_t)rowsq, (uintptr_t)rowsq + (size_t)total_rows * 4, "rowsq"});
   if ((st = check_overlap(spans)) != MATOPT_OK) return st;
@@ -543,55 +686,62 @@ matopt_status colcut_run(bool apply, const matopt_mat* mats, int32_t count, mato
   if ((st = check_device(&dev)) != MATOPT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   PlanKey key{(uint64_t)(apply ? PK_COLCUT_APPLY : PK_COLCUT_PARTIAL), (uint64_t)dt, (uint64_t)dev,
-              (uint64_t)count, (uint64_t)(uintptr_t)rowsq};
+              (uint64_t)count};
   for (int i = 0; i < count; ++i) {
     key.push_back((uint64_t)mats[i].rows);
     key.push_back((uint64_t)mats[i].cols);
-    key.push_back((uint64_t)(uintptr_t)(apply ? mats[i].w : mats[i].g));
-    key.push_back((uint64_t)(uintptr_t)mats[i].v);
     key.push_back((uint64_t)(apply && full_cols ? full_cols[i] : mats[i].cols));
   }
   std::shared_ptr<Plan> plan;
-  {
-    std::lock_guard<std::mutex> lk(g_plan_mu);
-    plan = plan_lookup(key);
-    if (!plan) {
-      plan = std::make_shared<Plan>();
-      plan->device = dev;
-      if ((st = build_colcut_plan(*plan, dt, mats, count, rowsq, apply ? full_cols : nullptr, s)) !=
-          MATOPT_OK)
-        return st;
-      plan_insert(key, plan);
-    }
-  }
+  st = get_plan(key, dev, s, [&](Plan& p) {
+    return build_colcut_plan(p, dt, mats, count, apply ? full_cols : nullptr);
+  }, plan);
+  if (st != MATOPT_OK) return st;
+  PlanUse use(*plan, s);
+  if (use.error() != hipSuccess) return hip_fail("plan stream wait", use.error());
+  MatDesc* slot = plan->dev<MatDesc>(plan->o_slot);
+  if ((st = bind_descs(plan->dev<MatDesc>(plan->o_tmpl), slot, (const char*)rowsq, BIND_COLCUT, ptrs,
+                 s)) != MATOPT_OK)
+    return st;
   const RmnpGroup& g = plan->rmnp[0];
-  ColcutParams cp{plan->d_mats, at<RmnpTask>(plan->dbuf, g.off), mu, lr, eps};
+  ColcutParams cp{slot, plan->dev<RmnpTask>(g.off), mu, lr, eps};
   hipError_t e = timed(apply ? 8 : 7, s, [&] { return launch_colcut(dt, apply, cp, g.n, s); });
   if (e != hipSuccess) return hip_fail(apply ? "colcut apply launch" : "colcut partial launch", e);
   return MATOPT_OK;
 }
 
-// AdamW plan: one descriptor per tensor and one task per kAdamwTask elements.
-matopt_status build_adamw_plan(Plan& P, const matopt_vec* vecs, int count, hipStream_t s) {
+// AdamW plan: one template per tensor and one task per kAdamwTask elements.
+matopt_status build_adamw_plan(Plan& P, const matopt_vec* vecs, int count) {
   std::vector<VecDesc> descs(count);
   std::vector<VecTask> tasks;
   for (int i = 0; i < count; ++i) {
-    descs[i] = VecDesc{vecs[i].p, vecs[i].g, vecs[i].m, vecs[i].v, vecs[i].n};
+    descs[i] = VecDesc{nullptr, nullptr, nullptr, nullptr, vecs[i].n};
     for (int64_t e = 0; e < vecs[i].n; e += kAdamwTask) tasks.push_back({i, 0, e});
   }
   HostBuf hb;
-  const size_t o_vecs = hb.put(descs);
+  P.o_tmpl = hb.put(descs);
+  P.o_slot = hb.reserve(descs.size() * sizeof(VecDesc));
   RmnpGroup g;
   g.wpr = 0;
   g.nch = 0;
   g.n = (int)tasks.size();
   g.off = hb.put(tasks);
   P.rmnp.push_back(g);
-  matopt_status st = upload(P, hb, s);
-  if (st != MATOPT_OK) return st;
-  P.d_vecs = at<VecDesc>(P.dbuf, o_vecs);
+  P.host = std::move(hb.bytes);
   P.count = count;
   return MATOPT_OK;
+}
+
+// Validation of a muon / NS workspace against the layout of `geo`.
+matopt_status check_workspace(const std::vector<Geo>& geo, int dt, void* workspace,
+                              size_t workspace_bytes, std::vector<Span>& spans) {
+  const size_t need = layout(geo, dt).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MATOPT_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                          std::to_string(workspace ? workspace_bytes : 0));
+  if (((uintptr_t)workspace & 255) != 0) return fail(MATOPT_ERR_ALIGN, "workspace not 256-byte aligned");
+  spans.push_back({(uintptr_t)workspace, (uintptr_t)workspace + need, "workspace"});
+  return check_overlap(spans);
 }
 
 }  // namespace
@@ -599,7 +749,7 @@ matopt_status build_adamw_plan(Plan& P, const matopt_vec* vecs, int count, hipSt
 // ==================================================================== C ABI
 extern "C" {
 
-int32_t matopt_version(void) { return 10000; }
+int32_t matopt_version(void) { return 10100; }
 
 const char* matopt_status_string(matopt_status s) {
   switch (s) {
@@ -648,7 +798,7 @@ static matopt_status muon_impl(const matopt_mat* mats, int32_t count, matopt_dty
   if ((st = check_ns_params(ns_steps, a, b, c, eps)) != MATOPT_OK) return st;
   std::vector<Geo> geo;
   std::vector<Span> spans;
-  std::vector<const void*> wv, gv, vv, ov;
+  std::vector<BindPtrs> ptrs(count);
   const size_t es = esize(dt);
   for (int i = 0; i < count; ++i) {
     const matopt_mat& m = mats[i];
@@ -662,43 +812,14 @@ static matopt_status muon_impl(const matopt_mat* mats, int32_t count, matopt_dty
     spans.push_back({(uintptr_t)m.g, (uintptr_t)m.g + bytes, tag + " G"});
     spans.push_back({(uintptr_t)m.v, (uintptr_t)m.v + bytes, tag + " V"});
     geo.push_back(geometry(m.rows, m.cols, dt));
-    wv.push_back(m.w);
-    gv.push_back(m.g);
-    vv.push_back(m.v);
-    ov.push_back(nullptr);
+    ptrs[i] = BindPtrs{{m.w, m.g, m.v, nullptr}};
   }
-  const size_t need = layout(geo, dt).total;
-  if (!workspace || workspace_bytes < need)
-    return fail(MATOPT_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
-                                          std::to_string(workspace ? workspace_bytes : 0));
-  if (((uintptr_t)workspace & 255) != 0) return fail(MATOPT_ERR_ALIGN, "workspace not 256-byte aligned");
-  spans.push_back({(uintptr_t)workspace, (uintptr_t)workspace + need, "workspace"});
-  if ((st = check_overlap(spans)) != MATOPT_OK) return st;
+  if ((st = check_workspace(geo, dt, workspace, workspace_bytes, spans)) != MATOPT_OK) return st;
   int dev;
   if ((st = check_device(&dev)) != MATOPT_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-
-  PlanKey key{PK_MUON, (uint64_t)dt, (uint64_t)dev, (uint64_t)(uintptr_t)workspace, (uint64_t)count};
-  for (int i = 0; i < count; ++i) {
-    key.push_back((uint64_t)mats[i].rows);
-    key.push_back((uint64_t)mats[i].cols);
-    key.push_back((uint64_t)(uintptr_t)mats[i].w);
-    key.push_back((uint64_t)(uintptr_t)mats[i].g);
-    key.push_back((uint64_t)(uintptr_t)mats[i].v);
-  }
-  std::shared_ptr<Plan> plan;
-  {
-    std::lock_guard<std::mutex> lk(g_plan_mu);
-    plan = plan_lookup(key);
-    if (!plan) {
-      plan = std::make_shared<Plan>();
-      plan->device = dev;
-      if ((st = build_ns_plan(*plan, PK_MUON, dt, geo, wv, gv, vv, ov, workspace, s)) != MATOPT_OK) return st;
-      plan_insert(key, plan);
-    }
-  }
   const double wdl = (double)lr * (double)wd;   // exact: a product of two floats
-  return run_ns(*plan, dt, true, mu, lr, wdl, ns_steps, a, b, c, eps, OUT_W_UPDATE, dt, s);
+  return ns_call(dt, geo, ptrs, workspace, dev, (hipStream_t)stream, true, mu, lr, wdl, ns_steps,
+                 a, b, c, eps, OUT_W_UPDATE, dt);
 }
 
 extern "C" {
@@ -732,7 +853,7 @@ matopt_status ns_orthogonalize_batched(const void* const* x, void* const* o, con
   if ((st = check_ns_params(ns_steps, a, b, c, eps)) != MATOPT_OK) return st;
   std::vector<Geo> geo;
   std::vector<Span> spans;
-  std::vector<const void*> wv, gv, vv, ov;
+  std::vector<BindPtrs> ptrs(count);
   const size_t es_in = esize(in_dt), es_out = esize(out_dt);
   for (int i = 0; i < count; ++i) {
     if (!x[i] || !o[i]) return fail(MATOPT_ERR_NULL, "matrix " + std::to_string(i) + ": NULL pointer");
@@ -744,41 +865,13 @@ matopt_status ns_orthogonalize_batched(const void* const* x, void* const* o, con
     spans.push_back({(uintptr_t)x[i], (uintptr_t)x[i] + n * es_in, tag + " x"});
     spans.push_back({(uintptr_t)o[i], (uintptr_t)o[i] + n * es_out, tag + " o"});
     geo.push_back(geometry(rows[i], cols[i], in_dt));
-    wv.push_back(nullptr);
-    gv.push_back(nullptr);
-    vv.push_back(x[i]);
-    ov.push_back(o[i]);
+    ptrs[i] = BindPtrs{{nullptr, nullptr, x[i], o[i]}};
   }
-  const size_t need = layout(geo, in_dt).total;
-  if (!workspace || workspace_bytes < need)
-    return fail(MATOPT_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
-                                          std::to_string(workspace ? workspace_bytes : 0));
-  if (((uintptr_t)workspace & 255) != 0) return fail(MATOPT_ERR_ALIGN, "workspace not 256-byte aligned");
-  spans.push_back({(uintptr_t)workspace, (uintptr_t)workspace + need, "workspace"});
-  if ((st = check_overlap(spans)) != MATOPT_OK) return st;
+  if ((st = check_workspace(geo, in_dt, workspace, workspace_bytes, spans)) != MATOPT_OK) return st;
   int dev;
   if ((st = check_device(&dev)) != MATOPT_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-
-  PlanKey key{PK_NS, (uint64_t)in_dt, (uint64_t)dev, (uint64_t)(uintptr_t)workspace, (uint64_t)count};
-  for (int i = 0; i < count; ++i) {
-    key.push_back((uint64_t)rows[i]);
-    key.push_back((uint64_t)cols[i]);
-    key.push_back((uint64_t)(uintptr_t)x[i]);
-    key.push_back((uint64_t)(uintptr_t)o[i]);
-  }
-  std::shared_ptr<Plan> plan;
-  {
-    std::lock_guard<std::mutex> lk(g_plan_mu);
-    plan = plan_lookup(key);
-    if (!plan) {
-      plan = std::make_shared<Plan>();
-      plan->device = dev;
-      if ((st = build_ns_plan(*plan, PK_NS, in_dt, geo, wv, gv, vv, ov, workspace, s)) != MATOPT_OK) return st;
-      plan_insert(key, plan);
-    }
-  }
-  return run_ns(*plan, in_dt, false, 0.f, 0.f, 0.0, ns_steps, a, b, c, eps, OUT_O, out_dt, s);
+  return ns_call(in_dt, geo, ptrs, workspace, dev, (hipStream_t)stream, false, 0.f, 0.f, 0.0,
+                 ns_steps, a, b, c, eps, OUT_O, out_dt);
 }
 
 matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dtype dt, float mu,
@@ -790,6 +883,8 @@ matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
   if (!finite(mu) || !finite(lr) || !finite(eps) || eps < 0.f)
     return fail(MATOPT_ERR_PARAM, "non-finite mu/lr/eps or eps < 0");
   std::vector<Span> spans;
+  std::vector<BindPtrs> ptrs(count);
+  std::vector<std::pair<int64_t, int64_t>> shp(count);
   const size_t es = esize(dt);
   for (int i = 0; i < count; ++i) {
     const matopt_mat& m = mats[i];
@@ -802,6 +897,8 @@ matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
     spans.push_back({(uintptr_t)m.w, (uintptr_t)m.w + bytes, tag + " W"});
     spans.push_back({(uintptr_t)m.g, (uintptr_t)m.g + bytes, tag + " G"});
     spans.push_back({(uintptr_t)m.v, (uintptr_t)m.v + bytes, tag + " V"});
+    ptrs[i] = BindPtrs{{m.w, m.g, m.v, nullptr}};
+    shp[i] = {m.rows, m.cols};
   }
   if ((st = check_overlap(spans)) != MATOPT_OK) return st;
   int dev;
@@ -811,24 +908,18 @@ matopt_status rmnp_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
   for (int i = 0; i < count; ++i) {
     key.push_back((uint64_t)mats[i].rows);
     key.push_back((uint64_t)mats[i].cols);
-    key.push_back((uint64_t)(uintptr_t)mats[i].w);
-    key.push_back((uint64_t)(uintptr_t)mats[i].g);
-    key.push_back((uint64_t)(uintptr_t)mats[i].v);
   }
   std::shared_ptr<Plan> plan;
-  {
-    std::lock_guard<std::mutex> lk(g_plan_mu);
-    plan = plan_lookup(key);
-    if (!plan) {
-      plan = std::make_shared<Plan>();
-      plan->device = dev;
-      if ((st = build_rmnp_plan(*plan, dt, mats, count, s)) != MATOPT_OK) return st;
-      plan_insert(key, plan);
-    }
-  }
-  RmnpParams rp{plan->d_mats, nullptr, mu, lr, eps};
+  st = get_plan(key, dev, s, [&](Plan& p) { return build_rmnp_plan(p, dt, shp); }, plan);
+  if (st != MATOPT_OK) return st;
+  PlanUse use(*plan, s);
+  if (use.error() != hipSuccess) return hip_fail("plan stream wait", use.error());
+  MatDesc* slot = plan->dev<MatDesc>(plan->o_slot);
+  if ((st = bind_descs(plan->dev<MatDesc>(plan->o_tmpl), slot, nullptr, BIND_ROWS, ptrs, s)) != MATOPT_OK)
+    return st;
+  RmnpParams rp{slot, nullptr, mu, lr, eps};
   for (const RmnpGroup& g : plan->rmnp) {
-    rp.tasks = at<RmnpTask>(plan->dbuf, g.off);
+    rp.tasks = plan->dev<RmnpTask>(g.off);
     hipError_t e = timed(6, s, [&] { return launch_rmnp(dt, g.wpr, g.nch, rp, g.n, s); });
     if (e != hipSuccess) return hip_fail("rmnp launch", e);
   }
@@ -859,6 +950,7 @@ matopt_status adamw_step_batched(const matopt_vec* vecs, int32_t count, matopt_d
     return fail(MATOPT_ERR_PARAM, "betas must lie in [0, 1)");
   if (step < 1) return fail(MATOPT_ERR_PARAM, "step must be >= 1");
   std::vector<Span> spans;
+  std::vector<BindPtrs> ptrs(count);
   const size_t es = esize(dt);
   for (int i = 0; i < count; ++i) {
     const matopt_vec& t = vecs[i];
@@ -871,34 +963,26 @@ matopt_status adamw_step_batched(const matopt_vec* vecs, int32_t count, matopt_d
     spans.push_back({(uintptr_t)t.g, (uintptr_t)t.g + (size_t)t.n * es, tag + " g"});
     spans.push_back({(uintptr_t)t.m, (uintptr_t)t.m + (size_t)t.n * 4, tag + " m"});
     spans.push_back({(uintptr_t)t.v, (uintptr_t)t.v + (size_t)t.n * 4, tag + " v"});
+    ptrs[i] = BindPtrs{{t.p, t.g, t.m, t.v}};
   }
   if ((st = check_overlap(spans)) != MATOPT_OK) return st;
   int dev;
   if ((st = check_device(&dev)) != MATOPT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   PlanKey key{PK_ADAMW, (uint64_t)dt, (uint64_t)dev, (uint64_t)count};
-  for (int i = 0; i < count; ++i) {
-    key.push_back((uint64_t)vecs[i].n);
-    key.push_back((uint64_t)(uintptr_t)vecs[i].p);
-    key.push_back((uint64_t)(uintptr_t)vecs[i].g);
-    key.push_back((uint64_t)(uintptr_t)vecs[i].m);
-    key.push_back((uint64_t)(uintptr_t)vecs[i].v);
-  }
+  for (int i = 0; i < count; ++i) key.push_back((uint64_t)vecs[i].n);
   std::shared_ptr<Plan> plan;
-  {
-    std::lock_guard<std::mutex> lk(g_plan_mu);
-    plan = plan_lookup(key);
-    if (!plan) {
-      plan = std::make_shared<Plan>();
-      plan->device = dev;
-      if ((st = build_adamw_plan(*plan, vecs, count, s)) != MATOPT_OK) return st;
-      plan_insert(key, plan);
-    }
-  }
+  st = get_plan(key, dev, s, [&](Plan& p) { return build_adamw_plan(p, vecs, count); }, plan);
+  if (st != MATOPT_OK) return st;
+  PlanUse use(*plan, s);
+  if (use.error() != hipSuccess) return hip_fail("plan stream wait", use.error());
+  VecDesc* slot = plan->dev<VecDesc>(plan->o_slot);
+  if ((st = bind_descs(plan->dev<VecDesc>(plan->o_tmpl), slot, nullptr, BIND_VEC, ptrs, s)) != MATOPT_OK)
+    return st;
   const double b1 = beta1, b2 = beta2;
   AdamwParams ap;
-  ap.vecs = plan->d_vecs;
-  ap.tasks = at<VecTask>(plan->dbuf, plan->rmnp[0].off);
+  ap.vecs = slot;
+  ap.tasks = plan->dev<VecTask>(plan->rmnp[0].off);
   ap.b1 = b1;
   ap.omb1 = 1.0 - b1;
   ap.b2 = b2;
@@ -937,6 +1021,13 @@ matopt_status matopt_profile_read(double* ms, int64_t* launches) {
     g_prof_ms[k] = 0.0;
     g_prof_n[k] = 0;
   }
+  return MATOPT_OK;
+}
+
+matopt_status matopt_counters(int64_t* out, int32_t n) {
+  if (!out) return fail(MATOPT_ERR_NULL, "NULL output");
+  if (n < 0 || n > MATOPT_COUNTERS) return fail(MATOPT_ERR_PARAM, "n outside [0, MATOPT_COUNTERS]");
+  for (int k = 0; k < n; ++k) out[k] = g_counters[k].load(std::memory_order_relaxed);
   return MATOPT_OK;
 }
 
