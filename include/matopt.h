@@ -119,6 +119,28 @@ matopt_status muon_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The Muon step of muon_step_batched with no workspace argument and no device
+ * allocation of any kind, for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Its workspace and its tile tables live in a file-scope device array of
+ * MATOPT_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU, held from the first
+ * call on that GPU until the process ends; each call rewrites the tables in it
+ * through kernel arguments (nothing is copied from host memory).  A list of
+ * shapes whose workspace (matopt_workspace_bytes) plus tables exceed the array
+ * is rejected with MATOPT_ERR_WORKSPACE before anything is enqueued -- about
+ * four 1280 x 1280 bf16 matrices fit.  Results are bit-identical to
+ * muon_step_batched's; arguments and errors are otherwise the same.  All calls
+ * on one GPU share that GPU's array, which keeps the last call's contents
+ * (nothing in it has to be zero on entry); calls that overlap on one GPU --
+ * on different streams without ordering between them -- race on it, so the
+ * caller must order them.
+ */
+#define MATOPT_NOALLOC_SCRATCH_BYTES (64u << 20)
+matopt_status muon_step_batched_noalloc(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                        float mu, float lr, int32_t ns_steps,
+                                        float a, float b, float c, float eps, void* stream);
+
+/*
  * The Muon step with decoupled weight decay folded into the update, the
  * configuration the MatrixFSDP paper trains with (section 5.1: weight decay
  * 1e-2, momentum 0.5, two Newton-Schulz steps):

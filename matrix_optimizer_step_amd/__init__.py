@@ -24,7 +24,7 @@ import threading
 import torch
 
 __all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
-           "muon_step_batched_wd", "rmnp_step_batched", "rmnp_colcut_partial_batched",
+           "muon_step_batched_wd", "muon_step_batched_noalloc", "rmnp_step_batched", "rmnp_colcut_partial_batched",
            "rmnp_colcut_apply_batched", "adamw_step_batched", "ns_orthogonalize_batched", "profile_enable",
            "profile_read", "counters", "PROFILE_CLASSES", "COUNTERS", "LIB_PATH", "EXPORTS"]
 
@@ -67,6 +67,8 @@ EXPORTS = {
                                  _f32, _f32, _f32, _vp, _sz, _vp]),
     "muon_step_batched_wd": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _i32,
                                     _f32, _f32, _f32, _f32, _vp, _sz, _vp]),
+    "muon_step_batched_noalloc": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _i32,
+                                         _f32, _f32, _f32, _f32, _vp]),
     "rmnp_step_batched": (_i32, [ctypes.POINTER(_Mat), _i32, _i32, _f32, _f32, _f32, _vp]),
     "adamw_step_batched": (_i32, [ctypes.POINTER(_Vec), _i32, _i32, _f32, _f32, _f32, _f32, _f32,
                                   _i32, _vp]),
@@ -231,6 +233,21 @@ def muon_step_batched_wd(weights, grads, moms, mu=0.5, lr=1e-3, wd=1e-2, ns_step
     a, b, c = coeffs
     _check(lib().muon_step_batched_wd(arr, n, _dt(dtype), mu, lr, wd, ns_steps, a, b, c,
                                       eps, wp, wb, _stream_ptr(device, stream)))
+
+
+def muon_step_batched_noalloc(weights, grads, moms, mu=0.95, lr=0.02, ns_steps=5,
+                              coeffs=NS_COEFFS, eps=1e-7, stream=None):
+    """The Muon step without a workspace and without any allocation: the
+    library's per-GPU device scratch array (MATOPT_NOALLOC_SCRATCH_BYTES) holds
+    workspace and tables; shape lists that do not fit raise MatoptError
+    (MATOPT_ERR_WORKSPACE).  Nothing is allocated here either."""
+    arr, n, dtype = _mats(weights, grads, moms)
+    if n == 0:
+        return
+    device = weights[0].device
+    a, b, c = coeffs
+    _check(lib().muon_step_batched_noalloc(arr, n, _dt(dtype), mu, lr, ns_steps, a, b, c, eps,
+                                           _stream_ptr(device, stream)))
 
 
 def rmnp_step_batched(weights, grads, moms, mu=0.95, lr=0.02, eps=1e-12, stream=None):

@@ -1,6 +1,6 @@
 // Per-call descriptor binding: the caller's device pointers of this call are
 // written into the descriptors the step's launches read (see BindMode in
-// common.hpp).  The pointers travel in the kernel's by-value arguments, so a
+// common.hpp); and table uploads through kernel arguments.  The pointers travel in the kernel's by-value arguments, so a
 // call allocates nothing, copies nothing from host memory and leaves no host
 // buffer that must outlive it; the descriptors land in stream order before the
 // launches that read them.
@@ -48,7 +48,20 @@ __global__ __launch_bounds__(128) void bind_kernel(BindArgs a) {
   ((MatDesc*)a.dst)[k] = d;
 }
 
+// Copies a.n bytes (a multiple of 16) from the arguments to a.dst.
+__global__ __launch_bounds__(256) void upload_kernel(UploadArgs a) {
+  const uint32_t i = threadIdx.x * 16u;
+  if (i >= a.n) return;
+  const uint4 v = *(const uint4*)(a.data + i);
+  *(uint4*)((uint8_t*)a.dst + i) = v;
+}
+
 }  // namespace
+
+hipError_t launch_upload(const UploadArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(kUploadBytes / 16), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_bind(const BindArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bind_kernel, dim3(1), dim3(128), 0, s, a);

@@ -169,6 +169,16 @@ struct BindArgs {
 };
 static_assert(sizeof(BindArgs) <= 3712, "bind arguments must stay well inside the kernarg limit");
 
+// Table upload through kernel arguments (the allocation-free entry point
+// fills its device-side tables this way: no host buffer has to outlive the
+// call and nothing is copied from pageable memory).  n is a multiple of 16.
+constexpr int kUploadBytes = 3584;
+struct UploadArgs {
+  void* dst;
+  uint32_t n, pad_;
+  alignas(16) uint8_t data[kUploadBytes];
+};
+
 // Tile geometry.
 constexpr int kPrepTile = 64;
 constexpr int kTileBf16 = 256;
@@ -193,5 +203,7 @@ hipError_t launch_adamw(int dt, const AdamwParams& p, int n_tasks, hipStream_t s
 hipError_t launch_colcut(int dt, bool apply, const ColcutParams& p, int n_tasks, hipStream_t s);
 // One bind launch (a.n <= kBindMax descriptors).
 hipError_t launch_bind(const BindArgs& a, hipStream_t s);
+// One upload launch (a.n <= kUploadBytes bytes).
+hipError_t launch_upload(const UploadArgs& a, hipStream_t s);
 
 }  // namespace matopt

@@ -525,9 +525,23 @@ matopt_status build_rmnp_plan(Plan& P, int dt, const std::vector<std::pair<int64
   return MATOPT_OK;
 }
 
-// Enqueue the Newton-Schulz pipeline of a plan on descriptors `mats` (this
-// call's, already bound).
-matopt_status run_ns(const Plan& P, const MatDesc* mats, int dt, bool momentum, float mu,
+// Where the tables of a Newton-Schulz plan are on the device: the plan's own
+// buffer, or the allocation-free entry point's scratch copy of it.
+struct NsTables {
+  const uint8_t* base;
+  size_t o_prep;
+  int n_prep, count;
+  TileTable gram, poly, apply;
+  NsTables(const Plan& p, const void* dev_base)
+      : base((const uint8_t*)dev_base), o_prep(p.o_prep), n_prep(p.n_prep), count(p.count),
+        gram(p.gram), poly(p.poly), apply(p.apply) {}
+  template <class T>
+  const T* dev(size_t off) const { return (const T*)(base + off); }
+};
+
+// Enqueue the Newton-Schulz pipeline on descriptors `mats` (this call's,
+// already bound) with the tables of P.
+matopt_status run_ns(const NsTables& P, const MatDesc* mats, int dt, bool momentum, float mu,
                      float lr, double wdl, int ns_steps, float a, float b, float c, float eps,
                      int out_kind, int out_dt, hipStream_t s) {
   hipError_t e;
@@ -596,8 +610,8 @@ matopt_status ns_call(int dt, const std::vector<Geo>& geo, const std::vector<Bin
   if ((st = bind_descs(plan->dev<MatDesc>(plan->o_tmpl), mats, (const char*)workspace, BIND_NS, ptrs,
                  s)) != MATOPT_OK)
     return st;
-  return run_ns(*plan, mats, dt, momentum, mu, lr, wdl, ns_steps, a, b, c, eps, out_kind, out_dt,
-                s);
+  return run_ns(NsTables(*plan, plan->dbuf), mats, dt, momentum, mu, lr, wdl, ns_steps, a, b, c,
+                eps, out_kind, out_dt, s);
 }
 
 matopt_status check_common(int32_t count, int dt) {
@@ -821,6 +835,127 @@ static matopt_status muon_impl(const matopt_mat* mats, int32_t count, matopt_dty
   return ns_call(dt, geo, ptrs, workspace, dev, (hipStream_t)stream, true, mu, lr, wdl, ns_steps,
                  a, b, c, eps, OUT_W_UPDATE, dt);
 }
+
+// ------------------------------------------------------ allocation-free step
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid allocation):
+// muon_step_batched_noalloc keeps its workspace and its plan tables in this
+// file-scope array instead -- one copy per GPU the library runs on, held
+// until the process ends.  In host code `scratch` only names the array; the
+// device address of a GPU's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is what every launch receives.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;   // held for the whole enqueue of one call
+std::map<int, uint8_t*>& g_scratch_ptr = *new std::map<int, uint8_t*>();
+// host-side tables of the allocation-free entry point (host memory only)
+PlanList& g_na_plans = *new PlanList();
+constexpr size_t kNaPlanCap = 16;
+
+// Device address of the current device's copy of `scratch` (g_scratch_mu held).
+matopt_status scratch_address(int dev, uint8_t** out) {
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail("scratch symbol address", e);
+    it = g_scratch_ptr.emplace(dev, (uint8_t*)p).first;
+  }
+  *out = it->second;
+  return MATOPT_OK;
+}
+
+// Copies `bytes` to dst on s through kernel arguments, kUploadBytes per launch.
+matopt_status upload_args(uint8_t* dst, const std::vector<uint8_t>& bytes, hipStream_t s) {
+  UploadArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (size_t off = 0; off < bytes.size(); off += kUploadBytes) {
+    const size_t n = std::min(bytes.size() - off, (size_t)kUploadBytes);
+    a.dst = dst + off;
+    a.n = (uint32_t)n;
+    std::memcpy(a.data, bytes.data() + off, n);
+    hipError_t e = launch_upload(a, s);
+    if (e != hipSuccess) return hip_fail("table upload launch", e);
+  }
+  return MATOPT_OK;
+}
+
+// Host tables for `key` (built once; g_scratch_mu held).
+const Plan& na_plan(const PlanKey& key, int dt, const std::vector<Geo>& geo) {
+  for (auto it = g_na_plans.begin(); it != g_na_plans.end(); ++it)
+    if (it->first == key) {
+      g_na_plans.splice(g_na_plans.begin(), g_na_plans, it);
+      return *g_na_plans.front().second;
+    }
+  auto p = std::make_shared<Plan>();
+  (void)build_ns_plan(*p, dt, geo);
+  g_na_plans.emplace_front(key, p);
+  while (g_na_plans.size() > kNaPlanCap) g_na_plans.pop_back();
+  return *p;
+}
+
+}  // namespace
+
+extern "C" {
+
+matopt_status muon_step_batched_noalloc(const matopt_mat* mats, int32_t count, matopt_dtype dt,
+                                        float mu, float lr, int32_t ns_steps, float a, float b,
+                                        float c, float eps, void* stream) {
+  matopt_status st = check_common(count, dt);
+  if (st != MATOPT_OK) return st;
+  if (count == 0) return MATOPT_OK;
+  if (!mats) return fail(MATOPT_ERR_NULL, "mats is NULL");
+  if (!finite(mu) || !finite(lr)) return fail(MATOPT_ERR_PARAM, "non-finite mu or lr");
+  if ((st = check_ns_params(ns_steps, a, b, c, eps)) != MATOPT_OK) return st;
+  std::vector<Geo> geo;
+  std::vector<Span> spans;
+  std::vector<BindPtrs> ptrs(count);
+  const size_t es = esize(dt);
+  PlanKey key{PK_NS, (uint64_t)dt, (uint64_t)count};
+  for (int i = 0; i < count; ++i) {
+    const matopt_mat& m = mats[i];
+    if (!m.w || !m.g || !m.v) return fail(MATOPT_ERR_NULL, "matrix " + std::to_string(i) + ": NULL pointer");
+    if ((st = check_shape(m.rows, m.cols, i)) != MATOPT_OK) return st;
+    if (!aligned16(m.w) || !aligned16(m.g) || !aligned16(m.v))
+      return fail(MATOPT_ERR_ALIGN, "matrix " + std::to_string(i) + ": pointer not 16-byte aligned");
+    const size_t bytes = (size_t)m.rows * m.cols * es;
+    const std::string tag = "matrix " + std::to_string(i);
+    spans.push_back({(uintptr_t)m.w, (uintptr_t)m.w + bytes, tag + " W"});
+    spans.push_back({(uintptr_t)m.g, (uintptr_t)m.g + bytes, tag + " G"});
+    spans.push_back({(uintptr_t)m.v, (uintptr_t)m.v + bytes, tag + " V"});
+    geo.push_back(geometry(m.rows, m.cols, dt));
+    ptrs[i] = BindPtrs{{m.w, m.g, m.v, nullptr}};
+    key.push_back((uint64_t)m.rows);
+    key.push_back((uint64_t)m.cols);
+  }
+  if ((st = check_overlap(spans)) != MATOPT_OK) return st;
+  const size_t ws_bytes = layout(geo, dt).total;   // a multiple of 256
+  int dev;
+  if ((st = check_device(&dev)) != MATOPT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  const Plan& plan = na_plan(key, dt, geo);
+  const size_t need = ws_bytes + plan.host.size();
+  if (need > kScratchBytes)
+    return fail(MATOPT_ERR_WORKSPACE, "this list of shapes needs " + std::to_string(need) +
+                                          " bytes of device scratch; the allocation-free step has " +
+                                          std::to_string(kScratchBytes));
+  uint8_t* base = nullptr;
+  if ((st = scratch_address(dev, &base)) != MATOPT_OK) return st;
+  uint8_t* tables = base + ws_bytes;
+  if ((st = upload_args(tables, plan.host, s)) != MATOPT_OK) return st;
+  MatDesc* descs = (MatDesc*)(base + plan.ws_desc);
+  if ((st = bind_descs(tables + plan.o_tmpl, descs, (const char*)base, BIND_NS, ptrs, s)) !=
+      MATOPT_OK)
+    return st;
+  return run_ns(NsTables(plan, tables), descs, dt, true, mu, lr, 0.0, ns_steps, a, b, c, eps,
+                OUT_W_UPDATE, dt, s);
+}
+
+}  // extern "C"
 
 extern "C" {
 

@@ -1,0 +1,60 @@
+"""The allocation-free Muon step (muon_step_batched_noalloc) against the
+workspace entry point muon_step_batched: the same kernels on the same inputs,
+so the results must be bit-identical -- on two calls in a row, the second with
+a smaller input (the scratch array keeps the first call's contents), in bf16
+and in float32.  The calls build no plan and allocate nothing on the device.
+A shape list beyond the scratch array is rejected before anything runs."""
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mo():
+    import matrix_optimizer_step_amd as m
+    m.lib()   # raises if the library is missing: no fallback
+    return m
+
+
+def _inputs(shapes, seed, dtype="bf16"):
+    wl = workloads.small_case("noalloc", shapes, dtype=dtype, seed=seed, v_std=1e-3, g_std=1e-3)
+    trip = workloads.workload_inputs(wl)
+    return ([t[0].cuda() for t in trip], [t[1].cuda() for t in trip],
+            [t[2].cuda() for t in trip])
+
+
+CALLS = [
+    ("bf16", [(1280, 1280), (300, 700), (700, 300), (256, 512), (1280, 3840)]),
+    ("bf16", [(256, 512), (37, 45)]),          # smaller than the first
+    ("f32", [(256, 512)]),                      # the float32 single-matrix case
+]
+
+
+def test_noalloc_bit_identical_to_workspace_step(mo):
+    for k, (dt, shapes) in enumerate(CALLS):
+        print(f"[noalloc] call {k}: {dt} {shapes}", flush=True)
+        W, V, G = _inputs(shapes, seed=200 + k, dtype=dt)
+        Wr, Vr = [w.clone() for w in W], [v.clone() for v in V]
+        Wn, Vn = [w.clone() for w in W], [v.clone() for v in V]
+        mo.muon_step_batched(Wr, G, Vr)
+        torch.cuda.synchronize()
+        before = mo.counters()
+        mo.muon_step_batched_noalloc(Wn, G, Vn)
+        torch.cuda.synchronize()
+        after = mo.counters()
+        assert after["plan_builds"] == before["plan_builds"]
+        assert after["device_allocs"] == before["device_allocs"]
+        for a, b in zip(Wr + Vr, Wn + Vn):
+            assert torch.equal(a, b)
+
+
+def test_noalloc_rejects_shapes_beyond_the_scratch(mo):
+    shapes = [(4096, 4096)] * 4
+    W = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    with pytest.raises(mo.MatoptError) as ei:
+        mo.muon_step_batched_noalloc(W, [w.clone() for w in W], [w.clone() for w in W])
+    assert ei.value.name == "MATOPT_ERR_WORKSPACE"
+    assert "scratch" in ei.value.detail
