@@ -8,9 +8,9 @@ What is computed, and where the pages define it
 Blog post "Optimizers In A Sharded World: Muon's O(mn) Vs RMNP's Zero":
 
 * Section 1: momentum is heavy ball, ``V_t = mu * V_{t-1} + G_t``; Muon's target
-  direction is the orthogonalized ``(V V^T)^{-1/2} V``, approximated by a
-  Newton-Schulz iteration ("five iterations with three matrix multiplications
-  per iteration"); RMNP's direction divides each row of ``V_t`` by its L2 norm.
+  direction is the orthogonalized ``(V V^T)^{-1/2} V``, approximated by five
+  Newton-Schulz iterations of three matrix products each; RMNP's direction
+  divides each row of ``V_t`` by its L2 norm.
 * Appendix "The Code That Ran": the Newton-Schulz routine (coefficients
   (3.4445, -4.7750, 2.0315), 5 steps, ``eps = 1e-7`` added to the Frobenius
   norm, transpose when rows > cols and back at the end); the ``muon_sc`` step
@@ -41,9 +41,12 @@ notes with its reason):
 
 * The iteration is written in the factored form ``A = X X^T``,
   ``B = p(A) = a I + b A + c A A``, ``X = B X`` -- the quintic polynomial in A,
-  then its product with X.  It equals the page's printed form (``B = A X``,
-  ``X = a X + b B + c A B``) in exact arithmetic; the printed form is kept as
-  ``ns_orthogonalize_page_form`` and the two are pinned together.
+  then its product with X.  The appendix associates the same polynomial the
+  other way, applying A to X and then to that product (``a X + b (A X) +
+  c A (A X)``); the two agree in exact arithmetic, which
+  ``ns_orthogonalize_page_form`` pins.  ``ns_orthogonalize_page_bf16`` is that
+  association in the appendix routine's own precision (bf16 tensors, each
+  result rounded), the yardstick for what bf16 storage costs on a given input.
 * Scalar parameters are the float32 values a caller passes through the C ABI,
   widened exactly to float64 (``f32_param``).
 * Momentum is rounded once to the storage dtype (the page rounds twice, once per
@@ -177,21 +180,42 @@ def ns_orthogonalize(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
 
 def ns_orthogonalize_page_form(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
                                eps: float = NS_EPS) -> np.ndarray:
-    """The iteration in the association the appendix prints:
-    ``A = X X^T``, ``B = A X``, ``X = a X + b B + c A B`` (exact arithmetic)."""
+    """The iteration with the polynomial associated as the appendix associates
+    it: each step applies ``X -> a X + b (A X) + c A (A X)`` with ``A = X X^T``,
+    so A meets X twice and no product of A with itself is formed (exact
+    arithmetic; normalisation and transposes as in ``ns_orthogonalize``)."""
     a, b, c = (f32_param(t) for t in coeffs)
     x = _f64(x)
-    rows, cols = x.shape
-    X = x * frobenius_scale(x, eps)
-    if rows > cols:
-        X = X.T
+    tall = x.shape[0] > x.shape[1]
+    X = (x.T if tall else x) * frobenius_scale(x, eps)
     for _ in range(steps):
         A = X @ X.T
-        B = A @ X
-        X = a * X + b * B + c * (A @ B)
-    if rows > cols:
-        X = X.T
-    return X
+        AX = A @ X
+        X = a * X + b * AX + c * (A @ AX)
+    return X.T if tall else X
+
+
+def ns_orthogonalize_page_bf16(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
+                               eps: float = NS_EPS) -> np.ndarray:
+    """``ns_orthogonalize_page_form`` in the precision the appendix runs it:
+    the input cast to bf16, and every tensor the routine produces rounded to
+    bf16 -- the norm, the normalised X, A, A X, A (A X), each of the three
+    scaled terms and the two sums (products accumulate exactly here, in
+    float64, before their one rounding).  Only used to measure how far a
+    bf16 implementation of the method itself lies from the exact iteration on
+    a given input; the returned matrix is the last rounded iterate."""
+    r = round_bf16
+    a, b, c = (f32_param(t) for t in coeffs)
+    x = r(_f64(x))
+    tall = x.shape[0] > x.shape[1]
+    X = x.T if tall else x
+    X = r(X / r(r(np.sqrt(np.sum(X * X))) + f32_param(eps)))
+    for _ in range(steps):
+        A = r(X @ X.T)
+        AX = r(A @ X)
+        AAX = r(A @ AX)
+        X = r(r(r(a * X) + r(b * AX)) + r(c * AAX))
+    return X.T if tall else X
 
 
 def muon_step(w, g, v, mu: float = MOMENTUM, lr: float = 0.02,

@@ -1,20 +1,27 @@
 """GPU parity at the full sizes of the benchmark workloads, in the launch
-configuration bench.py times: one muon_step_batched call (and one
-ns_orthogonalize_batched call) over every matrix of the set.
+configuration bench.py times: one muon_step_batched call and one
+ns_orthogonalize_batched call over every matrix of the set.
 
-The oracle cannot redo a whole set in seconds, so each test checks
-* sampled matrices against the oracle: one of every distinct shape whose
-  Newton-Schulz the float64 oracle finishes in a few seconds (min side <= 1280)
-  -- O against the bf16 storage model and the exact iteration, V bit-exact,
-  W within 1 ulp of round(W_old - lr*sqrt(max(1,r/c))*O_gpu);
-* every other shape through properties that hold at any size: the singular
-  values of O lie in the band the coefficients imply (sup of the quintic's
-  fifth iterate on [0,1] is 1.2024; its inf over sigma >= 0.0015 is 0.6818,
-  which wide Gaussian matrices satisfy -- square ones have singular values
-  near zero and are checked against the upper edge only),
-  stored momentum rows bit-exact on sampled rows, W rows within 1 ulp, and
-  the matrix alone gives the same bits as inside the batch.
-RMNP is row-local, so sampled rows are checked exactly against the oracle.
+One case per distinct matrix shape of every set (and per size of the
+single-matrix sweep), each compared element by element with the float64
+oracle on the GPU's own updated momentum:
+
+* O (read out in float32) against the oracle's bf16 storage model and against
+  the exact iteration, relative Frobenius error <= 2e-2 for both on the
+  Gaussian sets and the sweep;
+* on the ill-conditioned set the exact iteration is out of reach of any bf16
+  path: there O must be within 2e-2 of the storage model and, against the
+  exact iteration, no farther than the appendix routine in its own bf16
+  precision (oracle.ns_orthogonalize_page_bf16) on the same input, which is
+  computed for every matrix with min side <= 1024; the exact error is
+  printed either way;
+* stored momentum bit-exact and weights within 1 ulp of
+  round(W_old - lr*sqrt(max(1,r/c))*O_gpu) on sampled rows;
+* the singular values of O inside the band the coefficients imply.
+
+Each case prints its errors; the largest oracle runs (5120 x 27648, 8192^2)
+take about half a minute on 16 host cores.  RMNP is row-local, so sampled
+rows are checked exactly against the oracle.
 """
 import numpy as np
 import pytest
@@ -28,7 +35,41 @@ pytestmark = pytest.mark.gpu
 
 BAND_HI = 1.2024 + 2e-2   # sup of p^5 on [0, 1] plus bf16 slack
 BAND_LO = 0.68 - 5e-2     # Gaussian spectra: inf of p^5 over their sigma range, minus slack
-ORACLE_MAX_M = 1280
+PAGE_BF16_MAX_M = 1024    # min side up to which the page-precision yardstick is computed
+
+
+def _distinct(shapes):
+    seen, out = set(), []
+    for i, s in enumerate(shapes):
+        if s not in seen:
+            seen.add(s)
+            out.append(i)
+    return out
+
+
+def _cases():
+    out = []
+    for name in ("gpt2_large_144", "llama3_8b_share_28", "qwen32b_share_14", "ragged_illcond_64"):
+        wl = workloads.get(name)
+        out += [(name, i) for i in _distinct(wl.shapes)]
+    out += [(f"square_sweep_{s}", 0) for s in workloads.SWEEP_SIZES]
+    return out
+
+
+CASES = _cases()
+
+
+def _case_id(c):
+    name, i = c
+    wl = _workload(name)
+    r, cc = wl.shapes[i]
+    return f"{name}-{r}x{cc}"
+
+
+def _workload(name):
+    if name.startswith("square_sweep_"):
+        return workloads.square_sweep(int(name.rsplit("_", 1)[1]))
+    return workloads.get(name)
 
 
 @pytest.fixture(scope="module")
@@ -42,32 +83,37 @@ def _log(msg):
     print(msg, flush=True)
 
 
-def _distinct(shapes):
-    seen, out = set(), []
-    for i, s in enumerate(shapes):
-        if s not in seen:
-            seen.add(s)
-            out.append(i)
-    return out
+class _SetCache:
+    """GPU results of one whole set at a time (the cases are grouped by set)."""
+
+    def __init__(self):
+        self.name = None
+        self.data = None
+
+    def get(self, mo, name):
+        if self.name != name:
+            self.data = None
+            torch.cuda.empty_cache()
+            wl = _workload(name)
+            _log(f"[{name}] generating {len(wl.shapes)} matrices ({wl.numel / 1e6:.0f}M elements)")
+            trip = workloads.workload_inputs(wl)
+            W = [t[0].cuda() for t in trip]
+            V = [t[1].cuda() for t in trip]
+            G = [t[2].cuda() for t in trip]
+            mo.muon_step_batched(W, G, V, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps)
+            O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            _log(f"[{name}] step and Newton-Schulz done on the GPU")
+            self.name, self.data = name, (wl, trip, W, V, G, O)
+        return self.data
+
+
+_cache = _SetCache()
 
 
 def _sample_rows(rows, n=8, seed=0):
     rng = np.random.default_rng(seed)
     return torch.from_numpy(np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, n)])))
-
-
-def _full_step(mo, name):
-    wl = workloads.get(name)
-    _log(f"[{name}] generating {len(wl.shapes)} matrices ({wl.numel / 1e6:.0f}M elements)")
-    trip = workloads.workload_inputs(wl)
-    W = [t[0].cuda() for t in trip]
-    V = [t[1].cuda() for t in trip]
-    G = [t[2].cuda() for t in trip]
-    mo.muon_step_batched(W, G, V, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps)
-    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    _log(f"[{name}] step and Newton-Schulz done on the GPU")
-    return wl, trip, W, V, G, O
 
 
 def _check_v_rows(v_gpu, v_old, g, mu, rows):
@@ -94,65 +140,48 @@ def _band(o):
     return float(ev.min()), float(ev.max())
 
 
-def _check_set(mo, name, gaussian=True):
-    wl, trip, W, V, G, O = _full_step(mo, name)
-    errs = {}
-    for i in _distinct(wl.shapes):
-        r, c = wl.shapes[i]
-        w0, v0, g0 = trip[i]
-        rows = _sample_rows(r, seed=i)
-        _check_v_rows(V[i], v0, g0, wl.mu, rows)
-        _check_w_rows(W[i], w0, O[i], wl.lr, rows)
-        if min(r, c) <= (1024 if not gaussian else ORACLE_MAX_M):
-            v = f64(V[i])
-            o = f64(O[i])
-            em = relF(o, oracle.ns_orthogonalize(v, rounding="bf16"))
-            ee = relF(o, oracle.ns_orthogonalize(v))
-            errs[(r, c)] = (em, ee)
-            _log(f"[{name}] {r}x{c}: relF(O) vs bf16 model {em:.2e}, vs exact {ee:.2e}")
-            if gaussian:
-                assert em <= 2e-2 and ee <= 2e-2
-        lo, hi = _band(O[i])
-        _log(f"[{name}] {r}x{c}: singular values of O in [{lo:.4f}, {hi:.4f}]")
-        assert hi <= BAND_HI
-        if gaussian and max(r, c) >= 2 * min(r, c):
-            assert lo >= BAND_LO
-    return wl, V, O, errs
-
-
-def test_gpt2_large_full_set(mo):
-    _check_set(mo, "gpt2_large_144")
-
-
-def test_llama3_8b_share_full_set(mo):
-    wl, V, O, _ = _check_set(mo, "llama3_8b_share_28")
-    # the largest matrix alone gives the same bits as inside the batch
-    i = max(range(len(wl.shapes)), key=lambda j: wl.shapes[j][0] * wl.shapes[j][1])
-    alone = mo.ns_orthogonalize_batched([V[i]], out_dtype=torch.float32)[0]
-    torch.cuda.synchronize()
-    assert torch.equal(alone, O[i])
-
-
-def test_qwen32b_share_full_set(mo):
-    _check_set(mo, "qwen32b_share_14")
-
-
-def test_ragged_illcond_full_set(mo):
-    # Ill-conditioned spectra: singular values log-uniform in [1e-4, 1] sit on
-    # the steep part of the quintic (gain up to a^5 ~ 485), so bf16 storage
-    # rounding is amplified; gated against the bf16 storage model, reported
-    # against the exact iteration.
-    wl, V, O, errs = _check_set(mo, "ragged_illcond_64", gaussian=False)
-    assert errs, "no matrix small enough for the oracle"
-    worst_model = max(e[0] for e in errs.values())
-    worst_exact = max(e[1] for e in errs.values())
-    _log(f"[ragged_illcond_64] worst relF(O): vs bf16 model {worst_model:.2e}, "
-         f"vs exact {worst_exact:.2e} (reported)")
-    assert worst_model <= 2e-2
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", CASES, ids=[_case_id(c) for c in CASES])
+def test_fullsize_o_elementwise(mo, case):
+    name, i = case
+    wl, trip, W, V, G, O = _cache.get(mo, name)
+    r, c = wl.shapes[i]
+    w0, v0, g0 = trip[i]
+    rows = _sample_rows(r, seed=i)
+    _check_v_rows(V[i], v0, g0, wl.mu, rows)
+    _check_w_rows(W[i], w0, O[i], wl.lr, rows)
+    v = f64(V[i])
+    o = f64(O[i])
+    e_model = relF(o, oracle.ns_orthogonalize(v, rounding="bf16"))
+    exact = oracle.ns_orthogonalize(v)
+    e_exact = relF(o, exact)
+    gaussian = wl.kind == "gaussian"
+    msg = f"[{name}] {r}x{c}: relF(O) vs bf16 model {e_model:.2e}, vs exact {e_exact:.2e}"
+    e_page = None
+    if not gaussian and min(r, c) <= PAGE_BF16_MAX_M:
+        e_page = relF(oracle.ns_orthogonalize_page_bf16(v), exact)
+        msg += f", appendix routine in bf16 vs exact {e_page:.2e}"
+    lo, hi = _band(O[i])
+    _log(msg + f"; singular values of O in [{lo:.4f}, {hi:.4f}]")
+    assert e_model <= 2e-2
+    if gaussian:
+        assert e_exact <= 2e-2
+    elif e_page is not None:
+        assert e_exact <= e_page
+    assert hi <= BAND_HI
+    if gaussian and max(r, c) >= 2 * min(r, c):
+        assert lo >= BAND_LO
+    if name == "llama3_8b_share_28" and (r, c) == (14336, 4096):
+        # the largest matrix of the set alone gives the same bits as inside the batch
+        alone = mo.ns_orthogonalize_batched([V[i]], out_dtype=torch.float32)[0]
+        torch.cuda.synchronize()
+        assert torch.equal(alone, O[i])
 
 
 @pytest.mark.parametrize("name", ["gpt2_large_144", "qwen32b_share_14"])
 def test_rmnp_full_set_sampled_rows(mo, name):
+    _cache.data = None
+    _cache.name = None
     wl = workloads.get(name)
     _log(f"[rmnp {name}] generating")
     trip = workloads.workload_inputs(wl)

@@ -12,11 +12,12 @@ import json
 import os
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
 from oracle import (NS_COEFFS, f32_param, momentum, ns_orthogonalize,
-                    ns_orthogonalize_page_form, muon_step, rmnp_direction,
+                    ns_orthogonalize_page_form, ns_orthogonalize_page_bf16, muon_step, rmnp_direction,
                     rmnp_step, round_bf16, round_storage)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -198,6 +199,41 @@ def test_ns_page_association_equals_factored_form():
     for shape in [(16, 40), (40, 16), (33, 33)]:
         x = rng(6).standard_normal(shape)
         assert relF(ns_orthogonalize(x), ns_orthogonalize_page_form(x)) <= 1e-13
+
+
+def _torch_bf16_page_routine(x, steps=5, eps=1e-7):
+    """The appendix association run with torch's own bfloat16 CPU tensor
+    arithmetic (an independent implementation of bf16 rounding: float32
+    arithmetic per operation, then round to nearest even)."""
+    a, b, c = (np.float32(t) for t in (3.4445, -4.7750, 2.0315))
+    X = torch.from_numpy(x).to(torch.bfloat16)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.t().contiguous()
+    X = X / (X.norm() + eps)
+    for _ in range(steps):
+        A = X @ X.t().contiguous()
+        AX = A @ X
+        X = float(a) * X + float(b) * AX + float(c) * (A @ AX)
+    if tall:
+        X = X.t()
+    return X.to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("shape", [(48, 80), (80, 48), (64, 64)])
+def test_page_bf16_model_matches_torch_bf16_arithmetic(shape):
+    """The bf16 model of the appendix routine against torch's bf16 tensor ops
+    on the same input: the same rounding points give results far closer to
+    each other than either is to the exact iteration (a dropped or extra
+    rounding point, or a wrong association, would not)."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal(shape)
+    mine = ns_orthogonalize_page_bf16(x)
+    ref = _torch_bf16_page_routine(x)
+    exact = ns_orthogonalize(x)
+    d_mine, d_ref = relF(mine, exact), relF(ref, exact)
+    assert 1e-2 <= d_mine <= 5e-2 and 1e-2 <= d_ref <= 5e-2
+    assert relF(mine, ref) <= 0.35 * min(d_mine, d_ref)
 
 
 def test_ns_transpose_equivariance():

@@ -94,27 +94,35 @@ BF16_SHAPES = [(700, 1300), (1300, 700), (256, 256), (513, 1030), (1, 64), (64, 
                (37, 45), (8, 8), (1, 1), (300, 2000)]
 
 
+# Shapes of BF16_SHAPES exempt from the 2e-2 gate against the exact iteration,
+# with the reason.  This 8x8 Gaussian draw (seed 11, index 7) is
+# ill-conditioned: its smallest singular value is 1.7e-4 of the Frobenius norm,
+# on the steep part of the quintic's fifth iterate (gain up to a^5 ~ 485), and
+# with only 8 singular values that one direction carries an eighth of |O|^2, so
+# bf16 storage of the iterates costs ~3e-2 against the exact iteration.  It is
+# gated instead against the storage model (2e-2) and against the appendix
+# routine run in its own bf16 precision (no farther from the exact iteration).
+EXACT_GATE_EXEMPT = {(8, 8): "ill-conditioned draw: sigma_min = 1.7e-4 |X0|_F"}
+
+
 def test_ns_bf16_ragged_batch(mo):
     wl = workloads.small_case("ns_bf16", BF16_SHAPES, seed=11, v_std=1.0, g_std=1.0)
     _, V, _ = _inputs(wl)
     O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    errs_m, errs_e = [], []
-    for v, o in zip(V, O):
+    for shape, v, o in zip(BF16_SHAPES, V, O):
         x = f64(v)
+        exact = oracle.ns_orthogonalize(x)
         em = relF(f64(o), oracle.ns_orthogonalize(x, rounding="bf16"))
-        ee = relF(f64(o), oracle.ns_orthogonalize(x))
-        errs_m.append(em)
-        errs_e.append(ee)
-    print("bf16 relF vs model", np.round(errs_m, 5), "vs exact", np.round(errs_e, 5))
-    assert max(errs_m) <= 2e-2
-    # Against the exact iteration the bf16 path is gated on Gaussian matrices
-    # with many singular values.  Degenerate shapes (a single row or column,
-    # rank 1) put every singular value on the scalar map's repelling orbit
-    # through 1, where bf16 storage rounding is amplified up to ~2x per step;
-    # those are gated against the bf16 storage model above.
-    big = [e for e, s in zip(errs_e, BF16_SHAPES) if min(s) >= 64]
-    assert max(big) <= 2e-2
+        ee = relF(f64(o), exact)
+        ep = relF(oracle.ns_orthogonalize_page_bf16(x), exact)
+        print(f"{shape}: relF(O) vs bf16 model {em:.2e}, vs exact {ee:.2e} "
+              f"(appendix routine in bf16 vs exact {ep:.2e})", flush=True)
+        assert em <= 2e-2
+        if shape in EXACT_GATE_EXEMPT:
+            assert ee <= ep
+        else:
+            assert ee <= 2e-2, f"{shape}: {ee:.3e} against the exact iteration"
 
 
 # Gram and polynomial tables of this batch differ in length (72 and 48 entries:

@@ -26,6 +26,8 @@ Workloads (shapes are rows x cols of the stored matrix):
   momentum is zero so the momentum keeps that spectrum; bf16.
 * ``qwen32b_share_14``: 2 layers x {5120x5120 Q, 1024x5120 K, 1024x5120 V,
   5120x5120 O, 27648x5120 gate, 27648x5120 up, 5120x27648 down}, bf16.
+* ``square_sweep(s)``: one s x s bf16 matrix, s in 1024 .. 8192 (the blog
+  post's single-matrix size sweep).
 """
 
 from __future__ import annotations
@@ -37,7 +39,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "matrix_inputs", "workload_inputs",
-           "small_case"]
+           "small_case", "square_sweep", "SWEEP_SIZES"]
 
 
 @dataclass(frozen=True)
@@ -117,6 +119,15 @@ def small_case(name: str, shapes, dtype="bf16", seed=123, kind="gaussian",
     """An ad-hoc workload (tests: ragged tails, tiny and edge shapes)."""
     return Workload(name, tuple(tuple(s) for s in shapes), dtype, seed,
                     w_std=w_std, v_std=v_std, g_std=g_std, kind=kind)
+
+
+SWEEP_SIZES = (1024, 2048, 4096, 8192)
+
+
+def square_sweep(s: int) -> Workload:
+    """One s x s bf16 matrix of the blog post's single-matrix size sweep (sides
+    1024 .. 8192): W ~ N(0, 0.02), G and V ~ N(0, 1e-3), seed 1000 + s."""
+    return small_case(f"square_sweep_{s}", [(s, s)], seed=1000 + s)
 
 
 def _to_storage(a32: np.ndarray, dtype: str):
