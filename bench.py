@@ -10,8 +10,9 @@ events around the timed steps and the mean): W warmup steps, a synchronize,
 HIP events on the launch stream around exactly K steps, a synchronize.  A
 second pass of K steps runs with the library's per-launch HIP events on the
 same stream to split the step into kernels (the roofline figures).  While the
-first pass runs, the GPU's graphics clock is sampled (amdsmi), so that the
-GEMM rate can also be read against the peak at the clock actually observed.
+second pass also reads the clock the GEMM launches ran at, measured inside the
+kernels (each workgroup's shader-clock ticks over 100 MHz real-time ticks),
+so that the GEMM rate can also be read against the peak at that clock.
 
 The same JSON line also carries, unless switched off: RMNP, column-cut RMNP,
 AdamW tails, the MatrixFSDP training configuration, the other configurations
@@ -35,7 +36,6 @@ import json
 import os
 import re
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -112,69 +112,7 @@ def cpu_model():
     return "unknown"
 
 
-class ClockSampler:
-    """Samples the graphics clock of the GPU in use (amdsmi) from a thread
-    while a timed region runs; mean_mhz is None where amdsmi is unavailable."""
-
-    def __init__(self, period_s=0.002):
-        self.period = period_s
-        self.samples = []
-        self._stop = threading.Event()
-        self._thread = None
-        self._handle = None
-        try:
-            import amdsmi
-            import torch
-            amdsmi.amdsmi_init()
-            props = torch.cuda.get_device_properties(torch.cuda.current_device())
-            want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
-            for h in amdsmi.amdsmi_get_processor_handles():
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)   # "dddd:bb:dd.f"
-                dom, bus, rest = bdf.split(":")
-                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
-                    self._handle = h
-            self._amdsmi = amdsmi
-        except Exception as e:  # pragma: no cover - depends on the box
-            log(f"[bench] clock sampling unavailable: {e}")
-
-    def _read(self):
-        a, h = self._amdsmi, self._handle
-        try:
-            m = a.amdsmi_get_gpu_metrics_info(h)
-            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))
-                    and 0 < c < 10000]
-            if clks:
-                return sum(clks) / len(clks)
-        except Exception:
-            pass
-        info = a.amdsmi_get_clock_info(h, a.AmdSmiClkType.SYS)
-        return float(info["clk"])
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._read())
-            except Exception:
-                return
-            time.sleep(self.period)
-
-    def __enter__(self):
-        if self._handle is not None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread:
-            self._thread.join()
-
-    @property
-    def mean_mhz(self):
-        return sum(self.samples) / len(self.samples) if self.samples else None
-
-
-def time_steps(fn, steps, warmup, stream, sampler=None):
+def time_steps(fn, steps, warmup, stream):
     """Mean ms of `steps` calls of fn between HIP events on `stream`."""
     import torch
     for _ in range(warmup):
@@ -182,34 +120,40 @@ def time_steps(fn, steps, warmup, stream, sampler=None):
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    if sampler is not None:
-        with sampler:
-            e0.record(stream)
-            for _ in range(steps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-    else:
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
 
 
 def profiled(fn, steps, stream):
     """Per-kernel-class ms per step from the library's per-launch HIP events
-    (and the wall ms per step of the pass)."""
+    (and the wall ms per step of the pass); bf16 GEMM classes also carry the
+    clock (MHz) their launches ran at."""
     import matrix_optimizer_step_amd as mo
     mo.profile_read()
     mo.profile_enable(True)
+    mo.profile_read_clock()
     ms = time_steps(fn, steps, 0, stream)
     mo.profile_enable(False)
     prof = mo.profile_read()
+    clk = mo.profile_read_clock()
     per = {k: {"ms_per_step": v[0] / steps, "launches_per_step": v[1] / steps}
            for k, v in prof.items() if v[1]}
+    for k, mhz in clk.items():
+        if k in per:
+            per[k]["clock_mhz"] = mhz
     return ms, per
+
+
+def gemm_clock(per):
+    """Time-weighted clock of the GEMM classes (None without clock data)."""
+    parts = [(per[k]["ms_per_step"], per[k]["clock_mhz"]) for k in ("gram", "poly", "apply")
+             if k in per and "clock_mhz" in per[k]]
+    tot = sum(t for t, _ in parts)
+    return sum(t * c for t, c in parts) / tot if tot else None
 
 
 def gemm_rates(per, flops):
@@ -277,6 +221,7 @@ def workload_line(name, steps, warmup, stream, with_rmnp=False):
            "elements": wl.numel, "ms_per_step": round(ms, 4),
            "ns_alg_tflop_per_step": round(flops / 1e12, 4),
            "ns_tflops": round(tflops, 1), "ns_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "gemm_clock_mhz": round(gemm_clock(per) or 0.0, 0),
            "kernels_ms": {k: round(v["ms_per_step"], 4) for k, v in per.items()}}
     if "prep" in per:
         out["prep_GB_s"] = round(prep_alg_bytes(wl.shapes, wl.dtype)
@@ -489,13 +434,12 @@ def main():
     def step():
         mo.muon_step_batched(W, G, V, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps)
 
-    sampler = ClockSampler()
-    ms = time_steps(step, args.steps, args.warmup, stream, sampler)
-    clock = sampler.mean_mhz
-    log(f"[bench] muon step {ms:.3f} ms" + (f" at {clock:.0f} MHz sampled" if clock else ""))
+    ms = time_steps(step, args.steps, args.warmup, stream)
+    log(f"[bench] muon step {ms:.3f} ms")
 
     # second pass: per-launch HIP events inside the library, same stream
     ms_prof, per = profiled(step, args.steps, stream)
+    clock = gemm_clock(per)
     flops = ns_alg_flops(wl.shapes, wl.ns_steps)
     gemm_ms, gemm_launches, ns_tflops = gemm_rates(per, flops)
     numel = wl.numel
@@ -519,6 +463,9 @@ def main():
     if clock and ns_tflops:
         peak_obs = PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_MHZ
         roofline["observed_clock_mhz"] = round(clock, 0)
+        roofline["observed_clock_source"] = (
+            "measured in the GEMM kernels during the profiled pass: shader-clock ticks over "
+            "100 MHz real-time ticks per workgroup, time-weighted over Gram, polynomial, apply")
         roofline["peak_at_observed_clock"] = round(peak_obs, 1)
         roofline["frac_at_observed_clock"] = round(ns_tflops / peak_obs, 4)
 
@@ -542,8 +489,7 @@ def main():
         "ns_pct_bf16_peak": round(100 * ns_tflops / PEAK_BF16_TFLOPS, 2) if ns_tflops else None,
         "ns_alg_tflop_per_step": round(flops / 1e12, 4),
         "roofline": roofline,
-        "kernels": {k: {"ms_per_step": round(v["ms_per_step"], 4),
-                        "launches_per_step": v["launches_per_step"]} for k, v in per.items()},
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in per.items()},
         "ms_per_step_profiled": round(ms_prof, 4),
         "hbm_kernels": {
             "prep": {"bytes_per_elem": round(prep_bytes / numel, 3),
@@ -569,8 +515,8 @@ def main():
             mo.rmnp_colcut_partial_batched(G, V, rowsq=rowsq, mu=wl.mu)
             mo.rmnp_colcut_apply_batched(W, V, rowsq, lr=wl.lr)
 
-        time_steps(colcut, 1, args.warmup, stream)
-        cms, cp = profiled(colcut, args.steps, stream)
+        cms = time_steps(colcut, args.steps, args.warmup, stream)
+        _, cp = profiled(colcut, args.steps, stream)
         cgbs = 12 * esz / 2 * numel / (cms * 1e-3) / 1e9
         result["rmnp_colcut"] = {
             "ms_per_step": round(cms, 4), "bytes_per_elem": 6 * esz, "GB_s": round(cgbs, 1),
@@ -600,8 +546,8 @@ def main():
                 st[0] += 1
                 mo.adamw_step_batched(tp, tg, tm, tv, st[0])
 
-            time_steps(adamw, 1, args.warmup, stream)
-            wall, ap_ = profiled(adamw, args.steps, stream)
+            wall = time_steps(adamw, args.steps, args.warmup, stream)
+            _, ap_ = profiled(adamw, args.steps, stream)
             kms = ap_["adamw"]["ms_per_step"]
             nel = sum(lens)
             agbs = 22 * nel / (kms * 1e-3) / 1e9

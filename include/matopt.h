@@ -45,7 +45,8 @@
  *   frees nothing, copies nothing from host memory and never synchronises the
  *   host -- this call's pointers reach the device as kernel arguments of a
  *   small bind launch that writes the descriptors (into the workspace for the
- *   Newton-Schulz entry points, into the plan for the others).  Calls that use
+ *   Newton-Schulz entry points, into the plan for the others; there, a call
+ *   whose pointers equal those already bound skips the launch).  Calls that use
  *   one plan are therefore chained: a call on another stream than the previous
  *   call of the same plan first waits (on the device) for that call's work.
  *   At most 64 plans are cached; an evicted plan is freed, stream-ordered,
@@ -260,6 +261,16 @@ int32_t matopt_version(void);
 matopt_status matopt_profile_enable(int32_t on);
 /* ms[k], launches[k] for k < MATOPT_PROFILE_CLASSES; resets the accumulators. */
 matopt_status matopt_profile_read(double* ms, int64_t* launches);
+/*
+ * Shader clock (MHz) the bf16 GEMM launches of classes 2, 3 and 4 ran at while
+ * profiling was on (current device): each workgroup adds the ticks of the
+ * shader-clock and the 100 MHz real-time counters over its tile, mhz[k] is
+ * 100 * (sum of shader ticks) / (sum of real-time ticks); 0 for classes
+ * without data.  Synchronises the device; resets the counters.  Switching
+ * profiling on allocates a 176-byte device buffer per device (once).
+ * mhz: HOST array of MATOPT_PROFILE_CLASSES entries.
+ */
+matopt_status matopt_profile_read_clock(double* mhz);
 
 /*
  * Diagnostics of the plan cache, cumulative since the library was loaded:

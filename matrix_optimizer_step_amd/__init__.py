@@ -26,7 +26,7 @@ import torch
 __all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
            "muon_step_batched_wd", "muon_step_batched_noalloc", "rmnp_step_batched", "rmnp_colcut_partial_batched",
            "rmnp_colcut_apply_batched", "adamw_step_batched", "ns_orthogonalize_batched", "profile_enable",
-           "profile_read", "counters", "PROFILE_CLASSES", "COUNTERS", "LIB_PATH", "EXPORTS"]
+           "profile_read", "profile_read_clock", "counters", "PROFILE_CLASSES", "COUNTERS", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmatopt.so")
 
@@ -85,6 +85,7 @@ EXPORTS = {
     "matopt_profile_enable": (_i32, [_i32]),
     "matopt_profile_read": (_i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "matopt_counters": (_i32, [ctypes.POINTER(_i64), _i32]),
+    "matopt_profile_read_clock": (_i32, [ctypes.POINTER(ctypes.c_double)]),
 }
 
 _lib = None
@@ -383,6 +384,15 @@ def profile_read() -> dict:
     n = (_i64 * k)()
     _check(lib().matopt_profile_read(ms, n))
     return {name: (ms[i], n[i]) for i, name in enumerate(PROFILE_CLASSES)}
+
+
+def profile_read_clock() -> dict:
+    """Shader clock (MHz) per kernel class of the bf16 GEMM launches made while
+    profiling was on (resets the counters); classes without data are left out."""
+    k = len(PROFILE_CLASSES)
+    mhz = (ctypes.c_double * k)()
+    _check(lib().matopt_profile_read_clock(mhz))
+    return {name: mhz[i] for i, name in enumerate(PROFILE_CLASSES) if mhz[i] > 0}
 
 
 def counters() -> dict:

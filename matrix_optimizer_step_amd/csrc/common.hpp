@@ -87,6 +87,9 @@ struct GemmParams {
   int32_t out_dt;     // dtype of O for OUT_O
   float a, b, c, lr;
   double wdl;         // lr * weight decay (exact product), 0: no decay
+  // profiling only (else NULL): [0] += shader-clock ticks, [1] += 100 MHz
+  // real-time ticks, summed over the launch's workgroups (bf16 kernel)
+  unsigned long long* clk;
 };
 
 // ns_steps == 0: O = xs * V directly (prep tiles over the original orientation).

@@ -1463,14 +1463,11 @@ __device__ __forceinline__ void diag_pair(const MatDesc& d, const GemmParams& P,
 // operand each).  NW = 4 (four waves of 128 x 128, one per SIMD) remains a
 // build-time alternative (MATOPT_*_WAVES).
 template <int STAGE, int OUT, int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
-                          amdgpu_waves_per_eu(NW / 4, NW / 4)))
-void ns_gemm_bf16_kernel(GemmParams P) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
   static_assert(NW == 4 || NW == 8, "layout");
   constexpr int NBJ = NW == 4 ? 4 : 2;   // 32-column blocks per wave
   constexpr int WN = 32 * NBJ;           // columns per wave
   constexpr int BPW = NW == 4 ? 4 : 2;   // DMA blocks per wave and operand
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
   // Gram: P = Q = X rows.  A and B hold their upper tiles only (diagonal
   // tiles whole), so a row block of either is read k-major, through the upper
   // tiles above it, for the k blocks left of its diagonal block, and
@@ -1602,6 +1599,30 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   epilogue<STAGE, OUT, NBJ>(d, P, k.acc, (float*)(lds + wave * Ep<WN>::WAVE_BYTES), ep_src, ep_ld, out,
                        ld_out, i0 + g.wi0, j0 + g.wj0, lane, g.frow, g.fkc, s_first,
                        ecur);
+  }
+}
+
+// The kernel: one tile per workgroup.  With P.clk set (profiling only), the
+// first lane of each workgroup also adds the shader-clock ticks (s_memtime)
+// and the 100 MHz real-time ticks (s_memrealtime) that its tile took to
+// P.clk[0] and P.clk[1] -- their ratio is the clock the tiles ran at.
+template <int STAGE, int OUT, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
+                          amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void ns_gemm_bf16_kernel(GemmParams P) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  const bool clk = P.clk != nullptr;
+  uint64_t t0 = 0, r0 = 0;
+  if (clk) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  gemm_tile<STAGE, OUT, NW>(P, lds);
+  if (clk && threadIdx.x == 0) {
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    atomicAdd(&P.clk[0], (unsigned long long)(t1 - t0));
+    atomicAdd(&P.clk[1], (unsigned long long)(r1 - r0));
   }
 }
 
