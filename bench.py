@@ -194,9 +194,10 @@ def cpu_baseline(wl):
                       f"{threads} threads on {cpu_model()}"}
 
 
-def workload_line(name, steps, warmup, stream, with_rmnp=False):
+def workload_line(name, steps, warmup, stream, with_rmnp=False, with_split=False):
     """Compact line of one more configuration: Muon step ms, NS rate, prep
-    bandwidth (and the RMNP step on the same momenta)."""
+    bandwidth (and the RMNP step on the same momenta; the step in split
+    precision)."""
     import torch
     import matrix_optimizer_step_amd as mo
     import workloads
@@ -236,9 +237,26 @@ def workload_line(name, steps, warmup, stream, with_rmnp=False):
                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                        "muon_over_rmnp": round(ms / rms, 1)}
         log(f"[bench] {name}: rmnp step {rms:.3f} ms ({gbs:.0f} GB/s)")
+    if with_split:
+        out["split_precision"] = split_line(W, G, V, wl, steps, warmup, stream, ms)
     del W, V, G
     torch.cuda.empty_cache()
     return out
+
+
+def split_line(W, G, V, wl, steps, warmup, stream, ms_default):
+    """The Muon step in split precision (bf16 hi + lo iterates, B X over both
+    parts) on the same tensors, beside the default path's ms."""
+    import matrix_optimizer_step_amd as mo
+    step = lambda: mo.muon_step_batched(W, G, V, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps,
+                                        precision="split")
+    ms = time_steps(step, steps, warmup, stream)
+    _, per = profiled(step, steps, stream)
+    gemm_ms = sum(per[k]["ms_per_step"] for k in ("gram", "poly", "apply") if k in per)
+    log(f"[bench] {wl.name}: split-precision muon step {ms:.3f} ms ({ms / ms_default:.2f}x)")
+    return {"ms_per_step": round(ms, 4), "over_default": round(ms / ms_default, 3),
+            "gemm_ms": round(gemm_ms, 4),
+            "kernels_ms": {k: round(v["ms_per_step"], 4) for k, v in per.items()}}
 
 
 def single_f32_line(stream, steps=200, warmup=20):
@@ -565,6 +583,7 @@ def main():
         wms = time_steps(lambda: mo.muon_step_batched_wd(W, G, V, mu=0.5, lr=1e-3, wd=1e-2,
                                                          ns_steps=2),
                          args.steps, args.warmup, stream)
+        result["split_precision"] = split_line(W, G, V, wl, args.steps, args.warmup, stream, ms)
         result["training_config"] = {"ms_per_step": round(wms, 4), "mu": 0.5, "lr": 1e-3,
                                      "wd": 1e-2, "ns_steps": 2,
                                      "ns_alg_tflop_per_step": round(ns_alg_flops(wl.shapes, 2) / 1e12, 4)}
@@ -576,7 +595,8 @@ def main():
         result["configs"] = {"single_f32_256x512": single_f32_line(stream)}
         for name in OTHER_CONFIGS:
             result["configs"][name] = workload_line(name, args.steps, args.warmup, stream,
-                                                    with_rmnp=name == "qwen32b_share_14")
+                                                    with_rmnp=name == "qwen32b_share_14",
+                                                    with_split=name == "ragged_illcond_64")
     if not args.no_sweep:
         result["sweep"] = square_sweep(args.steps, args.warmup, stream)
     if not args.no_cpu_baseline:

@@ -64,7 +64,16 @@ extern "C" {
 
 typedef enum {
     MATOPT_F32 = 0,  /* IEEE float32 */
-    MATOPT_BF16 = 1  /* bfloat16 (round to nearest even on every store) */
+    MATOPT_BF16 = 1, /* bfloat16 (round to nearest even on every store) */
+    /* Newton-Schulz entry points only: bfloat16 storage and bf16 MFMA products
+     * as MATOPT_BF16, but each iterate is carried to the next product with X
+     * as a bf16 high part plus a bf16 low part (x - hi), about 16 significant
+     * bits: the products B*X run over both parts (twice the K of the plain
+     * path) and B is stored whole.  On ill-conditioned inputs, whose small
+     * singular values sit where the quintic's fifth iterate is steep, this
+     * keeps O within 2e-2 of the exact iteration where bf16 iterates cannot.
+     * Needs the workspace matopt_workspace_bytes reports for this dtype. */
+    MATOPT_BF16_SPLIT = 2
 } matopt_dtype;
 
 typedef enum {

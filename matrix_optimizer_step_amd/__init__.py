@@ -30,7 +30,7 @@ __all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmatopt.so")
 
-F32, BF16 = 0, 1
+F32, BF16, BF16_SPLIT = 0, 1, 2
 PROFILE_CLASSES = ("prep", "finalize", "gram", "poly", "apply", "scale_out", "rmnp",
                    "colcut_partial", "colcut_apply", "adamw", "bind")
 COUNTERS = ("plan_builds", "device_allocs", "device_frees", "bind_launches")
@@ -120,10 +120,16 @@ def _check(status: int):
         raise MatoptError(status, name, detail)
 
 
-def _dt(dtype) -> int:
+def _dt(dtype, precision: str = "default") -> int:
+    """Library dtype code of a tensor dtype; precision="split" selects the
+    split-precision Newton-Schulz path for bfloat16 (MATOPT_BF16_SPLIT)."""
+    if precision not in ("default", "split"):
+        raise ValueError(f"precision must be 'default' or 'split', got {precision!r}")
     if dtype == torch.bfloat16:
-        return BF16
+        return BF16_SPLIT if precision == "split" else BF16
     if dtype == torch.float32:
+        if precision == "split":
+            raise ValueError("precision='split' applies to bfloat16 tensors only")
         return F32
     raise TypeError(f"unsupported dtype {dtype} (bfloat16 or float32)")
 
@@ -152,11 +158,11 @@ def _stream_ptr(device, stream) -> int:
     return int(s.cuda_stream)
 
 
-def workspace_bytes(shapes, dtype) -> int:
+def workspace_bytes(shapes, dtype, precision="default") -> int:
     n = len(shapes)
     rows = (_i64 * max(n, 1))(*[int(r) for r, _ in shapes])
     cols = (_i64 * max(n, 1))(*[int(c) for _, c in shapes])
-    return int(lib().matopt_workspace_bytes(rows, cols, n, _dt(dtype)))
+    return int(lib().matopt_workspace_bytes(rows, cols, n, _dt(dtype, precision)))
 
 
 # Workspaces allocated by the binding, most recently used last; at most
@@ -166,8 +172,8 @@ _WS_CACHE_CAP = 4
 _ws_cache: "collections.OrderedDict" = collections.OrderedDict()
 
 
-def _workspace(device, dtype, shapes, workspace):
-    need = workspace_bytes(shapes, dtype)
+def _workspace(device, dtype, shapes, workspace, precision="default"):
+    need = workspace_bytes(shapes, dtype, precision)
     if workspace is not None:
         _check_dev(workspace, "workspace", device)
         if not workspace.is_contiguous():
@@ -175,7 +181,7 @@ def _workspace(device, dtype, shapes, workspace):
         if workspace.numel() * workspace.element_size() < need:
             raise ValueError(f"workspace too small: need {need} bytes")
         return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
-    key = (str(device), _dt(dtype), tuple(shapes))
+    key = (str(device), _dt(dtype, precision), tuple(shapes))
     ws = _ws_cache.pop(key, None)
     if ws is None:
         ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
@@ -208,21 +214,24 @@ def _mats(weights, grads, moms):
 
 
 def muon_step_batched(weights, grads, moms, mu=0.95, lr=0.02, ns_steps=5,
-                      coeffs=NS_COEFFS, eps=1e-7, workspace=None, stream=None):
-    """One Muon step on every (W, G, V) triple; W and V are updated in place."""
+                      coeffs=NS_COEFFS, eps=1e-7, workspace=None, stream=None,
+                      precision="default"):
+    """One Muon step on every (W, G, V) triple; W and V are updated in place.
+    precision="split" (bfloat16 only): the split-precision iterate."""
     arr, n, dtype = _mats(weights, grads, moms)
     if n == 0:
         return
     device = weights[0].device
     shapes = [tuple(w.shape) for w in weights]
-    wp, wb, _keep = _workspace(device, dtype, shapes, workspace)
+    wp, wb, _keep = _workspace(device, dtype, shapes, workspace, precision)
     a, b, c = coeffs
-    _check(lib().muon_step_batched(arr, n, _dt(dtype), mu, lr, ns_steps, a, b, c, eps,
-                                   wp, wb, _stream_ptr(device, stream)))
+    _check(lib().muon_step_batched(arr, n, _dt(dtype, precision), mu, lr, ns_steps, a, b, c,
+                                   eps, wp, wb, _stream_ptr(device, stream)))
 
 
 def muon_step_batched_wd(weights, grads, moms, mu=0.5, lr=1e-3, wd=1e-2, ns_steps=2,
-                         coeffs=NS_COEFFS, eps=1e-7, workspace=None, stream=None):
+                         coeffs=NS_COEFFS, eps=1e-7, workspace=None, stream=None,
+                         precision="default"):
     """The Muon step with decoupled weight decay, W <- W - lr*(wd*W + s*O); the
     defaults are the MatrixFSDP paper's training configuration (section 5.1)."""
     arr, n, dtype = _mats(weights, grads, moms)
@@ -230,14 +239,14 @@ def muon_step_batched_wd(weights, grads, moms, mu=0.5, lr=1e-3, wd=1e-2, ns_step
         return
     device = weights[0].device
     shapes = [tuple(w.shape) for w in weights]
-    wp, wb, _keep = _workspace(device, dtype, shapes, workspace)
+    wp, wb, _keep = _workspace(device, dtype, shapes, workspace, precision)
     a, b, c = coeffs
-    _check(lib().muon_step_batched_wd(arr, n, _dt(dtype), mu, lr, wd, ns_steps, a, b, c,
-                                      eps, wp, wb, _stream_ptr(device, stream)))
+    _check(lib().muon_step_batched_wd(arr, n, _dt(dtype, precision), mu, lr, wd, ns_steps, a, b,
+                                      c, eps, wp, wb, _stream_ptr(device, stream)))
 
 
 def muon_step_batched_noalloc(weights, grads, moms, mu=0.95, lr=0.02, ns_steps=5,
-                              coeffs=NS_COEFFS, eps=1e-7, stream=None):
+                              coeffs=NS_COEFFS, eps=1e-7, stream=None, precision="default"):
     """The Muon step without a workspace and without any allocation: the
     library's per-GPU device scratch array (MATOPT_NOALLOC_SCRATCH_BYTES) holds
     workspace and tables; shape lists that do not fit raise MatoptError
@@ -247,8 +256,8 @@ def muon_step_batched_noalloc(weights, grads, moms, mu=0.95, lr=0.02, ns_steps=5
         return
     device = weights[0].device
     a, b, c = coeffs
-    _check(lib().muon_step_batched_noalloc(arr, n, _dt(dtype), mu, lr, ns_steps, a, b, c, eps,
-                                           _stream_ptr(device, stream)))
+    _check(lib().muon_step_batched_noalloc(arr, n, _dt(dtype, precision), mu, lr, ns_steps, a, b,
+                                           c, eps, _stream_ptr(device, stream)))
 
 
 def rmnp_step_batched(weights, grads, moms, mu=0.95, lr=0.02, eps=1e-12, stream=None):
@@ -345,8 +354,10 @@ def adamw_step_batched(params, grads, exp_avgs, exp_avg_sqs, step, lr=1e-3, beta
 
 
 def ns_orthogonalize_batched(xs, out_dtype=torch.float32, ns_steps=5, coeffs=NS_COEFFS,
-                             eps=1e-7, outs=None, workspace=None, stream=None):
-    """Newton-Schulz only: returns (or fills ``outs`` with) O for every x."""
+                             eps=1e-7, outs=None, workspace=None, stream=None,
+                             precision="default"):
+    """Newton-Schulz only: returns (or fills ``outs`` with) O for every x.
+    precision="split" (bfloat16 inputs only): the split-precision iterate."""
     n = len(xs)
     if n == 0:
         return []
@@ -361,13 +372,14 @@ def ns_orthogonalize_batched(xs, out_dtype=torch.float32, ns_steps=5, coeffs=NS_
         if o.shape != x.shape:
             raise ValueError(f"outs[{i}] shape differs from xs[{i}]")
     shapes = [tuple(x.shape) for x in xs]
-    wp, wb, _keep = _workspace(device, in_dtype, shapes, workspace)
+    wp, wb, _keep = _workspace(device, in_dtype, shapes, workspace, precision)
     xp = (_vp * n)(*[x.data_ptr() for x in xs])
     op = (_vp * n)(*[o.data_ptr() for o in outs])
     rows = (_i64 * n)(*[s[0] for s in shapes])
     cols = (_i64 * n)(*[s[1] for s in shapes])
     a, b, c = coeffs
-    _check(lib().ns_orthogonalize_batched(xp, op, rows, cols, n, _dt(in_dtype), _dt(out_dtype),
+    _check(lib().ns_orthogonalize_batched(xp, op, rows, cols, n, _dt(in_dtype, precision),
+                                          _dt(out_dtype),
                                           ns_steps, a, b, c, eps, wp, wb,
                                           _stream_ptr(device, stream)))
     return outs

@@ -85,6 +85,10 @@ struct GemmParams {
   int32_t first;      // first iteration: fold the Frobenius scale in
   int32_t out_kind;   // OutKind (stage 2)
   int32_t out_dt;     // dtype of O for OUT_O
+  // split precision (bf16 path): the polynomial stores B whole, every apply
+  // but the last stores its iterate as bf16 hi over bf16 lo (2 mp x np), and
+  // the applies after the first run K over both parts
+  int32_t split;
   float a, b, c, lr;
   double wdl;         // lr * weight decay (exact product), 0: no decay
   // profiling only (else NULL): [0] += shader-clock ticks, [1] += 100 MHz

@@ -80,8 +80,12 @@ matopt_status check_device(int* dev_out) {
 // ---------------------------------------------------------------- geometry
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-int esize(int dt) { return dt == DT_BF16 ? 2 : 4; }
-int gemm_tile(int dt) { return dt == DT_BF16 ? kTileBf16 : kTileF32; }
+// Compute modes of the Newton-Schulz entry points beyond the storage dtypes:
+// bf16 storage with the split-precision iterate (MATOPT_BF16_SPLIT).
+constexpr int DT_BF16_SPLIT = 2;
+int sdt(int dt) { return dt == DT_BF16_SPLIT ? DT_BF16 : dt; }   // storage dtype
+int esize(int dt) { return sdt(dt) == DT_BF16 ? 2 : 4; }
+int gemm_tile(int dt) { return sdt(dt) == DT_BF16 ? kTileBf16 : kTileF32; }
 
 struct Geo {
   int64_t rows, cols;
@@ -121,8 +125,10 @@ Layout layout(const std::vector<Geo>& geo, int dt) {
   Layout L;
   const size_t es = esize(dt);
   size_t off = 0;
+  // split precision: each iterate buffer holds the bf16 high part over the low part
+  const size_t xparts = dt == DT_BF16_SPLIT ? 2 : 1;
   for (const Geo& g : geo) {
-    const size_t xb = align256((size_t)g.mp * g.np * es);
+    const size_t xb = align256((size_t)g.mp * g.np * es * xparts);
     const size_t ab = align256((size_t)g.mp * g.mp * es);
     L.x0.push_back(off); off += xb;
     L.x1.push_back(off); off += xb;
@@ -464,7 +470,7 @@ matopt_status build_ns_plan(Plan& P, int dt, const std::vector<Geo>& geo) {
     d.x[1] = as_off<void*>(L.x1[i]);
     // X0 is the stored V; when V has X0's layout the first iteration reads it
     // in place and the prep kernel skips the copy (bind sets x0in)
-    d.x0_is_v = (dt == DT_BF16 && !g.transposed && g.rows == g.mp && g.cols == g.np) ? 1 : 0;
+    d.x0_is_v = (sdt(dt) == DT_BF16 && !g.transposed && g.rows == g.mp && g.cols == g.np) ? 1 : 0;
     d.a = as_off<void*>(L.a[i]);
     d.b = as_off<void*>(L.b[i]);
     d.xs = as_off<float*>(L.xs + 4 * (size_t)i);
@@ -477,8 +483,8 @@ matopt_status build_ns_plan(Plan& P, int dt, const std::vector<Geo>& geo) {
     // diagonal tiles as the GEMM build treats them (bf16: 36 of their 64
     // blocks; the Gram's two per workgroup, in step with the matrix's other
     // tiles, which share their operand panels through L2)
-    const int dm3 = dt == DT_BF16 ? gemm_bf16_diag_mode(0) : 0;
-    const int dm4 = dt == DT_BF16 ? gemm_bf16_diag_mode(1) : 0;
+    const int dm3 = sdt(dt) == DT_BF16 ? gemm_bf16_diag_mode(0) : 0;
+    const int dm4 = sdt(dt) == DT_BF16 ? gemm_bf16_diag_mode(1) : 0;
     units_triangle(i, tm, g.np, u3, dm3 ? 9 : 16, dm3 == 2);
     units_triangle(i, tm, g.mp, u4, dm4 ? 9 : 16, dm4 == 2);
     units_full(i, tm, tn, g.mp, u5);
@@ -568,6 +574,8 @@ matopt_status run_ns(const NsTables& P, const MatDesc* mats, int dt, bool moment
                      float lr, double wdl, int ns_steps, float a, float b, float c, float eps,
                      int out_kind, int out_dt, hipStream_t s) {
   hipError_t e;
+  const bool split = dt == DT_BF16_SPLIT;
+  dt = sdt(dt);
   const PrepTile* prep = P.dev<const PrepTile>(P.o_prep);
   PrepParams pp{mats, prep, mu, momentum ? 1 : 0};
   e = timed(0, s, [&] { return launch_prep(dt, pp, P.n_prep, s); });
@@ -592,6 +600,7 @@ matopt_status run_ns(const NsTables& P, const MatDesc* mats, int dt, bool moment
     g.c = c;
     g.lr = lr;
     g.wdl = wdl;
+    g.split = split ? 1 : 0;
     g.stage = 0;
     g.out_kind = OUT_NEXT_X;
     g.clk = dt == DT_BF16 ? prof_clk(2) : nullptr;
@@ -640,9 +649,12 @@ matopt_status ns_call(int dt, const std::vector<Geo>& geo, const std::vector<Bin
                 eps, out_kind, out_dt, s);
 }
 
-matopt_status check_common(int32_t count, int dt) {
+matopt_status check_common(int32_t count, int dt, bool ns_entry = false) {
   if (count < 0) return fail(MATOPT_ERR_PARAM, "count < 0");
-  if (dt != DT_F32 && dt != DT_BF16) return fail(MATOPT_ERR_DTYPE, "dtype must be MATOPT_F32 or MATOPT_BF16");
+  if (ns_entry && dt == DT_BF16_SPLIT) return MATOPT_OK;
+  if (dt != DT_F32 && dt != DT_BF16)
+    return fail(MATOPT_ERR_DTYPE, ns_entry ? "dtype must be MATOPT_F32, MATOPT_BF16 or MATOPT_BF16_SPLIT"
+                                           : "dtype must be MATOPT_F32 or MATOPT_BF16");
   return MATOPT_OK;
 }
 
@@ -820,7 +832,7 @@ const char* matopt_last_error_detail(void) { return g_detail.c_str(); }
 size_t matopt_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count,
                               matopt_dtype dt) {
   if (count < 0 || (count > 0 && (!rows || !cols))) return 0;
-  if (dt != MATOPT_F32 && dt != MATOPT_BF16) return 0;
+  if (dt != MATOPT_F32 && dt != MATOPT_BF16 && dt != DT_BF16_SPLIT) return 0;
   std::vector<Geo> geo;
   for (int i = 0; i < count; ++i) {
     if (check_shape(rows[i], cols[i], i) != MATOPT_OK) return 0;
@@ -836,7 +848,7 @@ static matopt_status muon_impl(const matopt_mat* mats, int32_t count, matopt_dty
                                float mu, float lr, float wd, int32_t ns_steps, float a,
                                float b, float c, float eps, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  matopt_status st = check_common(count, dt);
+  matopt_status st = check_common(count, dt, true);
   if (st != MATOPT_OK) return st;
   if (count == 0) return MATOPT_OK;
   if (!mats) return fail(MATOPT_ERR_NULL, "mats is NULL");
@@ -866,7 +878,7 @@ static matopt_status muon_impl(const matopt_mat* mats, int32_t count, matopt_dty
   if ((st = check_device(&dev)) != MATOPT_OK) return st;
   const double wdl = (double)lr * (double)wd;   // exact: a product of two floats
   return ns_call(dt, geo, ptrs, workspace, dev, (hipStream_t)stream, true, mu, lr, wdl, ns_steps,
-                 a, b, c, eps, OUT_W_UPDATE, dt);
+                 a, b, c, eps, OUT_W_UPDATE, sdt(dt));
 }
 
 // ------------------------------------------------------ allocation-free step
@@ -937,7 +949,7 @@ extern "C" {
 matopt_status muon_step_batched_noalloc(const matopt_mat* mats, int32_t count, matopt_dtype dt,
                                         float mu, float lr, int32_t ns_steps, float a, float b,
                                         float c, float eps, void* stream) {
-  matopt_status st = check_common(count, dt);
+  matopt_status st = check_common(count, dt, true);
   if (st != MATOPT_OK) return st;
   if (count == 0) return MATOPT_OK;
   if (!mats) return fail(MATOPT_ERR_NULL, "mats is NULL");
@@ -985,7 +997,7 @@ matopt_status muon_step_batched_noalloc(const matopt_mat* mats, int32_t count, m
       MATOPT_OK)
     return st;
   return run_ns(NsTables(plan, tables), descs, dt, true, mu, lr, 0.0, ns_steps, a, b, c, eps,
-                OUT_W_UPDATE, dt, s);
+                OUT_W_UPDATE, sdt(dt), s);
 }
 
 }  // extern "C"
@@ -1013,7 +1025,7 @@ matopt_status ns_orthogonalize_batched(const void* const* x, void* const* o, con
                                        matopt_dtype out_dt, int32_t ns_steps, float a, float b,
                                        float c, float eps, void* workspace, size_t workspace_bytes,
                                        void* stream) {
-  matopt_status st = check_common(count, in_dt);
+  matopt_status st = check_common(count, in_dt, true);
   if (st != MATOPT_OK) return st;
   if (out_dt != MATOPT_F32 && out_dt != MATOPT_BF16) return fail(MATOPT_ERR_DTYPE, "invalid out_dt");
   if (count == 0) return MATOPT_OK;

@@ -181,6 +181,8 @@ struct OperandDma {
   uint32_t off_km0;     // lane offset of k-major blocks with b even
   uint32_t off_km1;     // lane offset of k-major blocks with b odd
   int t_km;             // steps t < t_km are k-major
+  int t_wrap;           // step t reads K step t - t_wrap from t_wrap on (the
+                        // split-precision apply reads B twice)
 
   // Plain: src is a row-major matrix with ld elements per row.  Blocked: src
   // is an iterate X stored in 32 x 32 blocks (2 KB each, row-major inside,
@@ -190,6 +192,7 @@ struct OperandDma {
   __device__ void init(const uint16_t* src, int64_t ld, int r0, int tkm, int lane,
                        bool blocked = false) {
     t_km = tkm;
+    t_wrap = 1 << 30;
     if (!blocked) {
       rs = (uint32_t)(ld * 2);
       us = 64u;
@@ -224,6 +227,7 @@ struct OperandDma {
   template <int Q, int BPW>
   __device__ __forceinline__ void block(bool km, int t, uint8_t* tile, int wave) const {
     const int b = BPW * wave + Q;   // parity of b is that of Q (BPW is even)
+    t = t >= t_wrap ? t - t_wrap : t;   // uniform
     const char* base = km ? org_km + t * km_t + 2 * b * (int64_t)rs
                           : org_rm + (b >> 1) * rm_b2 + (b & 1) * rm_b1 + t * rm_t;   // uniform
     const uint32_t kmoff = (Q & 1) ? off_km1 : off_km0;
@@ -572,6 +576,31 @@ __device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][NBJ], ui
     }
 }
 
+// The split-precision iterate (GemmParams::split): the high part bf16(v) as
+// store_acc_direct writes it, and the low part bf16(v - bf16(v)) -- v - bf16(v)
+// is exact in float32 -- at the same position of the matrix stacked below
+// (lo_off elements further on), so that hi + lo carries about 16 bits.
+template <int NBJ>
+__device__ __forceinline__ void store_acc_direct_split(const f32x16 (&acc)[4][NBJ], uint16_t* out,
+                                                       int64_t ld, int64_t i0, int64_t j0,
+                                                       int lane, float s, int64_t lo_off) {
+  const int64_t nb = ld / 32;
+  uint16_t* base = out + ((i0 >> 5) * nb + (j0 >> 5)) * 1024 + (lane & 31) * 32 + 8 * (lane >> 5);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NBJ; ++bj) {
+      float v[16], lo[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        v[r] = s * acc[bi][bj][r];
+        lo[r] = v[r] - bf2f(f2bf(v[r]));
+      }
+      store_block_direct(v, base + (bi * nb + bj) * 1024);
+      store_block_direct(lo, base + lo_off + (bi * nb + bj) * 1024);
+    }
+}
+
 // The polynomial's epilogue, straight from the accumulators as well (B has no
 // mirror): B = a I + b A + c (A A) with the A values read at the lanes' own
 // accumulator positions (8 bytes per register group), one 32-row stripe of
@@ -633,7 +662,7 @@ __device__ __forceinline__ void poly_store_direct(const f32x16 (&acc)[4][NBJ], u
 // of 8 consecutive columns (16-byte stores) per lane.  The polynomial's epilogue input (the A tile
 // of the same position) is prefetched one stripe ahead; Gram and apply read
 // nothing back.
-template <int STAGE, int OUT, int NBJ>
+template <int STAGE, int OUT, int NBJ, bool MIRROR = false>
 __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          const f32x16 (&acc)[4][NBJ], float* stg,
                                          const uint16_t* ep_src, int64_t ep_ld, uint16_t* out,
@@ -696,6 +725,27 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
         gstore<u32x4>(blk_at(out, ib + rr, j0 + c8, ld_out),
                       u32x4{pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y),
                             pack_bf2(a1.z, a1.w)});
+        if (MIRROR) {   // the mirror pass reads the final values (each lane its own items)
+          *(f32x4*)src = a0;
+          *(f32x4*)(src + 4) = a1;
+        }
+      }
+      if (MIRROR) {
+        // B stored whole (split precision): the stripe transposed into the
+        // mirror tile -- row j0 + jj, columns ib + 8 ic .. +7 (four lanes per
+        // row, as the transposed final pass reads the staging)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < G::IPL; ++p) {
+          const int q = lane + 64 * p;
+          const int ic = q & 3, jj = q >> 2;
+          float vv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vv[e] = stg[G::row(8 * ic + e) + jj];
+          gstore<u32x4>(blk_at(out, j0 + jj, ib + 8 * ic, ld_out),
+                        u32x4{pack_bf2(vv[0], vv[1]), pack_bf2(vv[2], vv[3]),
+                              pack_bf2(vv[4], vv[5]), pack_bf2(vv[6], vv[7])});
+        }
       }
     }
     if (OUT != OUT_NEXT_X) {
@@ -1462,7 +1512,7 @@ __device__ __forceinline__ void diag_pair(const MatDesc& d, const GemmParams& P,
 // the DMA of a step is spread over all eight waves (two 1 KB blocks per
 // operand each).  NW = 4 (four waves of 128 x 128, one per SIMD) remains a
 // build-time alternative (MATOPT_*_WAVES).
-template <int STAGE, int OUT, int NW>
+template <int STAGE, int OUT, int NW, bool MIR>
 __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
   static_assert(NW == 4 || NW == 8, "layout");
   constexpr int NBJ = NW == 4 ? 4 : 2;   // 32-column blocks per wave
@@ -1493,11 +1543,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
   if (i0 < 0 || i0 + BM > mp || j0 + BM > (STAGE == 2 ? np : mp) || (pair && STAGE == 2)) return;
   const uint16_t* xcur = (const uint16_t*)(P.first ? d.x0in : P.cur ? d.x[1] : d.x[0]);
   uint16_t* xnext = (uint16_t*)(P.cur ? d.x[0] : d.x[1]);
+  // split precision, apply after the first iteration: Q runs over the stacked
+  // [hi; lo] iterate (K = 2 mp) and P over B twice (B is stored whole then)
+  const bool ksplit = STAGE == 2 && P.split && !P.first;
   // K is a multiple of 256, so nk >= 8 > NS - 1
-  const int nk = (int)(STAGE == 0 ? np : mp) / BK;
-  // polynomial and apply: P is k-major for steps t < bP; polynomial: Q for
-  // steps t < bQ (bP <= bQ <= nk - 8)
-  const int bP = STAGE == 0 ? 0 : i0 / BK;
+  const int nk = (int)(STAGE == 0 ? np : ksplit ? 2 * mp : mp) / BK;
+  // polynomial and apply: P is k-major for steps t < bP (never for the
+  // split-precision apply: B whole); polynomial: Q for steps t < bQ
+  // (bP <= bQ <= nk - 8)
+  const int bP = STAGE == 0 || (STAGE == 2 && P.split) ? 0 : i0 / BK;
   const int bQ = STAGE == 1 ? j0 / BK : 0;
 
   const int lane = threadIdx.x & 63;
@@ -1515,6 +1569,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
     dq.init((const uint16_t*)d.a, mp, j0, bQ, lane, true);
   } else {
     dp.init((const uint16_t*)d.b, mp, i0, bP, lane, true);
+    if (ksplit) dp.t_wrap = (int)(mp / BK);
     dq.init(xcur, np, j0, nk, lane, xblk);
   }
 
@@ -1567,19 +1622,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
   u32x4 ecur[Ep<WN>::IPL];
   u32x2 afirst[NBJ][4];
   mfma16<NBJ>(k.acc, k.pa, k.qa);
-  if (STAGE == 1 && NW == 8)
+  if (STAGE == 1 && NW == 8 && !MIR)
     poly_a_stripe<NBJ>((const uint16_t*)d.a, mp, i0 + g.wi0, j0 + g.wj0, lane, afirst);
   else if (STAGE == 1)
     prefetch_stripe<WN>(ep_src, ep_ld, i0 + g.wi0, j0 + g.wj0, lane, ecur);
   mfma16<NBJ>(k.acc, k.pb, k.qb);
-  if (STAGE == 1 && NW == 8) {
+  if (STAGE == 1 && NW == 8 && !MIR) {
     poly_store_direct<NBJ>(k.acc, (uint16_t*)d.b, (const uint16_t*)d.a, mp, i0 + g.wi0, j0 + g.wj0,
                            lane, P.a, P.b, P.c, afirst);
     return;
   }
   if (STAGE == 2 && OUT == OUT_NEXT_X) {
     const float s_first = P.first ? gload<float>(d.xs) : 1.f;
-    store_acc_direct<NBJ>(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first);
+    if (P.split)
+      store_acc_direct_split<NBJ>(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first,
+                                  (int64_t)mp * np);
+    else
+      store_acc_direct<NBJ>(k.acc, xnext, np, i0 + g.wi0, j0 + g.wj0, lane, s_first);
     return;
   }
   if (STAGE == 0) {   // an upper tile of A, scaled by s^2 on the first iteration
@@ -1596,17 +1655,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
   uint16_t* out = STAGE == 1 ? (uint16_t*)d.b : xnext;
   const int64_t ld_out = STAGE == 2 ? np : mp;
   const float s_first = P.first ? gload<float>(d.xs) : 1.f;
-  epilogue<STAGE, OUT, NBJ>(d, P, k.acc, (float*)(lds + wave * Ep<WN>::WAVE_BYTES), ep_src, ep_ld, out,
+  epilogue<STAGE, OUT, NBJ, MIR>(d, P, k.acc, (float*)(lds + wave * Ep<WN>::WAVE_BYTES), ep_src, ep_ld, out,
                        ld_out, i0 + g.wi0, j0 + g.wj0, lane, g.frow, g.fkc, s_first,
                        ecur);
   }
 }
 
-// The kernel: one tile per workgroup.  With P.clk set (profiling only), the
+// The kernel: one tile per workgroup (MIR: the polynomial also writes B's
+// mirror tiles, for the split-precision apply).  With P.clk set (profiling only), the
 // first lane of each workgroup also adds the shader-clock ticks (s_memtime)
 // and the 100 MHz real-time ticks (s_memrealtime) that its tile took to
 // P.clk[0] and P.clk[1] -- their ratio is the clock the tiles ran at.
-template <int STAGE, int OUT, int NW>
+template <int STAGE, int OUT, int NW, bool MIR = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void ns_gemm_bf16_kernel(GemmParams P) {
@@ -1617,7 +1677,7 @@ void ns_gemm_bf16_kernel(GemmParams P) {
     t0 = __builtin_amdgcn_s_memtime();
     r0 = __builtin_amdgcn_s_memrealtime();
   }
-  gemm_tile<STAGE, OUT, NW>(P, lds);
+  gemm_tile<STAGE, OUT, NW, MIR>(P, lds);
   if (clk && threadIdx.x == 0) {
     const uint64_t t1 = __builtin_amdgcn_s_memtime();
     const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
@@ -1659,6 +1719,8 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s) {
   const dim3 grid(n_tiles);
   if (p.stage == 0)
     hipLaunchKernelGGL((ns_gemm_bf16_kernel<0, OUT_NEXT_X, GW>), grid, dim3(64 * GW), 0, s, p);
+  else if (p.stage == 1 && p.split)
+    hipLaunchKernelGGL((ns_gemm_bf16_kernel<1, OUT_NEXT_X, PW, true>), grid, dim3(64 * PW), 0, s, p);
   else if (p.stage == 1)
     hipLaunchKernelGGL((ns_gemm_bf16_kernel<1, OUT_NEXT_X, PW>), grid, dim3(64 * PW), 0, s, p);
   else if (p.out_kind == OUT_NEXT_X)

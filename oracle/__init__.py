@@ -42,6 +42,7 @@ from .muon import (  # noqa: F401
     ns_orthogonalize,
     ns_orthogonalize_page_form,
     ns_orthogonalize_page_bf16,
+    split_bf16,
     muon_step,
     rmnp_direction,
     rmnp_step,

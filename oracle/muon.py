@@ -59,6 +59,9 @@ notes with its reason):
   ``1/(||V||+eps)`` is carried as an exact factor into the first iteration's
   products instead of being rounded into a bf16 copy of V.  All accumulation
   stays float64.  ``rounding="exact"`` rounds nothing.
+* ``rounding="bf16_split"`` is the same model with each iterate after the first
+  kept as a bf16 high part plus a bf16 low part (``split_bf16``): the Gram
+  reads the high part alone, the product ``B X`` both parts.
 
 Parity status
 -------------
@@ -117,6 +120,13 @@ def round_storage(x, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown storage dtype {dtype!r}")
 
 
+def split_bf16(x) -> np.ndarray:
+    """``hi + lo`` with ``hi`` the nearest bfloat16 of each entry and ``lo`` the
+    nearest bfloat16 of ``x - hi``: about 16 significant bits."""
+    hi = round_bf16(x)
+    return hi + round_bf16(_f64(x) - hi)
+
+
 def momentum(v, g, mu: float, dtype: str) -> np.ndarray:
     """Heavy-ball momentum ``V_t = mu V_{t-1} + G_t`` (blog post, section 1),
     rounded once to the storage dtype."""
@@ -146,9 +156,10 @@ def ns_orthogonalize(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
     4. Transpose back.
 
     ``rounding="bf16"`` applies the bf16 storage model described in the module
-    header; the returned matrix (the last iterate) is never rounded.
+    header, ``rounding="bf16_split"`` its split-iterate variant; the returned
+    matrix (the last iterate) is never rounded.
     """
-    if rounding not in ("exact", "bf16"):
+    if rounding not in ("exact", "bf16", "bf16_split"):
         raise ValueError(rounding)
     a, b, c = (f32_param(t) for t in coeffs)
     x = _f64(x)
@@ -162,14 +173,19 @@ def ns_orthogonalize(x, steps: int = NS_STEPS, coeffs=NS_COEFFS,
     else:
         s = scale  # carried exactly into the first iteration's products
     eye = np.eye(X.shape[0])
+    rounded = rounding != "exact"
     for k in range(steps):
-        A = (s * s) * (X @ X.T)
-        if rounding == "bf16":
+        Xg = Xb = X
+        if rounding == "bf16_split" and k > 0:   # the stored iterate: hi, and hi + lo
+            Xg = round_bf16(X)
+            Xb = split_bf16(X)
+        A = (s * s) * (Xg @ Xg.T)
+        if rounded:
             A = round_bf16(A)
         B = a * eye + b * A + c * (A @ A)
-        if rounding == "bf16":
+        if rounded:
             B = round_bf16(B)
-        Xn = s * (B @ X)
+        Xn = s * (B @ Xb)
         if rounding == "bf16" and k < steps - 1:
             Xn = round_bf16(Xn)
         X = Xn

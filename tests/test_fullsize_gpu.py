@@ -9,12 +9,13 @@ oracle on the GPU's own updated momentum:
 * O (read out in float32) against the oracle's bf16 storage model and against
   the exact iteration, relative Frobenius error <= 2e-2 for both on the
   Gaussian sets and the sweep;
-* on the ill-conditioned set the exact iteration is out of reach of any bf16
-  path: there O must be within 2e-2 of the storage model and, against the
+* on the ill-conditioned set the exact iteration is out of reach of bf16
+  iterates: there O must be within 2e-2 of the storage model and, against the
   exact iteration, no farther than the appendix routine in its own bf16
   precision (oracle.ns_orthogonalize_page_bf16) on the same input, which is
   computed for every matrix with min side <= 1024; the exact error is
-  printed either way;
+  printed either way -- and the split-precision path (bf16 hi + lo iterates)
+  is then held to 2e-2 against the exact iteration on every shape of the set;
 * stored momentum bit-exact and weights within 1 ulp of
   round(W_old - lr*sqrt(max(1,r/c))*O_gpu) on sampled rows;
 * the singular values of O inside the band the coefficients imply.
@@ -84,14 +85,15 @@ def _log(msg):
 
 
 class _SetCache:
-    """GPU results of one whole set at a time (the cases are grouped by set)."""
+    """GPU results of one whole set at a time (the cases are grouped by set),
+    in the default or the split precision."""
 
     def __init__(self):
-        self.name = None
+        self.key = None
         self.data = None
 
-    def get(self, mo, name):
-        if self.name != name:
+    def get(self, mo, name, precision="default"):
+        if self.key != (name, precision):
             self.data = None
             torch.cuda.empty_cache()
             wl = _workload(name)
@@ -100,15 +102,19 @@ class _SetCache:
             W = [t[0].cuda() for t in trip]
             V = [t[1].cuda() for t in trip]
             G = [t[2].cuda() for t in trip]
-            mo.muon_step_batched(W, G, V, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps)
-            O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32)
+            mo.muon_step_batched(W, G, V, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps,
+                                 precision=precision)
+            O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, precision=precision)
             torch.cuda.synchronize()
-            _log(f"[{name}] step and Newton-Schulz done on the GPU")
-            self.name, self.data = name, (wl, trip, W, V, G, O)
+            _log(f"[{name}] step and Newton-Schulz ({precision} precision) done on the GPU")
+            self.key, self.data = (name, precision), (wl, trip, W, V, G, O)
         return self.data
 
 
 _cache = _SetCache()
+# exact-iteration results of the ill-conditioned set (float32 copies), computed
+# by the default-precision cases and reused by the split-precision ones
+_exact_illcond = {}
 
 
 def _sample_rows(rows, n=8, seed=0):
@@ -156,6 +162,8 @@ def test_fullsize_o_elementwise(mo, case):
     exact = oracle.ns_orthogonalize(v)
     e_exact = relF(o, exact)
     gaussian = wl.kind == "gaussian"
+    if not gaussian:
+        _exact_illcond[i] = exact.astype(np.float32)
     msg = f"[{name}] {r}x{c}: relF(O) vs bf16 model {e_model:.2e}, vs exact {e_exact:.2e}"
     e_page = None
     if not gaussian and min(r, c) <= PAGE_BF16_MAX_M:
@@ -178,10 +186,35 @@ def test_fullsize_o_elementwise(mo, case):
         assert torch.equal(alone, O[i])
 
 
+SPLIT_CASES = [i for i in _distinct(workloads.get("ragged_illcond_64").shapes)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("i", SPLIT_CASES, ids=[
+    "ragged_illcond_64-%dx%d" % workloads.get("ragged_illcond_64").shapes[i] for i in SPLIT_CASES])
+def test_fullsize_split_precision_illcond(mo, i):
+    """The split-precision path on the whole ill-conditioned set: every
+    distinct shape within 2e-2 of the exact iteration (the bf16 path's
+    tolerance, which bf16 iterates miss on these spectra), V bit-exact and W
+    within 1 ulp of the single rounding with the split path's own O."""
+    wl, trip, W, V, G, O = _cache.get(mo, "ragged_illcond_64", precision="split")
+    r, c = wl.shapes[i]
+    w0, v0, g0 = trip[i]
+    rows = _sample_rows(r, seed=i)
+    _check_v_rows(V[i], v0, g0, wl.mu, rows)
+    _check_w_rows(W[i], w0, O[i], wl.lr, rows)
+    v = f64(V[i])
+    exact = _exact_illcond.get(i)
+    exact = oracle.ns_orthogonalize(v) if exact is None else exact.astype(np.float64)
+    e_exact = relF(f64(O[i]), exact)
+    _log(f"[ragged_illcond_64 split] {r}x{c}: relF(O) vs exact {e_exact:.2e}")
+    assert e_exact <= 2e-2
+
+
 @pytest.mark.parametrize("name", ["gpt2_large_144", "qwen32b_share_14"])
 def test_rmnp_full_set_sampled_rows(mo, name):
     _cache.data = None
-    _cache.name = None
+    _cache.key = None
     wl = workloads.get(name)
     _log(f"[rmnp {name}] generating")
     trip = workloads.workload_inputs(wl)

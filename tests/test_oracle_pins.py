@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from oracle import (NS_COEFFS, f32_param, momentum, ns_orthogonalize,
-                    ns_orthogonalize_page_form, ns_orthogonalize_page_bf16, muon_step, rmnp_direction,
+                    ns_orthogonalize_page_form, ns_orthogonalize_page_bf16, split_bf16, muon_step, rmnp_direction,
                     rmnp_step, round_bf16, round_storage)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -234,6 +234,47 @@ def test_page_bf16_model_matches_torch_bf16_arithmetic(shape):
     d_mine, d_ref = relF(mine, exact), relF(ref, exact)
     assert 1e-2 <= d_mine <= 5e-2 and 1e-2 <= d_ref <= 5e-2
     assert relF(mine, ref) <= 0.35 * min(d_mine, d_ref)
+
+
+def test_split_bf16_carries_sixteen_bits():
+    """hi + lo reproduces every value of at most 15 significant bits exactly,
+    and any value within 2^-17 of its magnitude (hi is off by at most 2^-9,
+    lo by 2^-9 of that)."""
+    rng = np.random.default_rng(43)
+    m = rng.integers(-(2 ** 15) + 1, 2 ** 15, 20000).astype(np.float64)
+    x = np.ldexp(m, rng.integers(-40, 10, m.size))
+    assert np.array_equal(split_bf16(x), x)
+    y = rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))
+    assert (np.abs(split_bf16(y) - y) <= 2.0 ** -17 * np.abs(y)).all()
+    assert (round_bf16(y) != y).mean() > 0.99   # the high part alone is not enough
+
+
+def _illconditioned(rng, m, n, lo=1e-4):
+    """U diag(s) V^T with orthonormal U, V (QR of Gaussians) and singular values
+    log-uniform in [lo, 1]."""
+    k = min(m, n)
+    u = np.linalg.qr(rng.standard_normal((m, k)))[0]
+    v = np.linalg.qr(rng.standard_normal((n, k)))[0]
+    s = np.exp(rng.uniform(np.log(lo), 0.0, k))
+    return (u * s) @ v.T
+
+
+@pytest.mark.parametrize("shape", [(64, 128), (128, 96), (48, 48)])
+def test_split_model_reaches_exact_tolerance_where_bf16_cannot(shape):
+    """On ill-conditioned inputs the bf16 storage model lies several 1e-2 from
+    the exact iteration (pinned by the SVD closed form); carrying the iterate
+    as hi + lo into the products with X brings it within 2e-2 -- a dropped low
+    part would leave it at the bf16 level."""
+    rng = np.random.default_rng(47)
+    x = _illconditioned(rng, *shape)
+    exact = ns_orthogonalize(x)
+    e_bf16 = relF(ns_orthogonalize(x, rounding="bf16"), exact)
+    e_split = relF(ns_orthogonalize(x, rounding="bf16_split"), exact)
+    assert e_bf16 >= 2.5e-2
+    assert e_split <= 1.5e-2
+    # one step has no stored iterate yet: the split model is the bf16 model
+    assert np.array_equal(ns_orthogonalize(x, steps=1, rounding="bf16_split"),
+                          ns_orthogonalize(x, steps=1, rounding="bf16"))
 
 
 def test_ns_transpose_equivariance():

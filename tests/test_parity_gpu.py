@@ -125,6 +125,59 @@ def test_ns_bf16_ragged_batch(mo):
             assert ee <= 2e-2, f"{shape}: {ee:.3e} against the exact iteration"
 
 
+def _illcond_small():
+    """The ill-conditioned set's matrices with max side <= 512 (singular values
+    log-uniform in [1e-4, 1]) and their stored momenta."""
+    wl = workloads.get("ragged_illcond_64")
+    idx = [i for i, s in enumerate(wl.shapes) if max(s) <= 512]
+    trip = workloads.workload_inputs(wl, idx)
+    return [wl.shapes[i] for i in idx], [t[2].to("cuda") for t in trip]
+
+
+def test_ns_split_precision_meets_exact_tolerance(mo):
+    """The split-precision path (precision="split") against the exact
+    iteration at the bf16 path's tolerance, 2e-2, on every shape -- the
+    ill-conditioned 8x8 draw and the ill-conditioned set included -- and
+    against its own storage model."""
+    wl = workloads.small_case("ns_bf16", BF16_SHAPES, seed=11, v_std=1.0, g_std=1.0)
+    _, V, _ = _inputs(wl)
+    shapes_ic, V_ic = _illcond_small()
+    shapes = list(BF16_SHAPES) + shapes_ic
+    O = mo.ns_orthogonalize_batched(V + V_ic, out_dtype=torch.float32, precision="split")
+    O_plain = mo.ns_orthogonalize_batched(V + V_ic, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for shape, v, o, op in zip(shapes, V + V_ic, O, O_plain):
+        x = f64(v)
+        exact = oracle.ns_orthogonalize(x)
+        ee = relF(f64(o), exact)
+        em = relF(f64(o), oracle.ns_orthogonalize(x, rounding="bf16_split"))
+        ep = relF(f64(op), exact)
+        print(f"{shape}: split vs exact {ee:.2e} (plain bf16 {ep:.2e}), vs split model {em:.2e}",
+              flush=True)
+        assert ee <= 2e-2, f"{shape}: {ee:.3e} against the exact iteration"
+        assert em <= 2e-2
+        worst = max(worst, ee)
+    print(f"worst split-precision error against the exact iteration: {worst:.2e}", flush=True)
+
+
+def test_muon_step_split_precision(mo):
+    """The Muon step in split precision: momentum bit-exact, the update a single
+    rounding of W - lr*s*O with O the split path's own direction, O within 2e-2
+    of the exact iteration."""
+    shapes = [(700, 1300), (1300, 700), (256, 256), (37, 45), (1, 300), (300, 1)]
+    wl = workloads.small_case("muon_split", shapes, seed=27)
+    W, V, G = _inputs(wl)
+    W0, V0 = [w.clone() for w in W], [v.clone() for v in V]
+    mo.muon_step_batched(W, G, V, mu=0.95, lr=0.02, ns_steps=5, precision="split")
+    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, precision="split")
+    torch.cuda.synchronize()
+    for w, w0, v, v0, g, o in zip(W, W0, V, V0, G, O):
+        _check_v(v, v0, g, 0.95)
+        _check_w(w, w0, o, 0.02)
+        assert relF(f64(o), oracle.ns_orthogonalize(f64(v))) <= 2e-2
+
+
 # Gram and polynomial tables of this batch differ in length (72 and 48 entries:
 # both are packed longest-unit-first, with K = n and K = m per tile), so it
 # checks that each stage launches exactly its own table.

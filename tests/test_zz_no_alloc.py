@@ -2,7 +2,7 @@
 workspace entry point muon_step_batched: the same kernels on the same inputs,
 so the results must be bit-identical -- on two calls in a row, the second with
 a smaller input (the scratch array keeps the first call's contents), in bf16
-and in float32.  The calls build no plan and allocate nothing on the device.
+and in float32, and once in split precision.  The calls build no plan and allocate nothing on the device.
 A shape list beyond the scratch array is rejected before anything runs."""
 import pytest
 import torch
@@ -30,7 +30,9 @@ CALLS = [
     ("bf16", [(1280, 1280), (300, 700), (700, 300), (256, 512), (1280, 3840)]),
     ("bf16", [(256, 512), (37, 45)]),          # smaller than the first
     ("f32", [(256, 512)]),                      # the float32 single-matrix case
+    ("bf16", [(512, 1280), (300, 700)]),        # split precision (below)
 ]
+SPLIT_CALL = 3
 
 
 def test_noalloc_bit_identical_to_workspace_step(mo):
@@ -39,10 +41,11 @@ def test_noalloc_bit_identical_to_workspace_step(mo):
         W, V, G = _inputs(shapes, seed=200 + k, dtype=dt)
         Wr, Vr = [w.clone() for w in W], [v.clone() for v in V]
         Wn, Vn = [w.clone() for w in W], [v.clone() for v in V]
-        mo.muon_step_batched(Wr, G, Vr)
+        prec = "split" if k == SPLIT_CALL else "default"
+        mo.muon_step_batched(Wr, G, Vr, precision=prec)
         torch.cuda.synchronize()
         before = mo.counters()
-        mo.muon_step_batched_noalloc(Wn, G, Vn)
+        mo.muon_step_batched_noalloc(Wn, G, Vn, precision=prec)
         torch.cuda.synchronize()
         after = mo.counters()
         assert after["plan_builds"] == before["plan_builds"]
