@@ -140,10 +140,10 @@ __global__ __launch_bounds__(kThreads) void rmnp_stream_kernel(RmnpParams P) {
 //            order, then a fixed wave tree (deterministic, batch independent).
 //   apply:   W <- W - lr*s * V / max(sqrt(rowsq[r]), eps)   (one rounding),
 //            after the row sums were summed over all slices.
-// Each lane handles chunks lane, lane + 64, ...; four chunks' loads are issued
+// Each lane handles chunks lane, lane + 64, ...; eight chunks' loads are issued
 // before their stores.  Algorithmic bytes per element (bf16): partial 6 (read
 // G, V; write V), apply 6 (read V, W; write W).
-constexpr int kColcutUnroll = 4;
+constexpr int kColcutUnroll = 8;
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void colcut_partial_kernel(ColcutParams P) {

@@ -207,3 +207,16 @@ def test_binding_rejects_cpu_tensors(mod):
     w = torch.zeros(4, 4, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         mod.muon_step_batched([w], [w.clone()], [w.clone()])
+
+
+def test_flat_views_cover_one_buffer(mod):
+    import torch
+    flat = torch.arange(3 + 12 + 5, dtype=torch.float32)
+    v = mod.flat_views(flat, [(3,), (3, 4), (5,)])
+    assert [tuple(t.shape) for t in v] == [(3,), (3, 4), (5,)]
+    assert v[1][0, 0].item() == 3 and v[2][-1].item() == 19
+    v[1].zero_()
+    assert flat[3:15].abs().sum().item() == 0     # views, not copies
+    import pytest
+    with pytest.raises(ValueError):
+        mod.flat_views(flat, [(30,)])

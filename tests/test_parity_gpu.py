@@ -611,3 +611,23 @@ def test_adamw_ragged_tail(mo, dtype, step):
             err = np.abs(f64(p1) - pe)
             allowed = np.spacing(np.abs(pe).astype(np.float32)).astype(np.float64) + 1e-9 * upd
             assert (err <= allowed).all()
+
+
+def test_adamw_flat_tail_equals_separate_tensors(mo):
+    """The tail as views into one flat tensor of each kind (flat_views), passed
+    as one tensor, gives the bits of the same tensors passed one by one."""
+    gen = torch.Generator().manual_seed(77)
+    lens = ADAMW_LENS
+    shapes = [(n,) for n in lens]
+    total = sum(lens)
+    fp = torch.randn(total, generator=gen).bfloat16().cuda()
+    fg = (torch.randn(total, generator=gen) * 0.1).bfloat16().cuda()
+    fm = (torch.randn(total, generator=gen) * 0.01).cuda()
+    fv = (torch.rand(total, generator=gen) * 1e-3).cuda()
+    sep = [[t.clone() for t in mo.flat_views(f, shapes)] for f in (fp, fg, fm, fv)]
+    mo.adamw_step_batched(*sep, 3)
+    mo.adamw_step_batched([fp], [fg], [fm], [fv], 3)
+    torch.cuda.synchronize()
+    for flat, parts in ((fp, sep[0]), (fm, sep[2]), (fv, sep[3])):
+        for view, part in zip(mo.flat_views(flat, shapes), parts):
+            assert torch.equal(view, part)
