@@ -89,6 +89,7 @@ struct GemmParams {
   // but the last stores its iterate as bf16 hi over bf16 lo (2 mp x np), and
   // the applies after the first run K over both parts
   int32_t split;
+  int32_t n_tiles;    // entries of `tiles` (set by the launcher)
   float a, b, c, lr;
   double wdl;         // lr * weight decay (exact product), 0: no decay
   // profiling only (else NULL): [0] += shader-clock ticks, [1] += 100 MHz

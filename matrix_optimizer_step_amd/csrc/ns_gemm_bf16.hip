@@ -946,14 +946,17 @@ __device__ __forceinline__ void issue_pair(const Op& op, int s, uint8_t* a, uint
   op.template issue<BPW>(s + 1, b, wave);
 }
 
+// XW > 0: when xw is set, XW more vector memory instructions (stores issued
+// after this tile's prologue DMA, older than this step's DMA) may stay in
+// flight at the wait.
 template <bool P0, bool Q0, bool P1, bool Q1, int VMW, bool QPAIR, bool PPAIR, int NBJ, int BPW,
-          class OpP, class OpQ>
+          class OpP, class OpQ, int XW = 0>
 __device__ __forceinline__ void kstep2(f32x16 (&acc)[4][NBJ], bf16x8 (&pa)[4], bf16x8 (&qa)[NBJ],
                                        bf16x8 (&pb)[4], bf16x8 (&qb)[NBJ], int t, const OpP& dp,
                                        const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
                                        int wave, const uint8_t* __restrict__ cur,
                                        const uint8_t* __restrict__ nxt, uint8_t* __restrict__ d0,
-                                       uint8_t* __restrict__ d1) {
+                                       uint8_t* __restrict__ d1, bool xw = false) {
   constexpr int NM = 4 * NBJ;
   constexpr int RD0 = (P0 ? 8 : 4) + (Q0 ? 2 : 1) * NBJ;
   constexpr int RD1 = (P1 ? 8 : 4) + (Q1 ? 2 : 1) * NBJ;
@@ -970,7 +973,12 @@ __device__ __forceinline__ void kstep2(f32x16 (&acc)[4][NBJ], bf16x8 (&pa)[4], b
   if (NM > 8) __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM - 8, 0);
   __builtin_amdgcn_sched_barrier(0);
 
-  wait_vm<VMW>();
+  if constexpr (XW > 0) {
+    if (xw) wait_vm<VMW + XW>();
+    else wait_vm<VMW>();
+  } else {
+    wait_vm<VMW>();
+  }
   bar_raw();
   if (PPAIR) issue_pair<OpP, BPW>(dp, t + 3, d0, d1, wave);
   read_frags<P1, Q1, NBJ>(nxt, 0, g, fo, pa, qa);
@@ -987,15 +995,15 @@ __device__ __forceinline__ void kstep2(f32x16 (&acc)[4][NBJ], bf16x8 (&pa)[4], b
 
 // One even and one odd step with the paired DMA: layouts (PE, Q) -> (PM, Q)
 // -> (PO, Q) for steps t, t+1, t+2.
-template <bool PE, bool PM, bool PO, bool QF, int NBJ, int BPW, class OpP, class OpQ>
+template <bool PE, bool PM, bool PO, bool QF, int NBJ, int BPW, int XW = 0, class OpP, class OpQ>
 __device__ __forceinline__ void kpair(KState<NBJ>& k, const OpP& dp, const OpQ& dq,
                                       const WaveGeo& g, const FragOffsets& fo, int wave,
-                                      uint8_t* lds) {
+                                      uint8_t* lds, bool xw = false) {
   constexpr int DPS = 2 * BPW;
-  kstep2<PE, QF, PM, QF, 2 * DPS, true, false, NBJ, BPW>(
+  kstep2<PE, QF, PM, QF, 2 * DPS, true, false, NBJ, BPW, OpP, OpQ, XW>(
       k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
       lds + stage_wrap(k.sc + STG), lds + stage_wrap(k.sc + 2 * STG),
-      lds + stage_wrap(k.sc + 3 * STG));
+      lds + stage_wrap(k.sc + 3 * STG), xw);
   k.sc = stage_wrap(k.sc + STG);
   ++k.t;
   kstep2<PM, QF, PO, QF, BPW, false, true, NBJ, BPW>(
@@ -1006,31 +1014,63 @@ __device__ __forceinline__ void kpair(KState<NBJ>& k, const OpP& dp, const OpQ& 
   ++k.t;
 }
 
+// Step 0's fragments (P k-major when bP > 0).  The stage pointer is declared
+// restrict, as in kstep2, so that the compiler orders these reads after the
+// DMA through the explicit waits alone.
+template <bool PF, bool QF, int NBJ>
+__device__ __forceinline__ void first_frags(bool pkm, const uint8_t* __restrict__ s0,
+                                            const WaveGeo& g, const FragOffsets& fo,
+                                            bf16x8 (&pa)[4], bf16x8 (&qa)[NBJ]) {
+  if (pkm) read_frags<true, QF, NBJ>(s0, 0, g, fo, pa, qa);
+  else read_frags<PF, QF, NBJ>(s0, 0, g, fo, pa, qa);
+}
+
+// Prologue DMA of the paired schedule: P(0), Q(0), P(1), Q(1), P(2), P(3)
+// into stages 0..3 (all four free).
+template <int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void kprologue2_issue(const OpP& dp, const OpQ& dq, int wave,
+                                                 uint8_t* lds) {
+  dp.template issue<BPW>(0, lds, wave);
+  dq.template issue<BPW>(0, lds + OPB, wave);
+  dp.template issue<BPW>(1, lds + STG, wave);
+  dq.template issue<BPW>(1, lds + STG + OPB, wave);
+  issue_pair<OpP, BPW>(dp, 2, lds + 2 * STG, lds + 3 * STG, wave);
+}
+
 // All K steps of one tile but the last, paired DMA (same contract as kloop
-// without QS; nk and bP are even).  Prologue: P(0), Q(0), P(1), Q(1), P(2), P(3).
-template <bool PF, bool QF, int NBJ, int BPW, class OpP, class OpQ>
-__device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP& dp,
-                                       const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
-                                       int wave, uint8_t* lds) {
+// without QS; nk and bP are even), after the prologue DMA: wait for step 0
+// (the 2 DPS most recent vector memory instructions may still be in flight:
+// P(2), P(3), Q(1), P(1)), then the steady pairs and the drain.  pend: XW
+// vector memory instructions (at most as many as were issued) followed the
+// prologue DMA before this call -- the previous tile's stores -- and may stay
+// in flight at the waits of steps -1 and 0, which need only DMA older than
+// them; the wait of step 1 needs Q(2), issued after them, so they have landed
+// by then whatever the count.
+template <bool PF, bool QF, int NBJ, int BPW, int XW = 0, class OpP, class OpQ>
+__device__ __forceinline__ void kloop2_rest(KState<NBJ>& k, int nk, int bP, const OpP& dp,
+                                            const OpQ& dq, const WaveGeo& g,
+                                            const FragOffsets& fo, int wave, uint8_t* lds,
+                                            bool pend = false) {
   constexpr int DPS = 2 * BPW;
   {
-    dp.template issue<BPW>(0, lds, wave);
-    dq.template issue<BPW>(0, lds + OPB, wave);
-    dp.template issue<BPW>(1, lds + STG, wave);
-    dq.template issue<BPW>(1, lds + STG + OPB, wave);
-    issue_pair<OpP, BPW>(dp, 2, lds + 2 * STG, lds + 3 * STG, wave);
-    wait_vm<2 * DPS>();
+    if constexpr (XW > 0) {
+      if (pend) wait_vm<2 * DPS + XW>();
+      else wait_vm<2 * DPS>();
+    } else {
+      wait_vm<2 * DPS>();
+    }
     bar_raw();
-    if (bP > 0) read_frags<true, QF, NBJ>(lds, 0, g, fo, k.pa, k.qa);
-    else read_frags<PF, QF, NBJ>(lds, 0, g, fo, k.pa, k.qa);
+    first_frags<PF, QF, NBJ>(bP > 0, lds, g, fo, k.pa, k.qa);
   }
   k.sc = 0;
   k.t = 0;
   if (bP > 0) {
-    for (; k.t < bP - 2;) kpair<true, true, true, QF, NBJ, BPW>(k, dp, dq, g, fo, wave, lds);
-    kpair<true, true, PF, QF, NBJ, BPW>(k, dp, dq, g, fo, wave, lds);
+    for (; k.t < bP - 2;)
+      kpair<true, true, true, QF, NBJ, BPW, XW>(k, dp, dq, g, fo, wave, lds, pend && k.t == 0);
+    kpair<true, true, PF, QF, NBJ, BPW, XW>(k, dp, dq, g, fo, wave, lds, pend && k.t == 0);
   }
-  for (; k.t < nk - 4;) kpair<PF, PF, PF, QF, NBJ, BPW>(k, dp, dq, g, fo, wave, lds);
+  for (; k.t < nk - 4;)
+    kpair<PF, PF, PF, QF, NBJ, BPW, XW>(k, dp, dq, g, fo, wave, lds, pend && k.t == 0);
   // step nk-4 issues Q(nk-2), Q(nk-1), the last DMA; nk-3 and nk-2 issue none
   kstep2<PF, QF, PF, QF, 2 * DPS, true, false, NBJ, BPW>(
       k.acc, k.pa, k.qa, k.pb, k.qb, k.t, dp, dq, g, fo, wave, lds + k.sc,
@@ -1049,6 +1089,14 @@ __device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP
   k.sc = stage_wrap(k.sc + STG);
   ++k.t;
   read_frags<PF, QF, NBJ>(lds + k.sc, 1, g, fo, k.pb, k.qb);
+}
+
+template <bool PF, bool QF, int NBJ, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP& dp,
+                                       const OpQ& dq, const WaveGeo& g, const FragOffsets& fo,
+                                       int wave, uint8_t* lds) {
+  kprologue2_issue<BPW>(dp, dq, wave, lds);
+  kloop2_rest<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
 }
 
 // ------------------------------------------------------- diagonal tiles
@@ -1118,6 +1166,17 @@ __device__ __forceinline__ void read_slots(const uint8_t* stage, int kk, const u
       fr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
+}
+
+// Step 0's slots (k-major when pkm), through a restrict stage pointer so that
+// the explicit wait alone orders them after the DMA (as first_frags).
+template <int NSL>
+__device__ __forceinline__ void first_slots(bool pkm, const uint8_t* __restrict__ s0,
+                                            const uint32_t (&sok)[NSL],
+                                            const uint32_t (&so)[NSL], const FragOffsets& fo,
+                                            bf16x8 (&fr)[NSL]) {
+  if (pkm) read_slots<true, NSL>(s0, 0, sok, fo, fr);
+  else read_slots<false, NSL>(s0, 0, so, fo, fr);
 }
 
 // MFMAs of one k16 sub-step (first operand: the column fragment, second: the
@@ -1277,8 +1336,7 @@ __device__ __forceinline__ void diag_tile(const MatDesc& d, const GemmParams& P,
   for (int t = 0; t < NS - 1; ++t) dp.template issue<BPW>(t, lds + t * STG, wave);
   wait_vm<BPW * (NS - 2)>();
   bar_raw();
-  if (bP > 0) read_slots<true, NSL>(lds, 0, sok, fo, fa);
-  else read_slots<false, NSL>(lds, 0, so, fo, fa);
+  first_slots<NSL>(bP > 0, lds, sok, so, fo, fa);
   uint32_t sc = 0;
   int t = 0;
   // steady: DMA of step t+4; in flight after t+1's: t+2, t+3.  bP (a multiple
@@ -1686,6 +1744,164 @@ void ns_gemm_bf16_kernel(GemmParams P) {
   }
 }
 
+// ------------------------------------------- persistent non-final apply
+// X' = B X for every iteration but the last (iterate stored in blocks from
+// registers, LDS idle after the K loop).  Workgroup w walks XCD stream
+// x = w mod 8 (table positions 8k + x) at k = w/8, w/8 + G, w/8 + 2G, ...
+// (G workgroups per stream, at most one per compute unit of the XCD), so
+// that the tiles running together on an XCD stay consecutive in its stream,
+// as with one tile per workgroup.  Between two tiles nothing waits on the
+// epilogue: once every wave has read the last K step's fragments, the next
+// tile's prologue DMA is issued, then the finished tile's accumulators are
+// stored behind it, and the next K loop starts as soon as its first step has
+// landed (the stores may stay in flight through its step 0).
+
+// Tile and matrix tables are read through the constant address space
+// (scalar loads: they are not written while the kernel runs).
+#define MATOPT_CAS __attribute__((address_space(4)))
+
+struct ApplyTask {
+  const uint16_t* b;    // B, blocked, mp x mp
+  const uint16_t* xc;   // current iterate (plain X0 on the first iteration)
+  uint16_t* out;        // next iterate: this wave's 32 x 32 block origin
+  int32_t mp, np, i0, j0;
+  float s;              // Frobenius scale on the first iteration, else 1
+};
+
+// Table entry pos as a task; false for idle or out-of-range entries.
+__device__ __forceinline__ bool apply_task(const GemmParams& P, int pos, const WaveGeo& g,
+                                           int lane, ApplyTask& t) {
+  const MATOPT_CAS GemmTile& tile = ((const MATOPT_CAS GemmTile*)P.tiles)[pos];
+  const int mat = tile.mat, ti = tile.ti, tj = tile.tj;
+  if (mat < 0 || tj < 0) return false;
+  const MATOPT_CAS MatDesc& d = ((const MATOPT_CAS MatDesc*)P.mats)[mat];
+  t.mp = d.mp;
+  t.np = d.np;
+  t.i0 = ti * BM;
+  t.j0 = tj * BM;
+  if (t.i0 < 0 || t.i0 + BM > t.mp || t.j0 + BM > t.np) return false;
+  t.b = (const uint16_t*)d.b;
+  t.xc = (const uint16_t*)(P.first ? d.x0in : P.cur ? d.x[1] : d.x[0]);
+  uint16_t* xn = (uint16_t*)(P.cur ? d.x[0] : d.x[1]);
+  const int64_t nb = t.np / 32;
+  t.out = xn + (((int64_t)(t.i0 + g.wi0) >> 5) * nb + ((t.j0 + g.wj0) >> 5)) * 1024;
+  t.s = P.first ? *(const MATOPT_CAS float*)d.xs : 1.f;
+  (void)lane;
+  return true;
+}
+
+__device__ __forceinline__ void apply_persist(const GemmParams& P, uint8_t* lds) {
+  constexpr int NBJ = 2, BPW = 2;
+  constexpr int NST = 2 * 4 * NBJ;   // store instructions per wave and tile (bf16 iterate)
+  const int xcd = (int)(blockIdx.x & 7);
+  const int G = (int)(gridDim.x >> 3);
+  const int L = P.n_tiles >> 3;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WaveGeo g;
+  g.wi0 = (wave >> 2) * 128;
+  g.wj0 = (wave & 3) * 64;
+  g.frow = lane & 31;
+  g.fkc = lane >> 5;
+  FragOffsets fo;
+  fo.init(lane);
+  fo.init_q64(lane, g.wj0);
+
+  int kpos = (int)(blockIdx.x >> 3);
+  ApplyTask cur;
+  bool have = false;
+  for (; kpos < L; kpos += G)
+    if (apply_task(P, 8 * kpos + xcd, g, lane, cur)) {
+      have = true;
+      break;
+    }
+  if (!have) return;
+
+  const bool xblk = !P.first;
+  const bool ksplit = P.split && !P.first;
+  OperandDma<OP_SPLIT> dp;
+  OperandDma<OP_KM> dq;
+  int nk = 0, bP = 0;
+  auto setup = [&](const ApplyTask& t) {
+    // split precision: K runs over the stacked [hi; lo] iterate, P over B twice
+    nk = (ksplit ? 2 * t.mp : t.mp) / BK;
+    bP = P.split ? 0 : t.i0 / BK;
+    dp.init(t.b, t.mp, t.i0, bP, lane, true);
+    if (ksplit) dp.t_wrap = t.mp / BK;
+    dq.init(t.xc, t.np, t.j0, nk, lane, xblk);
+  };
+  setup(cur);
+  kprologue2_issue<BPW>(dp, dq, wave, lds);
+
+  KState<NBJ> k;
+  bool pend = false;
+  for (;;) {
+    ApplyTask nx;
+    bool more = false;
+    for (int kn = kpos + G; kn < L; kn += G)
+      if (apply_task(P, 8 * kn + xcd, g, lane, nx)) {
+        more = true;
+        kpos = kn;
+        break;
+      }
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NBJ; ++bj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) k.acc[bi][bj][r] = 0.f;
+    kloop2_rest<false, true, NBJ, BPW, NST>(k, nk, bP, dp, dq, g, fo, wave, lds, pend);
+    mfma16<NBJ>(k.acc, k.pa, k.qa);
+    mfma16<NBJ>(k.acc, k.pb, k.qb);
+    if (more) {
+      // every wave has read its last fragments: the stages are free
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      bar_raw();
+      setup(nx);
+      kprologue2_issue<BPW>(dp, dq, wave, lds);
+    }
+    const int64_t nb = cur.np / 32;
+    uint16_t* base = cur.out + (lane & 31) * 32 + 8 * (lane >> 5);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NBJ; ++bj) {
+        float v[16], lo[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v[r] = cur.s * k.acc[bi][bj][r];
+          lo[r] = v[r] - bf2f(f2bf(v[r]));
+        }
+        store_block_direct(v, base + (bi * nb + bj) * 1024);
+        if (P.split) store_block_direct(lo, base + (int64_t)cur.mp * cur.np + (bi * nb + bj) * 1024);
+      }
+    if (!more) break;
+    cur = nx;
+    pend = true;
+  }
+}
+
+template <int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
+                          amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void ns_apply_persist_kernel(GemmParams P) {
+  static_assert(NW == 8, "eight-wave layout only");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  const bool clk = P.clk != nullptr;
+  uint64_t t0 = 0, r0 = 0;
+  if (clk) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  apply_persist(P, lds);
+  if (clk && threadIdx.x == 0) {
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    atomicAdd(&P.clk[0], (unsigned long long)(t1 - t0));
+    atomicAdd(&P.clk[1], (unsigned long long)(r1 - r0));
+  }
+}
+
 }  // namespace
 
 #ifndef MATOPT_APPLY_WAVES
@@ -1712,11 +1928,41 @@ int gemm_bf16_diag_mode(int stage) {
   return 0;
 }
 
-hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s) {
+// Workgroups per XCD of the persistent apply: one per compute unit (0: one
+// tile per workgroup instead).
+#ifndef MATOPT_APPLY_PERSIST
+#define MATOPT_APPLY_PERSIST 1
+#endif
+
+int persist_per_xcd() {
+  static int per[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (per[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    per[dev] = std::max(1, cus / 8);
+  }
+  return per[dev];
+}
+
+hipError_t launch_gemm_bf16(const GemmParams& p_in, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
   constexpr int GW = MATOPT_GRAM_WAVES, PW = MATOPT_POLY_WAVES;
   constexpr int AW = MATOPT_APPLY_WAVES, FW = MATOPT_FINAL_WAVES;
+  GemmParams p = p_in;
+  p.n_tiles = n_tiles;
   const dim3 grid(n_tiles);
+  if (MATOPT_APPLY_PERSIST && AW == 8 && p.stage == 2 && p.out_kind == OUT_NEXT_X &&
+      n_tiles % 8 == 0) {
+    const int per = persist_per_xcd();
+    if (per > 0) {
+      const int g = std::min(per, n_tiles / 8);
+      hipLaunchKernelGGL((ns_apply_persist_kernel<8>), dim3(8 * g), dim3(512), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if (p.stage == 0)
     hipLaunchKernelGGL((ns_gemm_bf16_kernel<0, OUT_NEXT_X, GW>), grid, dim3(64 * GW), 0, s, p);
   else if (p.stage == 1 && p.split)
