@@ -16,7 +16,11 @@ model writes each schedule's program as the kernel's loops emit it --
            pair before the barrier of its even step, P after the barrier of
            its odd step), with P's switch at bP;
   diag    (a diagonal tile: P panel only);
-  pair    (a diagonal pair: both panels, the kloop schedule)
+  pair    (a diagonal pair: both panels, the kloop schedule);
+  persist (the persistent apply: kloop2 tiles back to back, the next tile's
+           prologue DMA issued after a barrier that follows the last MFMAs,
+           then the finished tile's stores, which the next tile's first two
+           waits let stay in flight)
 
 -- and checks that
   * every stage read sees its step's DMA landed for every wave (the reading
@@ -26,7 +30,9 @@ model writes each schedule's program as the kernel's loops emit it --
     (consumption happens at the MFMA; a barrier must separate it from the
     DMA issue);
   * every step's tile is read in the layout its DMA wrote;
-  * every step is issued, read and multiplied exactly once per sub-step.
+  * every step is issued, read and multiplied exactly once per sub-step;
+  * a wait that lets stores stay in flight still covers the DMA it guards
+    (stores count in the same vmcnt as the DMA, in issue order).
 """
 import pytest
 
@@ -36,16 +42,28 @@ DPS = 2 * BPW   # DMA instructions per wave and step (P and Q)
 
 
 class Program:
-    """The event list of one wave."""
+    """The event list of one wave.  A step is keyed (tile, t): the persistent
+    apply runs several tiles' K loops in one program; stage of step t = t mod
+    NS within each tile."""
 
     def __init__(self, km_p, km_q):
         self.ev = []
+        self.tile = 0
         self.km_p, self.km_q = km_p, km_q   # step -> k-major layout of the DMA
+
+    def next_tile(self, km_p, km_q):
+        self.tile += 1
+        self.km_p, self.km_q = km_p, km_q
 
     def issue(self, op, t):
         km = (self.km_p if op == "P" else self.km_q)(t)
         for _ in range(BPW):
-            self.ev.append(("issue", op, t, t % NS, km))
+            self.ev.append(("issue", op, (self.tile, t), t % NS, km))
+
+    def store(self, n):
+        """n vector memory stores: counted by the waits like DMA instructions."""
+        for _ in range(n):
+            self.ev.append(("store",))
 
     def wait(self, n):
         self.ev.append(("wait", n))
@@ -54,64 +72,71 @@ class Program:
         self.ev.append(("barrier",))
 
     def read(self, t, kk, p_km, q_km, ops="PQ"):
-        self.ev.append(("read", t, t % NS, kk, p_km, q_km, ops))
+        self.ev.append(("read", (self.tile, t), t % NS, kk, p_km, q_km, ops))
 
     def mfma(self, t, kk):
-        self.ev.append(("mfma", t, kk))
+        self.ev.append(("mfma", (self.tile, t), kk))
 
 
 def check(prog, nk, ops="PQ"):
-    """Verify the invariants of one wave program (all waves run it)."""
-    issued = []        # DMA instructions in issue order: (op, t, stage, km)
-    by_step = {}       # step -> indices into `issued`
+    """Verify the invariants of one wave program (all waves run it).  nk: the
+    K steps of each tile (an int: one tile; a list: one entry per tile)."""
+    nks = nk if isinstance(nk, list) else [nk]
+    issued = []        # vector memory instructions in issue order: (op, key, stage, km)
+    by_step = {}       # step key -> indices into `issued`
+    owner = {}         # stage -> key of the step its last DMA brought in
     landed = 0         # instructions [0, landed) known landed at the last wait
     landed_at_barrier = 0
     barriers = 0
-    consumed_before_barrier = {}   # (t, kk) -> barrier count when its MFMA ran
+    consumed_before_barrier = {}   # (key, kk) -> barrier count when its MFMA ran
     read_steps = {}
     mfma_steps = set()
     for ev in prog.ev:
         kind = ev[0]
         if kind == "issue":
-            _, op, t, s, km = ev
-            prev = t - NS
-            if prev >= 0:
+            _, op, key, s, km = ev
+            prev = owner.get(s)
+            if prev is not None and prev != key:
                 # the previous occupant of this stage must have been consumed
                 # (both sub-steps) before a barrier that this issue follows
                 for kk in (0, 1):
                     b = consumed_before_barrier.get((prev, kk))
                     assert b is not None and b < barriers, \
-                        f"DMA {op}({t}) into stage {s} before step {prev} sub-step {kk} was consumed"
-            by_step.setdefault(t, []).append(len(issued))
-            issued.append((op, t, s, km))
+                        f"DMA {op}{key} into stage {s} before step {prev} sub-step {kk} was consumed"
+            owner[s] = key
+            by_step.setdefault(key, []).append(len(issued))
+            issued.append((op, key, s, km))
+        elif kind == "store":
+            issued.append(("S", None, None, None))
         elif kind == "wait":
             landed = max(landed, len(issued) - ev[1])
         elif kind == "barrier":
             landed_at_barrier = landed
             barriers += 1
         elif kind == "read":
-            _, t, s, kk, p_km, q_km, rops = ev
-            need = [i for i in by_step.get(t, []) if issued[i][0] in rops]
-            assert len(need) == BPW * len(rops), f"step {t}: {len(need)} DMA instructions issued"
+            _, key, s, kk, p_km, q_km, rops = ev
+            need = [i for i in by_step.get(key, []) if issued[i][0] in rops]
+            assert len(need) == BPW * len(rops), f"step {key}: {len(need)} DMA instructions issued"
             # every wave: landed before the last barrier; this wave: landed now
             assert max(need) < landed_at_barrier <= landed, \
-                f"read of step {t} sub-step {kk} before its DMA landed"
+                f"read of step {key} sub-step {kk} before its DMA landed"
             for i in need:
                 op, _, st, km = issued[i]
                 assert st == s, "read from another stage than the DMA wrote"
                 assert km == (p_km if op == "P" else q_km), \
-                    f"step {t}: {op} read in the other layout than its DMA wrote"
-            read_steps.setdefault(t, set()).add(kk)
+                    f"step {key}: {op} read in the other layout than its DMA wrote"
+            read_steps.setdefault(key, set()).add(kk)
         elif kind == "mfma":
-            _, t, kk = ev
-            assert kk in read_steps.get(t, set()), f"MFMA of step {t} sub-step {kk} before its read"
-            assert (t, kk) not in mfma_steps
-            mfma_steps.add((t, kk))
-            consumed_before_barrier[(t, kk)] = barriers
-    assert mfma_steps == {(t, kk) for t in range(nk) for kk in (0, 1)}
+            _, key, kk = ev
+            assert kk in read_steps.get(key, set()), f"MFMA of step {key} sub-step {kk} before its read"
+            assert (key, kk) not in mfma_steps
+            mfma_steps.add((key, kk))
+            consumed_before_barrier[(key, kk)] = barriers
+    assert mfma_steps == {((i, t), kk) for i, n in enumerate(nks) for t in range(n) for kk in (0, 1)}
     for op in ops:
-        assert sorted(t for (o, t, _, _) in issued if o == op) == \
-            sorted(t for t in range(nk) for _ in range(BPW))
+        for i, n in enumerate(nks):
+            assert sorted(key[1] for (o, key, _, _) in issued if o == op and key[0] == i) == \
+                sorted(t for t in range(n) for _ in range(BPW))
 
 
 # ------------------------------------------------------------------ schedules
@@ -157,19 +182,19 @@ def kloop_program(nk, bP, bQ, qs):
     return p
 
 
-def kloop2_program(nk, bP):
-    """kloop2 (paired DMA): P k-major for t < bP, Q k-major throughout."""
-    km_p = lambda t: t < bP
-    km_q = lambda t: True
-    p = Program(km_p, km_q)
-    lay = lambda t: (km_p(t), km_q(t))
+def kloop2_issue_prologue(p):
     p.issue("P", 0)
     p.issue("Q", 0)
     p.issue("P", 1)
     p.issue("Q", 1)
     p.issue("P", 2)
     p.issue("P", 3)
-    p.wait(2 * DPS)
+
+
+def kloop2_rest(p, nk, lay, xw=0):
+    """Everything after the prologue DMA; xw: stores that may stay in flight
+    at the waits of steps -1 and 0 (the persistent apply's previous tile)."""
+    p.wait(2 * DPS + xw)
     p.barrier()
     p.read(0, 0, *lay(0))
 
@@ -179,7 +204,7 @@ def kloop2_program(nk, bP):
             p.issue("Q", t + 2)
             p.issue("Q", t + 3)
         p.mfma(t, 0)
-        p.wait(vmw)
+        p.wait(vmw + (xw if t == 0 else 0))
         p.barrier()
         if ppair:
             p.issue("P", t + 3)
@@ -199,6 +224,42 @@ def kloop2_program(nk, bP):
     p.read(nk - 1, 1, *lay(nk - 1))
     p.mfma(nk - 1, 0)
     p.mfma(nk - 1, 1)
+
+
+def kloop2_program(nk, bP):
+    """kloop2 (paired DMA): P k-major for t < bP, Q k-major throughout."""
+    km_p = lambda t: t < bP
+    km_q = lambda t: True
+    p = Program(km_p, km_q)
+    kloop2_issue_prologue(p)
+    kloop2_rest(p, nk, lambda t: (km_p(t), km_q(t)))
+    return p
+
+
+XW = 16   # stores the persistent apply lets stay in flight (bf16 iterate: 2 per 32 x 32 block)
+
+
+def persist_program(tiles, nst, xw=XW):
+    """The persistent apply: tiles = [(nk, bP), ...] run back to back.  After a
+    tile's last MFMAs: every wave waits for its LDS reads and passes a barrier,
+    the next tile's prologue DMA is issued, then the finished tile's nst
+    stores; the next K loop lets xw of them stay in flight."""
+    def lays(bp):
+        return (lambda t: t < bp), (lambda t: True)
+
+    km_p, km_q = lays(tiles[0][1])
+    p = Program(km_p, km_q)
+    kloop2_issue_prologue(p)
+    pend = False
+    for i, (nk, bp) in enumerate(tiles):
+        km_p, km_q = lays(bp)
+        kloop2_rest(p, nk, lambda t, a=km_p, b=km_q: (a(t), b(t)), xw if pend else 0)
+        if i + 1 < len(tiles):
+            p.barrier()
+            p.next_tile(*lays(tiles[i + 1][1]))
+            kloop2_issue_prologue(p)
+        p.store(nst)
+        pend = True
     return p
 
 
@@ -287,6 +348,40 @@ def test_diagonal_pair_schedule(nk):
     check(pair_program(nk), nk)
 
 
+@pytest.mark.parametrize("nk", M_NKS + [2 * n for n in M_NKS])
+def test_persistent_apply_schedule(nk):
+    # consecutive tiles of one matrix (every split of the first, the diagonal
+    # one next) and a change of K between tiles; bf16 (16 stores per tile)
+    # and split-precision (32) iterates
+    for nst in (XW, 2 * XW):
+        for bp in range(0, nk - 7, 8):
+            tiles = [(nk, bp), (nk, min(bp + 8, nk - 8)), (8, 0), (nk, 0)]
+            check(persist_program(tiles, nst), [t[0] for t in tiles])
+
+
+def test_model_catches_too_few_stores_for_the_allowance():
+    """The allowance is only sound when at least that many stores followed
+    the prologue: with fewer, step 0's DMA may still be in flight."""
+    tiles = [(40, 0), (40, 8)]
+    with pytest.raises(AssertionError):
+        check(persist_program(tiles, XW - 4), [40, 40])
+
+
+def test_model_catches_a_prologue_before_the_barrier():
+    """The next tile's prologue overwrites stages the last steps were read
+    from: without the barrier after the last MFMAs it must be caught."""
+    tiles = [(40, 0), (40, 0)]
+    p = persist_program(tiles, XW)
+    # drop the barrier that precedes tile 1's first DMA
+    first = next(i for i, ev in enumerate(p.ev) if ev[0] == "issue" and ev[2][0] == 1)
+    j = first - 1
+    while p.ev[j][0] != "barrier":
+        j -= 1
+    del p.ev[j]
+    with pytest.raises(AssertionError):
+        check(p, [40, 40])
+
+
 def test_model_catches_a_short_wait():
     """A wait that leaves one more DMA instruction in flight must be caught."""
     p = kloop_program(40, 0, 0, False)
@@ -304,7 +399,7 @@ def test_model_catches_an_early_dma():
     consumed after the barrier of step 0; moved before the barrier of step 1
     it would overwrite fragments other waves may still be reading."""
     p = kloop_program(40, 0, 0, False)
-    first = next(i for i, ev in enumerate(p.ev) if ev[0] == "issue" and ev[1] == "P" and ev[2] == NS)
+    first = next(i for i, ev in enumerate(p.ev) if ev[0] == "issue" and ev[1] == "P" and ev[2] == (0, NS))
     j = first - 1
     while p.ev[j][0] != "barrier":
         j -= 1
@@ -318,7 +413,7 @@ def test_model_catches_an_early_dma():
 def test_model_catches_a_layout_mismatch():
     p = kloop_program(40, 16, 24, True)
     for i, ev in enumerate(p.ev):
-        if ev[0] == "read" and ev[1] == 15 and ev[3] == 0:
+        if ev[0] == "read" and ev[1] == (0, 15) and ev[3] == 0:
             p.ev[i] = ev[:4] + (False,) + ev[5:]   # P of step 15 read as row-major
             break
     with pytest.raises(AssertionError):
