@@ -194,6 +194,33 @@ def cpu_baseline(wl):
                       f"{threads} threads on {cpu_model()}"}
 
 
+def vendor_gemm(wl, per, steps, warmup, stream):
+    """The same Newton-Schulz products through torch.bmm in bf16 (hipBLASLt),
+    as full dense products per distinct shape (X X^T, B B, B X, m <= n), next
+    to this library's per-iteration launch times.  Context only: the library
+    computes the symmetric Gram and polynomial as upper tiles and fuses the
+    polynomial's a I + b A and the Frobenius scale."""
+    import torch
+    from collections import Counter
+    cnt = Counter((min(r, c), max(r, c)) for r, c in wl.shapes)
+    tot = {"gram": 0.0, "poly": 0.0, "apply": 0.0}
+    for (m, n), c in sorted(cnt.items()):
+        X = torch.randn(c, m, n, device="cuda", dtype=torch.bfloat16)
+        Xt = X.transpose(1, 2).contiguous()
+        B = torch.randn(c, m, m, device="cuda", dtype=torch.bfloat16)
+        tot["gram"] += time_steps(lambda: torch.bmm(X, Xt), steps, warmup, stream)
+        tot["poly"] += time_steps(lambda: torch.bmm(B, B), steps, warmup, stream)
+        tot["apply"] += time_steps(lambda: torch.bmm(B, X), steps, warmup, stream)
+        del X, Xt, B
+    torch.cuda.empty_cache()
+    ours = {k: per[k]["ms_per_step"] / per[k]["launches_per_step"] for k in tot if k in per}
+    return {"library": "torch.bmm bf16 (hipBLASLt), full dense products",
+            "note": "ours: average launch of the step (the last apply also writes W)",
+            "blas_ms_per_iteration": {k: round(v, 4) for k, v in tot.items()},
+            "ours_ms_per_iteration": {k: round(v, 4) for k, v in ours.items()},
+            "ours_over_blas": {k: round(ours[k] / tot[k], 3) for k in ours}}
+
+
 def workload_line(name, steps, warmup, stream, with_rmnp=False, with_split=False):
     """Compact line of one more configuration: Muon step ms, NS rate, prep
     bandwidth (and the RMNP step on the same momenta; the step in split
@@ -319,7 +346,9 @@ GEMM_CLASS = {"0": "gram", "1": "poly"}
 
 def kernel_class(name):
     """Kernel class of a rocprofv3 kernel name (the library's kernels only)."""
-    m = re.search(r"ns_gemm_bf16_kernel<(\d+), (\d+), \d+>", name)
+    if "ns_apply_persist_kernel" in name:
+        return "apply"
+    m = re.search(r"ns_gemm_bf16_kernel<(\d+), (\d+), \d+(?:, (?:true|false))?>", name)
     if m:
         st, out = m.group(1), m.group(2)
         if st in GEMM_CLASS:
@@ -365,6 +394,7 @@ def summarize_profile(directory, flops_per_step=None, steps=None):
             d["avg_us"] = rows[cls]["ns"] / rows[cls]["n"] / 1e3
         for name, vals in counters.get(cls, {}).items():
             d[name + "_avg"] = sum(vals) / len(vals)
+            d[name + "_max"] = max(vals)
         if "avg_us" in d and "GRBM_GUI_ACTIVE_avg" in d:
             # GRBM_GUI_ACTIVE counts GPU cycles summed over the 8 XCDs
             ghz = d["GRBM_GUI_ACTIVE_avg"] / 8 / (d["avg_us"] * 1e3)
@@ -468,7 +498,7 @@ def main():
         prep_gbs = prep_bytes / (per["prep"]["ms_per_step"] * 1e-3) / 1e9
     traffic = load_traffic(wl.name)
     roofline = {
-        "kernel": "ns_gemm_bf16_kernel (Gram, polynomial and apply launches)",
+        "kernel": "ns_gemm_bf16_kernel and ns_apply_persist_kernel (Gram, polynomial and apply launches)",
         "bound": "mfma",
         "achieved": round(ns_tflops, 1) if ns_tflops else None,
         "peak": PEAK_BF16_TFLOPS,
@@ -517,6 +547,8 @@ def main():
     }
 
     if not args.no_rmnp:
+        result["vendor_gemm"] = vendor_gemm(wl, per, args.steps, args.warmup, stream)
+        log(f"[bench] vendor GEMM reference: {result['vendor_gemm']['ours_over_blas']}")
         rms = time_steps(lambda: mo.rmnp_step_batched(W, G, V, mu=wl.mu, lr=wl.lr),
                          args.steps, args.warmup, stream)
         gbs = 5 * esz * numel / (rms * 1e-3) / 1e9
