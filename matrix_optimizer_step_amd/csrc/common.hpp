@@ -90,6 +90,7 @@ struct GemmParams {
   // the applies after the first run K over both parts
   int32_t split;
   int32_t n_tiles;    // entries of `tiles` (set by the launcher)
+  int32_t uniform_k;  // every tile of the table has the same K extent
   float a, b, c, lr;
   double wdl;         // lr * weight decay (exact product), 0: no decay
   // profiling only (else NULL): [0] += shader-clock ticks, [1] += 100 MHz

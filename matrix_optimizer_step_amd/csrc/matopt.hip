@@ -248,6 +248,7 @@ struct RmnpGroup {
 struct TileTable {
   size_t off = 0;   // byte offset in the plan buffer
   int n = 0;
+  int uniform_k = 0;   // every tile has the same K extent (GemmParams::uniform_k)
 };
 
 // Everything a call's launches need that depends on the list of shapes only:
@@ -505,7 +506,9 @@ matopt_status build_ns_plan(Plan& P, int dt, const std::vector<Geo>& geo) {
   P.o_prep = o_prep;
   P.gram = TileTable{o_k3, (int)k3.size()};
   P.poly = TileTable{o_k4, (int)k4.size()};
-  P.apply = TileTable{o_k5, (int)k5.size()};
+  bool same_k = true;
+  for (const Geo& g : geo) same_k = same_k && g.mp == geo[0].mp;
+  P.apply = TileTable{o_k5, (int)k5.size(), same_k ? 1 : 0};
   return MATOPT_OK;
 }
 
@@ -586,6 +589,7 @@ matopt_status run_ns(const NsTables& P, const MatDesc* mats, int dt, bool moment
   // every stage launches exactly its own table
   auto gemm = [&](GemmParams g, const TileTable& t) {
     g.tiles = P.dev<const GemmTile>(t.off);
+    g.uniform_k = t.uniform_k;
     return dt == DT_BF16 ? launch_gemm_bf16(g, t.n, s) : launch_gemm_f32(g, t.n, s);
   };
   for (int it = 0; it < ns_steps; ++it) {

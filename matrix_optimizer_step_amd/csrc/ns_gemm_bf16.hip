@@ -580,6 +580,19 @@ __device__ __forceinline__ void store_acc_direct(const f32x16 (&acc)[4][NBJ], ui
 // store_acc_direct writes it, and the low part bf16(v - bf16(v)) -- v - bf16(v)
 // is exact in float32 -- at the same position of the matrix stacked below
 // (lo_off elements further on), so that hi + lo carries about 16 bits.
+// v = s * a rounded to float32, and lo = v - bf16(v), exact in float32.  No
+// contraction: fused as fma(s, a, -bf16(v)) the low part would carry the
+// product's own rounding error on some paths and not on others.
+__device__ __forceinline__ void split_parts(const f32x16& a, float s, float (&v)[16],
+                                            float (&lo)[16]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    v[r] = s * a[r];
+    lo[r] = v[r] - bf2f(f2bf(v[r]));
+  }
+}
+
 template <int NBJ>
 __device__ __forceinline__ void store_acc_direct_split(const f32x16 (&acc)[4][NBJ], uint16_t* out,
                                                        int64_t ld, int64_t i0, int64_t j0,
@@ -591,11 +604,7 @@ __device__ __forceinline__ void store_acc_direct_split(const f32x16 (&acc)[4][NB
 #pragma unroll
     for (int bj = 0; bj < NBJ; ++bj) {
       float v[16], lo[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        v[r] = s * acc[bi][bj][r];
-        lo[r] = v[r] - bf2f(f2bf(v[r]));
-      }
+      split_parts(acc[bi][bj], s, v, lo);
       store_block_direct(v, base + (bi * nb + bj) * 1024);
       store_block_direct(lo, base + lo_off + (bi * nb + bj) * 1024);
     }
@@ -1862,19 +1871,28 @@ __device__ __forceinline__ void apply_persist(const GemmParams& P, uint8_t* lds)
     }
     const int64_t nb = cur.np / 32;
     uint16_t* base = cur.out + (lane & 31) * 32 + 8 * (lane >> 5);
+    if (P.split) {   // the stacked low part starts mp x np elements further on
+      const int64_t lo_off = (int64_t)cur.mp * cur.np;
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+      for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < NBJ; ++bj) {
-        float v[16], lo[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          v[r] = cur.s * k.acc[bi][bj][r];
-          lo[r] = v[r] - bf2f(f2bf(v[r]));
+        for (int bj = 0; bj < NBJ; ++bj) {
+          float v[16], lo[16];
+          split_parts(k.acc[bi][bj], cur.s, v, lo);
+          store_block_direct(v, base + (bi * nb + bj) * 1024);
+          store_block_direct(lo, base + lo_off + (bi * nb + bj) * 1024);
         }
-        store_block_direct(v, base + (bi * nb + bj) * 1024);
-        if (P.split) store_block_direct(lo, base + (int64_t)cur.mp * cur.np + (bi * nb + bj) * 1024);
-      }
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NBJ; ++bj) {
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = cur.s * k.acc[bi][bj][r];
+          store_block_direct(v, base + (bi * nb + bj) * 1024);
+        }
+    }
     if (!more) break;
     cur = nx;
     pend = true;
@@ -1929,7 +1947,11 @@ int gemm_bf16_diag_mode(int stage) {
 }
 
 // Workgroups per XCD of the persistent apply: one per compute unit (0: one
-// tile per workgroup instead).
+// tile per workgroup instead).  Taken only where every tile of the launch has
+// the same K extent: the fixed walk of a stream balances equal tiles as well
+// as the dispatcher does, but not tiles of unequal length (measured on sets
+// that mix K = 1024 .. 8192: apply 1-3% slower than one tile per workgroup,
+// against 0.7% faster on equal tiles).
 #ifndef MATOPT_APPLY_PERSIST
 #define MATOPT_APPLY_PERSIST 1
 #endif
@@ -1955,7 +1977,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p_in, int n_tiles, hipStream_t s) 
   p.n_tiles = n_tiles;
   const dim3 grid(n_tiles);
   if (MATOPT_APPLY_PERSIST && AW == 8 && p.stage == 2 && p.out_kind == OUT_NEXT_X &&
-      n_tiles % 8 == 0) {
+      p.uniform_k && n_tiles % 8 == 0) {
     const int per = persist_per_xcd();
     if (per > 0) {
       const int g = std::min(per, n_tiles / 8);

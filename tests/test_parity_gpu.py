@@ -200,6 +200,33 @@ def test_ns_bf16_mixed_batch_stage_tables_differ(mo):
         assert torch.equal(o, a)
 
 
+# Every matrix padded to m = 512 rows, so every apply tile has K = 512 and the
+# non-final applies run as the persistent kernel (one workgroup per CU walking
+# its XCD stream: 552 tiles here, two or three per workgroup).  Adding a matrix
+# of another height makes the launch take one tile per workgroup instead.
+SAME_K_SHAPES = [(512, 8192)] * 6 + [(300, 8192), (8192, 512), (512, 4096), (512, 1000)]
+
+
+@pytest.mark.parametrize("precision", ["default", "split"])
+def test_persistent_apply_matches_one_tile_per_workgroup(mo, precision):
+    wl = workloads.small_case("same_k", SAME_K_SHAPES + [(256, 256)], seed=31, v_std=1.0)
+    _, V, _ = _inputs(wl)
+    n = len(SAME_K_SHAPES)
+    O_persist = mo.ns_orthogonalize_batched(V[:n], out_dtype=torch.float32, precision=precision)
+    O_tiles = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, precision=precision)
+    torch.cuda.synchronize()
+    for a, b in zip(O_persist, O_tiles[:n]):
+        assert torch.equal(a, b)
+    for i in (6, 7, 9):
+        x = f64(V[i])
+        ee = relF(f64(O_persist[i]), oracle.ns_orthogonalize(x))
+        rounding = "bf16_split" if precision == "split" else "bf16"
+        em = relF(f64(O_persist[i]), oracle.ns_orthogonalize(x, rounding=rounding))
+        print(f"{SAME_K_SHAPES[i]} ({precision}): relF(O) vs exact {ee:.2e}, vs model {em:.2e}",
+              flush=True)
+        assert ee <= 2e-2 and em <= 2e-2
+
+
 F32_SHAPES = [(256, 512), (150, 333), (333, 150), (64, 64), (1, 7), (7, 1), (65, 129)]
 
 
