@@ -186,20 +186,23 @@ def test_plan_eviction_frees_idle_plans(mo):
         assert torch.equal(again, o)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_nan_poisoned_workspace(mo, dtype):
+@pytest.mark.parametrize("dtype,precision", [("bf16", "default"), ("f32", "default"),
+                                             ("bf16", "split")])
+def test_nan_poisoned_workspace(mo, dtype, precision):
     shapes = SHAPES if dtype == "bf16" else [(300, 700), (700, 300), (64, 64), (37, 45)]
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     W, V, G = _inputs(shapes, seed=121, dtype=dtype)
-    need = mo.workspace_bytes(shapes, tdt)
+    need = mo.workspace_bytes(shapes, tdt, precision=precision)
     clean = torch.zeros(need, dtype=torch.uint8, device="cuda")
     poison = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN in bf16 and f32
     Wc, Vc = [w.clone() for w in W], [v.clone() for v in V]
     Wp, Vp = [w.clone() for w in W], [v.clone() for v in V]
-    mo.muon_step_batched(Wc, G, Vc, workspace=clean)
-    mo.muon_step_batched(Wp, G, Vp, workspace=poison)
-    Oc = mo.ns_orthogonalize_batched(Vc, out_dtype=torch.float32, workspace=clean.zero_())
-    Op = mo.ns_orthogonalize_batched(Vc, out_dtype=torch.float32, workspace=poison.fill_(0xFF))
+    mo.muon_step_batched(Wc, G, Vc, workspace=clean, precision=precision)
+    mo.muon_step_batched(Wp, G, Vp, workspace=poison, precision=precision)
+    Oc = mo.ns_orthogonalize_batched(Vc, out_dtype=torch.float32, workspace=clean.zero_(),
+                                     precision=precision)
+    Op = mo.ns_orthogonalize_batched(Vc, out_dtype=torch.float32,
+                                     workspace=poison.fill_(0xFF), precision=precision)
     torch.cuda.synchronize()
     for a, b in zip(Wc + Vc, Wp + Vp):
         assert torch.isfinite(b.float()).all()
