@@ -54,12 +54,18 @@
 // global store is a contiguous row segment.  The Gram, the polynomial and a
 // non-final apply skip the staging: their accumulators go straight to whole
 // 2 KB blocks of A, B or X' with cross-half-wave lane swaps, the polynomial
-// reading A at the lanes' own accumulator positions one 32-row stripe ahead.  On the last iteration the result is
+// reading A at the lanes' own accumulator positions one 32-row stripe ahead;
+// where every tile of the non-final apply has the same K extent, that launch
+// runs persistent (one workgroup per CU) and issues the next tile's DMA
+// before these stores.  On the last iteration the result is
 // written in the original orientation as O, or folded straight into
 // W <- W - lr*sqrt(max(1,rows/cols))*O (so O never round-trips through HBM).
 //
 // Roofline: a dense contraction; algorithmic flops per tile are 2*256*256*K
 // (K = n for stage 0, m for stages 1 and 2).  Bound: bf16 MFMA peak.
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "device_util.hpp"
 
@@ -1779,7 +1785,7 @@ struct ApplyTask {
 
 // Table entry pos as a task; false for idle or out-of-range entries.
 __device__ __forceinline__ bool apply_task(const GemmParams& P, int pos, const WaveGeo& g,
-                                           int lane, ApplyTask& t) {
+                                           ApplyTask& t) {
   const MATOPT_CAS GemmTile& tile = ((const MATOPT_CAS GemmTile*)P.tiles)[pos];
   const int mat = tile.mat, ti = tile.ti, tj = tile.tj;
   if (mat < 0 || tj < 0) return false;
@@ -1795,7 +1801,6 @@ __device__ __forceinline__ bool apply_task(const GemmParams& P, int pos, const W
   const int64_t nb = t.np / 32;
   t.out = xn + (((int64_t)(t.i0 + g.wi0) >> 5) * nb + ((t.j0 + g.wj0) >> 5)) * 1024;
   t.s = P.first ? *(const MATOPT_CAS float*)d.xs : 1.f;
-  (void)lane;
   return true;
 }
 
@@ -1820,7 +1825,7 @@ __device__ __forceinline__ void apply_persist(const GemmParams& P, uint8_t* lds)
   ApplyTask cur;
   bool have = false;
   for (; kpos < L; kpos += G)
-    if (apply_task(P, 8 * kpos + xcd, g, lane, cur)) {
+    if (apply_task(P, 8 * kpos + xcd, g, cur)) {
       have = true;
       break;
     }
@@ -1848,7 +1853,7 @@ __device__ __forceinline__ void apply_persist(const GemmParams& P, uint8_t* lds)
     ApplyTask nx;
     bool more = false;
     for (int kn = kpos + G; kn < L; kn += G)
-      if (apply_task(P, 8 * kn + xcd, g, lane, nx)) {
+      if (apply_task(P, 8 * kn + xcd, g, nx)) {
         more = true;
         kpos = kn;
         break;
@@ -1956,17 +1961,20 @@ int gemm_bf16_diag_mode(int stage) {
 #define MATOPT_APPLY_PERSIST 1
 #endif
 
+// Compute units per XCD of the current device (0 if unknown), cached per device.
 int persist_per_xcd() {
-  static int per[64] = {0};
+  static std::atomic<int> per[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (per[dev] == 0) {
+  int v = per[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    per[dev] = std::max(1, cus / 8);
+    v = std::max(1, cus / 8);
+    per[dev].store(v, std::memory_order_relaxed);
   }
-  return per[dev];
+  return v;
 }
 
 hipError_t launch_gemm_bf16(const GemmParams& p_in, int n_tiles, hipStream_t s) {
