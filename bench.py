@@ -128,6 +128,24 @@ def time_steps(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def step_stats(fn, steps, stream):
+    """Mean, median and min ms of `steps` calls of fn, each between its own
+    HIP events on `stream` (a separate pass from the headline timing)."""
+    import statistics
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    return {"mean": round(sum(t) / len(t), 4), "median": round(statistics.median(t), 4),
+            "min": round(min(t), 4)}
+
+
 def profiled(fn, steps, stream):
     """Per-kernel-class ms per step from the library's per-launch HIP events
     (and the wall ms per step of the pass); bf16 GEMM classes also carry the
@@ -286,7 +304,7 @@ def split_line(W, G, V, wl, steps, warmup, stream, ms_default):
             "kernels_ms": {k: round(v["ms_per_step"], 4) for k, v in per.items()}}
 
 
-def single_f32_line(stream, steps=200, warmup=20):
+def single_f32_line(stream, steps=200, warmup=20, with_oracle=True):
     """The float32 single 256 x 512 matrix: latency-bound (bind, prep,
     finalize, 15 GEMM launches), reported in microseconds per step."""
     import torch
@@ -304,9 +322,20 @@ def single_f32_line(stream, steps=200, warmup=20):
     kern_us = sum(v["ms_per_step"] for v in per.values()) * 1e3
     launches = sum(v["launches_per_step"] for v in per.values())
     log(f"[bench] single_f32_256x512: {ms * 1e3:.1f} us/step")
-    return {"workload": wl.name, "dtype": "f32", "us_per_step": round(ms * 1e3, 2),
-            "kernel_us_per_step": round(kern_us, 2), "launches_per_step": launches,
-            "steps": steps}
+    out = {"workload": wl.name, "dtype": "f32", "us_per_step": round(ms * 1e3, 2),
+           "kernel_us_per_step": round(kern_us, 2), "launches_per_step": launches,
+           "steps": steps}
+    if with_oracle:
+        # the oracle (exact float64) on the same matrix, one step at a time
+        import oracle
+        w, v, g = (x.to(torch.float64).numpy() for x in trip[0])
+        reps = 20
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.muon_step(w, g, v.copy(), mu=wl.mu, lr=wl.lr, steps=wl.ns_steps,
+                             dtype=wl.dtype, rounding="exact")
+        out["cpu_oracle_us_per_step"] = round((time.perf_counter() - t0) / reps * 1e6, 1)
+    return out
 
 
 def square_sweep(steps, warmup, stream):
@@ -484,6 +513,7 @@ def main():
 
     ms = time_steps(step, args.steps, args.warmup, stream)
     log(f"[bench] muon step {ms:.3f} ms")
+    per_step = step_stats(step, args.steps, stream)
 
     # second pass: per-launch HIP events inside the library, same stream
     ms_prof, per = profiled(step, args.steps, stream)
@@ -539,6 +569,7 @@ def main():
         "roofline": roofline,
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in per.items()},
         "ms_per_step_profiled": round(ms_prof, 4),
+        "ms_per_step_each": per_step,
         "hbm_kernels": {
             "prep": {"bytes_per_elem": round(prep_bytes / numel, 3),
                      "GB_s": round(prep_gbs, 1) if prep_gbs else None,
