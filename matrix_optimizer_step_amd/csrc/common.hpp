@@ -191,7 +191,8 @@ struct UploadArgs {
 // Tile geometry.
 constexpr int kPrepTile = 64;
 constexpr int kTileBf16 = 256;
-constexpr int kTileF32 = 64;
+constexpr int kTileF32 = 64;   // float32 padding granule
+constexpr int kGridF32 = 32;   // float32 GEMM output tile (divides kTileF32)
 
 // Launchers (each defined next to its kernel).
 hipError_t launch_prep(int dt, const PrepParams& p, int n_tiles, hipStream_t s);

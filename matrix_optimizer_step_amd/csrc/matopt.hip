@@ -448,7 +448,8 @@ P as_off(size_t off) {
 matopt_status build_ns_plan(Plan& P, int dt, const std::vector<Geo>& geo) {
   const int count = (int)geo.size();
   const Layout L = layout(geo, dt);
-  const int tile = gemm_tile(dt);
+  // GEMM output tile: the padding granule for bf16, a divisor of it for float32
+  const int tile = sdt(dt) == DT_BF16 ? kTileBf16 : kGridF32;
   std::vector<MatDesc> mats(count);
   std::vector<PrepTile> prep;
   std::vector<TileUnit> u3, u4, u5;

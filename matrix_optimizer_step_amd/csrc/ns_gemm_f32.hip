@@ -1,11 +1,18 @@
 // Newton-Schulz matrix products in float32 (the fp32 storage path), grouped over
-// a ragged batch.  The same three stages and tile tables as the bf16 MFMA
-// kernel (ns_gemm_bf16.hip), on a simpler engine: 64 x 64 output tiles, 256
-// threads each owning a 4 x 4 block, K step 16, float32 FMA accumulation.  The
-// polynomial is split between the stages here (B = b A + c A A, then
-// X' = a X + B X): nothing is rounded to bf16 in between, so the split and the
-// folded form (B = aI + bA + cAA, X' = B X) agree to float32 rounding.
-// No reduced-precision products are used anywhere on this path.
+// a ragged batch.  The same three stages as the bf16 MFMA kernel
+// (ns_gemm_bf16.hip) on a simpler engine: 32 x 32 output tiles (kGridF32; the
+// matrices are padded to kTileF32 = 64), four waves per tile, each wave
+// running its own K loop over every fourth K step of 16 and holding a 4 x 4
+// block of the tile per lane in float32 FMA accumulators; the four partial
+// tiles are summed in a fixed order through LDS at the end (deterministic).
+// Small tiles and the K split keep a small matrix's launch short: a 256 x 512
+// Gram is 36 tiles of 512 / 4 K values per wave.  The polynomial is split
+// between the stages here (B = b A + c A A, then X' = a X + B X): nothing is
+// rounded to bf16 in between, so the split and the folded form
+// (B = aI + bA + cAA, X' = B X) agree to float32 rounding.  A and B are
+// stored as their upper 32 x 32 tiles only (the Gram and polynomial tables
+// hold ti <= tj), X whole.  No reduced-precision products are used anywhere
+// on this path.
 //
 // Roofline: a dense contraction bound by the float32 vector FMA rate; in
 // practice this path serves small fp32 matrices and is latency bound.
@@ -16,10 +23,11 @@ namespace matopt {
 
 namespace {
 
-constexpr int TM = 64;     // tile rows == cols == symmetric block
-constexpr int TK = 16;
-constexpr int NTHR = 256;
-constexpr int PITCH = TM + 4;
+constexpr int TM = kGridF32;   // tile rows == cols == symmetric block
+constexpr int TK = 16;         // K step of one wave
+constexpr int NWAVE = 4;
+constexpr int NTHR = 64 * NWAVE;
+constexpr int PITCH = TM + 4;  // floats per staged k row
 
 enum OpMode { MODE_DIRECT = 0, MODE_TRANS = 1, MODE_SYM = 2 };
 
@@ -30,27 +38,49 @@ struct OpSrc {
   int mode;
 };
 
-// Fill s[k][r] (k < TK, r < TM) with operand rows r0.. and k columns k0..
-__device__ __forceinline__ void load_op(const OpSrc& o, int k0, float (*s)[PITCH]) {
-  const int t = threadIdx.x;
-  const bool tr = o.mode == MODE_TRANS || (o.mode == MODE_SYM && (k0 / TM) < (o.r0 / TM));
-  if (!tr) {
-    const int row = t >> 2, kc = (t & 3) * 4;
-    const f32x4 v = gload<f32x4>(o.ptr + (int64_t)(o.r0 + row) * o.ld + k0 + kc);
-    s[kc + 0][row] = v.x;
-    s[kc + 1][row] = v.y;
-    s[kc + 2][row] = v.z;
-    s[kc + 3][row] = v.w;
+// One operand slice of a wave's K step (TM rows x TK k values, k0 a multiple
+// of TK), 8 floats per lane, loaded into registers.
+struct OpRegs {
+  f32x4 v[2];
+};
+
+__device__ __forceinline__ bool op_trans(const OpSrc& o, int k0) {
+  // symmetric A stored as upper tiles: left of the diagonal block, rows r0..
+  // of A are columns r0.. of the upper tile above
+  return o.mode == MODE_TRANS || (o.mode == MODE_SYM && (k0 / TM) < (o.r0 / TM));
+}
+
+__device__ __forceinline__ void op_load(const OpSrc& o, int k0, int lane, OpRegs& r) {
+  if (!op_trans(o, k0)) {   // element (row, k) at ptr[(r0 + row) * ld + k0 + k]
+    const float* p = o.ptr + (int64_t)(o.r0 + (lane >> 1)) * o.ld + k0 + (lane & 1) * 8;
+    r.v[0] = gload<f32x4>(p);
+    r.v[1] = gload<f32x4>(p + 4);
+  } else {                  // element (row, k) at ptr[(k0 + k) * ld + r0 + row]
+    const float* p = o.ptr + (int64_t)(k0 + (lane >> 2)) * o.ld + o.r0 + (lane & 3) * 8;
+    r.v[0] = gload<f32x4>(p);
+    r.v[1] = gload<f32x4>(p + 4);
+  }
+}
+
+// Stage the slice as s[k][row].
+__device__ __forceinline__ void op_store(const OpSrc& o, int k0, int lane, const OpRegs& r,
+                                         float (*s)[PITCH]) {
+  if (!op_trans(o, k0)) {
+    const int row = lane >> 1, kc = (lane & 1) * 8;
+    const float f[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w,
+                        r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s[kc + q][row] = f[q];
   } else {
-    const int k = t >> 4, rc = (t & 15) * 4;
-    const f32x4 v = gload<f32x4>(o.ptr + (int64_t)(k0 + k) * o.ld + o.r0 + rc);
-    *(f32x4*)&s[k][rc] = v;
+    const int k = lane >> 2, rc = (lane & 3) * 8;
+    *(f32x4*)&s[k][rc] = r.v[0];
+    *(f32x4*)&s[k][rc + 4] = r.v[1];
   }
 }
 
 __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
-  __shared__ __attribute__((aligned(16))) float ps[TK][PITCH];
-  __shared__ __attribute__((aligned(16))) float qs[TK][PITCH];
+  // per wave: two buffers of P and Q slices; reused for the partial tiles
+  __shared__ __attribute__((aligned(16))) float stg[NWAVE][2][2][TK][PITCH];
 
   const GemmTile tile = P.tiles[blockIdx.x];
   if (tile.mat < 0) return;   // idle entry padding an XCD stream
@@ -79,24 +109,82 @@ __global__ __launch_bounds__(NTHR) void ns_gemm_f32_kernel(GemmParams P) {
     K = (int)mp;
   }
 
-  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ty = lane >> 3, tx = lane & 7;   // 4 x 4 block at rows 4 ty, columns 4 tx
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += TK) {
-    load_op(sp, k0, ps);
-    load_op(sq, k0, qs);
-    __syncthreads();
+  // wave w takes K steps w, w + 4, ... (K is a multiple of 64: every wave
+  // gets the same count); its loads of step s+1 are in flight while step s
+  // is multiplied out of the other buffer
+  const int nsteps = K / TK;
+  float (*buf)[2][TK][PITCH] = stg[wave];
+  int b = 0;
+  if (wave < nsteps) {
+    OpRegs rp, rq;
+    op_load(sp, wave * TK, lane, rp);
+    op_load(sq, wave * TK, lane, rq);
+    op_store(sp, wave * TK, lane, rp, buf[0][0]);
+    op_store(sq, wave * TK, lane, rq, buf[0][1]);
+  }
+  for (int st = wave; st < nsteps; st += NWAVE) {
+    const bool more = st + NWAVE < nsteps;
+    OpRegs rp, rq;
+    if (more) {
+      op_load(sp, (st + NWAVE) * TK, lane, rp);
+      op_load(sq, (st + NWAVE) * TK, lane, rq);
+    }
+    // the staged slice was written by this wave's own lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int k = 0; k < TK; ++k) {
-      const float4 a = *(const float4*)&ps[k][ty * 4];
-      const float4 b = *(const float4*)&qs[k][tx * 4];
+      const float4 a = *(const float4*)&buf[b][0][k][ty * 4];
+      const float4 c = *(const float4*)&buf[b][1][k][tx * 4];
       const float av[4] = {a.x, a.y, a.z, a.w};
-      const float bv[4] = {b.x, b.y, b.z, b.w};
+      const float cv[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+        for (int q = 0; q < 4; ++q) acc[r][q] = fmaf(av[r], cv[q], acc[r][q]);
     }
-    __syncthreads();
+    if (more) {
+      // the other buffer was last read one step ago, by this wave only
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      op_store(sp, (st + NWAVE) * TK, lane, rp, buf[b ^ 1][0]);
+      op_store(sq, (st + NWAVE) * TK, lane, rq, buf[b ^ 1][1]);
+    }
+    b ^= 1;
+  }
+
+  // partial tiles: wave w's 32 x 32 block at red[w] (row-major, pitch TM + 4)
+  __syncthreads();
+  float* red = &stg[0][0][0][0][0];
+  constexpr int RP = TM + 4;
+  static_assert(NWAVE * TM * RP <= NWAVE * 2 * 2 * TK * PITCH, "partials fit the staging");
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *(f32x4*)&red[wave * TM * RP + (ty * 4 + r) * RP + tx * 4] =
+        f32x4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    f32x4 t = *(const f32x4*)&red[(ty * 4 + r) * RP + tx * 4];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) {
+      const f32x4 u = *(const f32x4*)&red[w * TM * RP + (ty * 4 + r) * RP + tx * 4];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    acc[r][0] = t.x;
+    acc[r][1] = t.y;
+    acc[r][2] = t.z;
+    acc[r][3] = t.w;
   }
 
   const float xs = gload<float>(d.xs);
