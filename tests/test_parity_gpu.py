@@ -240,15 +240,22 @@ def test_ns_f32_ragged_batch(mo):
     assert max(errs) <= 1e-4
 
 
-@pytest.mark.parametrize("steps", [0, 1, 2])
-def test_ns_step_counts(mo, steps):
+# Both matrices pad to m = 512: every non-final apply runs as the persistent
+# kernel, and seven steps take each iterate buffer through it three times.
+@pytest.mark.parametrize("precision", ["default", "split"])
+@pytest.mark.parametrize("steps", [0, 1, 2, 7])
+def test_ns_step_counts(mo, steps, precision):
     wl = workloads.small_case("ns_steps", [(300, 500), (500, 300)], seed=13, v_std=1.0)
     _, V, _ = _inputs(wl)
-    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, ns_steps=steps)
+    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, ns_steps=steps,
+                                    precision=precision)
     torch.cuda.synchronize()
+    rounding = "bf16_split" if precision == "split" else "bf16"
     for v, o in zip(V, O):
-        ref = oracle.ns_orthogonalize(f64(v), steps=steps, rounding="bf16")
+        ref = oracle.ns_orthogonalize(f64(v), steps=steps, rounding=rounding)
         assert relF(f64(o), ref) <= (1e-6 if steps == 0 else 2e-2)
+        if steps:
+            assert relF(f64(o), oracle.ns_orthogonalize(f64(v), steps=steps)) <= 2e-2
 
 
 def test_ns_bf16_output_dtype(mo):
