@@ -20,7 +20,8 @@ of the benchmark (the float32 single matrix, the Llama-3-8B and 32B-class
 owner shares, the ill-conditioned ragged set), the single-matrix size sweep,
 and the CPU oracle timed on the whole GPT-2 Large set.
 
-Output: ONE JSON line on stdout (this build runs on one GPU only).
+Output: ONE JSON line on stdout (one GPU only: the owner-local step has no
+cross-GPU exchange).
 
 ``--summarize-profile DIR`` instead reads the CSV output of rocprofv3 runs of
 this script (kernel trace, counters) under DIR and prints a per-kernel-class
