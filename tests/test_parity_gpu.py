@@ -388,19 +388,21 @@ def test_muon_step_ns_steps_zero_and_lr_zero(mo):
 # weight decay 1e-2 at lr 1e-3; the second case makes the decay large enough to
 # move most bf16 weights.
 @pytest.mark.parametrize("lr,wd", [(1e-3, 1e-2), (0.05, 0.5)])
-def test_muon_wd_training_config_bf16(mo, lr, wd):
+@pytest.mark.parametrize("precision", ["default", "split"])
+def test_muon_wd_training_config_bf16(mo, lr, wd, precision):
     shapes = [(700, 1300), (1300, 700), (256, 256), (37, 45), (1, 300), (300, 1)]
     wl = workloads.small_case("muon_wd", shapes, seed=23)
     W, V, G = _inputs(wl)
     W0, V0 = [w.clone() for w in W], [v.clone() for v in V]
-    mo.muon_step_batched_wd(W, G, V, mu=0.5, lr=lr, wd=wd, ns_steps=2)
-    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, ns_steps=2)
+    mo.muon_step_batched_wd(W, G, V, mu=0.5, lr=lr, wd=wd, ns_steps=2, precision=precision)
+    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, ns_steps=2, precision=precision)
     torch.cuda.synchronize()
+    rounding = "bf16_split" if precision == "split" else "bf16"
     moved = 0
     for w, w0, v, v0, g, o in zip(W, W0, V, V0, G, O):
         _check_v(v, v0, g, 0.5)
         _check_w(w, w0, o, lr, wd)
-        ref = oracle.ns_orthogonalize(f64(v), steps=2, rounding="bf16")
+        ref = oracle.ns_orthogonalize(f64(v), steps=2, rounding=rounding)
         assert relF(f64(o), ref) <= 2e-2
         moved += int((w != w0).sum())
     assert moved > 0
