@@ -48,13 +48,26 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
   // All loads of the row first (V, G and W are distinct buffers, but the
   // compiler cannot know that, so a load written after the V store would wait
   // for it), then the momentum, its sum of squares and the V stores.
+  //
+  // float32 rows load without a branch: a lane whose chunk lies past the
+  // row's end loads the row's first chunk (a valid address) and never uses
+  // it.  Behind a branch per chunk the compiler copies the float32 register
+  // arrays around (eight chunks per lane took ~500 registers); the bfloat16
+  // variants keep the branch, which costs them fewer registers than the
+  // unconditional float64 momentum of the unused chunks would.
+  constexpr bool CLAMP = sizeof(T) == 4;
   u32x4 vreg[NCH], greg[NCH], wreg[NCH];
   float ss = 0.f;
   if (active) {
 #pragma unroll
     for (int p = 0; p < NCH; ++p) {
       const int64_t ch = lr_idx + (int64_t)LPR * p;
-      if (ch < nchunks) {
+      if (CLAMP) {
+        const int64_t cl = ch < nchunks ? ch : 0;
+        vreg[p] = gload_nt<u32x4>(vrow + cl * E);
+        greg[p] = gload_nt<u32x4>(grow + cl * E);
+        wreg[p] = gload_nt<u32x4>(wrow + cl * E);
+      } else if (ch < nchunks) {
         vreg[p] = gload_nt<u32x4>(vrow + ch * E);
         greg[p] = gload_nt<u32x4>(grow + ch * E);
         wreg[p] = gload_nt<u32x4>(wrow + ch * E);

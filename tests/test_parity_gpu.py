@@ -497,8 +497,11 @@ def test_muon_two_steps_resume(mo):
 # RMNP
 # --------------------------------------------------------------------------
 
+# widths that reach every register-resident variant in both dtypes (rows of
+# one wave with 1, 2, 4 and 8 chunks per lane, of a workgroup with 4, 8 and 16)
+# with lanes past the row's end, and the streaming variant
 RMNP_SHAPES = [(96, 1280), (40, 5120), (8, 27648), (3, 40000), (50, 45), (64, 8),
-               (200, 64), (17, 3000)]
+               (200, 64), (17, 3000), (9, 400), (11, 1000), (5, 12000)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
