@@ -22,9 +22,11 @@
 // is read row-major by the Gram and k-major (through its columns) by apply.
 //
 // Engine.  A 256 x 256 output tile per workgroup of 8 waves, two per SIMD
-// (each wave 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16, accumulators
-// in AGPRs; while one wave of a SIMD waits on LDS the other issues MFMAs).  A
-// 4-wave variant (128 x 128 per wave) is kept behind MATOPT_*_WAVES.  The
+// (each wave 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16, the 128
+// accumulators per lane in VGPRs within the 256 a wave has at two waves per
+// SIMD; while one wave of a SIMD waits on LDS the other issues MFMAs).  A
+// 4-wave variant (128 x 128 per wave, accumulators in AGPRs) is kept behind
+// MATOPT_*_WAVES.  The
 // K loop runs in steps of 32 through NS = 5 LDS stages of 32 KB (one 256 x 32
 // tile per operand), filled by global_load_lds_dwordx4 (HBM -> LDS without
 // registers) three steps ahead of use, in the layout the tile has in HBM.
