@@ -258,6 +258,33 @@ def test_ns_step_counts(mo, steps, precision):
             assert relF(f64(o), oracle.ns_orthogonalize(f64(v), steps=steps)) <= 2e-2
 
 
+# Coefficients other than the default quintic reach the kernels unchanged: the
+# classic cubic (c = 0, the polynomial is a I + b A), the quintic with the
+# flattest fixed point at 1 (15/8, -10/8, 3/8), and a quintic with fixed point
+# 1 and a negative slope there (3, -3.2, 1.2).  Wide, tall (transposed) and
+# aligned (read in place) matrices, in both precisions.
+OTHER_COEFFS = [(1.5, -0.5, 0.0), (1.875, -1.25, 0.375), (3.0, -3.2, 1.2)]
+
+
+@pytest.mark.parametrize("coeffs", OTHER_COEFFS, ids=["cubic", "quintic-flat", "quintic-oscillating"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ns_other_coefficients(mo, coeffs, dtype):
+    shapes = [(300, 700), (520, 260), (256, 256)]
+    wl = workloads.small_case("ns_coeffs", shapes, dtype=dtype, seed=17, v_std=1.0)
+    _, V, _ = _inputs(wl)
+    O = mo.ns_orthogonalize_batched(V, out_dtype=torch.float32, coeffs=coeffs)
+    torch.cuda.synchronize()
+    for shape, v, o in zip(shapes, V, O):
+        x = f64(v)
+        ee = relF(f64(o), oracle.ns_orthogonalize(x, coeffs=coeffs))
+        if dtype == "f32":
+            assert ee <= 1e-4, (shape, ee)
+        else:
+            em = relF(f64(o), oracle.ns_orthogonalize(x, coeffs=coeffs, rounding="bf16"))
+            print(f"{coeffs} {shape}: relF(O) vs bf16 model {em:.2e}, vs exact {ee:.2e}", flush=True)
+            assert em <= 2e-2 and ee <= 2e-2, (shape, em, ee)
+
+
 def test_ns_bf16_output_dtype(mo):
     wl = workloads.small_case("ns_out", [(512, 768)], seed=14, v_std=1.0)
     _, V, _ = _inputs(wl)
