@@ -102,6 +102,43 @@ __device__ __forceinline__ uint32_t w_update_bf16(float w, float upd, float o, d
   return f2bf(s);
 }
 
+// The weight update of N bfloat16 weights at once, as float32 values whose
+// nearest-even bfloat16 (pack_bf2) is the bits of w_update_bf16 element by
+// element.  The midpoint test is taken for all N first, and one branch --
+// rarely taken: a float32 sum lands on a bfloat16 midpoint about once in
+// 65536 elements -- covers the float64 side decision of the whole group,
+// instead of one branch per element around it.  With decay, each value is the
+// float64 update rounded to odd (whose nearest-even bfloat16 is the float64
+// value rounded once); wdl is uniform, so that is one branch too.
+template <int N>
+__device__ __forceinline__ void w_update_f32_n(const float (&w)[N], float upd,
+                                               const float (&o)[N], double wdl,
+                                               float (&s)[N]) {
+  if (wdl != 0.0) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) s[e] = f64_to_f32_odd(w_update(w[e], upd, o[e], wdl));
+    return;
+  }
+  uint32_t z = 0xffffffffu;   // zero iff some element sits on a midpoint
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    s[e] = fmaf(upd, o[e], w[e]);
+    z = min(z, (__float_as_uint(s[e]) ^ 0x8000u) & 0xffffu);
+  }
+  if (z == 0u) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      uint32_t u = __float_as_uint(s[e]);
+      if ((u & 0xffffu) == 0x8000u) {
+        const double x = fma((double)upd, (double)o[e], (double)w[e]);
+        const double sd = (double)s[e];
+        if (x != sd) u += ((x > sd) == (s[e] > 0.f)) ? 1u : 0xffffffffu;
+        s[e] = __uint_as_float(u);
+      }
+    }
+  }
+}
+
 // Element traits: 16-byte vectors hold E elements of T.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -415,10 +415,9 @@ __device__ __forceinline__ void write_out4(const MatDesc& d, const GemmParams& P
       uint16_t* w = (uint16_t*)d.w + off;
       const u32x2 wo = gload<u32x2>(w);
       const float w4[4] = {lo_bf(wo.x), hi_bf(wo.x), lo_bf(wo.y), hi_bf(wo.y)};
-      uint32_t h[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = w_update_bf16(w4[e], upd, v[e], P.wdl);
-      gstore<u32x2>(w, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+      float u[4];
+      w_update_f32_n<4>(w4, upd, v, P.wdl, u);
+      gstore<u32x2>(w, u32x2{pack_bf2(u[0], u[1]), pack_bf2(u[2], u[3])});
     }
     return;
   }
@@ -510,14 +509,11 @@ __device__ __forceinline__ void final_pass(const MatDesc& d, const GemmParams& P
         const u32x4 wo = wpre[p];
         const float w8[8] = {lo_bf(wo.x), hi_bf(wo.x), lo_bf(wo.y), hi_bf(wo.y),
                              lo_bf(wo.z), hi_bf(wo.z), lo_bf(wo.w), hi_bf(wo.w)};
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          h[e] = w_update_bf16(w8[e], upd, lo[e], P.wdl);
-          h[4 + e] = w_update_bf16(w8[4 + e], upd, hi[e], P.wdl);
-        }
-        gstore<u32x4>((uint16_t*)d.w + off, u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                                  h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+        const float o8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        float u[8];
+        w_update_f32_n<8>(w8, upd, o8, P.wdl, u);
+        gstore<u32x4>((uint16_t*)d.w + off, u32x4{pack_bf2(u[0], u[1]), pack_bf2(u[2], u[3]),
+                                                  pack_bf2(u[4], u[5]), pack_bf2(u[6], u[7])});
       }
     }
   } else {
