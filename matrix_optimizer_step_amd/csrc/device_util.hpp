@@ -102,14 +102,44 @@ __device__ __forceinline__ uint32_t w_update_bf16(float w, float upd, float o, d
   return f2bf(s);
 }
 
+// a * b[e] + c[e] for N elements, as float32 values whose nearest-even
+// bfloat16 is the exact value rounded once to bfloat16 -- the same bits as
+// f64_to_bf16 of the float64 fma, element by element.  The float32 fma is the
+// exact value rounded once; rounding that to bfloat16 can differ from rounding
+// the exact value only when it lands on a bfloat16 midpoint (low 16 bits
+// 0x8000), and there the float64 value decides the side (the float32 is moved
+// one unit toward it, as rounding to odd does).  The midpoint test is taken
+// for all N first, and one branch -- rarely taken: about once in 65536
+// elements -- covers the float64 decision of the whole group, instead of one
+// branch per element around it.
+template <int N>
+__device__ __forceinline__ void fma_bf16_f32_n(float a, const float (&b)[N], const float (&c)[N],
+                                               float (&s)[N]) {
+  uint32_t z = 0xffffffffu;   // zero iff some element sits on a midpoint
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    s[e] = fmaf(a, b[e], c[e]);
+    z = min(z, (__float_as_uint(s[e]) ^ 0x8000u) & 0xffffu);
+  }
+  if (z == 0u) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      uint32_t u = __float_as_uint(s[e]);
+      if ((u & 0xffffu) == 0x8000u) {
+        const double x = fma((double)a, (double)b[e], (double)c[e]);
+        const double sd = (double)s[e];
+        if (x != sd) u += ((x > sd) == (s[e] > 0.f)) ? 1u : 0xffffffffu;
+        s[e] = __uint_as_float(u);
+      }
+    }
+  }
+}
+
 // The weight update of N bfloat16 weights at once, as float32 values whose
 // nearest-even bfloat16 (pack_bf2) is the bits of w_update_bf16 element by
-// element.  The midpoint test is taken for all N first, and one branch --
-// rarely taken: a float32 sum lands on a bfloat16 midpoint about once in
-// 65536 elements -- covers the float64 side decision of the whole group,
-// instead of one branch per element around it.  With decay, each value is the
-// float64 update rounded to odd (whose nearest-even bfloat16 is the float64
-// value rounded once); wdl is uniform, so that is one branch too.
+// element: fma_bf16_f32_n without decay; with decay each value is the float64
+// update rounded to odd (whose nearest-even bfloat16 is the float64 value
+// rounded once), behind one branch on the uniform wdl.
 template <int N>
 __device__ __forceinline__ void w_update_f32_n(const float (&w)[N], float upd,
                                                const float (&o)[N], double wdl,
@@ -119,24 +149,7 @@ __device__ __forceinline__ void w_update_f32_n(const float (&w)[N], float upd,
     for (int e = 0; e < N; ++e) s[e] = f64_to_f32_odd(w_update(w[e], upd, o[e], wdl));
     return;
   }
-  uint32_t z = 0xffffffffu;   // zero iff some element sits on a midpoint
-#pragma unroll
-  for (int e = 0; e < N; ++e) {
-    s[e] = fmaf(upd, o[e], w[e]);
-    z = min(z, (__float_as_uint(s[e]) ^ 0x8000u) & 0xffffu);
-  }
-  if (z == 0u) {
-#pragma unroll
-    for (int e = 0; e < N; ++e) {
-      uint32_t u = __float_as_uint(s[e]);
-      if ((u & 0xffffu) == 0x8000u) {
-        const double x = fma((double)upd, (double)o[e], (double)w[e]);
-        const double sd = (double)s[e];
-        if (x != sd) u += ((x > sd) == (s[e] > 0.f)) ? 1u : 0xffffffffu;
-        s[e] = __uint_as_float(u);
-      }
-    }
-  }
+  fma_bf16_f32_n<N>(upd, o, w, s);
 }
 
 // Element traits: 16-byte vectors hold E elements of T.
@@ -153,6 +166,12 @@ template <> struct Elem<float> {
   }
   // a*b + c rounded once to storage (float32 fma is exact-then-round)
   __device__ static float fma_store(float a, float b, float c) { return fmaf(a, b, c); }
+  template <int N>
+  __device__ static void fma_store_n(float a, const float (&b)[N], const float (&c)[N],
+                                     float (&out)[N]) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) out[e] = fmaf(a, b[e], c[e]);
+  }
   // a float64 value rounded to storage
   __device__ static float round_store(double x) { return (float)x; }
   __device__ static float load1(const void* p, int64_t i) {
@@ -175,6 +194,15 @@ template <> struct Elem<uint16_t> {  // bfloat16
   // momentum); otherwise its own rounding sits 45 bits below bfloat16 precision.
   __device__ static float fma_store(float a, float b, float c) {
     return bf2f(f64_to_bf16(fma((double)a, (double)b, (double)c)));
+  }
+  // fma_store of N elements (the same values), through fma_bf16_f32_n
+  template <int N>
+  __device__ static void fma_store_n(float a, const float (&b)[N], const float (&c)[N],
+                                     float (&out)[N]) {
+    float s[N];
+    fma_bf16_f32_n<N>(a, b, c, s);
+#pragma unroll
+    for (int e = 0; e < N; ++e) out[e] = bf2f(f2bf(s[e]));
   }
   __device__ static float round_store(double x) { return bf2f(f64_to_bf16(x)); }
   __device__ static float load1(const void* p, int64_t i) {

@@ -77,15 +77,13 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
     for (int p = 0; p < NCH; ++p) {
       const int64_t ch = lr_idx + (int64_t)LPR * p;
       if (ch < nchunks) {
-        float fv[E], fg[E];
+        float fv[E], fg[E], vn[E];
         Tr::unpack(vreg[p], fv);
         Tr::unpack(greg[p], fg);
+        Tr::template fma_store_n<E>(P.mu, fv, fg, vn);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          fv[e] = Tr::fma_store(P.mu, fv[e], fg[e]);
-          ss = fmaf(fv[e], fv[e], ss);
-        }
-        vreg[p] = Tr::pack(fv);
+        for (int e = 0; e < E; ++e) ss = fmaf(vn[e], vn[e], ss);
+        vreg[p] = Tr::pack(vn);
         gstore_nt<u32x4>(vrow + ch * E, vreg[p]);
       }
     }
@@ -103,12 +101,11 @@ __global__ __launch_bounds__(kThreads) void rmnp_kernel(RmnpParams P) {
   for (int p = 0; p < NCH; ++p) {
     const int64_t ch = lr_idx + (int64_t)LPR * p;
     if (ch < nchunks) {
-      float fv[E], fw[E];
+      float fv[E], fw[E], wn[E];
       Tr::unpack(vreg[p], fv);
       Tr::unpack(wreg[p], fw);
-#pragma unroll
-      for (int e = 0; e < E; ++e) fw[e] = Tr::fma_store(step, fv[e], fw[e]);
-      gstore_nt<u32x4>(wrow + ch * E, Tr::pack(fw));
+      Tr::template fma_store_n<E>(step, fv, fw, wn);
+      gstore_nt<u32x4>(wrow + ch * E, Tr::pack(wn));
     }
   }
 }
@@ -187,15 +184,13 @@ __global__ __launch_bounds__(kThreads) void colcut_partial_kernel(ColcutParams P
       for (int u = 0; u < kColcutUnroll; ++u) {
         const int64_t ch = base + 64 * u;
         if (ch < nch) {
-          float fv[E], fg[E];
+          float fv[E], fg[E], vn[E];
           Tr::unpack(vv[u], fv);
           Tr::unpack(gg[u], fg);
+          Tr::template fma_store_n<E>(P.mu, fv, fg, vn);
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            fv[e] = Tr::fma_store(P.mu, fv[e], fg[e]);
-            ss = fmaf(fv[e], fv[e], ss);
-          }
-          gstore_nt<u32x4>(vrow + ch * E, Tr::pack(fv));
+          for (int e = 0; e < E; ++e) ss = fmaf(vn[e], vn[e], ss);
+          gstore_nt<u32x4>(vrow + ch * E, Tr::pack(vn));
         }
       }
     }
@@ -240,12 +235,11 @@ __global__ __launch_bounds__(kThreads) void colcut_apply_kernel(ColcutParams P) 
       for (int u = 0; u < kColcutUnroll; ++u) {
         const int64_t ch = base + 64 * u;
         if (ch < nch) {
-          float fv[E], fw[E];
+          float fv[E], fw[E], wn[E];
           Tr::unpack(vv[u], fv);
           Tr::unpack(ww[u], fw);
-#pragma unroll
-          for (int e = 0; e < E; ++e) fw[e] = Tr::fma_store(step, fv[e], fw[e]);
-          gstore_nt<u32x4>(wrow + ch * E, Tr::pack(fw));
+          Tr::template fma_store_n<E>(step, fv, fw, wn);
+          gstore_nt<u32x4>(wrow + ch * E, Tr::pack(wn));
         }
       }
     }
