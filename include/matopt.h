@@ -143,10 +143,10 @@ matopt_status muon_step_batched(const matopt_mat* mats, int32_t count, matopt_dt
  * on one GPU share that GPU's array, which keeps the last call's contents
  * (nothing in it has to be zero on entry); calls that overlap on one GPU --
  * on different streams without ordering between them -- race on it, so the
- * caller must order them.  A call enqueues kernel launches only (no memory
- * operation, event or synchronisation), so it can be captured into a HIP
- * graph; a captured step replays with the pointers and scalars it was
- * captured with.
+ * caller must order them.  With profiling off (matopt_profile_enable), a
+ * call enqueues kernel launches only (no memory operation, event or
+ * synchronisation), so it can be captured into a HIP graph; a captured step
+ * replays with the pointers and scalars it was captured with.
  */
 #define MATOPT_NOALLOC_SCRATCH_BYTES (64u << 20)
 matopt_status muon_step_batched_noalloc(const matopt_mat* mats, int32_t count, matopt_dtype dt,
