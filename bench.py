@@ -437,6 +437,33 @@ def summarize_profile(directory, flops_per_step=None, steps=None):
     return out
 
 
+def zero_data_line(wl, W, G, V, steps, warmup, stream):
+    """The step on the set's own G, V and on all-zero G, V: the same launches,
+    tables and instructions (the iterates are then zero throughout), so any
+    difference in time comes from what the data does to the clock."""
+    import torch
+    import matrix_optimizer_step_amd as mo
+    out = {"diagnostic": "same launches on Gaussian and on all-zero G, V", "workload": wl.name,
+           "steps": steps, "warmup": warmup}
+    zeros = ([torch.zeros_like(g) for g in G], [torch.zeros_like(v) for v in V])
+    for label, (g_, v_) in (("gaussian", (G, V)), ("zero", zeros)):
+        def step():
+            mo.muon_step_batched(W, g_, v_, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps)
+        ms = time_steps(step, steps, warmup, stream)
+        _, per = profiled(step, steps, stream)
+        _, _, tf = gemm_rates(per, ns_alg_flops(wl.shapes, wl.ns_steps))
+        out[label] = {
+            "ms_per_step": round(ms, 4),
+            "gemm_clock_mhz": round(gemm_clock(per) or 0.0),
+            "ns_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4) if tf else None,
+            "us_per_launch": {k: round(v["ms_per_step"] * 1e3 / v["launches_per_step"], 1)
+                              for k, v in per.items() if k in ("gram", "poly", "apply")},
+            "clock_mhz": {k: round(v.get("clock_mhz", 0.0)) for k, v in per.items()
+                          if k in ("gram", "poly", "apply")},
+        }
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,6 +482,10 @@ def main():
                          "lines), e.g. for a profiler run")
     ap.add_argument("--sweep", action="store_true",
                     help="only the single-matrix sweep (s = 1024..8192), as its own JSON line")
+    ap.add_argument("--zero-data", action="store_true",
+                    help="diagnostic only: the same step on the set's Gaussian G, V and on "
+                         "all-zero G, V (identical launches and instructions, no data toggling), "
+                         "one JSON line with both times and the GEMM clocks; no headline line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (float32), the "
                          "known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
@@ -508,6 +539,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+
+    if args.zero_data:
+        print(json.dumps(zero_data_line(wl, W, G, V, args.steps, args.warmup, stream)), flush=True)
+        return
 
     def step():
         mo.muon_step_batched(W, G, V, mu=wl.mu, lr=wl.lr, ns_steps=wl.ns_steps)
