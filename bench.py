@@ -378,6 +378,8 @@ def kernel_class(name):
     """Kernel class of a rocprofv3 kernel name (the library's kernels only)."""
     if "ns_apply_persist_kernel" in name:
         return "apply"
+    if "prep_t_kernel" in name:   # the transposed bf16 matrices' prep launch
+        return "prep"
     m = re.search(r"ns_gemm_bf16_kernel<(\d+), (\d+), \d+(?:, (?:true|false))?>", name)
     if m:
         st, out = m.group(1), m.group(2)

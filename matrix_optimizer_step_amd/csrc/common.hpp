@@ -53,7 +53,9 @@ struct MatDesc {
                         // of the stored V in the same layout, so it is not written
 };
 
-// Prep tile: 64 x 64 block of the padded original-orientation matrix.
+// Prep tile: 64 x 64 block of the padded original-orientation matrix (64 x
+// kPrepTileT for a transposed bf16 matrix); an untransposed matrix's prep
+// kernel reads the tile index idx as a run of 4096 elements of X0 instead.
 struct PrepTile {
   int32_t mat, tr, tc, idx;   // idx: tile index within the matrix
 };
@@ -188,14 +190,18 @@ struct UploadArgs {
   alignas(16) uint8_t data[kUploadBytes];
 };
 
-// Tile geometry.
+// Tile geometry.  Prep tiles are 64 x 64 (64 x kPrepTileT for bf16 matrices
+// that are transposed: 256-byte runs of every row they read and write).
 constexpr int kPrepTile = 64;
+constexpr int kPrepTileT = 128;
 constexpr int kTileBf16 = 256;
 constexpr int kTileF32 = 64;   // float32 padding granule
 constexpr int kGridF32 = 32;   // float32 GEMM output tile (divides kTileF32)
 
 // Launchers (each defined next to its kernel).
 hipError_t launch_prep(int dt, const PrepParams& p, int n_tiles, hipStream_t s);
+// Prep of the bf16 matrices that are transposed (64 x kPrepTileT tiles).
+hipError_t launch_prep_t(const PrepParams& p, int n_tiles, hipStream_t s);
 hipError_t launch_finalize(const FinalizeParams& p, int count, hipStream_t s);
 hipError_t launch_scale_out(int dt, const ScaleOutParams& p, int n_tiles, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s);

@@ -107,7 +107,7 @@ Geo geometry(int64_t rows, int64_t cols, int dt) {
   const int rows_p = g.transposed ? g.np : g.mp;
   const int cols_p = g.transposed ? g.mp : g.np;
   g.prep_tr = rows_p / kPrepTile;
-  g.prep_tc = cols_p / kPrepTile;
+  g.prep_tc = cols_p / (g.transposed && sdt(dt) == DT_BF16 ? kPrepTileT : kPrepTile);
   return g;
 }
 
@@ -264,7 +264,8 @@ struct Plan {
   size_t o_slot = 0;                 // descriptors of calls without a workspace
   size_t ws_desc = 0;                // Newton-Schulz plans: descriptor offset in the workspace
   size_t o_prep = 0;
-  int n_prep = 0;
+  int n_prep = 0;     // prep tiles: prep_kernel's first, then prep_t_kernel's
+  int n_prep_u = 0;   // prep_kernel's (all but transposed bf16 matrices)
   TileTable gram, poly, apply;
   int count = 0;
   std::vector<RmnpGroup> rmnp;
@@ -478,9 +479,11 @@ matopt_status build_ns_plan(Plan& P, int dt, const std::vector<Geo>& geo) {
     d.xs = as_off<float*>(L.xs + 4 * (size_t)i);
     d.partials = as_off<float*>(L.partials + 4 * (size_t)L.prep_off[i]);
     d.n_prep = g.prep_tr * g.prep_tc;
-    int idx = 0;
-    for (int tr = 0; tr < g.prep_tr; ++tr)
-      for (int tc = 0; tc < g.prep_tc; ++tc) prep.push_back({i, tr, tc, idx++});
+    if (!(g.transposed && sdt(dt) == DT_BF16)) {
+      int idx = 0;
+      for (int tr = 0; tr < g.prep_tr; ++tr)
+        for (int tc = 0; tc < g.prep_tc; ++tc) prep.push_back({i, tr, tc, idx++});
+    }
     const int tm = g.mp / tile, tn = g.np / tile;
     // diagonal tiles as the GEMM build treats them (bf16: 36 of their 64
     // blocks; the Gram's two per workgroup, in step with the matrix's other
@@ -490,6 +493,15 @@ matopt_status build_ns_plan(Plan& P, int dt, const std::vector<Geo>& geo) {
     units_triangle(i, tm, g.np, u3, dm3 ? 9 : 16, dm3 == 2);
     units_triangle(i, tm, g.mp, u4, dm4 ? 9 : 16, dm4 == 2);
     units_full(i, tm, tn, g.mp, u5);
+  }
+  // the transposed bf16 matrices' tiles, for their own launch
+  P.n_prep_u = (int)prep.size();
+  for (int i = 0; i < count; ++i) {
+    const Geo& g = geo[i];
+    if (!(g.transposed && sdt(dt) == DT_BF16)) continue;
+    int idx = 0;
+    for (int tr = 0; tr < g.prep_tr; ++tr)
+      for (int tc = 0; tc < g.prep_tc; ++tc) prep.push_back({i, tr, tc, idx++});
   }
   static_assert(sizeof(TileRef) == sizeof(GemmTile), "tile record layout");
   const std::vector<TileRef> k3 = xcd_schedule(u3), k4 = xcd_schedule(u4), k5 = xcd_schedule(u5);
@@ -563,10 +575,11 @@ matopt_status build_rmnp_plan(Plan& P, int dt, const std::vector<std::pair<int64
 struct NsTables {
   const uint8_t* base;
   size_t o_prep;
-  int n_prep, count;
+  int n_prep, n_prep_u, count;
   TileTable gram, poly, apply;
   NsTables(const Plan& p, const void* dev_base)
-      : base((const uint8_t*)dev_base), o_prep(p.o_prep), n_prep(p.n_prep), count(p.count),
+      : base((const uint8_t*)dev_base), o_prep(p.o_prep), n_prep(p.n_prep),
+        n_prep_u(p.n_prep_u), count(p.count),
         gram(p.gram), poly(p.poly), apply(p.apply) {}
   template <class T>
   const T* dev(size_t off) const { return (const T*)(base + off); }
@@ -582,8 +595,13 @@ matopt_status run_ns(const NsTables& P, const MatDesc* mats, int dt, bool moment
   dt = sdt(dt);
   const PrepTile* prep = P.dev<const PrepTile>(P.o_prep);
   PrepParams pp{mats, prep, mu, momentum ? 1 : 0};
-  e = timed(0, s, [&] { return launch_prep(dt, pp, P.n_prep, s); });
+  e = timed(0, s, [&] { return launch_prep(dt, pp, P.n_prep_u, s); });
   if (e != hipSuccess) return hip_fail("prep launch", e);
+  if (P.n_prep > P.n_prep_u) {
+    const PrepParams pt{mats, prep + P.n_prep_u, mu, momentum ? 1 : 0};
+    e = timed(0, s, [&] { return launch_prep_t(pt, P.n_prep - P.n_prep_u, s); });
+    if (e != hipSuccess) return hip_fail("prep launch", e);
+  }
   FinalizeParams fp{mats, eps};
   e = timed(1, s, [&] { return launch_finalize(fp, P.count, s); });
   if (e != hipSuccess) return hip_fail("finalize launch", e);

@@ -34,6 +34,7 @@ NS = "void matopt::(anonymous namespace)::"
     (NS + "ns_gemm_bf16_kernel<0, 0, 8>(matopt::GemmParams)", "gram"),
     (NS + "ns_apply_persist_kernel<8>(matopt::GemmParams)", "apply"),
     (NS + "prep_kernel<unsigned short>(matopt::PrepParams)", "prep"),
+    (NS + "prep_t_kernel(matopt::PrepParams)", "prep"),
     (NS + "rmnp_kernel<unsigned short, 1, 4>(matopt::RmnpParams)", "rmnp"),
     (NS + "bind_kernel(matopt::BindArgs)", "bind"),
     ("__amd_rocclr_copyBuffer", "copy"),
