@@ -87,6 +87,10 @@
 #ifndef MATOPT_PAIR_APPLY
 #define MATOPT_PAIR_APPLY 1
 #endif
+// Apply launches on the 16 x 16 x 32 engine (1) or on 32 x 32 x 16 MFMAs (0).
+#ifndef MATOPT_APPLY_MFMA16
+#define MATOPT_APPLY_MFMA16 1
+#endif
 // Diagonal Gram and polynomial tiles compute only their upper 36 of 64 blocks.
 #ifndef MATOPT_DIAG_TILES
 #define MATOPT_DIAG_TILES 1
@@ -1112,6 +1116,347 @@ __device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP
   kloop2_rest<PF, QF, NBJ, BPW>(k, nk, bP, dp, dq, g, fo, wave, lds);
 }
 
+// ------------------------------------------- 16 x 16 x 32 MFMA engine
+// The apply stage's K loop on v_mfma_f32_16x16x32_bf16 in place of the
+// 32 x 32 x 16 form: each wave's 128 x 64 sub-tile is 8 x 4 slabs of 16 x 16,
+// each K step of 32 one MFMA per slab (32 per wave and step: the same flops
+// and the same LDS fragment bytes).  On this part the 16 x 16 form draws less
+// power per flop on random data, so the clock it sustains under load is
+// higher (a register-only MFMA loop: 1.93 against 1.71 GHz; with its LDS
+// reads: 1.86 against 1.71 GHz).  A K step is issued as two halves (P slabs
+// 0-3, then 4-7, each against the step's four Q slabs); the barrier and the
+// DMA sit between the halves as in kstep2, and Q is double-buffered across
+// steps (the next step's Q slabs are read while the second half still uses
+// this step's).
+//
+// Fragments cover 16 operand rows and the whole K step: lane l holds row
+// (l & 15) of the slab at k = 8(l >> 4) .. +7.
+//   row-major: one ds_read_b128 at rm_off(l & 15, l >> 4) from the slab's
+//              first row (the chunk swizzle depends on row & 12 only);
+//   k-major:   two ds_read_b64_tr_b16; lane c = 4e + h of 16-lane group G
+//              points at k row 8G + e (8G + 4 + e for the second read, 2048
+//              bytes on) and slab rows 4h .. 4h+3, so that lane c receives
+//              slab row c at four consecutive k.
+// Accumulator slab (i, j) of a lane holds C[16i + (l & 15)][16j + 4(l >> 4)
+// + 0..3] (operands swapped, as in mfma16).
+struct Frag16 {
+  uint32_t rm;       // row-major, from the slab's first row
+  uint32_t kmp[4];   // k-major P slabs, by slab pair s >> 1 (wave origin added at the read)
+  uint32_t kmq[2];   // k-major Q slabs of the wave, by slab pair, origin included
+  __device__ void init(int lane, int wq0) {
+    const int G = lane >> 4, c = lane & 15, e = c >> 2, h = c & 3;
+    rm = rm_off(c, G);
+    const int kr = 8 * G + e;
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp) kmp[sp] = kr * 512 + ((sp ^ e) << 6) + 8 * h;
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+      kmq[sp] = kr * 512 + (((((wq0 >> 5) + sp) ^ e) & 7) << 6) + 8 * h;
+  }
+};
+
+// P slabs S0 .. S0+3 of the wave (origin wo, a multiple of 128: its unit bits
+// never meet the swizzle).
+template <bool KM, int S0>
+__device__ __forceinline__ void read_p16(const uint8_t* __restrict__ stage, int wo,
+                                         const Frag16& f,
+                                         bf16x8 (&p)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = S0 + i;
+    if (!KM) {
+      p[i] = *(const bf16x8*)(stage + (wo + 16 * s) * 64 + f.rm);
+    } else {
+      const uint8_t* base = stage + 2 * wo + 32 * (s & 1) + f.kmp[s >> 1];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base + 2048));
+      p[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+}
+
+// The wave's four Q slabs (k-major).
+__device__ __forceinline__ void read_q16(const uint8_t* __restrict__ stage, const Frag16& f,
+                                         bf16x8 (&q)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint8_t* base = stage + OPB + 32 * (j & 1) + f.kmq[j >> 1];
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base + 2048));
+    q[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+template <int I0>
+__device__ __forceinline__ void mfma_half16(f32x4 (&acc)[8][4], const bf16x8 (&p)[4],
+                                            const bf16x8 (&q)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[I0 + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[j], p[i], acc[I0 + i][j], 0, 0, 0);
+}
+
+struct KState16 {
+  f32x4 acc[8][4];
+  bf16x8 pa[4], pb[4], qa[4], qb[4];
+  uint32_t sc;
+  int t;
+};
+
+// 16 MFMAs with RD LDS reads and ND DMA instructions spread among them, in
+// four groups of four MFMAs.
+template <int RD, int ND>
+__device__ __forceinline__ void sched16() {
+  static_assert(RD % 4 == 0 && ND % 4 == 0, "reads and DMA in whole groups");
+  constexpr int R = RD / 4, RA = (R + 1) / 2, RB = R / 2, V = ND / 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    if (RA > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RA, 0);
+    if (V > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, V, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+    if (RB > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RB, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One K step (the contract of kstep2): P in layout P0 this step and P1 the
+// next; Q k-major; qc holds this step's Q slabs, qn receives the next step's.
+template <bool P0, bool P1, int VMW, bool QPAIR, bool PPAIR, int BPW, class OpP, class OpQ,
+          int XW = 0>
+__device__ __forceinline__ void kstep16(KState16& k, bf16x8 (&qc)[4], bf16x8 (&qn)[4],
+                                        const OpP& dp, const OpQ& dq, const WaveGeo& g,
+                                        const Frag16& f, int wave,
+                                        const uint8_t* __restrict__ cur,
+                                        const uint8_t* __restrict__ nxt, uint8_t* __restrict__ d0,
+                                        uint8_t* __restrict__ d1, bool xw = false) {
+  constexpr int RD0 = P0 ? 8 : 4;
+  constexpr int RD1 = (P1 ? 8 : 4) + 8;
+  constexpr int ND0 = QPAIR ? 2 * BPW : 0, ND1 = PPAIR ? 2 * BPW : 0;
+  read_p16<P0, 4>(cur, g.wi0, f, k.pb);
+  if (QPAIR) issue_pair<OpQ, BPW>(dq, k.t + 2, d0 + OPB, d1 + OPB, wave);
+  mfma_half16<0>(k.acc, k.pa, qc);
+  sched16<RD0, ND0>();
+
+  if constexpr (XW > 0) {
+    if (xw) wait_vm<VMW + XW>();
+    else wait_vm<VMW>();
+  } else {
+    wait_vm<VMW>();
+  }
+  bar_raw();
+  if (PPAIR) issue_pair<OpP, BPW>(dp, k.t + 3, d0, d1, wave);
+  read_p16<P1, 0>(nxt, g.wi0, f, k.pa);
+  read_q16(nxt, f, qn);
+  mfma_half16<4>(k.acc, k.pb, qc);
+  sched16<RD1, ND1>();
+}
+
+template <bool PE, bool PM, bool PO, int BPW, int XW = 0, class OpP, class OpQ>
+__device__ __forceinline__ void kpair16(KState16& k, const OpP& dp, const OpQ& dq,
+                                        const WaveGeo& g, const Frag16& f, int wave,
+                                        uint8_t* lds, bool xw = false) {
+  constexpr int DPS = 2 * BPW;
+  kstep16<PE, PM, 2 * DPS, true, false, BPW, OpP, OpQ, XW>(
+      k, k.qa, k.qb, dp, dq, g, f, wave, lds + k.sc, lds + stage_wrap(k.sc + STG),
+      lds + stage_wrap(k.sc + 2 * STG), lds + stage_wrap(k.sc + 3 * STG), xw);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep16<PM, PO, BPW, false, true, BPW>(k, k.qb, k.qa, dp, dq, g, f, wave, lds + k.sc,
+                                         lds + stage_wrap(k.sc + STG),
+                                         lds + stage_wrap(k.sc + 3 * STG),
+                                         lds + stage_wrap(k.sc + 4 * STG));
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+}
+
+// Step 0's fragments (P k-major when pkm), through a restrict stage pointer as
+// in first_frags.
+template <bool PF>
+__device__ __forceinline__ void first_frags16(bool pkm, const uint8_t* __restrict__ s0,
+                                              const WaveGeo& g, const Frag16& f, bf16x8 (&pa)[4],
+                                              bf16x8 (&qa)[4]) {
+  if (pkm) {
+    read_p16<true, 0>(s0, g.wi0, f, pa);
+    read_q16(s0, f, qa);
+  } else {
+    read_p16<PF, 0>(s0, g.wi0, f, pa);
+    read_q16(s0, f, qa);
+  }
+}
+
+// kloop2_rest on 16 x 16 x 32 MFMAs (the same DMA schedule and waits).  On
+// return the last step (nk - 1, odd) has its fragments in pa, pb and qb.
+template <bool PF, int BPW, int XW = 0, class OpP, class OpQ>
+__device__ __forceinline__ void kloop16_rest(KState16& k, int nk, int bP, const OpP& dp,
+                                             const OpQ& dq, const WaveGeo& g, const Frag16& f,
+                                             int wave, uint8_t* lds, bool pend = false) {
+  constexpr int DPS = 2 * BPW;
+  {
+    if constexpr (XW > 0) {
+      if (pend) wait_vm<2 * DPS + XW>();
+      else wait_vm<2 * DPS>();
+    } else {
+      wait_vm<2 * DPS>();
+    }
+    bar_raw();
+    first_frags16<PF>(bP > 0, lds, g, f, k.pa, k.qa);
+  }
+  k.sc = 0;
+  k.t = 0;
+  if (bP > 0) {
+    for (; k.t < bP - 2;) kpair16<true, true, true, BPW, XW>(k, dp, dq, g, f, wave, lds, pend && k.t == 0);
+    kpair16<true, true, PF, BPW, XW>(k, dp, dq, g, f, wave, lds, pend && k.t == 0);
+  }
+  for (; k.t < nk - 4;) kpair16<PF, PF, PF, BPW, XW>(k, dp, dq, g, f, wave, lds, pend && k.t == 0);
+  kstep16<PF, PF, 2 * DPS, true, false, BPW>(k, k.qa, k.qb, dp, dq, g, f, wave, lds + k.sc,
+                                             lds + stage_wrap(k.sc + STG),
+                                             lds + stage_wrap(k.sc + 2 * STG),
+                                             lds + stage_wrap(k.sc + 3 * STG));
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep16<PF, PF, BPW, false, false, BPW>(k, k.qb, k.qa, dp, dq, g, f, wave, lds + k.sc,
+                                          lds + stage_wrap(k.sc + STG), lds, lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep16<PF, PF, 0, false, false, BPW>(k, k.qa, k.qb, dp, dq, g, f, wave, lds + k.sc,
+                                        lds + stage_wrap(k.sc + STG), lds, lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  read_p16<PF, 4>(lds + k.sc, g.wi0, f, k.pb);
+}
+
+// Two horizontally adjacent slabs (16 x 32 of a 32 x 32 block) of a lane,
+// values already final, packed to bf16 and stored as one 16-byte piece per
+// lane.  Lane l holds columns 4q .. 4q+3 (q = l >> 4) of each slab; one
+// v_permlane16_swap per packed register trades the odd 16-lane groups' left
+// slab values for the even groups' right slab values, so that lane l then
+// holds 8 consecutive columns: 8(q >> 1) + 16(q & 1) .. +7 of row (l & 15).
+__device__ __forceinline__ void store_pair16(const float (&a)[4], const float (&b)[4],
+                                             uint16_t* dst) {
+  const auto r0 = __builtin_amdgcn_permlane16_swap(pack_bf2(a[0], a[1]), pack_bf2(b[0], b[1]),
+                                                   false, false);
+  const auto r1 = __builtin_amdgcn_permlane16_swap(pack_bf2(a[2], a[3]), pack_bf2(b[2], b[3]),
+                                                   false, false);
+  gstore<u32x4>(dst, u32x4{r0[0], r1[0], r0[1], r1[1]});
+}
+
+// A wave's 128 x 64 accumulator sub-tile (16 x 16 layout), times s, into the
+// 32 x 32 blocks of a blocked matrix: blk0 is the wave's first block, nb the
+// blocks per block row.  With split, the low parts go lo_off elements on.
+__device__ __forceinline__ void store_acc16(const f32x4 (&acc)[8][4], uint16_t* blk0, int64_t nb,
+                                            int lane, float s, bool split, int64_t lo_off) {
+  const int q = lane >> 4;
+  uint16_t* base = blk0 + (lane & 15) * 32 + 8 * (q >> 1) + 16 * (q & 1);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const f32x4& a = acc[2 * bi + i2][2 * bj];
+        const f32x4& b = acc[2 * bi + i2][2 * bj + 1];
+        uint16_t* dst = base + (bi * nb + bj) * 1024 + i2 * 512;
+        if (split) {
+#pragma clang fp contract(off)
+          float va[4], vb[4], la[4], lb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[e] = s * a[e];
+            vb[e] = s * b[e];
+            la[e] = va[e] - bf2f(f2bf(va[e]));
+            lb[e] = vb[e] - bf2f(f2bf(vb[e]));
+          }
+          store_pair16(va, vb, dst);
+          store_pair16(la, lb, dst + lo_off);
+        } else {
+          float va[4], vb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[e] = s * a[e];
+            vb[e] = s * b[e];
+          }
+          store_pair16(va, vb, dst);
+        }
+      }
+}
+
+// Stage stripe BI (rows 32 BI .. +31: slabs 2 BI, 2 BI + 1) of a 16 x 16
+// layout sub-tile into the wave's LDS region, in the layout stage_stripe
+// writes (float32 rows of Ep<64>), for final_pass.
+template <int BI>
+__device__ __forceinline__ void stage_stripe16(const f32x4 (&acc)[8][4], float* stg, int lane) {
+  using G = Ep<64>;
+#pragma unroll
+  for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(f32x4*)(stg + G::row(16 * i2 + (lane & 15)) + 16 * j + 4 * (lane >> 4)) =
+          acc[2 * BI + i2][j];
+}
+
+// The last apply's epilogue (O or the fused weight update) of a 16 x 16
+// layout sub-tile: as epilogue() for the last iteration, one staged 32-row
+// stripe at a time.
+template <int OUT>
+__device__ __forceinline__ void epilogue_final16(const MatDesc& d, const GemmParams& P,
+                                                 const f32x4 (&acc)[8][4], float* stg, int i0,
+                                                 int j0, int lane, float s_first) {
+  const bool out_trans = d.transposed;
+  const float upd = -P.lr * d.upd_scale;
+#pragma unroll 1
+  for (int bi = 0; bi < 4; ++bi) {
+    switch (bi) {
+      case 0: stage_stripe16<0>(acc, stg, lane); break;
+      case 1: stage_stripe16<1>(acc, stg, lane); break;
+      case 2: stage_stripe16<2>(acc, stg, lane); break;
+      default: stage_stripe16<3>(acc, stg, lane); break;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int64_t ib = i0 + 32 * bi;
+    if (out_trans) final_pass<OUT, true, 64>(d, P, stg, ib, j0, lane, upd, s_first);
+    else final_pass<OUT, false, 64>(d, P, stg, ib, j0, lane, upd, s_first);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// One apply tile (one tile per workgroup) on the 16 x 16 x 32 engine, with
+// the paired DMA schedule of kloop2.
+template <int OUT, class OpP, class OpQ>
+__device__ __forceinline__ void apply_tile16(const MatDesc& d, const GemmParams& P, const OpP& dp,
+                                             const OpQ& dq, const WaveGeo& g, int nk, int bP,
+                                             uint16_t* xnext, int i0, int j0, int wave, int lane,
+                                             uint8_t* lds) {
+  constexpr int BPW = 2;
+  Frag16 f;
+  f.init(lane, g.wj0);
+  KState16 k;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k.acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kprologue2_issue<BPW>(dp, dq, wave, lds);
+  kloop16_rest<false, BPW>(k, nk, bP, dp, dq, g, f, wave, lds);
+  mfma_half16<0>(k.acc, k.pa, k.qb);
+  mfma_half16<4>(k.acc, k.pb, k.qb);
+  const float s_first = P.first ? gload<float>(d.xs) : 1.f;
+  const int64_t mp = d.mp, np = d.np;
+  if (OUT == OUT_NEXT_X) {
+    const int64_t nb = np / 32;
+    uint16_t* blk0 = xnext + (((int64_t)(i0 + g.wi0) >> 5) * nb + ((j0 + g.wj0) >> 5)) * 1024;
+    store_acc16(k.acc, blk0, nb, lane, s_first, P.split, mp * np);
+    return;
+  }
+  // all fragment reads done: the stages become epilogue staging
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  bar_raw();
+  epilogue_final16<OUT>(d, P, k.acc, (float*)(lds + wave * Ep<64>::WAVE_BYTES), i0 + g.wi0,
+                        j0 + g.wj0, lane, s_first);
+}
+
+
 // ------------------------------------------------------- diagonal tiles
 // A Gram or polynomial tile on the diagonal (ti == tj) has P = Q (the same 256
 // operand rows) and a symmetric output, so only the 36 blocks on and above
@@ -1667,6 +2012,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
   g.wj0 = NW == 4 ? (wave & 1) * 128 : (wave & 3) * 64;      // wave sub-tile origin (cols)
   g.frow = lane & 31;
   g.fkc = lane >> 5;
+  if constexpr (STAGE == 2 && NW == 8 && MATOPT_APPLY_MFMA16 && MATOPT_PAIR_APPLY) {
+    apply_tile16<OUT>(d, P, dp, dq, g, nk, bP, xnext, i0, j0, wave, lane, lds);
+    return;
+  }
   FragOffsets fo;
   fo.init(lane);
   if (NW == 8) fo.init_q64(lane, g.wj0);
@@ -1902,6 +2251,79 @@ __device__ __forceinline__ void apply_persist(const GemmParams& P, uint8_t* lds)
   }
 }
 
+// apply_persist on the 16 x 16 x 32 engine.
+__device__ __forceinline__ void apply_persist16(const GemmParams& P, uint8_t* lds) {
+  constexpr int BPW = 2;
+  constexpr int NST = 16;   // store instructions per wave and tile (bf16 iterate)
+  const int xcd = (int)(blockIdx.x & 7);
+  const int G = (int)(gridDim.x >> 3);
+  const int L = P.n_tiles >> 3;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WaveGeo g;
+  g.wi0 = (wave >> 2) * 128;
+  g.wj0 = (wave & 3) * 64;
+  g.frow = lane & 31;
+  g.fkc = lane >> 5;
+  Frag16 f;
+  f.init(lane, g.wj0);
+
+  int kpos = (int)(blockIdx.x >> 3);
+  ApplyTask cur;
+  bool have = false;
+  for (; kpos < L; kpos += G)
+    if (apply_task(P, 8 * kpos + xcd, g, cur)) {
+      have = true;
+      break;
+    }
+  if (!have) return;
+
+  const bool xblk = !P.first;
+  const bool ksplit = P.split && !P.first;
+  OperandDma<OP_SPLIT> dp;
+  OperandDma<OP_KM> dq;
+  int nk = 0, bP = 0;
+  auto setup = [&](const ApplyTask& t) {
+    nk = (ksplit ? 2 * t.mp : t.mp) / BK;
+    bP = P.split ? 0 : t.i0 / BK;
+    dp.init(t.b, t.mp, t.i0, bP, lane, true);
+    if (ksplit) dp.t_wrap = t.mp / BK;
+    dq.init(t.xc, t.np, t.j0, nk, lane, xblk);
+  };
+  setup(cur);
+  kprologue2_issue<BPW>(dp, dq, wave, lds);
+
+  KState16 k;
+  bool pend = false;
+  for (;;) {
+    ApplyTask nx;
+    bool more = false;
+    for (int kn = kpos + G; kn < L; kn += G)
+      if (apply_task(P, 8 * kn + xcd, g, nx)) {
+        more = true;
+        kpos = kn;
+        break;
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k.acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    kloop16_rest<false, BPW, NST>(k, nk, bP, dp, dq, g, f, wave, lds, pend);
+    mfma_half16<0>(k.acc, k.pa, k.qb);
+    mfma_half16<4>(k.acc, k.pb, k.qb);
+    if (more) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      bar_raw();
+      setup(nx);
+      kprologue2_issue<BPW>(dp, dq, wave, lds);
+    }
+    store_acc16(k.acc, cur.out, cur.np / 32, lane, cur.s, P.split, (int64_t)cur.mp * cur.np);
+    if (!more) break;
+    cur = nx;
+    pend = true;
+  }
+}
+
 template <int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(NW / 4, NW / 4)))
@@ -1914,7 +2336,8 @@ void ns_apply_persist_kernel(GemmParams P) {
     t0 = __builtin_amdgcn_s_memtime();
     r0 = __builtin_amdgcn_s_memrealtime();
   }
-  apply_persist(P, lds);
+  if (MATOPT_APPLY_MFMA16) apply_persist16(P, lds);
+  else apply_persist(P, lds);
   if (clk && threadIdx.x == 0) {
     const uint64_t t1 = __builtin_amdgcn_s_memtime();
     const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
