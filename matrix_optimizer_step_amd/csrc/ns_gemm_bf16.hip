@@ -87,9 +87,16 @@
 #ifndef MATOPT_PAIR_APPLY
 #define MATOPT_PAIR_APPLY 1
 #endif
-// Apply launches on the 16 x 16 x 32 engine (1) or on 32 x 32 x 16 MFMAs (0).
+// Stages on the 16 x 16 x 32 engine (1) or on 32 x 32 x 16 MFMAs (0): apply,
+// and the off-diagonal tiles of the Gram and the polynomial.
 #ifndef MATOPT_APPLY_MFMA16
 #define MATOPT_APPLY_MFMA16 1
+#endif
+#ifndef MATOPT_GRAM_MFMA16
+#define MATOPT_GRAM_MFMA16 1
+#endif
+#ifndef MATOPT_POLY_MFMA16
+#define MATOPT_POLY_MFMA16 1
 #endif
 // Diagonal Gram and polynomial tiles compute only their upper 36 of 64 blocks.
 #ifndef MATOPT_DIAG_TILES
@@ -1175,15 +1182,20 @@ __device__ __forceinline__ void read_p16(const uint8_t* __restrict__ stage, int 
   }
 }
 
-// The wave's four Q slabs (k-major).
-__device__ __forceinline__ void read_q16(const uint8_t* __restrict__ stage, const Frag16& f,
-                                         bf16x8 (&q)[4]) {
+// The wave's four Q slabs (origin wq0, a multiple of 64; k-major or row-major).
+template <bool KM = true>
+__device__ __forceinline__ void read_q16(const uint8_t* __restrict__ stage, int wq0,
+                                         const Frag16& f, bf16x8 (&q)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint8_t* base = stage + OPB + 32 * (j & 1) + f.kmq[j >> 1];
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base + 2048));
-    q[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (!KM) {
+      q[j] = *(const bf16x8*)(stage + OPB + (wq0 + 16 * j) * 64 + f.rm);
+    } else {
+      const uint8_t* base = stage + OPB + 32 * (j & 1) + f.kmq[j >> 1];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MATOPT_LDS s16x4*)(base + 2048));
+      q[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   }
 }
 
@@ -1204,17 +1216,17 @@ struct KState16 {
   int t;
 };
 
-// 16 MFMAs with RD LDS reads and ND DMA instructions spread among them, in
-// four groups of four MFMAs.
+// 16 MFMAs with RD LDS reads and ND (<= 4) DMA instructions spread among
+// them, in four groups of four MFMAs.
 template <int RD, int ND>
 __device__ __forceinline__ void sched16() {
-  static_assert(RD % 4 == 0 && ND % 4 == 0, "reads and DMA in whole groups");
-  constexpr int R = RD / 4, RA = (R + 1) / 2, RB = R / 2, V = ND / 4;
+  static_assert(RD % 4 == 0 && ND <= 4, "reads in whole groups, at most one DMA per group");
+  constexpr int R = RD / 4, RA = (R + 1) / 2, RB = R / 2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
     if (RA > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RA, 0);
-    if (V > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, V, 0);
+    if ((i + 1) * ND / 4 > i * ND / 4) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
     if (RB > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RB, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
@@ -1249,7 +1261,7 @@ __device__ __forceinline__ void kstep16(KState16& k, bf16x8 (&qc)[4], bf16x8 (&q
   bar_raw();
   if (PPAIR) issue_pair<OpP, BPW>(dp, k.t + 3, d0, d1, wave);
   read_p16<P1, 0>(nxt, g.wi0, f, k.pa);
-  read_q16(nxt, f, qn);
+  read_q16<true>(nxt, g.wj0, f, qn);
   mfma_half16<4>(k.acc, k.pb, qc);
   sched16<RD1, ND1>();
 }
@@ -1280,11 +1292,19 @@ __device__ __forceinline__ void first_frags16(bool pkm, const uint8_t* __restric
                                               bf16x8 (&qa)[4]) {
   if (pkm) {
     read_p16<true, 0>(s0, g.wi0, f, pa);
-    read_q16(s0, f, qa);
+    read_q16<true>(s0, g.wj0, f, qa);
   } else {
     read_p16<PF, 0>(s0, g.wi0, f, pa);
-    read_q16(s0, f, qa);
+    read_q16<true>(s0, g.wj0, f, qa);
   }
+}
+
+template <bool PKM, bool QKM>
+__device__ __forceinline__ void first_frags16q(const uint8_t* __restrict__ s0, const WaveGeo& g,
+                                               const Frag16& f, bf16x8 (&pa)[4],
+                                               bf16x8 (&qa)[4]) {
+  read_p16<PKM, 0>(s0, g.wi0, f, pa);
+  read_q16<QKM>(s0, g.wj0, f, qa);
 }
 
 // kloop2_rest on 16 x 16 x 32 MFMAs (the same DMA schedule and waits).  On
@@ -1323,6 +1343,110 @@ __device__ __forceinline__ void kloop16_rest(KState16& k, int nk, int bP, const 
   ++k.t;
   kstep16<PF, PF, 0, false, false, BPW>(k, k.qa, k.qb, dp, dq, g, f, wave, lds + k.sc,
                                         lds + stage_wrap(k.sc + STG), lds, lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  read_p16<PF, 4>(lds + k.sc, g.wi0, f, k.pb);
+}
+
+// One K step with each step's DMA spread over its two halves (the contract of
+// kstep): P in layouts P0 -> P1 and Q in Q0 -> Q1 from this step to the next.
+template <bool P0, bool Q0, bool P1, bool Q1, int VMW, bool DQ, bool DP, int BPW, class OpP,
+          class OpQ>
+__device__ __forceinline__ void kstep16s(KState16& k, bf16x8 (&qc)[4], bf16x8 (&qn)[4],
+                                         const OpP& dp, const OpQ& dq, const WaveGeo& g,
+                                         const Frag16& f, int wave,
+                                         const uint8_t* __restrict__ cur,
+                                         const uint8_t* __restrict__ nxt,
+                                         uint8_t* __restrict__ dst_q, uint8_t* __restrict__ dst_p) {
+  constexpr int RD0 = P0 ? 8 : 4;
+  constexpr int RD1 = (P1 ? 8 : 4) + (Q1 ? 8 : 4);
+  read_p16<P0, 4>(cur, g.wi0, f, k.pb);
+  if (DQ) dq.template issue<BPW>(k.t + NS - 2, dst_q + OPB, wave);
+  mfma_half16<0>(k.acc, k.pa, qc);
+  sched16<RD0, DQ ? BPW : 0>();
+
+  wait_vm<VMW>();
+  bar_raw();
+  if (DP) dp.template issue<BPW>(k.t + NS - 1, dst_p, wave);
+  read_p16<P1, 0>(nxt, g.wi0, f, k.pa);
+  read_q16<Q1>(nxt, g.wj0, f, qn);
+  mfma_half16<4>(k.acc, k.pb, qc);
+  sched16<RD1, DP ? BPW : 0>();
+}
+
+// Steady steps in pairs (t even) up to t_end (even), layouts (PE, QE) ->
+// (PM, QM) -> (PO, QO) for steps t, t+1, t+2 of each pair.
+template <bool PE, bool QE, bool PM, bool QM, bool PO, bool QO, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void ksteps16(KState16& k, int t_end, const OpP& dp, const OpQ& dq,
+                                         const WaveGeo& g, const Frag16& f, int wave,
+                                         uint8_t* lds) {
+  for (; k.t < t_end;) {
+    kstep16s<PE, QE, PM, QM, 4 * BPW, true, true, BPW>(
+        k, k.qa, k.qb, dp, dq, g, f, wave, lds + k.sc, lds + stage_wrap(k.sc + STG),
+        lds + stage_wrap(k.sc + (NS - 2) * STG), lds + stage_wrap(k.sc + (NS - 1) * STG));
+    k.sc = stage_wrap(k.sc + STG);
+    ++k.t;
+    kstep16s<PM, QM, PO, QO, 4 * BPW, true, true, BPW>(
+        k, k.qb, k.qa, dp, dq, g, f, wave, lds + k.sc, lds + stage_wrap(k.sc + STG),
+        lds + stage_wrap(k.sc + (NS - 2) * STG), lds + stage_wrap(k.sc + (NS - 1) * STG));
+    k.sc = stage_wrap(k.sc + STG);
+    ++k.t;
+  }
+}
+
+// kloop on 16 x 16 x 32 MFMAs (the same DMA schedule, waits and layout
+// switches; bP and bQ are multiples of 8, so every switch falls between the
+// two steps of a pair).  On return the last step (nk - 1, odd) has its
+// fragments in pa, pb and qb.
+template <bool PF, bool QF, bool QS, bool QEQ, int BPW, class OpP, class OpQ>
+__device__ __forceinline__ void kloop16(KState16& k, int nk, int bP, int bQ, const OpP& dp,
+                                        const OpQ& dq, const WaveGeo& g, const Frag16& f,
+                                        int wave, uint8_t* lds) {
+  constexpr bool QA = QS ? true : QF;   // Q layout before bQ
+  constexpr int DPS = 2 * BPW;
+  // prologue DMA: steps 0 .. NS-3 and the P half of step NS-2
+  dp.template issue<BPW>(0, lds, wave);
+  dq.template issue<BPW>(0, lds + OPB, wave);
+#pragma unroll
+  for (int t = 1; t < NS - 2; ++t) {
+    dp.template issue<BPW>(t, lds + t * STG, wave);
+    dq.template issue<BPW>(t, lds + t * STG + OPB, wave);
+  }
+  dp.template issue<BPW>(NS - 2, lds + (NS - 2) * STG, wave);
+  wait_vm<DPS * (NS - 3) + DPS / 2>();
+  bar_raw();
+  if (bP > 0) first_frags16q<true, QA>(lds, g, f, k.pa, k.qa);
+  else if (QS && bQ > 0) first_frags16q<PF, QA>(lds, g, f, k.pa, k.qa);
+  else first_frags16q<PF, QF>(lds, g, f, k.pa, k.qa);
+  k.sc = 0;
+  k.t = 0;
+  if (bP > 0) {
+    ksteps16<true, QA, true, QA, true, QA, BPW>(k, bP - 2, dp, dq, g, f, wave, lds);
+    if constexpr (QS && QEQ) {
+      if (bQ == bP) ksteps16<true, QA, true, QA, PF, QF, BPW>(k, bP, dp, dq, g, f, wave, lds);
+      else ksteps16<true, QA, true, QA, PF, QA, BPW>(k, bP, dp, dq, g, f, wave, lds);
+    } else {
+      ksteps16<true, QA, true, QA, PF, QA, BPW>(k, bP, dp, dq, g, f, wave, lds);
+    }
+  }
+  if (QS && bQ > bP) {
+    ksteps16<PF, QA, PF, QA, PF, QA, BPW>(k, bQ - 2, dp, dq, g, f, wave, lds);
+    ksteps16<PF, QA, PF, QA, PF, QF, BPW>(k, bQ, dp, dq, g, f, wave, lds);
+  }
+  ksteps16<PF, QF, PF, QF, PF, QF, BPW>(k, nk - NS + 1, dp, dq, g, f, wave, lds);
+  // drain: step nk-4 issues the last DMA (the Q half of step nk-1)
+  kstep16s<PF, QF, PF, QF, DPS * 2, true, false, BPW>(
+      k, k.qa, k.qb, dp, dq, g, f, wave, lds + k.sc, lds + stage_wrap(k.sc + STG),
+      lds + stage_wrap(k.sc + (NS - 2) * STG), lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep16s<PF, QF, PF, QF, DPS, false, false, BPW>(k, k.qb, k.qa, dp, dq, g, f, wave,
+                                                   lds + k.sc, lds + stage_wrap(k.sc + STG),
+                                                   lds, lds);
+  k.sc = stage_wrap(k.sc + STG);
+  ++k.t;
+  kstep16s<PF, QF, PF, QF, 0, false, false, BPW>(k, k.qa, k.qb, dp, dq, g, f, wave, lds + k.sc,
+                                                 lds + stage_wrap(k.sc + STG), lds, lds);
   k.sc = stage_wrap(k.sc + STG);
   ++k.t;
   read_p16<PF, 4>(lds + k.sc, g.wi0, f, k.pb);
@@ -1420,6 +1544,95 @@ __device__ __forceinline__ void epilogue_final16(const MatDesc& d, const GemmPar
     else final_pass<OUT, false, 64>(d, P, stg, ib, j0, lane, upd, s_first);
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// An off-diagonal Gram tile (an upper tile of A = s^2 X X^T) on the 16 x 16 x
+// 32 engine: P and Q row-major, the spread DMA schedule of kloop.
+template <class OpP, class OpQ>
+__device__ __forceinline__ void gram_tile16(const MatDesc& d, const GemmParams& P, const OpP& dp,
+                                            const OpQ& dq, const WaveGeo& g, int nk, int i0,
+                                            int j0, int wave, int lane, uint8_t* lds) {
+  constexpr int BPW = 2;
+  Frag16 f;
+  f.init(lane, g.wj0);
+  KState16 k;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k.acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop16<false, false, false, false, BPW>(k, nk, 0, 0, dp, dq, g, f, wave, lds);
+  mfma_half16<0>(k.acc, k.pa, k.qb);
+  mfma_half16<4>(k.acc, k.pb, k.qb);
+  const float s_first = P.first ? gload<float>(d.xs) : 1.f;
+  const int64_t nb = d.mp / 32;
+  uint16_t* blk0 = (uint16_t*)d.a + (((int64_t)(i0 + g.wi0) >> 5) * nb + ((j0 + g.wj0) >> 5)) * 1024;
+  store_acc16(k.acc, blk0, nb, lane, s_first * s_first, false, 0);
+}
+
+// An off-diagonal polynomial tile (B = a I + b A + c A A, an upper tile) on the
+// 16 x 16 x 32 engine.  The epilogue swaps each lane's float32 values across
+// 16-lane groups (v_permlane16_swap) so that a lane holds 8 consecutive
+// columns of one row, reads A's 8 values there (16 bytes, all sixteen reads
+// issued before the last MFMAs) and writes B's 8 values in one store.
+template <bool QEQ, class OpP, class OpQ>
+__device__ __forceinline__ void poly_tile16(const MatDesc& d, const GemmParams& P, const OpP& dp,
+                                            const OpQ& dq, const WaveGeo& g, int nk, int bP,
+                                            int bQ, int i0, int j0, int wave, int lane,
+                                            uint8_t* lds) {
+  constexpr int BPW = 2;
+  Frag16 f;
+  f.init(lane, g.wj0);
+  KState16 k;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k.acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop16<false, false, true, QEQ, BPW>(k, nk, bP, bQ, dp, dq, g, f, wave, lds);
+  const int64_t mp = d.mp;
+  const uint16_t* A = (const uint16_t*)d.a;
+  const int q = lane >> 4;
+  const int64_t r0 = i0 + g.wi0 + (lane & 15);
+  const int64_t c0 = j0 + g.wj0 + 8 * (q >> 1) + 16 * (q & 1);
+  // slab i, block column bj of the wave: (i >> 1) block rows and bj blocks on
+  // from the lane's first element, plus 16 rows (512 elements) for odd i
+  const uint32_t nb = (uint32_t)(mp / 32);
+  const int64_t boff = blk_at((const uint16_t*)nullptr, r0, c0, mp) - (const uint16_t*)nullptr;
+  const uint16_t* Ab = A + boff;
+  uint16_t* Bb = (uint16_t*)d.b + boff;
+  auto eoff = [&](int i, int bj) -> uint32_t {
+    return ((uint32_t)(i >> 1) * nb + (uint32_t)bj) * 1024u + (uint32_t)(i & 1) * 512u;
+  };
+  u32x4 av[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) av[i][bj] = gload<u32x4>(Ab + eoff(i, bj));
+  mfma_half16<0>(k.acc, k.pa, k.qb);
+  mfma_half16<4>(k.acc, k.pb, k.qb);
+  const float a = P.a, b = P.b, c = P.c;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(k.acc[i][2 * bj][e]),
+                                                        __float_as_uint(k.acc[i][2 * bj + 1][e]),
+                                                        false, false);
+        x[e] = __uint_as_float(r[0]);
+        x[4 + e] = __uint_as_float(r[1]);
+      }
+      const int64_t row = r0 + 16 * i, col = c0 + 32 * bj;
+      const u32x4 A8 = av[i][bj];
+      const float aa[8] = {lo_bf(A8.x), hi_bf(A8.x), lo_bf(A8.y), hi_bf(A8.y),
+                           lo_bf(A8.z), hi_bf(A8.z), lo_bf(A8.w), hi_bf(A8.w)};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = fmaf(b, aa[e], fmaf(c, x[e], row == col + e ? a : 0.f));
+      gstore<u32x4>(Bb + eoff(i, bj), u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]),
+                                            pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])});
+    }
 }
 
 // One apply tile (one tile per workgroup) on the 16 x 16 x 32 engine, with
@@ -2014,6 +2227,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
   g.fkc = lane >> 5;
   if constexpr (STAGE == 2 && NW == 8 && MATOPT_APPLY_MFMA16 && MATOPT_PAIR_APPLY) {
     apply_tile16<OUT>(d, P, dp, dq, g, nk, bP, xnext, i0, j0, wave, lane, lds);
+    return;
+  }
+  if constexpr (STAGE == 0 && NW == 8 && MATOPT_GRAM_MFMA16 && !MATOPT_PAIR_GRAM) {
+    gram_tile16(d, P, dp, dq, g, nk, i0, j0, wave, lane, lds);
+    return;
+  }
+  if constexpr (STAGE == 1 && NW == 8 && !MIR && MATOPT_POLY_MFMA16 && !MATOPT_PAIR_POLY) {
+    poly_tile16<!(NW == 8 && MATOPT_DIAG_TILES)>(d, P, dp, dq, g, nk, bP, bQ, i0, j0, wave, lane,
+                                                 lds);
     return;
   }
   FragOffsets fo;
