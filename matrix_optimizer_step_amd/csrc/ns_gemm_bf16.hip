@@ -1819,6 +1819,11 @@ __device__ __forceinline__ void kstep_diag(f32x16 (&acc)[DiagGeo<TA>::NB],
 // Gram: value s^2 * acc.  Polynomial: a*I + b*A + c*acc with the A block
 // read first (ain: this lane's two items).
 template <int STAGE>
+__device__ __forceinline__ void diag_block_write(float* stg, uint16_t* out, int64_t ld, int64_t r0,
+                                                 int64_t c0, bool mirror, int lane, float sc,
+                                                 const GemmParams& P, const u32x4 (&ain)[2]);
+
+template <int STAGE>
 __device__ __forceinline__ void diag_block_out(const f32x16& acc, float* stg, uint16_t* out,
                                                int64_t ld, int64_t r0, int64_t c0, bool mirror,
                                                int lane, float sc, const GemmParams& P,
@@ -1830,6 +1835,15 @@ __device__ __forceinline__ void diag_block_out(const f32x16& acc, float* stg, ui
     *(f32x4*)(stg + frow * PITCH + 8 * g + 4 * fkc) =
         f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
   __builtin_amdgcn_wave_barrier();
+  diag_block_write<STAGE>(stg, out, ld, r0, c0, mirror, lane, sc, P, ain);
+}
+
+// The write-out of a staged diagonal-tile block (32 rows of 36 floats).
+template <int STAGE>
+__device__ __forceinline__ void diag_block_write(float* stg, uint16_t* out, int64_t ld, int64_t r0,
+                                                 int64_t c0, bool mirror, int lane, float sc,
+                                                 const GemmParams& P, const u32x4 (&ain)[2]) {
+  constexpr int PITCH = 36;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int q = lane + 64 * p;
@@ -2134,6 +2148,189 @@ __device__ __forceinline__ void diag_pair(const MatDesc& d, const GemmParams& P,
                           geo.br[b] != geo.bc[b], lane, sc2, P, ain[b]);
 }
 
+// MFMAs with RD LDS reads (at most three per MFMA) and ND DMA instructions
+// (at most one per MFMA) spread evenly among NM of them.
+template <int NM, int RD, int ND>
+__device__ __forceinline__ void sched_spread() {
+  static_assert(RD <= 3 * NM && ND <= NM, "spread");
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    const int nr = (i + 1) * RD / NM - i * RD / NM;
+    if (nr >= 1) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+    if (nr >= 2) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+    if (nr >= 3) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+    if ((i + 1) * ND / NM > i * ND / NM) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// A diagonal pair on the 16 x 16 x 32 engine (the blocks and slots of
+// PairGeo; row-major panels).  Each 32-row slot is two 16-row slab fragments
+// over the whole K step, each 32 x 32 block 2 x 2 slabs; a block on the
+// 32-block diagonal computes only its upper three slabs (its lower slab is
+// written as the mirror of the upper right one), 34 MFMAs per wave and step
+// instead of the 36 of the 32 x 32 form.  A step runs in two halves: the
+// type-A blocks (0-4, slots 0-4) while slots 5-8 of the step are read, then
+// after the barrier the type-B blocks (5-8) while slots 0-4 of the next step
+// are read.
+__device__ __forceinline__ void mfma_pair16a(f32x4 (&acc)[9][2][2], const bf16x8 (&fr)[9][2]) {
+  // blocks 0 and 2 are on the diagonal (row slot == column slot)
+  constexpr int R[5] = {0, 0, 1, 2, 2}, C[5] = {0, 1, 1, 3, 4};
+#pragma unroll
+  for (int b = 0; b < 5; ++b)
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        if ((b == 0 || b == 2) && i2 == 1 && j2 == 0) continue;
+        acc[b][i2][j2] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[C[b]][j2], fr[R[b]][i2], acc[b][i2][j2], 0, 0, 0);
+      }
+}
+
+__device__ __forceinline__ void mfma_pair16b(f32x4 (&acc)[9][2][2], const bf16x8 (&fr)[9][2]) {
+  constexpr int R[4] = {5, 5, 6, 6}, C[4] = {7, 8, 7, 8};
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2)
+        acc[5 + b][i2][j2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            fr[C[b]][j2], fr[R[b]][i2], acc[5 + b][i2][j2], 0, 0, 0);
+}
+
+// Slots J0 .. J1-1 (both slab halves) of a row-major panel stage.
+template <int J0, int J1>
+__device__ __forceinline__ void read_pair16(const uint8_t* __restrict__ stage,
+                                            const uint32_t (&so)[9], bf16x8 (&fr)[9][2]) {
+#pragma unroll
+  for (int j = J0; j < J1; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fr[j][h] = *(const bf16x8*)(stage + so[j] + 1024 * h);
+}
+
+template <int VMW, bool DQ, bool DP, class OpP, class OpQ>
+__device__ __forceinline__ void kstep_pair16(f32x4 (&acc)[9][2][2], bf16x8 (&fr)[9][2], int t,
+                                             const OpP& dp, const OpQ& dq,
+                                             const uint32_t (&so)[9], int wave,
+                                             const uint8_t* __restrict__ cur,
+                                             const uint8_t* __restrict__ nxt,
+                                             uint8_t* __restrict__ dst_q,
+                                             uint8_t* __restrict__ dst_p) {
+  read_pair16<5, 9>(cur, so, fr);
+  if (DQ) dq.template issue<2>(t + NS - 2, dst_q + OPB, wave);
+  mfma_pair16a(acc, fr);
+  sched_spread<18, 8, DQ ? 2 : 0>();
+  wait_vm<VMW>();
+  bar_raw();
+  if (DP) dp.template issue<2>(t + NS - 1, dst_p, wave);
+  read_pair16<0, 5>(nxt, so, fr);
+  mfma_pair16b(acc, fr);
+  sched_spread<16, 10, DP ? 2 : 0>();
+}
+
+template <int STAGE, class OpP, class OpQ>
+__device__ __forceinline__ void diag_pair16(const MatDesc& d, const GemmParams& P, const OpP& dp,
+                                            const OpQ& dq, int nk, int i0, int i1, int wave,
+                                            int lane, uint8_t* lds) {
+  constexpr int BPW = 2, DPS = 2 * BPW;
+  PairGeo geo;
+  geo.init(wave & 3);
+  const uint32_t panel = wave < 4 ? 0u : (uint32_t)OPB;
+  const uint32_t rm = rm_off(lane & 15, lane >> 4);
+  uint32_t so[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j) so[j] = 2048u * geo.f[j] + panel + rm;
+  f32x4 acc[9][2][2];
+#pragma unroll
+  for (int b = 0; b < 9; ++b)
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) acc[b][i2][j2] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 fr[9][2];
+
+  // prologue (as kprologue): steps 0 .. NS-3 and the P half of step NS-2
+  dp.template issue<BPW>(0, lds, wave);
+  dq.template issue<BPW>(0, lds + OPB, wave);
+#pragma unroll
+  for (int t = 1; t < NS - 2; ++t) {
+    dp.template issue<BPW>(t, lds + t * STG, wave);
+    dq.template issue<BPW>(t, lds + t * STG + OPB, wave);
+  }
+  dp.template issue<BPW>(NS - 2, lds + (NS - 2) * STG, wave);
+  wait_vm<DPS * (NS - 3) + BPW>();
+  bar_raw();
+  read_pair16<0, 5>(lds, so, fr);
+  uint32_t sc = 0;
+  int t = 0;
+  for (; t < nk - NS + 1; ++t) {
+    kstep_pair16<2 * DPS, true, true>(acc, fr, t, dp, dq, so, wave, lds + sc,
+                                      lds + stage_wrap(sc + STG),
+                                      lds + stage_wrap(sc + (NS - 2) * STG),
+                                      lds + stage_wrap(sc + (NS - 1) * STG));
+    sc = stage_wrap(sc + STG);
+  }
+  kstep_pair16<2 * DPS, true, false>(acc, fr, t, dp, dq, so, wave, lds + sc,
+                                     lds + stage_wrap(sc + STG),
+                                     lds + stage_wrap(sc + (NS - 2) * STG), lds);
+  sc = stage_wrap(sc + STG);
+  ++t;
+  kstep_pair16<DPS, false, false>(acc, fr, t, dp, dq, so, wave, lds + sc,
+                                  lds + stage_wrap(sc + STG), lds, lds);
+  sc = stage_wrap(sc + STG);
+  ++t;
+  kstep_pair16<0, false, false>(acc, fr, t, dp, dq, so, wave, lds + sc,
+                                lds + stage_wrap(sc + STG), lds, lds);
+  sc = stage_wrap(sc + STG);
+  read_pair16<5, 9>(lds + sc, so, fr);
+  mfma_pair16a(acc, fr);
+  mfma_pair16b(acc, fr);
+
+  const int64_t ld = d.mp;
+  const int r0 = wave < 4 ? i0 : i1;   // this wave's tile
+  u32x4 ain[9][2];
+  if (STAGE == 1) {
+    const uint16_t* A = (const uint16_t*)d.a;
+#pragma unroll
+    for (int b = 0; b < 9; ++b)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int q = lane + 64 * p;
+        ain[b][p] = gload<u32x4>(blk_at(A, r0 + 32 * geo.br[b] + (q >> 2),
+                                        r0 + 32 * geo.bc[b] + (q & 3) * 8, ld));
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  bar_raw();
+  constexpr int PITCH = 36;
+  float* stg = (float*)(lds + wave * (32 * PITCH * 4));
+  uint16_t* out = STAGE == 0 ? (uint16_t*)d.a : (uint16_t*)d.b;
+  const float s_first = P.first ? gload<float>(d.xs) : 1.f;
+  const float sc2 = s_first * s_first;
+  const int q = lane >> 4, rr = lane & 15;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const bool dblk = b == 0 || b == 2;   // on the 32-block diagonal
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        if (dblk && i2 == 1 && j2 == 0) continue;
+        *(f32x4*)(stg + (16 * i2 + rr) * PITCH + 16 * j2 + 4 * q) = acc[b][i2][j2];
+      }
+    if (dblk) {   // lower left slab = the upper right one transposed
+#pragma unroll
+      for (int e = 0; e < 4; ++e) stg[(16 + 4 * q + e) * PITCH + rr] = acc[b][0][1][e];
+    }
+    __builtin_amdgcn_wave_barrier();
+    diag_block_write<STAGE>(stg, out, ld, r0 + 32 * geo.br[b], r0 + 32 * geo.bc[b],
+                            geo.br[b] != geo.bc[b], lane, sc2, P, ain[b]);
+  }
+}
+
 // One kernel per stage (and, for apply, per output kind), so that each carries
 // only its own operand layouts and epilogue.
 // NW = 8 (every stage, by default): eight waves of 128 x 64, two per SIMD, so
@@ -2209,7 +2406,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
         if (i1 < 0 || i1 + BM > mp) return;
         OperandDma<PK> dq1;
         dq1.init(xcur, np, i1, 0, lane, xblk);
-        diag_pair<STAGE>(d, P, dp, dq1, nk, i0, i1, wave, lane, lds);
+        if constexpr (MATOPT_GRAM_MFMA16) diag_pair16<STAGE>(d, P, dp, dq1, nk, i0, i1, wave, lane, lds);
+        else diag_pair<STAGE>(d, P, dp, dq1, nk, i0, i1, wave, lane, lds);
       }
       return;
     }
