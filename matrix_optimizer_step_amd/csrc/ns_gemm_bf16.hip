@@ -1137,23 +1137,37 @@ __device__ __forceinline__ void kloop2(KState<NBJ>& k, int nk, int bP, const OpP
 // this step's).
 //
 // Fragments cover 16 operand rows and the whole K step: lane l holds row
-// (l & 15) of the slab at k = 8(l >> 4) .. +7.
-//   row-major: one ds_read_b128 at rm_off(l & 15, l >> 4) from the slab's
-//              first row (the chunk swizzle depends on row & 12 only);
+// (l & 15) of the slab at the 8 k of octet o = oct16(l >> 4).
+//   row-major: one ds_read_b128 at rm_off(l & 15, o) from the slab's first
+//              row (the chunk swizzle depends on row & 12 only);
 //   k-major:   two ds_read_b64_tr_b16; lane c = 4e + h of 16-lane group G
-//              points at k row 8G + e (8G + 4 + e for the second read, 2048
+//              points at k row 8o + e (8o + 4 + e for the second read, 2048
 //              bytes on) and slab rows 4h .. 4h+3, so that lane c receives
 //              slab row c at four consecutive k.
 // Accumulator slab (i, j) of a lane holds C[16i + (l & 15)][16j + 4(l >> 4)
 // + 0..3] (operands swapped, as in mfma16).
+// The k octet (16 bytes of a row-major row, 8 k rows of a k-major tile) that
+// 16-lane group G of a fragment holds: 0, 3, 1, 2 for G = 0..3, the same in
+// every fragment of both operands (any fixed assignment computes the same
+// sums).  With this one the row-major reads (ds_read_b128, the row swizzle of
+// rm_off) are free of bank conflicts: rocprofv3 counts bank-conflict cycles
+// equal to half the LDS active cycles with octet G, none with this order.
+// The transposing reads still meet a 2-way conflict (the two 16-lane groups
+// one of them serves read the same unit positions of two octets); a layout
+// that swapped unit halves in odd octets removed it, but the per-read offset
+// arithmetic it needs cost more than the conflict (same-box A/B: apply +1.6%,
+// polynomial -2%, last apply -1%).
+__device__ __forceinline__ int oct16(int G) { return (0x2130 >> (4 * G)) & 15; }
+
 struct Frag16 {
   uint32_t rm;       // row-major, from the slab's first row
   uint32_t kmp[4];   // k-major P slabs, by slab pair s >> 1 (wave origin added at the read)
   uint32_t kmq[2];   // k-major Q slabs of the wave, by slab pair, origin included
   __device__ void init(int lane, int wq0) {
     const int G = lane >> 4, c = lane & 15, e = c >> 2, h = c & 3;
-    rm = rm_off(c, G);
-    const int kr = 8 * G + e;
+    const int o = oct16(G);
+    rm = rm_off(c, o);
+    const int kr = 8 * o + e;
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp) kmp[sp] = kr * 512 + ((sp ^ e) << 6) + 8 * h;
 #pragma unroll
@@ -2239,7 +2253,7 @@ __device__ __forceinline__ void diag_pair16(const MatDesc& d, const GemmParams& 
   PairGeo geo;
   geo.init(wave & 3);
   const uint32_t panel = wave < 4 ? 0u : (uint32_t)OPB;
-  const uint32_t rm = rm_off(lane & 15, lane >> 4);
+  const uint32_t rm = rm_off(lane & 15, oct16(lane >> 4));
   uint32_t so[9];
 #pragma unroll
   for (int j = 0; j < 9; ++j) so[j] = 2048u * geo.f[j] + panel + rm;
