@@ -22,11 +22,16 @@
 // is read row-major by the Gram and k-major (through its columns) by apply.
 //
 // Engine.  A 256 x 256 output tile per workgroup of 8 waves, two per SIMD
-// (each wave 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16, the 128
-// accumulators per lane in VGPRs within the 256 a wave has at two waves per
-// SIMD; while one wave of a SIMD waits on LDS the other issues MFMAs).  A
-// 4-wave variant (128 x 128 per wave, accumulators in AGPRs) is kept behind
-// MATOPT_*_WAVES.  The
+// (each wave 128 x 64, the 128 accumulators per lane in VGPRs within the 256
+// a wave has at two waves per SIMD; while one wave of a SIMD waits on LDS the
+// other issues MFMAs).  The Gram, polynomial and apply launches compute on
+// v_mfma_f32_16x16x32_bf16 (8 x 4 slabs of 16 x 16 per wave; see "16 x 16 x
+// 32 MFMA engine" below); an unpaired diagonal tile and the split-precision
+// polynomial keep the 32 x 32 x 16 form (4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16 per wave, two k16 sub-steps per K step), which the
+// rest of this comment describes where the two differ.  A 4-wave variant
+// (128 x 128 per wave, accumulators in AGPRs) is kept behind MATOPT_*_WAVES.
+// The
 // K loop runs in steps of 32 through NS = 5 LDS stages of 32 KB (one 256 x 32
 // tile per operand), filled by global_load_lds_dwordx4 (HBM -> LDS without
 // registers) three steps ahead of use, in the layout the tile has in HBM.
