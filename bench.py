@@ -466,6 +466,81 @@ def zero_data_line(wl, W, G, V, steps, warmup, stream):
     return out
 
 
+def card_power_files():
+    """The GPU's hwmon power readings (microwatts), where the box exposes them."""
+    import glob
+    out = []
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")):
+        try:
+            int(open(f).read())
+            out.append(f)
+        except (OSError, ValueError):
+            pass
+    return out
+
+
+def mfma_probe_line(stream, launches=40, iters=3000, workgroups=2048):
+    """Diagnostic: the library's MFMA rate probe (matopt_mfma_probe) for both
+    MFMA forms, operands in registers or read from LDS each step, on Gaussian
+    and on all-zero bf16 data: TFLOP/s, the clock the loop ran at (shader over
+    real-time ticks), MFMA utilisation at that clock, and the card's power
+    reading sampled every 20 ms while the timed launches ran."""
+    import threading
+    import torch
+    import matrix_optimizer_step_amd as mo
+    g = torch.Generator().manual_seed(5)
+    data = {"gaussian": torch.randn(49152, generator=g).to(torch.bfloat16).cuda(),
+            "zero": torch.zeros(49152, dtype=torch.bfloat16, device="cuda")}
+    out = torch.empty(workgroups * 512, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    pw_files = card_power_files()
+    flops = workgroups * 8 * iters * 524288
+    cases = [(32, False, "gaussian"), (16, False, "gaussian"), (32, True, "gaussian"),
+             (16, True, "gaussian"), (32, True, "zero"), (16, True, "zero")]
+    res = []
+    for form, lds, dname in cases:
+        for _ in range(3):
+            mo.mfma_probe(form, lds, data[dname], out, clk, iters, workgroups, stream)
+        torch.cuda.synchronize()
+        clk.zero_()
+        samples, stop = [], threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                for f in pw_files:
+                    try:
+                        samples.append(int(open(f).read()) / 1e6)
+                    except (OSError, ValueError):
+                        pass
+                time.sleep(0.02)
+        th = threading.Thread(target=sample)
+        th.start()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            mo.mfma_probe(form, lds, data[dname], out, clk, iters, workgroups, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        ms = e0.elapsed_time(e1) / launches
+        c = clk.cpu().tolist()
+        mhz = 100.0 * c[0] / c[1] if c[1] else 0.0
+        tf = flops / (ms * 1e-3) / 1e12
+        half = samples[len(samples) // 2:]   # the ramp-up excluded
+        res.append({"mfma": {32: "32x32x16", 16: "16x16x32"}[form],
+                    "operands": "LDS, read one step ahead" if lds else "registers",
+                    "data": dname, "ms_per_launch": round(ms, 3), "tflops": round(tf, 1),
+                    "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "clock_mhz": round(mhz),
+                    "busy_at_clock": round(tf / PEAK_BF16_TFLOPS * 2400.0 / mhz, 3) if mhz else None,
+                    "power_w_mean": round(sum(half) / len(half), 1) if half else None,
+                    "power_w_max": round(max(half), 1) if half else None})
+    return {"diagnostic": "MFMA rate probe (matopt_mfma_probe): both MFMA forms on register or "
+                          "LDS operands, Gaussian and all-zero bf16 data",
+            "workgroups": workgroups, "iters": iters, "launches": launches,
+            "flop_per_launch": flops, "power_source": pw_files or None, "cases": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -488,6 +563,10 @@ def main():
                     help="diagnostic only: the same step on the set's Gaussian G, V and on "
                          "all-zero G, V (identical launches and instructions, no data toggling), "
                          "one JSON line with both times and the GEMM clocks; no headline line")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="diagnostic only: the library's MFMA rate probe for both MFMA forms "
+                         "(registers / LDS operands, Gaussian / zero data) with the card's power "
+                         "reading, one JSON line; no headline line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (float32), the "
                          "known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
@@ -514,6 +593,9 @@ def main():
 
     mo.lib()
     stream = torch.cuda.current_stream()
+    if args.mfma_probe:
+        print(json.dumps(mfma_probe_line(stream)), flush=True)
+        return
     if args.sweep:
         print(json.dumps({"metric": "single s x s bf16 matrix: Muon step vs RMNP step (ms)",
                           "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

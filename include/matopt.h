@@ -293,6 +293,30 @@ matopt_status matopt_profile_read_clock(double* mhz);
 #define MATOPT_COUNTERS 4
 matopt_status matopt_counters(int64_t* out, int32_t n);
 
+/*
+ * MFMA rate probe: a measurement aid, not part of the optimizer step.  It
+ * bounds what a bf16 MFMA schedule can reach on this part with given operand
+ * data, for comparing the two MFMA forms the GEMM engine can use.  Each of
+ * `workgroups` workgroups (512 threads: 8 waves, one workgroup per compute
+ * unit) runs `iters` steps per wave of 524288 flops each: 16
+ * v_mfma_f32_32x32x16_bf16 (form 32) or 32 v_mfma_f32_16x16x32_bf16 (form
+ * 16) on 12 operand fragments per lane, which stay in registers (from_lds 0)
+ * or are read fresh from LDS one step ahead (from_lds 1, as the GEMM engine
+ * reads them).  No DMA, no epilogue.
+ *   src: DEVICE, 49152 bfloat16 values (98304 bytes), the operand data;
+ *   out: DEVICE, workgroups * 512 floats (written: per-thread sums, so that
+ *        no MFMA is dead code);
+ *   clk: DEVICE, 2 uint64 accumulators, ADDED to: the shader-clock ticks and
+ *        the 100 MHz real-time ticks of each workgroup's MFMA loop (their
+ *        ratio times 100 is the clock in MHz).
+ * Flops per call: workgroups * 8 * iters * 524288.  iters even, in
+ * [2, 2^22]; workgroups in [1, 2^20]; pointers 16-byte aligned.  Enqueued on
+ * `stream`; argument errors are reported before anything is enqueued.
+ */
+matopt_status matopt_mfma_probe(int32_t form, int32_t from_lds, const void* src, float* out,
+                                int32_t iters, int32_t workgroups, uint64_t* clk,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

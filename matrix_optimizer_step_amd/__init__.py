@@ -26,7 +26,8 @@ import torch
 __all__ = ["MatoptError", "lib", "workspace_bytes", "muon_step_batched",
            "muon_step_batched_wd", "muon_step_batched_noalloc", "rmnp_step_batched", "rmnp_colcut_partial_batched",
            "rmnp_colcut_apply_batched", "adamw_step_batched", "flat_views", "ns_orthogonalize_batched", "profile_enable",
-           "profile_read", "profile_read_clock", "counters", "PROFILE_CLASSES", "COUNTERS", "LIB_PATH", "EXPORTS"]
+           "profile_read", "profile_read_clock", "counters", "mfma_probe", "PROFILE_CLASSES", "COUNTERS",
+           "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmatopt.so")
 
@@ -86,6 +87,7 @@ EXPORTS = {
     "matopt_profile_read": (_i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "matopt_counters": (_i32, [ctypes.POINTER(_i64), _i32]),
     "matopt_profile_read_clock": (_i32, [ctypes.POINTER(ctypes.c_double)]),
+    "matopt_mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp]),
 }
 
 _lib = None
@@ -433,6 +435,22 @@ def profile_read_clock() -> dict:
     mhz = (ctypes.c_double * k)()
     _check(lib().matopt_profile_read_clock(mhz))
     return {name: mhz[i] for i, name in enumerate(PROFILE_CLASSES) if mhz[i] > 0}
+
+
+def mfma_probe(form: int, from_lds: bool, src: torch.Tensor, out: torch.Tensor,
+               clk: torch.Tensor, iters: int, workgroups: int, stream=None):
+    """Enqueue the MFMA rate probe (matopt_mfma_probe, a measurement aid):
+    ``src`` 49152 bf16 operand values, ``out`` workgroups * 512 float32 values,
+    ``clk`` two int64 tick accumulators (added to), all on one GPU."""
+    for t, what, dt, n in ((src, "src", torch.bfloat16, 49152),
+                           (out, "out", torch.float32, workgroups * 512),
+                           (clk, "clk", torch.int64, 2)):
+        _check_dev(t, what, src.device)
+        if t.dtype != dt or not t.is_contiguous() or t.numel() < n:
+            raise ValueError(f"{what} must be a contiguous {dt} tensor of at least {n} elements")
+    _check(lib().matopt_mfma_probe(int(form), 1 if from_lds else 0, src.data_ptr(), out.data_ptr(),
+                                   int(iters), int(workgroups), clk.data_ptr(),
+                                   _stream_ptr(src.device, stream)))
 
 
 def counters() -> dict:

@@ -205,6 +205,10 @@ hipError_t launch_prep_t(const PrepParams& p, int n_tiles, hipStream_t s);
 hipError_t launch_finalize(const FinalizeParams& p, int count, hipStream_t s);
 hipError_t launch_scale_out(int dt, const ScaleOutParams& p, int n_tiles, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, int n_tiles, hipStream_t s);
+// MFMA rate probe (probe.hip), a measurement aid: 32 x 32 x 16 or 16 x 16 x 32
+// MFMAs on register or LDS operands; clk accumulates shader and real-time ticks.
+hipError_t launch_mfma_probe(bool f16, bool from_lds, const void* src, float* out, int iters,
+                             int workgroups, unsigned long long* clk, hipStream_t s);
 // Diagonal tiles of the bf16 Gram (stage 0) / polynomial (stage 1): 0 whole,
 // 1 upper 36 of 64 blocks, 2 the same two per workgroup (entries with tj < 0).
 int gemm_bf16_diag_mode(int stage);

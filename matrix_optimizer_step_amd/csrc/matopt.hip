@@ -1272,6 +1272,26 @@ matopt_status matopt_profile_read(double* ms, int64_t* launches) {
   return MATOPT_OK;
 }
 
+matopt_status matopt_mfma_probe(int32_t form, int32_t from_lds, const void* src, float* out,
+                                int32_t iters, int32_t workgroups, uint64_t* clk,
+                                void* stream) {
+  if (!src || !out || !clk) return fail(MATOPT_ERR_NULL, "NULL src, out or clk");
+  if (form != 16 && form != 32) return fail(MATOPT_ERR_PARAM, "form must be 16 or 32");
+  if (iters < 2 || iters > (1 << 22) || (iters & 1))
+    return fail(MATOPT_ERR_PARAM, "iters must be even, in [2, 2^22]");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(MATOPT_ERR_PARAM, "workgroups outside [1, 2^20]");
+  if (((uintptr_t)src | (uintptr_t)out | (uintptr_t)clk) & 15)
+    return fail(MATOPT_ERR_ALIGN, "src, out and clk must be 16-byte aligned");
+  int dev = -1;
+  matopt_status st;
+  if ((st = check_device(&dev)) != MATOPT_OK) return st;
+  const hipError_t e = launch_mfma_probe(form == 16, from_lds != 0, src, out, iters, workgroups,
+                                         (unsigned long long*)clk, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("mfma probe launch", e);
+  return MATOPT_OK;
+}
+
 matopt_status matopt_counters(int64_t* out, int32_t n) {
   if (!out) return fail(MATOPT_ERR_NULL, "NULL output");
   if (n < 0 || n > MATOPT_COUNTERS) return fail(MATOPT_ERR_PARAM, "n outside [0, MATOPT_COUNTERS]");

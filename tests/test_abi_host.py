@@ -223,3 +223,19 @@ def test_flat_views_cover_one_buffer(mod):
     import pytest
     with pytest.raises(ValueError):
         mod.flat_views(flat, [(30,)])
+
+
+def test_mfma_probe_argument_errors(L, mod):
+    def call(form=16, lds=0, src=BASE, out=BASE + (1 << 30), iters=8, wg=4, clk=BASE + (2 << 30)):
+        return L.matopt_mfma_probe(form, lds, src, out, iters, wg, clk, None)
+    assert call(src=None) == NULL
+    assert call(clk=None) == NULL
+    assert call(form=8) == PARAM
+    assert call(iters=7) == PARAM
+    assert call(iters=0) == PARAM
+    assert call(wg=0) == PARAM
+    assert call(out=BASE + 8) == ALIGN
+    import torch
+    with pytest.raises(TypeError):
+        mod.mfma_probe(16, False, torch.zeros(49152, dtype=torch.bfloat16),
+                       torch.zeros(512), torch.zeros(2, dtype=torch.int64), 2, 1)
