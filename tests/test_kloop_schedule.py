@@ -22,6 +22,12 @@ model writes each schedule's program as the kernel's loops emit it --
            then the finished tile's stores, which the next tile's first two
            waits let stay in flight)
 
+The 16 x 16 x 32 forms of these loops (kloop16, kloop16_rest, the diagonal
+pair on slabs) emit the same events per step: the two halves of a step take
+the places of its two k16 sub-steps (the first half's reads, of this step's
+stage, before the barrier; the second half's, of the next step's stage, after
+it), with the same DMA, waits and barriers, so the model covers them too.
+
 -- and checks that
   * every stage read sees its step's DMA landed for every wave (the reading
     wave waited for its own DMA, and every wave waited before the barrier
