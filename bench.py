@@ -479,7 +479,7 @@ def card_power_files():
     return out
 
 
-def mfma_probe_line(stream, launches=40, iters=3000, workgroups=2048):
+def mfma_probe_line(stream, launches=40, iters=3000, workgroups=2048, cases=None):
     """Diagnostic: the library's MFMA rate probe (matopt_mfma_probe) for both
     MFMA forms, operands in registers or read from LDS each step, on Gaussian
     and on all-zero bf16 data: TFLOP/s, the clock the loop ran at (shader over
@@ -495,8 +495,8 @@ def mfma_probe_line(stream, launches=40, iters=3000, workgroups=2048):
     clk = torch.zeros(2, dtype=torch.int64, device="cuda")
     pw_files = card_power_files()
     flops = workgroups * 8 * iters * 524288
-    cases = [(32, False, "gaussian"), (16, False, "gaussian"), (32, True, "gaussian"),
-             (16, True, "gaussian"), (32, True, "zero"), (16, True, "zero")]
+    cases = cases or [(32, False, "gaussian"), (16, False, "gaussian"), (32, True, "gaussian"),
+                      (16, True, "gaussian"), (32, True, "zero"), (16, True, "zero")]
     res = []
     for form, lds, dname in cases:
         for _ in range(3):
@@ -666,6 +666,19 @@ def main():
             "100 MHz real-time ticks per workgroup, time-weighted over Gram, polynomial, apply")
         roofline["peak_at_observed_clock"] = round(peak_obs, 1)
         roofline["frac_at_observed_clock"] = round(ns_tflops / peak_obs, 4)
+    if ns_tflops and not args.step_only:
+        # the rate MFMAs fed from LDS alone sustain on this part with Gaussian
+        # bf16 operands (no DMA, no epilogue): a bound for any schedule of the
+        # chain on the same data; about a second of launches, so that the
+        # clock has settled as it has in the chain's timed steps
+        probe = mfma_probe_line(stream, launches=60, iters=3000, cases=[(16, True, "gaussian")])
+        c = probe["cases"][0]
+        roofline["mfma_lds_ceiling"] = {
+            "tflops": c["tflops"], "frac_bf16_peak": c["frac_bf16_peak"],
+            "clock_mhz": c["clock_mhz"],
+            "source": "matopt_mfma_probe in this run: 16x16x32 bf16 MFMAs on fragments read "
+                      "from LDS one step ahead, Gaussian operands, no DMA, no epilogue"}
+        roofline["frac_of_mfma_lds_ceiling"] = round(ns_tflops / c["tflops"], 4)
 
     result = {
         "metric": METRIC,
