@@ -26,8 +26,8 @@
 // a wave has at two waves per SIMD; while one wave of a SIMD waits on LDS the
 // other issues MFMAs).  The Gram, polynomial and apply launches compute on
 // v_mfma_f32_16x16x32_bf16 (8 x 4 slabs of 16 x 16 per wave; see "16 x 16 x
-// 32 MFMA engine" below); an unpaired diagonal tile and the split-precision
-// polynomial keep the 32 x 32 x 16 form (4 x 2 blocks of
+// 32 MFMA engine" below); the single diagonal tiles keep the 32 x 32 x 16
+// form (4 x 2 blocks of
 // v_mfma_f32_32x32x16_bf16 per wave, two k16 sub-steps per K step), which the
 // rest of this comment describes where the two differ.  A 4-wave variant
 // (128 x 128 per wave, accumulators in AGPRs) is kept behind MATOPT_*_WAVES.
@@ -691,6 +691,25 @@ __device__ __forceinline__ void poly_store_direct(const f32x16 (&acc)[4][NBJ], u
 // of 8 consecutive columns (16-byte stores) per lane.  The polynomial's epilogue input (the A tile
 // of the same position) is prefetched one stripe ahead; Gram and apply read
 // nothing back.
+// Staging of stripe BI of a 32 x 32 x 16 layout sub-tile (stage_stripe).
+template <int NBJ>
+struct Stage32 {
+  const f32x16 (&acc)[4][NBJ];
+  int frow, fkc;
+  template <int BI>
+  __device__ __forceinline__ void stage(float* stg) const {
+    stage_stripe<BI, NBJ>(acc, stg, frow, fkc);
+  }
+};
+
+template <int STAGE, int OUT, int NBJ, bool MIRROR, class Stager>
+__device__ __forceinline__ void epilogue_staged(const MatDesc& d, const GemmParams& P,
+                                                const Stager& st, float* stg,
+                                                const uint16_t* ep_src, int64_t ep_ld,
+                                                uint16_t* out, int64_t ld_out, int i0, int j0,
+                                                int lane, float s_first,
+                                                u32x4 (&ecur)[Ep<32 * NBJ>::IPL]);
+
 template <int STAGE, int OUT, int NBJ, bool MIRROR = false>
 __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          const f32x16 (&acc)[4][NBJ], float* stg,
@@ -698,6 +717,21 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
                                          int64_t ld_out, int i0, int j0, int lane, int frow,
                                          int fkc, float s_first,
                                          u32x4 (&ecur)[Ep<32 * NBJ>::IPL]) {
+  const Stage32<NBJ> st{acc, frow, fkc};
+  epilogue_staged<STAGE, OUT, NBJ, MIRROR>(d, P, st, stg, ep_src, ep_ld, out, ld_out, i0, j0,
+                                           lane, s_first, ecur);
+}
+
+// The staged epilogue for any accumulator layout: Stager::stage<BI>(stg)
+// writes stripe BI (rows 32 BI .. +31 of the wave's sub-tile) as float32 rows
+// of Ep<32 NBJ> into the wave's LDS region.
+template <int STAGE, int OUT, int NBJ, bool MIRROR, class Stager>
+__device__ __forceinline__ void epilogue_staged(const MatDesc& d, const GemmParams& P,
+                                                const Stager& st, float* stg,
+                                                const uint16_t* ep_src, int64_t ep_ld,
+                                                uint16_t* out, int64_t ld_out, int i0, int j0,
+                                                int lane, float s_first,
+                                                u32x4 (&ecur)[Ep<32 * NBJ>::IPL]) {
   constexpr int WN = 32 * NBJ;
   using G = Ep<WN>;
   static_assert(STAGE != 0, "the Gram stores its tiles from the accumulators");
@@ -710,10 +744,10 @@ __device__ __forceinline__ void epilogue(const MatDesc& d, const GemmParams& P,
     if (EP_IN && bi + 1 < 4)
       prefetch_stripe<WN>(ep_src, ep_ld, i0 + 32 * (bi + 1), j0, lane, enext);
     switch (bi) {
-      case 0: stage_stripe<0, NBJ>(acc, stg, frow, fkc); break;
-      case 1: stage_stripe<1, NBJ>(acc, stg, frow, fkc); break;
-      case 2: stage_stripe<2, NBJ>(acc, stg, frow, fkc); break;
-      default: stage_stripe<3, NBJ>(acc, stg, frow, fkc); break;
+      case 0: st.template stage<0>(stg); break;
+      case 1: st.template stage<1>(stg); break;
+      case 2: st.template stage<2>(stg); break;
+      default: st.template stage<3>(stg); break;
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -1540,6 +1574,16 @@ __device__ __forceinline__ void stage_stripe16(const f32x4 (&acc)[8][4], float* 
           acc[2 * BI + i2][j];
 }
 
+// Staging of stripe BI of a 16 x 16 x 32 layout sub-tile (stage_stripe16).
+struct Stage16 {
+  const f32x4 (&acc)[8][4];
+  int lane;
+  template <int BI>
+  __device__ __forceinline__ void stage(float* stg) const {
+    stage_stripe16<BI>(acc, stg, lane);
+  }
+};
+
 // The last apply's epilogue (O or the fused weight update) of a 16 x 16
 // layout sub-tile: as epilogue() for the last iteration, one staged 32-row
 // stripe at a time.
@@ -1652,6 +1696,36 @@ __device__ __forceinline__ void poly_tile16(const MatDesc& d, const GemmParams& 
       gstore<u32x4>(Bb + eoff(i, bj), u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]),
                                             pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])});
     }
+}
+
+// An off-diagonal tile of the split-precision polynomial (B stored whole: the
+// staged epilogue also writes the mirror tile) on the 16 x 16 x 32 engine.
+template <bool QEQ, class OpP, class OpQ>
+__device__ __forceinline__ void poly_mirror_tile16(const MatDesc& d, const GemmParams& P,
+                                                   const OpP& dp, const OpQ& dq, const WaveGeo& g,
+                                                   int nk, int bP, int bQ, int i0, int j0,
+                                                   int wave, int lane, uint8_t* lds) {
+  constexpr int BPW = 2;
+  Frag16 f;
+  f.init(lane, g.wj0);
+  KState16 k;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k.acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop16<false, false, true, QEQ, BPW>(k, nk, bP, bQ, dp, dq, g, f, wave, lds);
+  const int64_t mp = d.mp;
+  u32x4 ecur[Ep<64>::IPL];
+  prefetch_stripe<64>((const uint16_t*)d.a, mp, i0 + g.wi0, j0 + g.wj0, lane, ecur);
+  mfma_half16<0>(k.acc, k.pa, k.qb);
+  mfma_half16<4>(k.acc, k.pb, k.qb);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  bar_raw();
+  const float s_first = P.first ? gload<float>(d.xs) : 1.f;
+  const Stage16 st{k.acc, lane};
+  epilogue_staged<1, OUT_NEXT_X, 2, true>(d, P, st, (float*)(lds + wave * Ep<64>::WAVE_BYTES),
+                                          (const uint16_t*)d.a, mp, (uint16_t*)d.b, mp,
+                                          i0 + g.wi0, j0 + g.wj0, lane, s_first, ecur);
 }
 
 // One apply tile (one tile per workgroup) on the 16 x 16 x 32 engine, with
@@ -2448,6 +2522,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, uint8_t* lds) {
   }
   if constexpr (STAGE == 0 && NW == 8 && MATOPT_GRAM_MFMA16 && !MATOPT_PAIR_GRAM) {
     gram_tile16(d, P, dp, dq, g, nk, i0, j0, wave, lane, lds);
+    return;
+  }
+  if constexpr (STAGE == 1 && NW == 8 && MIR && MATOPT_POLY_MFMA16 && !MATOPT_PAIR_POLY) {
+    poly_mirror_tile16<!(NW == 8 && MATOPT_DIAG_TILES)>(d, P, dp, dq, g, nk, bP, bQ, i0, j0, wave,
+                                                        lane, lds);
     return;
   }
   if constexpr (STAGE == 1 && NW == 8 && !MIR && MATOPT_POLY_MFMA16 && !MATOPT_PAIR_POLY) {
