@@ -43,7 +43,8 @@
 // LDS banks (64 banks of 4 B); the DMA lanes pick their source addresses to
 // realise the swizzle.
 //
-// One barrier per K step, placed between its two k16 sub-steps: before it each
+// One barrier per K step, placed between its two k16 sub-steps (on the 16 x
+// 16 x 32 engine: between the step's two halves of MFMAs): before it each
 // wave waits for its own DMA of the next step (explicit vmcnt), after it the
 // DMA of a step three ahead is issued into the stage everyone has finished
 // with.  The fragment reads of the next sub-step are interleaved with the
@@ -54,14 +55,16 @@
 // Diagonal tiles (ti == tj) of the Gram and the polynomial compute only the 36
 // of their 64 32 x 32 blocks on and above the diagonal, from one operand
 // panel, 9 MFMAs per SIMD and k16 sub-step instead of 16, and write the blocks
-// above the diagonal twice (diag_tile).
+// above the diagonal twice (diag_tile; the Gram's diagonal pairs, diag_pair16,
+// also skip the lower 16 x 16 slab of blocks on the diagonal).
 //
 // Epilogue: the last apply (which writes the caller's orientation) stages
 // each wave's accumulators through its own LDS region (float32) so that every
 // global store is a contiguous row segment.  The Gram, the polynomial and a
 // non-final apply skip the staging: their accumulators go straight to whole
-// 2 KB blocks of A, B or X' with cross-half-wave lane swaps, the polynomial
-// reading A at the lanes' own accumulator positions one 32-row stripe ahead;
+// 2 KB blocks of A, B or X' with lane swaps across 16-lane groups
+// (v_permlane16_swap; v_permlane32_swap on the 32 x 32 x 16 form), the
+// polynomial reading A at the lanes' own output positions;
 // where every tile of the non-final apply has the same K extent, that launch
 // runs persistent (one workgroup per CU) and issues the next tile's DMA
 // before these stores.  On the last iteration the result is
